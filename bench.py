@@ -1,0 +1,177 @@
+"""Batch-1 decode benchmark on one MI355X: tokens/s and HBM-roofline fraction.
+
+Workload (default ``dec2b_25l_greedy``): the synthetic ~2.2B fp16 decoder (25
+layers, d 2560, 20 heads x 128, SwiGLU 6912, vocab 32768 untied, weights
+N(0, 0.02) from seed 0), a 128-token random prompt, greedy decode.  The prompt's
+first 127 tokens go through one teacher-forced launch (untimed); a step is one
+decoded token; W warmup steps run in one launch from position 127, then the
+position is reset to 127 and EXACTLY K steps run in ONE lf_generate launch,
+bracketed by device synchronisations and HIP events on the stream the kernel is
+launched on.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  ``roofline.achieved`` = algorithmic bytes of the K steps
+(every weight once per token, the KV rows read and written; see
+persistent_runtime_amd/roofline.py) / the launch's duration.  ``cpu_baseline`` is
+the CPU oracle timed on this host on a bounded sample of the same model.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("lf_kernel.hip", "lf_internal.h", "lf_api.cpp"):
+        with open(os.path.join(ROOT, "persistent_runtime_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, steps: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source and the same workload and step count."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash() or d.get("steps") != steps:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, weights, prompt, seconds: float):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.set_threads(threads)
+    m = oracle.Model(cfg, weights)
+    times = []
+    t_start = time.perf_counter()
+    for pos, tok in enumerate(prompt):
+        t0 = time.perf_counter()
+        m.decode_step(int(tok), pos)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > seconds and len(times) >= 2:
+            break
+    per = sorted(times)[len(times) // 2]
+    return {"value": round(1.0 / per, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} teacher-forced decode steps of the same model at positions 0..{len(times) - 1}, "
+                      f"median step time {per * 1e3:.1f} ms"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="dec2b_25l_greedy")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--stats", action="store_true", help="build the state with LF_STATS (wait-time counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no sharding, no collectives); "
+              "--gpus N with N > 1 is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from persistent_runtime_amd import lf, roofline
+
+    cfg = dict(synth.CONFIGS[args.workload])
+    if cfg.get("vocab", 0) == 0 or "prompt_len" not in cfg:
+        log(f"workload {args.workload} is not a prompt + decode workload")
+        return 2
+    P = cfg["prompt_len"]
+    pos0 = P - 1
+    K, W = args.steps, args.warmup
+    cfg["max_seq"] = max(cfg["max_seq"], pos0 + max(K, W) + 1)
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    weights = synth.model_weights(cfg)
+    prompt = synth.prompt(cfg, P)
+    log(f"weights generated in {time.time() - t0:.1f}s")
+    dev = lf.upload_weights(weights)
+    eng = lf.Engine(cfg, dev, flags=lf.LF_STATS if args.stats else 0)
+    del dev
+    torch.cuda.empty_cache()
+    log(f"engine: grid={eng.grid} lds={eng.lds_bytes}")
+    eng.prefill(prompt[:pos0], 0)
+    torch.cuda.synchronize()
+    if W > 0:
+        eng.set_position(int(prompt[pos0]), pos0)
+        eng.generate(W)
+    eng.set_position(int(prompt[pos0]), pos0)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    out = eng.generate(K)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    log(f"timed launch: {K} tokens in {ms:.3f} ms; first tokens {out[:8].tolist()}")
+    stats = None
+    if args.stats:
+        s = eng.stats().astype(np.float64)
+        spin = s[:, 0] / np.maximum(s[:, 3], 1)
+        stats = {"wait_fraction_mean": round(float(spin.mean()), 4), "wait_fraction_max": round(float(spin.max()), 4),
+                 "waits_per_token": round(float(s[:, 1].mean()) / K, 2),
+                 "xcd_ids": sorted(set(int(x) for x in s[:, 2]))}
+        log(f"stats: {stats}")
+
+    nbytes = roofline.bytes_for_steps(cfg, pos0, K)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload, K)
+    res = {
+        "metric": "batch-1 decode tokens/s + % of HBM-bandwidth roofline (MBU), 1x MI355X",
+        "value": round(K / (ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_layers": cfg["n_layers"], "d_model": cfg["d_model"],
+                   "n_heads": cfg["n_heads"], "n_kv_heads": cfg["n_kv_heads"], "head_dim": cfg["head_dim"],
+                   "ffn_dim": cfg["ffn_dim"], "vocab": cfg["vocab"], "batch": 1, "prompt_len": P,
+                   "positions": f"{pos0}..{pos0 + K - 1}", "sampling": "greedy" if cfg["temperature"] == 0 else
+                   f"T={cfg['temperature']} top_p={cfg['top_p']}", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": "lf_monokernel<false>", "launch_ms": round(ms, 4)},
+    }
+    if stats:
+        res["wait_stats"] = stats
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(cfg, weights, prompt, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    eng.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,155 @@
+/*
+ * lf.h -- C ABI of the batch-1 FP16 decode library (liblf.so), MI355X / gfx950.
+ *
+ * One decode step of a dense pre-norm decoder (RMSNorm, QKV with rotary
+ * embedding, causal attention over an fp16 KV cache, output projection, SwiGLU
+ * FFN, final norm, lm_head, next-token choice) runs as ONE persistent GPU
+ * kernel; lf_generate runs n such steps in one launch and feeds each sampled
+ * token back on the device, without returning to the host between tokens.
+ *
+ * Source pages: "KOG LaneFormer-2B & the monokernel" (shivam2003.com),
+ * sections "The problem" (batch-1 decode streams every weight once per token
+ * through matrix-vector products), "Pillar 3 - the monokernel runtime" (the
+ * whole decode pass, sampling included, in one resident kernel that hands the
+ * token back only when it is produced), "Compile-time work partition" (a fixed
+ * grid of one block per compute unit with a static assignment of work) and
+ * "The fused operations, briefly".
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (LF_OK) or a negative LF_E* code; no exception crosses the ABI.
+ *     lf_last_error(state) (or lf_last_error(NULL) before a state exists)
+ *     returns a text description of the last failure on this thread.
+ *   - Pointers named *_dev are device pointers (hipMalloc or torch CUDA tensors),
+ *     all others host pointers.  fp16 means IEEE binary16.
+ *   - Calls are synchronous with respect to the state's stream: they enqueue on
+ *     it and wait for completion before returning.  One state per host thread.
+ */
+#ifndef LF_H
+#define LF_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LF_OK = 0,
+  LF_EINVAL = -1,      /* bad configuration, null or misaligned pointer */
+  LF_ENOMEM = -2,      /* device allocation failed */
+  LF_EHIP = -3,        /* HIP runtime or launch failure (incl. co-residency refused) */
+  LF_ERANGE = -4,      /* pos >= max_seq, token outside [0, vocab), n out of range */
+  LF_ETIMEOUT = -5,    /* a bounded in-kernel wait expired; the kernel exited cleanly */
+  LF_EUNSUPPORTED = -6 /* valid but not implemented (e.g. head_dim not 64 or 128) */
+};
+
+/* config.flags */
+#define LF_HIDDEN_IO 1u  /* no embedding / lm_head: the layers run on a hidden vector
+                            set with lf_set_hidden and read with lf_get_hidden */
+#define LF_STATS 4u      /* record per-workgroup wait time (lf_get_stats) */
+
+typedef struct lf_state lf_state;
+
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_seq;
+  float rms_eps;       /* RMSNorm epsilon, inside the square root (1e-5) */
+  float rope_base;     /* rotary base (10000) */
+  float temperature;   /* 0: greedy argmax; > 0: nucleus sampling */
+  float top_p;         /* nucleus mass fraction in (0, 1] when temperature > 0 */
+  uint64_t seed;       /* Philox4x32-10 key of the sampler */
+  uint32_t flags;      /* LF_HIDDEN_IO | LF_STATS */
+} lf_config;
+
+/* One layer's weights: fp16 device pointers, row-major [out][in]:
+ *   attn_norm, ffn_norm [d]; wq [n_heads*head_dim][d] (row h*head_dim + j is
+ *   dimension j of query head h); wk, wv [n_kv_heads*head_dim][d];
+ *   wo [d][n_heads*head_dim]; w_gate, w_up [ffn_dim][d]; w_down [d][ffn_dim]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} lf_layer_weights;
+
+/* Model weights: tok_emb, lm_head [vocab][d] (untied), final_norm [d]; all fp16
+ * device pointers (NULL with LF_HIDDEN_IO).  layers: host array of n_layers. */
+typedef struct {
+  const void *tok_emb, *final_norm, *lm_head;
+  const lf_layer_weights *layers;
+} lf_weights;
+
+/* Validate the config, repack the weights into library-owned device memory (the
+ * caller may free its copies afterwards), allocate the KV cache (zeroed),
+ * activations and synchronisation words, and build the static work plan.
+ * stream: a hipStream_t (NULL = default stream).  On success *out owns all of it.
+ * Errors: LF_EINVAL (config, null pointer), LF_EUNSUPPORTED, LF_ENOMEM, LF_EHIP. */
+int lf_model_create(const lf_config *config, const lf_weights *weights, void *stream,
+                    lf_state **out);
+
+/* Free everything the state owns.  NULL is ignored. */
+void lf_model_destroy(lf_state *st);
+
+/* One decode step in one launch: consume `token` at position `pos`, write K/V at
+ * pos, compute logits, choose the next token (RNG counter = pos) and store it as
+ * the pending (next, pos + 1) for lf_generate.  next_token (host, nullable)
+ * receives it.  With LF_HIDDEN_IO: token is ignored, the layers run on the hidden
+ * vector and *next_token = -1.
+ * Errors: LF_ERANGE (pos outside [0, max_seq), token outside [0, vocab)),
+ * LF_ETIMEOUT, LF_EHIP. */
+int lf_decode_step(lf_state *st, int32_t token, int32_t pos, int32_t *next_token);
+
+/* n decode steps from the pending (token, pos) in ONE launch; each sampled token
+ * is fed back on the device.  out_tokens (host, n entries) receives the sampled
+ * tokens.  Errors: LF_ERANGE (no pending token, n < 1, pos + n > max_seq),
+ * LF_ETIMEOUT, LF_EHIP. */
+int lf_generate(lf_state *st, int32_t n, int32_t *out_tokens);
+
+/* Teacher-forced prompt in ONE launch: tokens[i] (host array) is consumed at
+ * position pos0 + i and its K/V written; no logits, no sampling, and the pending
+ * token is cleared (follow with lf_set_position or lf_decode_step).
+ * Errors: LF_ERANGE (token outside [0, vocab), pos0 + n > max_seq), LF_ETIMEOUT, LF_EHIP. */
+int lf_prefill(lf_state *st, const int32_t *tokens, int32_t n, int32_t pos0);
+
+/* Set the pending (token, pos) used by the next lf_generate. */
+int lf_set_position(lf_state *st, int32_t token, int32_t pos);
+
+/* Text of the last failure of a call on this thread ("" if none). */
+const char *lf_last_error(const lf_state *st);
+
+/* Logits (fp32, vocab entries) of the last step.  dst is a device pointer when
+ * dst_is_device != 0, else a host pointer. */
+int lf_get_logits(lf_state *st, float *dst, int dst_is_device);
+
+/* Copy n cache rows (positions pos0 .. pos0+n-1) of one layer from / to device
+ * buffers k_dev, v_dev laid out [n][n_kv_heads][head_dim] fp16.  Prefilled keys
+ * are used as given (no rotary embedding is applied to them). */
+int lf_kv_fill(lf_state *st, int32_t layer, int32_t pos0, int32_t n, const void *k_dev,
+               const void *v_dev);
+int lf_kv_read(lf_state *st, int32_t layer, int32_t pos0, int32_t n, void *k_dev, void *v_dev);
+
+/* LF_HIDDEN_IO: set the fp32 [d] input of the first layer / read the fp32 [d]
+ * residual after the last layer (device pointers). */
+int lf_set_hidden(lf_state *st, const float *x_dev);
+int lf_get_hidden(lf_state *st, float *x_dev);
+
+/* LF_STATS: per workgroup {wait ticks, waits, XCD id, kernel ticks} as uint64,
+ * 100 MHz ticks, for the last launch.  bytes >= 32 * grid size. */
+int lf_get_stats(lf_state *st, void *dst, size_t bytes);
+
+/* Grid size (workgroups = compute units used) and words of the launch plan. */
+int lf_query(const lf_state *st, int32_t what);
+#define LF_Q_GRID 0
+#define LF_Q_THREADS 1
+#define LF_Q_LDS_BYTES 2
+
+/* Test hooks, device pointers, on `stream`:
+ * lf_test_expdef: y[i] = E(x[i]) with the library's defined exponential.
+ * lf_test_sample: for each case c < m, the token the in-kernel sampler picks
+ * from logits_dev[c*n .. c*n+n) with (temperature, top_p, seed) and RNG counter
+ * pos_dev[c]; tokens_dev[c] receives it. */
+int lf_test_expdef(const float *x_dev, float *y_dev, int64_t n, void *stream);
+int lf_test_sample(const float *logits_dev, int32_t n, float temperature, float top_p,
+                   uint64_t seed, const int32_t *pos_dev, int32_t m, int32_t *tokens_dev,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

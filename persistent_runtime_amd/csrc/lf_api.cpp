@@ -1,0 +1,553 @@
+// lf_api.cpp -- the C ABI of include/lf.h: configuration checks, weight repack,
+// allocation of the KV cache / activations / synchronisation words, the static
+// launch plan, and the single cooperative launch per lf_decode_step /
+// lf_generate call.
+//
+// The pages fix the work partition at compile time and never leave the kernel
+// mid-token ("KOG LaneFormer-2B & the monokernel", sections "Compile-time work
+// partition" and "Pillar 3"); here the partition is fixed when the state is
+// created: contiguous row blocks of every matrix per workgroup, and
+// (KV head, key chunk) attention units derived from the position.  Weights are
+// repacked once ("Offline, weights are pre-transformed" in "Weight streaming")
+// so the rotary pairs (i, i + head_dim/2) of each head and the SwiGLU pairs
+// (gate j, up j) sit in adjacent rows and every row block holds whole pairs.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/lf.h"
+#include "lf_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(std::string *dst, int code, const std::string &msg) {
+  g_err = msg;
+  if (dst) *dst = msg;
+  return code;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct lf_state {
+  lf_config cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  lf::Params P{};
+  std::vector<void *> allocs;
+  int out_cap = 0, in_cap = 0;
+  unsigned level_base = 0;
+  int pending_token = -1, pending_pos = 0;
+  bool has_pending = false;
+  std::string err;
+};
+
+namespace {
+
+int hip_fail(lf_state *st, hipError_t e, const char *what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return fail(st ? &st->err : nullptr, LF_EHIP, m);
+}
+
+void *dev_alloc(lf_state *st, size_t bytes, hipError_t *e) {
+  void *p = nullptr;
+  *e = hipMalloc(&p, bytes ? bytes : 16);
+  if (*e != hipSuccess) return nullptr;
+  st->allocs.push_back(p);
+  return p;
+}
+
+int validate(const lf_config *c) {
+  if (!c) return fail(nullptr, LF_EINVAL, "config is NULL");
+  const bool hidden = (c->flags & LF_HIDDEN_IO) != 0;
+  if (c->n_layers < 1 || c->d_model < 8 || c->n_heads < 1 || c->n_kv_heads < 1 || c->ffn_dim < 1 ||
+      c->max_seq < 1)
+    return fail(nullptr, LF_EINVAL, "sizes must be positive");
+  if (c->d_model % 8 || c->ffn_dim % 8)
+    return fail(nullptr, LF_EINVAL, "d_model and ffn_dim must be multiples of 8");
+  if (c->d_model > 8192) return fail(nullptr, LF_EUNSUPPORTED, "d_model above 8192");
+  if (c->n_heads % c->n_kv_heads)
+    return fail(nullptr, LF_EINVAL, "n_heads must be a multiple of n_kv_heads");
+  if (c->n_heads / c->n_kv_heads > 8) return fail(nullptr, LF_EUNSUPPORTED, "more than 8 query heads per KV head");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(nullptr, LF_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (!hidden && (c->vocab < 2 || c->vocab % 2))
+    return fail(nullptr, LF_EINVAL, "vocab must be even and at least 2");
+  if (!(c->rms_eps >= 0.0f) || !(c->rope_base > 0.0f)) return fail(nullptr, LF_EINVAL, "bad rms_eps or rope_base");
+  if (!(c->temperature >= 0.0f)) return fail(nullptr, LF_EINVAL, "temperature must be >= 0");
+  if (c->temperature > 0.0f && !(c->top_p > 0.0f)) return fail(nullptr, LF_EINVAL, "top_p must be > 0");
+  if (c->flags & ~(LF_HIDDEN_IO | LF_STATS)) return fail(nullptr, LF_EINVAL, "unknown flag bits");
+  return LF_OK;
+}
+
+int nchunks(int K) {   // same chunking as the kernel's GEMV: 4 or 8 vectors per lane
+  const int per_lane = (K / 8 + 63) / 64;
+  const int cv = per_lane <= 4 ? 4 : 8;
+  return (per_lane + cv - 1) / cv;
+}
+
+int items_per_wg(int pairs, int G, int K) {
+  const int rows = 2 * ((pairs + G - 1) / G);
+  return rows * nchunks(K);
+}
+
+hipError_t copy_rows_strided(void *dst, size_t dpitch, const void *src, size_t spitch, size_t width,
+                             size_t height, hipStream_t s) {
+  if (height == 0) return hipSuccess;
+  return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToDevice, s);
+}
+
+int do_launch(lf_state *st, int token0, int pos0, int n, std::vector<int> *out, bool prefill = false) {
+  lf::Params &P = st->P;
+  P.levels_per_token = lf::PH_PER_LAYER * P.L + ((P.hidden_io || prefill) ? 0 : 2);
+  const unsigned need = (unsigned)(n + 1) * (unsigned)P.levels_per_token;
+  hipError_t e;
+  if ((unsigned long long)st->level_base + need >= 0x7fffffffull) {
+    if ((e = hipMemsetAsync(P.progress, 0, sizeof(unsigned) * P.G, st->stream)) != hipSuccess)
+      return hip_fail(st, e, "reset progress");
+    st->level_base = 0;
+  }
+  P.n_tokens = n;
+  P.token0 = token0;
+  P.pos0 = pos0;
+  P.level_base = st->level_base;
+  if ((e = hipMemsetAsync(P.err, 0, 4 * sizeof(unsigned), st->stream)) != hipSuccess)
+    return hip_fail(st, e, "clear error word");
+  if ((e = lf::launch_monokernel(P, prefill, st->stream)) != hipSuccess) return hip_fail(st, e, "cooperative launch");
+  if ((e = hipStreamSynchronize(st->stream)) != hipSuccess) return hip_fail(st, e, "kernel execution");
+  unsigned herr[4];
+  if ((e = hipMemcpy(herr, P.err, sizeof(herr), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(st, e, "read error word");
+  if (herr[0]) {
+    // a bounded wait expired: the grid drained; restart the level numbering
+    (void)hipMemsetAsync(P.progress, 0, sizeof(unsigned) * P.G, st->stream);
+    (void)hipMemsetAsync(P.tickets, 0, sizeof(unsigned) * P.L * P.Hkv, st->stream);
+    (void)hipStreamSynchronize(st->stream);
+    st->level_base = 0;
+    char buf[160];
+    std::snprintf(buf, sizeof buf, "in-kernel wait timed out (workgroup %u, level %u)", herr[1], herr[2]);
+    return fail(&st->err, LF_ETIMEOUT, buf);
+  }
+  st->level_base += (unsigned)n * (unsigned)P.levels_per_token;
+  if (herr[3]) return fail(&st->err, LF_EHIP, "the token choice produced no valid token (non-finite logits?)");
+  if (out && !P.hidden_io && !prefill) {
+    out->resize(n);
+    if ((e = hipMemcpy(out->data(), P.out_tokens, sizeof(int) * n, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(st, e, "read tokens");
+  }
+  return LF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lf_last_error(const lf_state *st) { return st ? st->err.c_str() : g_err.c_str(); }
+
+void lf_model_destroy(lf_state *st) {
+  if (!st) return;
+  for (void *p : st->allocs) (void)hipFree(p);
+  delete st;
+}
+
+int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, lf_state **out) {
+  if (!out) return fail(nullptr, LF_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = validate(config);
+  if (rc) return rc;
+  const lf_config &c = *config;
+  const bool hidden = (c.flags & LF_HIDDEN_IO) != 0;
+  if (!w || !w->layers) return fail(nullptr, LF_EINVAL, "weights are NULL");
+  if (!hidden && (!w->tok_emb || !w->lm_head || !w->final_norm))
+    return fail(nullptr, LF_EINVAL, "tok_emb, final_norm and lm_head are required");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const lf_layer_weights &L = w->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down)
+      return fail(nullptr, LF_EINVAL, "a layer weight pointer is NULL");
+  }
+
+  lf_state *st = new lf_state();
+  st->cfg = c;
+  st->stream = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  auto bail = [&](int code) {
+    g_err = st->err;
+    lf_model_destroy(st);
+    return code;
+  };
+  if ((e = hipGetDevice(&st->device)) != hipSuccess) return bail(hip_fail(st, e, "hipGetDevice"));
+  int ncu = 0, coop = 0;
+  (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, st->device);
+  (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, st->device);
+  if (!coop) return bail(fail(&st->err, LF_EHIP, "device does not support cooperative launch"));
+  int G = ncu;
+  if (const char *s = std::getenv("LF_GRID")) {
+    int g = std::atoi(s);
+    if (g >= 1 && g <= ncu) G = g;
+  }
+
+  lf::Params &P = st->P;
+  const int d = c.d_model, Hq = c.n_heads, Hkv = c.n_kv_heads, dh = c.head_dim, F = c.ffn_dim;
+  const int V = hidden ? 0 : c.vocab;
+  P.L = c.n_layers; P.d = d; P.Hq = Hq; P.Hkv = Hkv; P.dh = dh; P.F = F; P.V = V;
+  P.max_seq = c.max_seq; P.G = G; P.qpg = Hq / Hkv; P.nqkv = (Hq + 2 * Hkv) * dh;
+  P.eps = c.rms_eps;
+  P.inv_sqrt_dh = 1.0f / std::sqrt((float)dh);
+  P.sampling = (!hidden && c.temperature > 0.0f) ? 1 : 0;
+  P.inv_temp = P.sampling ? (float)(1.0 / (double)c.temperature) : 0.0f;
+  P.top_p = c.top_p;
+  P.seed = c.seed;
+  P.flags = c.flags;
+  P.hidden_io = hidden ? 1 : 0;
+  P.levels_per_token = lf::PH_PER_LAYER * c.n_layers + (hidden ? 0 : 2);
+  double tmo_ms = 2000.0;
+  if (const char *s = std::getenv("LF_TIMEOUT_MS")) tmo_ms = std::atof(s);
+  P.timeout_ticks = (unsigned long long)(tmo_ms * 1e5);   // s_memrealtime runs at 100 MHz
+
+  // ---- packed weights
+  const size_t rowB_d = (size_t)d * 2;
+  const size_t sz_norm = align_up(rowB_d, 256);
+  const size_t sz_qkv = align_up((size_t)P.nqkv * rowB_d, 256);
+  const size_t sz_o = align_up((size_t)d * Hq * dh * 2, 256);
+  const size_t sz_gu = align_up((size_t)2 * F * rowB_d, 256);
+  const size_t sz_d = align_up((size_t)d * F * 2, 256);
+  const size_t per_layer = 2 * sz_norm + sz_qkv + sz_o + sz_gu + sz_d;
+  const size_t sz_head = hidden ? 0 : sz_norm + 2 * align_up((size_t)V * rowB_d, 256);
+  char *wb = (char *)dev_alloc(st, per_layer * c.n_layers + sz_head, &e);
+  if (!wb) return bail(fail(&st->err, LF_ENOMEM, "weight buffer allocation failed"));
+  std::vector<lf::LayerW> layers(c.n_layers);
+  hipStream_t s = st->stream;
+  const int half = dh / 2;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const lf_layer_weights &L = w->layers[l];
+    char *base = wb + per_layer * l;
+    char *an = base, *fn = base + sz_norm, *qkv = fn + sz_norm, *wo = qkv + sz_qkv, *wgu = wo + sz_o,
+         *wd = wgu + sz_gu;
+    if ((e = hipMemcpyAsync(an, L.attn_norm, rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(fn, L.ffn_norm, rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return bail(hip_fail(st, e, "copy norms"));
+    // q and k heads: packed row (h*dh + 2i) = source row (h*dh + i), (h*dh + 2i + 1) = (h*dh + i + dh/2)
+    for (int part = 0; part < 2; ++part) {
+      const char *src = (const char *)(part == 0 ? L.wq : L.wk);
+      const int nh = part == 0 ? Hq : Hkv;
+      char *dst0 = qkv + (part == 0 ? 0 : (size_t)Hq * dh * rowB_d);
+      for (int h = 0; h < nh; ++h) {
+        const char *sh = src + (size_t)h * dh * rowB_d;
+        char *dsth = dst0 + (size_t)h * dh * rowB_d;
+        if ((e = copy_rows_strided(dsth, 2 * rowB_d, sh, rowB_d, rowB_d, half, s)) != hipSuccess ||
+            (e = copy_rows_strided(dsth + rowB_d, 2 * rowB_d, sh + (size_t)half * rowB_d, rowB_d, rowB_d, half,
+                                   s)) != hipSuccess)
+          return bail(hip_fail(st, e, "repack q/k rows"));
+      }
+    }
+    if ((e = hipMemcpyAsync(qkv + (size_t)(Hq + Hkv) * dh * rowB_d, L.wv, (size_t)Hkv * dh * rowB_d,
+                            hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return bail(hip_fail(st, e, "copy v rows"));
+    if ((e = hipMemcpyAsync(wo, L.wo, (size_t)d * Hq * dh * 2, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return bail(hip_fail(st, e, "copy wo"));
+    if ((e = copy_rows_strided(wgu, 2 * rowB_d, L.w_gate, rowB_d, rowB_d, F, s)) != hipSuccess ||
+        (e = copy_rows_strided(wgu + rowB_d, 2 * rowB_d, L.w_up, rowB_d, rowB_d, F, s)) != hipSuccess)
+      return bail(hip_fail(st, e, "interleave gate/up rows"));
+    if ((e = hipMemcpyAsync(wd, L.w_down, (size_t)d * F * 2, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return bail(hip_fail(st, e, "copy w_down"));
+    layers[l] = lf::LayerW{qkv, wo, wgu, wd, an, fn};
+  }
+  if (!hidden) {
+    char *base = wb + per_layer * c.n_layers;
+    char *fnorm = base, *lm = base + sz_norm, *emb = lm + align_up((size_t)V * rowB_d, 256);
+    if ((e = hipMemcpyAsync(fnorm, w->final_norm, rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(lm, w->lm_head, (size_t)V * rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(emb, w->tok_emb, (size_t)V * rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return bail(hip_fail(st, e, "copy embedding / lm_head"));
+    P.final_norm = fnorm;
+    P.lm_head = lm;
+    P.tok_emb = emb;
+  }
+  lf::LayerW *dl = (lf::LayerW *)dev_alloc(st, sizeof(lf::LayerW) * c.n_layers, &e);
+  if (!dl) return bail(fail(&st->err, LF_ENOMEM, "layer table allocation failed"));
+  if ((e = hipMemcpyAsync(dl, layers.data(), sizeof(lf::LayerW) * c.n_layers, hipMemcpyHostToDevice, s)) !=
+      hipSuccess)
+    return bail(hip_fail(st, e, "upload layer table"));
+  P.layers = dl;
+
+  // ---- KV cache, rotary table, activations, sync words
+  const size_t kv_elems = (size_t)c.n_layers * c.max_seq * Hkv * dh;
+  P.kcache = dev_alloc(st, kv_elems * 2, &e);
+  P.vcache = P.kcache ? dev_alloc(st, kv_elems * 2, &e) : nullptr;
+  if (!P.vcache) return bail(fail(&st->err, LF_ENOMEM, "KV cache allocation failed"));
+  (void)hipMemsetAsync(P.kcache, 0, kv_elems * 2, s);
+  (void)hipMemsetAsync(P.vcache, 0, kv_elems * 2, s);
+
+  std::vector<float> rope((size_t)c.max_seq * half * 2);
+  for (int p = 0; p < c.max_seq; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double theta = std::pow((double)c.rope_base, -2.0 * (double)i / (double)dh);
+      const double phi = (double)p * theta;
+      rope[((size_t)p * half + i) * 2 + 0] = (float)std::cos(phi);
+      rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(phi);
+    }
+  float *drope = (float *)dev_alloc(st, rope.size() * 4, &e);
+  if (!drope) return bail(fail(&st->err, LF_ENOMEM, "rotary table allocation failed"));
+  if ((e = hipMemcpy(drope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
+    return bail(hip_fail(st, e, "upload rotary table"));
+  P.rope = drope;
+
+  int smax = G / Hkv;
+  if (smax < 1) smax = 1;
+  const size_t units_max = (size_t)Hkv * smax;
+  const size_t f_part = units_max * P.qpg * (dh + 2);
+  // one arena for the small buffers, each 256-byte aligned
+  struct Slot { void **dst; size_t bytes; };
+  void *x_hidden, *x_mid, *x_out, *q, *attn_part, *o16, *a16, *logits, *lm_val, *lm_idx, *progress, *tickets,
+      *tok_slot, *errw, *stats;
+  Slot slots[] = {
+      {&x_hidden, (size_t)d * 4}, {&x_mid, (size_t)d * 4}, {&x_out, (size_t)d * 4},
+      {&q, (size_t)Hq * dh * 4}, {&attn_part, f_part * 4}, {&o16, (size_t)Hq * dh * 2},
+      {&a16, (size_t)F * 2}, {&logits, (size_t)(V > 0 ? V : 1) * 4}, {&lm_val, (size_t)G * 4},
+      {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4}, {&tickets, (size_t)c.n_layers * Hkv * 4},
+      {&tok_slot, 16}, {&errw, 16}, {&stats, (size_t)G * 32}};
+  size_t arena = 0;
+  for (auto &sl : slots) arena += align_up(sl.bytes, 256);
+  char *ar = (char *)dev_alloc(st, arena, &e);
+  if (!ar) return bail(fail(&st->err, LF_ENOMEM, "activation arena allocation failed"));
+  (void)hipMemsetAsync(ar, 0, arena, s);
+  size_t off = 0;
+  for (auto &sl : slots) { *sl.dst = ar + off; off += align_up(sl.bytes, 256); }
+  P.x_hidden = (float *)x_hidden; P.x_mid = (float *)x_mid; P.x_out = (float *)x_out; P.q = (float *)q;
+  P.attn_part = (float *)attn_part; P.o16 = o16; P.a16 = a16; P.logits = (float *)logits;
+  P.lm_val = (float *)lm_val; P.lm_idx = (int *)lm_idx; P.progress = (unsigned *)progress;
+  P.tickets = (unsigned *)tickets; P.tok_slot = (int *)tok_slot; P.err = (unsigned *)errw;
+  P.stats = (unsigned long long *)stats;
+  st->out_cap = 1;
+  P.out_tokens = (int *)dev_alloc(st, sizeof(int) * 1, &e);
+  st->in_cap = 1;
+  P.in_tokens = (const int *)dev_alloc(st, sizeof(int) * 1, &e);
+  if (!P.out_tokens || !P.in_tokens) return bail(fail(&st->err, LF_ENOMEM, "token buffer allocation failed"));
+
+  // ---- LDS layout
+  int part_max = 0;
+  auto upd = [&](int v) { part_max = v > part_max ? v : part_max; };
+  upd(items_per_wg(P.nqkv / 2, G, d));
+  upd(items_per_wg(d / 2, G, Hq * dh));
+  upd(items_per_wg(F, G, d));
+  upd(items_per_wg(d / 2, G, F));
+  if (!hidden) upd(items_per_wg(V / 2, G, d));
+  int hmax = d;
+  if (Hq * dh > hmax) hmax = Hq * dh;
+  if (F > hmax) hmax = F;
+  const size_t attn_b = (size_t)P.qpg * dh * 4 + (size_t)P.qpg * lf::kAttnBlock * 4 +
+                        (size_t)lf::kWaves * P.qpg * dh * 4;
+  const size_t samp_b = 4096;
+  size_t lo = 0;
+  P.lds_h = 0;                         lo += align_up((size_t)hmax * 2, 16);
+  P.lds_part = (int)lo;                lo += align_up((size_t)part_max * 4, 16);
+  P.lds_red = (int)lo;                 lo += 80 * 4;
+  P.lds_attn = (int)align_up(lo, 16);  lo = P.lds_attn + (attn_b > samp_b ? attn_b : samp_b);
+  P.part_max = part_max;
+  P.hmax = hmax;
+  int lds_limit = 0;
+  (void)hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, st->device);
+  if (lds_limit <= 0) lds_limit = 65536;
+  // above half of the CU's LDS so that exactly one workgroup runs per compute unit
+  size_t want = 96 * 1024;
+  if (want > (size_t)lds_limit) want = (size_t)lds_limit;
+  if (lo > want) want = lo;
+  if (want > (size_t)lds_limit)
+    return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
+  P.lds_bytes = (int)want;
+  for (int pf = 0; pf < 2; ++pf) {
+    if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 P.lds_bytes)) != hipSuccess)
+      return bail(hip_fail(st, e, "set dynamic LDS size"));
+    int nblk = 0;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, lf::monokernel_symbol(pf != 0), lf::kThreads,
+                                                          P.lds_bytes)) != hipSuccess)
+      return bail(hip_fail(st, e, "occupancy query"));
+    if (nblk < 1) return bail(fail(&st->err, LF_EHIP, "the kernel cannot be resident on a compute unit"));
+  }
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return bail(hip_fail(st, e, "create"));
+  *out = st;
+  g_err.clear();
+  return LF_OK;
+}
+
+int lf_set_position(lf_state *st, int32_t token, int32_t pos) {
+  if (!st) return fail(nullptr, LF_EINVAL, "state is NULL");
+  if (pos < 0 || pos >= st->cfg.max_seq) return fail(&st->err, LF_ERANGE, "pos outside [0, max_seq)");
+  if (!st->P.hidden_io && (token < 0 || token >= st->cfg.vocab))
+    return fail(&st->err, LF_ERANGE, "token outside [0, vocab)");
+  st->pending_token = token;
+  st->pending_pos = pos;
+  st->has_pending = true;
+  return LF_OK;
+}
+
+int lf_decode_step(lf_state *st, int32_t token, int32_t pos, int32_t *next_token) {
+  if (!st) return fail(nullptr, LF_EINVAL, "state is NULL");
+  if (pos < 0 || pos >= st->cfg.max_seq) return fail(&st->err, LF_ERANGE, "pos outside [0, max_seq)");
+  if (st->P.hidden_io) {
+    int rc = do_launch(st, 0, pos, 1, nullptr);
+    if (rc) return rc;
+    if (next_token) *next_token = -1;
+    return LF_OK;
+  }
+  if (token < 0 || token >= st->cfg.vocab) return fail(&st->err, LF_ERANGE, "token outside [0, vocab)");
+  std::vector<int> out;
+  int rc = do_launch(st, token, pos, 1, &out);
+  if (rc) return rc;
+  if (next_token) *next_token = out[0];
+  if (pos + 1 < st->cfg.max_seq) {
+    st->pending_token = out[0];
+    st->pending_pos = pos + 1;
+    st->has_pending = true;
+  } else {
+    st->has_pending = false;
+  }
+  return LF_OK;
+}
+
+int lf_generate(lf_state *st, int32_t n, int32_t *out_tokens) {
+  if (!st) return fail(nullptr, LF_EINVAL, "state is NULL");
+  if (st->P.hidden_io) return fail(&st->err, LF_EINVAL, "lf_generate needs a vocabulary");
+  if (!out_tokens) return fail(&st->err, LF_EINVAL, "out_tokens is NULL");
+  if (!st->has_pending) return fail(&st->err, LF_ERANGE, "no pending token: call lf_decode_step or lf_set_position");
+  if (n < 1 || st->pending_pos + n > st->cfg.max_seq)
+    return fail(&st->err, LF_ERANGE, "n < 1 or pos + n > max_seq");
+  if (n > st->out_cap) {
+    hipError_t e;
+    int *p = (int *)dev_alloc(st, sizeof(int) * n, &e);
+    if (!p) return fail(&st->err, LF_ENOMEM, "token buffer allocation failed");
+    st->P.out_tokens = p;
+    st->out_cap = n;
+  }
+  std::vector<int> out;
+  int rc = do_launch(st, st->pending_token, st->pending_pos, n, &out);
+  if (rc) return rc;
+  std::memcpy(out_tokens, out.data(), sizeof(int) * n);
+  st->pending_pos += n;
+  st->pending_token = out[n - 1];
+  st->has_pending = st->pending_pos < st->cfg.max_seq;
+  return LF_OK;
+}
+
+int lf_prefill(lf_state *st, const int32_t *tokens, int32_t n, int32_t pos0) {
+  if (!st) return fail(nullptr, LF_EINVAL, "state is NULL");
+  if (st->P.hidden_io) return fail(&st->err, LF_EINVAL, "lf_prefill needs a vocabulary");
+  if (!tokens && n > 0) return fail(&st->err, LF_EINVAL, "tokens is NULL");
+  if (n < 0 || pos0 < 0 || pos0 + n > st->cfg.max_seq)
+    return fail(&st->err, LF_ERANGE, "n < 0 or positions outside [0, max_seq)");
+  for (int i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= st->cfg.vocab) return fail(&st->err, LF_ERANGE, "token outside [0, vocab)");
+  if (n == 0) return LF_OK;
+  hipError_t e;
+  if (n > st->in_cap) {
+    int *p = (int *)dev_alloc(st, sizeof(int) * n, &e);
+    if (!p) return fail(&st->err, LF_ENOMEM, "token buffer allocation failed");
+    st->P.in_tokens = p;
+    st->in_cap = n;
+  }
+  if ((e = hipMemcpy(const_cast<int *>(st->P.in_tokens), tokens, sizeof(int) * n, hipMemcpyHostToDevice)) !=
+      hipSuccess)
+    return hip_fail(st, e, "upload prompt tokens");
+  int rc = do_launch(st, tokens[0], pos0, n, nullptr, true);
+  if (rc) return rc;
+  st->has_pending = false;
+  return LF_OK;
+}
+
+int lf_get_logits(lf_state *st, float *dst, int dst_is_device) {
+  if (!st || !dst) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
+  if (st->P.hidden_io) return fail(&st->err, LF_EINVAL, "no logits with LF_HIDDEN_IO");
+  hipError_t e = hipMemcpy(dst, st->P.logits, sizeof(float) * st->P.V,
+                           dst_is_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost);
+  return e == hipSuccess ? LF_OK : hip_fail(st, e, "copy logits");
+}
+
+static int kv_copy(lf_state *st, int32_t layer, int32_t pos0, int32_t n, void *k, void *v, bool fill) {
+  if (!st || !k || !v) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= st->cfg.n_layers || pos0 < 0 || n < 0 || pos0 + n > st->cfg.max_seq)
+    return fail(&st->err, LF_ERANGE, "layer / position range outside the cache");
+  const size_t row = (size_t)st->P.Hkv * st->P.dh * 2;
+  const size_t off = ((size_t)layer * st->cfg.max_seq + pos0) * row;
+  char *kc = (char *)st->P.kcache + off, *vc = (char *)st->P.vcache + off;
+  hipError_t e;
+  if (fill) {
+    if ((e = hipMemcpyAsync(kc, k, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess ||
+        (e = hipMemcpyAsync(vc, v, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess)
+      return hip_fail(st, e, "kv fill");
+  } else {
+    if ((e = hipMemcpyAsync(k, kc, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess ||
+        (e = hipMemcpyAsync(v, vc, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess)
+      return hip_fail(st, e, "kv read");
+  }
+  e = hipStreamSynchronize(st->stream);
+  return e == hipSuccess ? LF_OK : hip_fail(st, e, "kv copy");
+}
+
+int lf_kv_fill(lf_state *st, int32_t layer, int32_t pos0, int32_t n, const void *k, const void *v) {
+  return kv_copy(st, layer, pos0, n, const_cast<void *>(k), const_cast<void *>(v), true);
+}
+
+int lf_kv_read(lf_state *st, int32_t layer, int32_t pos0, int32_t n, void *k, void *v) {
+  return kv_copy(st, layer, pos0, n, k, v, false);
+}
+
+int lf_set_hidden(lf_state *st, const float *x) {
+  if (!st || !x) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
+  if (!st->P.hidden_io) return fail(&st->err, LF_EINVAL, "state was not created with LF_HIDDEN_IO");
+  hipError_t e = hipMemcpy(st->P.x_hidden, x, sizeof(float) * st->P.d, hipMemcpyDeviceToDevice);
+  return e == hipSuccess ? LF_OK : hip_fail(st, e, "set hidden");
+}
+
+int lf_get_hidden(lf_state *st, float *x) {
+  if (!st || !x) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
+  if (!st->P.hidden_io) return fail(&st->err, LF_EINVAL, "state was not created with LF_HIDDEN_IO");
+  hipError_t e = hipMemcpy(x, st->P.x_out, sizeof(float) * st->P.d, hipMemcpyDeviceToDevice);
+  return e == hipSuccess ? LF_OK : hip_fail(st, e, "get hidden");
+}
+
+int lf_get_stats(lf_state *st, void *dst, size_t bytes) {
+  if (!st || !dst) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
+  const size_t need = (size_t)st->P.G * 32;
+  if (bytes < need) return fail(&st->err, LF_EINVAL, "stats buffer too small");
+  hipError_t e = hipMemcpy(dst, st->P.stats, need, hipMemcpyDeviceToHost);
+  return e == hipSuccess ? LF_OK : hip_fail(st, e, "copy stats");
+}
+
+int lf_query(const lf_state *st, int32_t what) {
+  if (!st) return LF_EINVAL;
+  switch (what) {
+    case LF_Q_GRID: return st->P.G;
+    case LF_Q_THREADS: return lf::kThreads;
+    case LF_Q_LDS_BYTES: return st->P.lds_bytes;
+    default: return LF_EINVAL;
+  }
+}
+
+int lf_test_expdef(const float *x, float *y, int64_t n, void *stream) {
+  if ((!x || !y) && n > 0) return fail(nullptr, LF_EINVAL, "NULL argument");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = lf::launch_test_expdef(x, y, n, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? LF_OK : hip_fail(nullptr, e, "lf_test_expdef");
+}
+
+int lf_test_sample(const float *logits, int32_t n, float temperature, float top_p, uint64_t seed,
+                   const int32_t *pos, int32_t m, int32_t *tokens, void *stream) {
+  if (!logits || !pos || !tokens || n < 1 || m < 0) return fail(nullptr, LF_EINVAL, "bad argument");
+  if (!(temperature > 0.0f) || !(top_p > 0.0f)) return fail(nullptr, LF_EINVAL, "temperature and top_p must be > 0");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const float inv_temp = (float)(1.0 / (double)temperature);
+  hipError_t e = lf::launch_test_sample(logits, n, inv_temp, top_p, seed, pos, m, tokens, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? LF_OK : hip_fail(nullptr, e, "lf_test_sample");
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// lf_internal.h -- parameter block shared by the host planner (lf_api.cpp) and
+// the persistent kernel (lf_kernel.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lf {
+
+constexpr int kThreads = 512;          // 8 wave64s per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kAttnBlock = 512;        // key positions scored per attention sub-block
+constexpr int kMinKeysPerUnit = 16;    // smallest attention split-K chunk
+
+// Phases of one layer; each completes one "level" of the dependency chain.
+enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYER = 5 };
+
+struct LayerW {
+  const void *wqkv;       // [(Hq+2Hkv)*dh][d]  q/k rows pair-interleaved per head (i, i+dh/2)
+  const void *wo;         // [d][Hq*dh]
+  const void *wgu;        // [2F][d]  row 2j = gate j, row 2j+1 = up j
+  const void *wd;         // [d][F]
+  const void *attn_norm;  // [d]
+  const void *ffn_norm;   // [d]
+};
+
+struct Params {
+  // shape
+  int L, d, Hq, Hkv, dh, F, V, max_seq, G, qpg, nqkv;
+  float eps, inv_sqrt_dh, inv_temp, top_p;
+  unsigned long long seed;
+  unsigned flags;
+  int hidden_io, sampling;
+  int levels_per_token;
+  // weights (library-owned, packed)
+  const LayerW *layers;    // device array [L]
+  const void *tok_emb, *final_norm, *lm_head;
+  // state
+  void *kcache, *vcache;   // fp16 [L][max_seq][Hkv][dh]
+  const float *rope;       // [max_seq][dh/2][2] (cos, sin)
+  float *x_hidden, *x_mid, *x_out;   // fp32 [d]
+  float *q;                // fp32 [Hq*dh] post-rotary queries
+  float *attn_part;        // fp32 [units][qpg][dh+2] split-K partials (m, l, o)
+  void *o16;               // fp16 [Hq*dh] merged attention output
+  void *a16;               // fp16 [F] SwiGLU output
+  float *logits;           // fp32 [V]
+  float *lm_val;           // [G] per-workgroup max logit
+  int *lm_idx;             // [G] its index
+  unsigned *progress;      // [G] last completed level of each workgroup
+  unsigned *tickets;       // [L][Hkv] split-K arrival counters
+  int *tok_slot;           // [1] token chosen by the last step
+  int *out_tokens;         // [n_tokens]
+  const int *in_tokens;    // [n_tokens] teacher-forced tokens (prefill launches)
+  unsigned *err;           // [4] {code, workgroup, level, 0}
+  unsigned long long *stats;  // [G][4]
+  // this launch
+  int n_tokens, token0, pos0;
+  unsigned level_base;
+  unsigned long long timeout_ticks;
+  // LDS layout (byte offsets into dynamic shared memory)
+  int lds_h, lds_part, lds_red, lds_attn, lds_bytes, part_max, hmax;
+};
+
+hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream);
+hipError_t launch_test_expdef(const float *x, float *y, int64_t n, hipStream_t stream);
+hipError_t launch_test_sample(const float *logits, int n, float inv_temp, float top_p,
+                              unsigned long long seed, const int *pos, int m, int *tokens,
+                              hipStream_t stream);
+const void *monokernel_symbol(bool prefill);
+
+}  // namespace lf
