@@ -56,11 +56,16 @@ __device__ __forceinline__ int tid_x() {
 __device__ __forceinline__ int lane_id() { return tid_x() & 63; }
 __device__ __forceinline__ int wave_id() { return tid_x() >> 6; }
 
+// Eight fp16 products accumulated in fp32 with four v_dot2_f32_f16.  The halves
+// are taken by bit-casting the whole 16-byte vector and shuffling pairs out of
+// it: hipcc mis-compiles a bit-cast of a single ext-vector element (w.y) into a
+// read of element 0.
 __device__ __forceinline__ float dot8(u32x4 w, u32x4 h, float acc) {
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.x), __builtin_bit_cast(f16x2, h.x), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.y), __builtin_bit_cast(f16x2, h.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.z), __builtin_bit_cast(f16x2, h.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.w), __builtin_bit_cast(f16x2, h.w), acc, false);
+  const f16x8 a = __builtin_bit_cast(f16x8, w), b = __builtin_bit_cast(f16x8, h);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), acc, false);
   return acc;
 }
 
