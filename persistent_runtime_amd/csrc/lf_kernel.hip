@@ -135,20 +135,22 @@ __device__ __forceinline__ bool wait_level(Sync &s, int first, int count, unsign
         mn = min(mn, __hip_atomic_load(&P.progress[first + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       mn = wave_min_u32(mn);
       if (mn >= level) { status = 1; break; }
-      if ((++it & 15u) == 0) {
-        if (__hip_atomic_load(&P.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { status = 2; break; }
-        if (now_ticks() - t0 > P.timeout_ticks) {
-          if (tid_x() == 0) {
-            unsigned zero = 0u;
-            if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)) {
-              __hip_atomic_store(&P.err[1], (unsigned)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              __hip_atomic_store(&P.err[2], level, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+      if ((++it & 15u) == 0 &&
+          __hip_atomic_load(&P.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        status = 2;
+        break;
+      }
+      if (now_ticks() - t0 > P.timeout_ticks) {
+        if (tid_x() == 0) {
+          unsigned zero = 0u;
+          if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)) {
+            __hip_atomic_store(&P.err[1], (unsigned)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&P.err[2], level, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          status = 2;
-          break;
         }
+        status = 2;
+        break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
