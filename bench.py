@@ -145,9 +145,14 @@ def main() -> int:
     stats = None
     if args.stats:
         s = eng.stats().astype(np.float64)
-        spin = s[:, 0] / np.maximum(s[:, 3], 1)
-        stats = {"wait_fraction_mean": round(float(spin.mean()), 4), "wait_fraction_max": round(float(spin.max()), 4),
+        tot = np.maximum(s[:, 3], 1)
+        frac = lambda k: round(float((s[:, k] / tot).mean()), 4)
+        stats = {"wait_fraction_mean": frac(0), "wait_fraction_max": round(float((s[:, 0] / tot).max()), 4),
                  "waits_per_token": round(float(s[:, 1].mean()) / K, 2),
+                 "sync_wave_fraction": {"poll": frac(0), "stage": frac(4), "wait_streams": frac(5),
+                                        "epilogue": frac(6), "attention": frac(7), "lm_sample": frac(8)},
+                 "stream_wave1_fraction": {"wait_input": frac(9), "consume": frac(10)},
+                 "stream_wave1_ns_per_piece": round(float((s[:, 10] * 10.0 / np.maximum(s[:, 11], 1)).mean()), 1),
                  "xcd_ids": sorted(set(int(x) for x in s[:, 2]))}
         log(f"stats: {stats}")
 

@@ -129,8 +129,12 @@ int lf_kv_read(lf_state *st, int32_t layer, int32_t pos0, int32_t n, void *k_dev
 int lf_set_hidden(lf_state *st, const float *x_dev);
 int lf_get_hidden(lf_state *st, float *x_dev);
 
-/* LF_STATS: per workgroup {wait ticks, waits, XCD id, kernel ticks} as uint64,
- * 100 MHz ticks, for the last launch.  bytes >= 32 * grid size. */
+/* LF_STATS: 16 uint64 per workgroup for the last launch, in 100 MHz ticks:
+ * [0] wave 0 time polling other workgroups, [1] number of polls, [2] XCD id,
+ * [3] kernel time, [4] input staging, [5] waiting for the stream waves,
+ * [6] epilogues and publishing, [7] attention, [8] lm_head + token choice,
+ * [9] stream wave 1 waiting for phase inputs, [10] stream wave 1 consuming,
+ * [11] pieces stream wave 1 consumed, [12..15] zero.  bytes >= 128 * grid. */
 int lf_get_stats(lf_state *st, void *dst, size_t bytes);
 
 /* Grid size (workgroups = compute units used) and words of the launch plan. */

@@ -87,17 +87,6 @@ int validate(const lf_config *c) {
   return LF_OK;
 }
 
-int nchunks(int K) {   // same chunking as the kernel's GEMV: 4 or 8 vectors per lane
-  const int per_lane = (K / 8 + 63) / 64;
-  const int cv = per_lane <= 4 ? 4 : 8;
-  return (per_lane + cv - 1) / cv;
-}
-
-int items_per_wg(int pairs, int G, int K) {
-  const int rows = 2 * ((pairs + G - 1) / G);
-  return rows * nchunks(K);
-}
-
 hipError_t copy_rows_strided(void *dst, size_t dpitch, const void *src, size_t spitch, size_t width,
                              size_t height, hipStream_t s) {
   if (height == 0) return hipSuccess;
@@ -222,7 +211,6 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   const size_t sz_head = hidden ? 0 : sz_norm + 2 * align_up((size_t)V * rowB_d, 256);
   char *wb = (char *)dev_alloc(st, per_layer * c.n_layers + sz_head, &e);
   if (!wb) return bail(fail(&st->err, LF_ENOMEM, "weight buffer allocation failed"));
-  std::vector<lf::LayerW> layers(c.n_layers);
   hipStream_t s = st->stream;
   const int half = dh / 2;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -257,7 +245,6 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
       return bail(hip_fail(st, e, "interleave gate/up rows"));
     if ((e = hipMemcpyAsync(wd, L.w_down, (size_t)d * F * 2, hipMemcpyDeviceToDevice, s)) != hipSuccess)
       return bail(hip_fail(st, e, "copy w_down"));
-    layers[l] = lf::LayerW{qkv, wo, wgu, wd, an, fn};
   }
   if (!hidden) {
     char *base = wb + per_layer * c.n_layers;
@@ -270,12 +257,14 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     P.lm_head = lm;
     P.tok_emb = emb;
   }
-  lf::LayerW *dl = (lf::LayerW *)dev_alloc(st, sizeof(lf::LayerW) * c.n_layers, &e);
-  if (!dl) return bail(fail(&st->err, LF_ENOMEM, "layer table allocation failed"));
-  if ((e = hipMemcpyAsync(dl, layers.data(), sizeof(lf::LayerW) * c.n_layers, hipMemcpyHostToDevice, s)) !=
-      hipSuccess)
-    return bail(hip_fail(st, e, "upload layer table"));
-  P.layers = dl;
+  P.wbase = wb;
+  P.layer_stride = per_layer;
+  P.part_off[lf::LW_ATTN_NORM] = 0;
+  P.part_off[lf::LW_FFN_NORM] = sz_norm;
+  P.part_off[lf::LW_QKV] = 2 * sz_norm;
+  P.part_off[lf::LW_O] = 2 * sz_norm + sz_qkv;
+  P.part_off[lf::LW_GU] = 2 * sz_norm + sz_qkv + sz_o;
+  P.part_off[lf::LW_D] = 2 * sz_norm + sz_qkv + sz_o + sz_gu;
 
   // ---- KV cache, rotary table, activations, sync words
   const size_t kv_elems = (size_t)c.n_layers * c.max_seq * Hkv * dh;
@@ -300,6 +289,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.rope = drope;
 
   int smax = G / Hkv;
+  if (smax > lf::kMaxSplit) smax = lf::kMaxSplit;
   if (smax < 1) smax = 1;
   const size_t units_max = (size_t)Hkv * smax;
   const size_t f_part = units_max * P.qpg * (dh + 2);
@@ -312,7 +302,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
       {&q, (size_t)Hq * dh * 4}, {&attn_part, f_part * 4}, {&o16, (size_t)Hq * dh * 2},
       {&a16, (size_t)F * 2}, {&logits, (size_t)(V > 0 ? V : 1) * 4}, {&lm_val, (size_t)G * 4},
       {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4}, {&tickets, (size_t)c.n_layers * Hkv * 4},
-      {&tok_slot, 16}, {&errw, 16}, {&stats, (size_t)G * 32}};
+      {&tok_slot, 16}, {&errw, 16}, {&stats, (size_t)G * lf::kStatWords * 8}};
   size_t arena = 0;
   for (auto &sl : slots) arena += align_up(sl.bytes, 256);
   char *ar = (char *)dev_alloc(st, arena, &e);
@@ -331,37 +321,42 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.in_tokens = (const int *)dev_alloc(st, sizeof(int) * 1, &e);
   if (!P.out_tokens || !P.in_tokens) return bail(fail(&st->err, LF_ENOMEM, "token buffer allocation failed"));
 
-  // ---- LDS layout
-  int part_max = 0;
-  auto upd = [&](int v) { part_max = v > part_max ? v : part_max; };
-  upd(items_per_wg(P.nqkv / 2, G, d));
-  upd(items_per_wg(d / 2, G, Hq * dh));
-  upd(items_per_wg(F, G, d));
-  upd(items_per_wg(d / 2, G, F));
-  if (!hidden) upd(items_per_wg(V / 2, G, d));
+  // ---- LDS layout: [h | part] (also attention / sampler scratch), red, ctl, rings
+  int rows_max = 0;
+  {
+    const int pairs[5] = {P.nqkv / 2, d / 2, F, d / 2, hidden ? 0 : V / 2};
+    for (int k = 0; k < 5; ++k) {
+      const int r = 2 * ((pairs[k] + G - 1) / G);
+      rows_max = r > rows_max ? r : rows_max;
+    }
+  }
   int hmax = d;
   if (Hq * dh > hmax) hmax = Hq * dh;
   if (F > hmax) hmax = F;
+  const size_t h_b = align_up((size_t)hmax * 2 + 1024, 16);   // + one piece of slack for masked lanes
+  const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);
   const size_t attn_b = (size_t)P.qpg * dh * 4 + (size_t)P.qpg * lf::kAttnBlock * 4 +
                         (size_t)lf::kWaves * P.qpg * dh * 4;
   const size_t samp_b = 4096;
-  size_t lo = 0;
-  P.lds_h = 0;                         lo += align_up((size_t)hmax * 2, 16);
-  P.lds_part = (int)lo;                lo += align_up((size_t)part_max * 4, 16);
-  P.lds_red = (int)lo;                 lo += 80 * 4;
-  P.lds_attn = (int)align_up(lo, 16);  lo = P.lds_attn + (attn_b > samp_b ? attn_b : samp_b);
-  P.part_max = part_max;
+  size_t region_a = h_b + part_b;
+  if (attn_b > region_a) region_a = attn_b;
+  if (samp_b > region_a) region_a = samp_b;
+  P.lds_h = 0;
+  P.lds_part = (int)h_b;
+  P.lds_red = (int)align_up(region_a, 256);
+  P.lds_ctl = P.lds_red + 256;
+  P.lds_ring = P.lds_ctl + 256;
+  P.part_rows = rows_max;
   P.hmax = hmax;
   int lds_limit = 0;
   (void)hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, st->device);
   if (lds_limit <= 0) lds_limit = 65536;
-  // above half of the CU's LDS so that exactly one workgroup runs per compute unit
-  size_t want = 96 * 1024;
-  if (want > (size_t)lds_limit) want = (size_t)lds_limit;
-  if (lo > want) want = lo;
-  if (want > (size_t)lds_limit)
+  const int rings = (lf::kWaves - 1) * lf::kRingSlots * 1024;
+  if (P.lds_ring + rings > lds_limit)
     return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
-  P.lds_bytes = (int)want;
+  P.lds_bytes = P.lds_ring + rings;
+  P.fenced = (std::getenv("LF_FENCED") && std::atoi(std::getenv("LF_FENCED")) != 0) ? 1 : 0;
+  P.plain_launch = (std::getenv("LF_PLAIN_LAUNCH") && std::atoi(std::getenv("LF_PLAIN_LAUNCH")) != 0) ? 1 : 0;
   for (int pf = 0; pf < 2; ++pf) {
     if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  P.lds_bytes)) != hipSuccess)
@@ -515,7 +510,7 @@ int lf_get_hidden(lf_state *st, float *x) {
 
 int lf_get_stats(lf_state *st, void *dst, size_t bytes) {
   if (!st || !dst) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
-  const size_t need = (size_t)st->P.G * 32;
+  const size_t need = (size_t)st->P.G * lf::kStatWords * 8;
   if (bytes < need) return fail(&st->err, LF_EINVAL, "stats buffer too small");
   hipError_t e = hipMemcpy(dst, st->P.stats, need, hipMemcpyDeviceToHost);
   return e == hipSuccess ? LF_OK : hip_fail(st, e, "copy stats");

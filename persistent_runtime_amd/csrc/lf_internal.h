@@ -10,18 +10,16 @@ constexpr int kThreads = 512;          // 8 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kAttnBlock = 512;        // key positions scored per attention sub-block
 constexpr int kMinKeysPerUnit = 16;    // smallest attention split-K chunk
+constexpr int kMaxSplit = 64;          // most split-K chunks per KV head
+constexpr int kStatWords = 16;         // uint64 statistics per workgroup (LF_STATS)
+constexpr int kRingSlots = 16;         // 1-KB slots of each stream wave's LDS ring
 
 // Phases of one layer; each completes one "level" of the dependency chain.
 enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYER = 5 };
 
-struct LayerW {
-  const void *wqkv;       // [(Hq+2Hkv)*dh][d]  q/k rows pair-interleaved per head (i, i+dh/2)
-  const void *wo;         // [d][Hq*dh]
-  const void *wgu;        // [2F][d]  row 2j = gate j, row 2j+1 = up j
-  const void *wd;         // [d][F]
-  const void *attn_norm;  // [d]
-  const void *ffn_norm;   // [d]
-};
+// Offsets (bytes) of one layer's pieces inside the packed weight buffer; layer l
+// starts at wbase + l * layer_stride.
+enum LayerPart { LW_ATTN_NORM = 0, LW_FFN_NORM, LW_QKV, LW_O, LW_GU, LW_D, LW_COUNT };
 
 struct Params {
   // shape
@@ -32,7 +30,12 @@ struct Params {
   int hidden_io, sampling;
   int levels_per_token;
   // weights (library-owned, packed)
-  const LayerW *layers;    // device array [L]
+  // Per layer: attn_norm [d], ffn_norm [d], Wqkv [(Hq+2Hkv)*dh][d] (q/k rows
+  // pair-interleaved per head: i, i+dh/2), Wo [d][Hq*dh], Wgu [2F][d] (row 2j =
+  // gate j, 2j+1 = up j), Wd [d][F]; all fp16.
+  const char *wbase;
+  unsigned long long layer_stride;
+  unsigned long long part_off[LW_COUNT];
   const void *tok_emb, *final_norm, *lm_head;
   // state
   void *kcache, *vcache;   // fp16 [L][max_seq][Hkv][dh]
@@ -51,13 +54,16 @@ struct Params {
   int *out_tokens;         // [n_tokens]
   const int *in_tokens;    // [n_tokens] teacher-forced tokens (prefill launches)
   unsigned *err;           // [4] {code, workgroup, level, 0}
-  unsigned long long *stats;  // [G][4]
+  unsigned long long *stats;  // [G][kStatWords]
   // this launch
   int n_tokens, token0, pos0;
   unsigned level_base;
   unsigned long long timeout_ticks;
+  int fenced;              // 1: agent-scope acquire/release fences around every level
+  int plain_launch;        // 1: ordinary launch instead of a cooperative one
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_attn, lds_bytes, part_max, hmax;
+  int lds_h, lds_part, lds_red, lds_ctl, lds_ring, lds_bytes;
+  int part_rows, hmax;
 };
 
 hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream);

@@ -7,28 +7,37 @@
 // matrix is cut into contiguous row blocks, one per workgroup, fixed for the
 // life of the state; attention is cut into (KV head, key chunk) units.
 //
-// Synchronisation.  There is no grid barrier.  Each workgroup owns one 32-bit
-// progress word holding the last dependency level it completed; a level is one
-// phase of one layer of one token, numbered monotonically across launches.  A
-// consumer waits until the words of the producers it depends on reach the
-// level it needs ("Cross-GPU synchronization without atomics": consumers poll
-// memory the producer publishes, instead of an atomic-counter barrier).  The
-// producer's wave 0 writes every datum the level publishes, then issues an
-// agent-scope release fence and stores the level; the consumer's wave 0 polls
-// with agent-scope loads, issues an agent-scope acquire fence, and releases its
-// workgroup through a barrier.  Split-K attention partials are merged by the
-// last-arriving unit of each KV head (an atomic ticket), so the merge costs no
-// extra level.  Every wait is bounded: on expiry the workgroup records an error
-// word and returns, and every other wait sees the error word and returns too,
-// so the grid always drains.
+// Roles inside a workgroup.  Wave 0 is the SYNC wave: it polls the producers a
+// phase depends on, stages the phase's input vector in LDS (RMSNorm folded in),
+// and after the phase writes the outputs and publishes them.  Waves 1..7 are
+// STREAM waves: each walks its own contiguous slice of the workgroup's weight
+// rows, phase after phase, layer after layer, token after token, and copies it
+// into a private LDS ring with global_load_lds_dwordx4 (16 B per lane, 1 KB per
+// instruction).  A stream wave issues up to D pieces ahead of the piece it
+// consumes, across dependency waits and phase boundaries, and never waits on
+// another workgroup: it only waits on an LDS word the sync wave sets when the
+// phase's input vector is ready ("Weight streaming - keeping HBM saturated":
+// weights are prefetched while earlier stages still wait, and the LDS path keeps
+// registers free).  Keeping every dependency-sensitive load on wave 0 keeps the
+// stream waves' vmcnt pipeline free of anything but weights, so their waits are
+// exact.
+//
+// Synchronisation between workgroups.  No grid barrier.  Each workgroup owns
+// one 32-bit progress word = the last dependency level it completed (one level
+// per phase per layer per token, numbered across launches).  A consumer polls
+// the words of the producers it needs ("Cross-GPU synchronization without
+// atomics": consumers poll memory the producer writes, instead of an
+// atomic-counter barrier).  All data exchanged between workgroups is written
+// and read with device-scope (sc1) accesses; the producer waits for its stores
+// to complete before storing its progress word.  Split-K attention partials are
+// merged by the last-arriving unit of each KV head (an atomic ticket).  Every
+// wait is bounded: on expiry the workgroup writes the error word and returns,
+// every other wait sees it and returns too, so the grid always drains.
 //
 // Matrix-vector products run on the vector ALUs with v_dot2_f32_f16 (fp16 x
 // fp16 products, fp32 accumulation) and cross-lane sums, not on MFMA: at batch 1
 // there is no dense contraction to feed matrix cores ("The fused operations,
-// briefly").  Weights are read once per token with non-temporal 128-bit loads,
-// 1 KB contiguous per wave instruction; the first batch of each phase is issued
-// before the dependency wait so the weight stream overlaps the wait ("Weight
-// streaming - keeping HBM saturated").
+// briefly").
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,9 +50,14 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kMaxQpg = 8;     // query heads per KV head supported
-constexpr int kMaxDpl = 2;     // head dims per lane (head_dim <= 128)
-constexpr int kMaxDPerThread = 16;  // d_model <= 16 * 512
+constexpr int kNcw = kWaves - 1;       // stream waves per workgroup
+constexpr int kRing = kRingSlots;      // 1-KB slots in each stream wave's LDS ring
+constexpr int kMaxQpg = 8;             // query heads per KV head supported
+constexpr int kMaxDpl = 2;             // head dims per lane (head_dim <= 128)
+enum Kind { K_QKV = 0, K_O = 1, K_GU = 2, K_D = 3, K_LM = 4, K_COUNT = 5 };
+// sync-wave activities timed with LF_STATS: staging, waiting for the stream
+// waves, epilogue + publish, attention, lm_head + token choice
+enum StatPhase { ST_STAGE = 0, ST_STREAMS = 1, ST_EPI = 2, ST_ATTN = 3, ST_LM = 4, kStatPhases = 5 };
 
 // Thread index through an opaque copy: the kernel's outer token and layer loops
 // would otherwise let the compiler hoist every per-thread address of every phase
@@ -54,7 +68,8 @@ __device__ __forceinline__ int tid_x() {
   return t;
 }
 __device__ __forceinline__ int lane_id() { return tid_x() & 63; }
-__device__ __forceinline__ int wave_id() { return tid_x() >> 6; }
+// The wave index is uniform: keep it (and all work derived from it) scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(tid_x() >> 6); }
 
 // Eight fp16 products accumulated in fp32 with four v_dot2_f32_f16.  The halves
 // are taken by bit-casting the whole 16-byte vector and shuffling pairs out of
@@ -69,10 +84,22 @@ __device__ __forceinline__ float dot8(u32x4 w, u32x4 h, float acc) {
   return acc;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+#define LF_DPP(v, ctrl, rmask) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), (rmask), 0xf, false))
+
+// Wave-wide sum with DPP row operations; the total ends up in lane 63.
+__device__ __forceinline__ float wave_sum_to63(float v) {
+  v += LF_DPP(v, 0xB1, 0xf);    // quad_perm [1,0,3,2]
+  v += LF_DPP(v, 0x4E, 0xf);    // quad_perm [2,3,0,1]
+  v += LF_DPP(v, 0x141, 0xf);   // row_half_mirror
+  v += LF_DPP(v, 0x140, 0xf);   // row_mirror
+  v += LF_DPP(v, 0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+  v += LF_DPP(v, 0x143, 0xc);   // row_bcast:31 into rows 2 and 3
   return v;
+}
+// Wave-wide sum, the same value in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_to63(v)), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -90,18 +117,6 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   return v;
 }
 
-// Sum over the workgroup, same order on every call (deterministic).
-__device__ __forceinline__ float block_sum(float v, float *red) {
-  v = wave_sum(v);
-  if (lane_id() == 0) red[wave_id()] = v;
-  __syncthreads();
-  float t = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += red[w];
-  __syncthreads();
-  return t;
-}
-
 __device__ __forceinline__ void block_range(int total, int parts, int b, int &p0, int &p1) {
   const int base = total / parts, rem = total % parts;
   p0 = b * base + (b < rem ? b : rem);
@@ -110,190 +125,397 @@ __device__ __forceinline__ void block_range(int total, int parts, int b, int &p0
 
 __device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
-// ------------------------------------------------------------------ sync
+// ---------------------------------------------------------------- device-scope accesses
+// Data exchanged between workgroups: coherent at device scope (sc1), so a
+// consumer on another XCD never reads a stale line of its own L2.
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_dev(const unsigned *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_dev(const int *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned *p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int *p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_h(void *base, size_t i, float v) {
+  const _Float16 h = (_Float16)v;
+  __hip_atomic_store(reinterpret_cast<unsigned short *>(base) + i, __builtin_bit_cast(unsigned short, h),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS words shared between the waves of one workgroup.
+__device__ __forceinline__ unsigned lds_ld(const unsigned *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(unsigned *p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Complete this wave's earlier LDS accesses (e.g. before a flag that announces them).
+__device__ __forceinline__ void lds_drain() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------- LDS control block
+
+struct Geo {            // one phase kind's row block in this workgroup
+  int r0, nrows, kv, ppr;   // first row, rows, 16-B vectors per row, 1-KB pieces per row
+};
+
+struct Ctl {
+  unsigned h_ready;         // last GEMV phase (1-based) whose input vector is staged
+  unsigned abort;           // the sync wave gave up (the error word is set)
+  unsigned done[kWaves];    // per stream wave: last GEMV phase (1-based) it finished
+  int status;               // outcome of a barrier-based wait
+  int pad[5];
+  Geo geo[K_COUNT];
+};
+
+// ---------------------------------------------------------------- global sync (wave 0)
 
 struct Sync {
   const Params *P;
-  int *bcast;                 // LDS int used to broadcast the wait outcome
-  unsigned long long spin;    // ticks spent waiting (wave 0)
+  Ctl *ctl;
+  unsigned long long spin;    // ticks spent polling other workgroups
   unsigned long long waits;
+  unsigned long long tm[kStatPhases];   // sync-wave time by activity (LF_STATS)
 };
 
-// Wait until progress[first .. first+count) >= level.  All threads call it.
-// Wave 0 polls with agent-scope relaxed loads, then takes an agent-scope acquire
-// fence; the barrier hands the result to the other waves.  Returns false if the
-// wait timed out or another workgroup reported an error.
-__device__ __forceinline__ bool wait_level(Sync &s, int first, int count, unsigned level) {
+// Add the ticks since t0 to activity k; returns the current tick.
+__device__ __forceinline__ unsigned long long lap(Sync &s, int k, unsigned long long t0) {
+  const unsigned long long t1 = now_ticks();
+  s.tm[k] += t1 - t0;
+  return t1;
+}
+
+// Wave 0 only: poll progress[first .. first+count) >= level.  Returns false when
+// the bound expired or another workgroup reported an error.
+__device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsigned level) {
   const Params &P = *s.P;
-  if (tid_x() < 64) {
-    const unsigned long long t0 = now_ticks();
-    int status = 0;
-    unsigned it = 0;
-    for (;;) {
-      unsigned mn = 0xffffffffu;
-      for (int i = tid_x(); i < count; i += 64)
-        mn = min(mn, __hip_atomic_load(&P.progress[first + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      mn = wave_min_u32(mn);
-      if (mn >= level) { status = 1; break; }
-      if ((++it & 15u) == 0 &&
-          __hip_atomic_load(&P.err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-        status = 2;
-        break;
-      }
-      if (now_ticks() - t0 > P.timeout_ticks) {
-        if (tid_x() == 0) {
-          unsigned zero = 0u;
-          if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)) {
-            __hip_atomic_store(&P.err[1], (unsigned)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&P.err[2], level, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+  const unsigned long long t0 = now_ticks();
+  bool ok = false;
+  unsigned it = 0;
+  for (;;) {
+    unsigned mn = 0xffffffffu;
+    for (int i = lane_id(); i < count; i += 64) mn = min(mn, ld_dev(&P.progress[first + i]));
+    mn = wave_min_u32(mn);
+    if (mn >= level) { ok = true; break; }
+    if ((++it & 15u) == 0 && ld_dev(&P.err[0]) != 0u) break;
+    if (now_ticks() - t0 > P.timeout_ticks) {
+      if (lane_id() == 0) {
+        unsigned zero = 0u;
+        if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+          st_dev(&P.err[1], (unsigned)blockIdx.x);
+          st_dev(&P.err[2], level);
         }
-        status = 2;
-        break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      break;
     }
-    if (status == 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    __builtin_amdgcn_s_waitcnt(0);
-    s.spin += now_ticks() - t0;
-    s.waits += 1;
-    if (tid_x() == 0) *s.bcast = status;
+  }
+  if (ok && P.fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  s.spin += now_ticks() - t0;
+  s.waits += 1;
+  return ok;
+}
+
+// Wave 0 only: publish `level` after wave 0's own stores of the level's data.
+__device__ __forceinline__ void publish(const Params &P, unsigned level) {
+  if (P.fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);        // every store of this wave has completed
+  asm volatile("" ::: "memory");
+  if (lane_id() == 0) st_dev(&P.progress[blockIdx.x], level);
+}
+
+// All waves: barrier-based wait (wave 0 polls).  Used where the whole workgroup
+// works together (attention, nucleus sampling).
+__device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, unsigned level,
+                                               bool acquire = false) {
+  if (wave_id() == 0) {
+    const bool ok = poll_level(s, first, count, level);
+    if (ok && acquire && !s.P->fenced) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    if (lane_id() == 0) s.ctl->status = ok ? 1 : 2;
   }
   __syncthreads();
-  const bool ok = *s.bcast == 1;
+  const bool ok = s.ctl->status == 1;
   __syncthreads();
   return ok;
 }
 
-// Publish `level` for this workgroup.  Called by wave 0 only, after wave 0 itself
-// wrote every global datum the level stands for.
-__device__ __forceinline__ void publish(const Params &P, unsigned level) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  if (tid_x() == 0)
-    __hip_atomic_store(&P.progress[blockIdx.x], level, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------- staging (wave 0)
+
+constexpr int kStageBatch = 32;   // 8-byte loads in flight per lane while staging
+
+// Two consecutive elements of the layer input: fp32 written by other workgroups
+// (device-scope load), fp32 from the host, or an fp16 embedding row.
+__device__ __forceinline__ unsigned long long load_pair_bits(const float *x_dev, const float *x_host,
+                                                             const _Float16 *x16, int i) {
+  if (x_dev) return ld_dev(reinterpret_cast<const unsigned long long *>(x_dev + i));
+  float a, b;
+  if (x_host) {
+    a = x_host[i];
+    b = x_host[i + 1];
+  } else {
+    const f16x2 v = *reinterpret_cast<const f16x2 *>(x16 + i);
+    a = (float)v.x;
+    b = (float)v.y;
+  }
+  return (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
 }
 
-// ------------------------------------------------------------------ prologues
-
-// h = fp16(g * (x / sqrt(mean(x^2) + eps))) into LDS; x is fp32 or fp16 in global.
-__device__ __forceinline__ void rmsnorm_to_lds(const float *x32, const _Float16 *x16, const _Float16 *g, int d, float eps,
-                               _Float16 *h, float *red) {
-  float v[kMaxDPerThread];
+// h = fp16(g * (x / sqrt(mean(x^2) + eps))) into LDS (wave 0).  Every load of a
+// batch is issued before the first is used, so a batch costs one memory round
+// trip (d <= 4096: one batch per pass).
+__device__ __forceinline__ void stage_rmsnorm(const float *x_dev, const float *x_host, const _Float16 *x16,
+                                              const _Float16 *g, int d, float eps, _Float16 *h) {
+  const int lane = lane_id();
   float ss = 0.0f;
+  for (int base = 0; base < d; base += 128 * kStageBatch) {
+    unsigned long long v[kStageBatch];
 #pragma unroll
-  for (int k = 0; k < kMaxDPerThread; ++k) {
-    const int i = tid_x() + k * kThreads;
-    v[k] = 0.0f;
-    if (i < d) v[k] = x32 ? x32[i] : (float)x16[i];
-    ss += v[k] * v[k];
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int i = base + 128 * j + 2 * lane;
+      v[j] = i < d ? load_pair_bits(x_dev, x_host, x16, i) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+      const float a = __uint_as_float((unsigned)v[j]), b = __uint_as_float((unsigned)(v[j] >> 32));
+      ss += a * a + b * b;
+    }
   }
-  const float total = block_sum(ss, red);
-  const float r = sqrtf(total / (float)d + eps);
+  ss = wave_sum(ss);
+  const float r = sqrtf(ss / (float)d + eps);
+  for (int base = 0; base < d; base += 128 * kStageBatch) {
+    unsigned long long v[kStageBatch];
 #pragma unroll
-  for (int k = 0; k < kMaxDPerThread; ++k) {
-    const int i = tid_x() + k * kThreads;
-    if (i < d) h[i] = (_Float16)((float)g[i] * (v[k] / r));
-  }
-  __syncthreads();
-}
-
-// Copy an fp16 vector of n elements (n % 8 == 0) from global to LDS.
-__device__ __forceinline__ void copy16_to_lds(const _Float16 *src, int n, _Float16 *h) {
-  const u32x4 *s = reinterpret_cast<const u32x4 *>(src);
-  u32x4 *dst = reinterpret_cast<u32x4 *>(h);
-  for (int i = tid_x(); i < n / 8; i += kThreads) dst[i] = s[i];
-  __syncthreads();
-}
-
-// ------------------------------------------------------------------ GEMV
-
-// Rows [0, nrows) of a row-major fp16 matrix with kv 16-byte vectors per row,
-// times the fp16 vector in LDS.  Work items are (row, chunk) with a chunk of
-// 64*CV vectors; wave w takes items w, w+8, ...; the lane-sum of each item goes
-// to part[item].  pre() (the dependency wait and the input prologue) runs after
-// the first batch of weight loads has been issued.
-template <int CV, class Pre>
-__device__ __forceinline__ bool gemv_rows(const u32x4 *__restrict__ W, int kv, int nrows, int nc, const u32x4 *hl,
-                          float *part, Pre &&pre) {
-  constexpr int U = (16 / CV) > 0 ? (16 / CV) : 1;
-  const int wave = wave_id(), lane = lane_id();
-  const int nitems = nrows * nc;
-  const int nb = (nitems + kWaves * U - 1) / (kWaves * U);
-  u32x4 buf[U][CV];
-  auto load = [&](int bi) __attribute__((always_inline)) {
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int i = base + 128 * j + 2 * lane;
+      v[j] = i < d ? load_pair_bits(x_dev, x_host, x16, i) : 0ull;
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = (bi * U + u) * kWaves + wave;
-      const int r = i / nc, c = i - r * nc;
-#pragma unroll
-      for (int k = 0; k < CV; ++k) {
-        const int v = c * 64 * CV + 64 * k + lane;
-        if (i < nitems && v < kv)
-          buf[u][k] = __builtin_nontemporal_load(W + (size_t)r * kv + v);
-        else
-          buf[u][k] = (u32x4){0u, 0u, 0u, 0u};
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int i = base + 128 * j + 2 * lane;
+      if (i < d) {
+        const float a = __uint_as_float((unsigned)v[j]), b = __uint_as_float((unsigned)(v[j] >> 32));
+        const f16x2 gg = *reinterpret_cast<const f16x2 *>(g + i);
+        f16x2 o;
+        o.x = (_Float16)((float)gg.x * (a / r));
+        o.y = (_Float16)((float)gg.y * (b / r));
+        *reinterpret_cast<f16x2 *>(h + i) = o;
       }
     }
-  };
-  if (nb > 0) load(0);
-  if (!pre()) return false;
-  for (int bi = 0; bi < nb; ++bi) {
-    if (bi > 0) load(bi);
+  }
+}
+
+// Copy an fp16 vector written by other workgroups (n % 4 == 0) into LDS (wave 0),
+// one batch of loads per 8192 elements.
+__device__ __forceinline__ void stage_f16(const void *src, int n, _Float16 *h) {
+  const unsigned long long *s = reinterpret_cast<const unsigned long long *>(src);
+  unsigned long long *dst = reinterpret_cast<unsigned long long *>(h);
+  const int n4 = n / 4, lane = lane_id();
+  for (int base = 0; base < n4; base += 64 * kStageBatch) {
+    unsigned long long v[kStageBatch];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = (bi * U + u) * kWaves + wave;
-      const int r = i / nc, c = i - r * nc;
-      (void)r;
-      float acc = 0.0f;
-#pragma unroll
-      for (int k = 0; k < CV; ++k) {
-        const int v = c * 64 * CV + 64 * k + lane;
-        if (v < kv) acc = dot8(buf[u][k], hl[v], acc);
-      }
-      acc = wave_sum(acc);
-      if (i < nitems && lane == 0) part[i] = acc;
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int i = base + 64 * j + lane;
+      v[j] = i < n4 ? ld_dev(s + i) : 0ull;
     }
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int i = base + 64 * j + lane;
+      if (i < n4) dst[i] = v[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stream waves
+
+// Weight rows of phase kind k in layer l for this workgroup: row r0 of its block.
+__device__ __forceinline__ const void *layer_part(const Params &P, int l, int part) {
+  return P.wbase + (size_t)l * P.layer_stride + P.part_off[part];
+}
+
+// Weight rows of phase kind k in layer l for this workgroup: row r0 of its block.
+// Pure address arithmetic (no loads), so crossing a phase never drains the
+// stream wave's load pipeline.
+__device__ __forceinline__ const u32x4 *phase_base(const Params &P, const Geo &g, int kind, int l) {
+  const void *w;
+  switch (kind) {
+    case K_QKV: w = layer_part(P, l, LW_QKV); break;
+    case K_O: w = layer_part(P, l, LW_O); break;
+    case K_GU: w = layer_part(P, l, LW_GU); break;
+    case K_D: w = layer_part(P, l, LW_D); break;
+    default: w = P.lm_head; break;
+  }
+  return reinterpret_cast<const u32x4 *>(w) + (size_t)g.r0 * g.kv;
+}
+
+// Stream wave cw's share [lo, hi) of the np pieces of a row block (contiguous).
+__device__ __forceinline__ void wave_slice(int np, int cw, int &lo, int &hi) {
+  lo = (cw * np) / kNcw;
+  hi = ((cw + 1) * np) / kNcw;
+}
+
+// The issue side of a stream wave: walks GEMV phases q = 0, 1, ... of the launch
+// (token t = q / ngp, phase g = q % ngp; g < 4L is (layer g/4, kind g%4), else
+// the lm_head) and issues one 1-KB piece per call into the wave's LDS ring.
+struct Streamer {
+  const Params *P;
+  const Ctl *ctl;
+  unsigned char *ring;        // this wave's ring: D slots of 1 KB
+  int cw, ngp, qend;
+  int q, p, phi, row, kp, kv, ppr;
+  const u32x4 *base;
+  unsigned issued;
+  bool timed;                                 // LF_STATS on stream wave 1
+  unsigned long long t_ready, t_work, pieces;
+
+  // advance to the first GEMV phase >= q_ in which this wave has pieces
+  __device__ __forceinline__ void locate(int q_) {
+    q = q_;
+    while (q < qend) {
+      const int g = q % ngp;
+      const bool lm = g >= 4 * P->L;
+      const int kind = lm ? K_LM : (g & 3);
+      const int l = lm ? 0 : (g >> 2);
+      const Geo ge = ctl->geo[kind];
+      int lo, hi;
+      wave_slice(ge.nrows * ge.ppr, cw, lo, hi);
+      if (lo < hi) {
+        p = lo;
+        phi = hi;
+        row = lo / ge.ppr;
+        kp = lo - row * ge.ppr;
+        kv = ge.kv;
+        ppr = ge.ppr;
+        base = phase_base(*P, ge, kind, l);
+        return;
+      }
+      ++q;
+    }
+  }
+
+  __device__ __forceinline__ void issue() {
+    if (q >= qend) return;
+    const int v = kp * 64 + lane_id();
+    const int vc = v < kv ? v : kv - 1;      // masked lanes re-read a valid vector
+    const u32x4 *src = base + (size_t)row * kv + vc;
+    unsigned char *dst = ring + (issued % (unsigned)kRing) * 1024u;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
+                                     (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
+    ++issued;
+    ++p;
+    if (++kp == ppr) { kp = 0; ++row; }
+    if (p == phi) locate(q + 1);
+  }
+};
+
+// A stream wave's share of GEMV phase q: consume its pieces from the ring,
+// refilling the ring as it goes, and leave one partial row sum per (row, wave)
+// in part[row * 8 + cw].  Returns false if the sync wave aborted.
+__device__ __forceinline__ bool stream_phase(Streamer &st, unsigned &consumed, int q, int kind, Ctl *ctl,
+                                             const _Float16 *h, float *part) {
+  const Geo ge = ctl->geo[kind];
+  int lo, hi;
+  wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
+  // the dependency wait happens on wave 0; here only its LDS announcement
+  const bool timed = st.timed;
+  unsigned long long t0 = timed ? now_ticks() : 0ull;
+  while (lds_ld(&ctl->h_ready) < (unsigned)(q + 1)) {
+    if (lds_ld(&ctl->abort)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (timed) {
+    const unsigned long long t1 = now_ticks();
+    st.t_ready += t1 - t0;
+    t0 = t1;
+  }
+  const int lane = lane_id();
+  const u32x4 *hv = reinterpret_cast<const u32x4 *>(h);
+  int row = lo / ge.ppr, kp = lo - row * ge.ppr;
+  float acc = 0.0f;
+  for (int p = lo; p < hi; ++p) {
+    // in steady state kRing pieces are in flight and the oldest is the one wanted
+    if (st.issued - consumed >= (unsigned)kRing)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((kRing - 1) & 15) | (((kRing - 1) >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+    const u32x4 x = reinterpret_cast<const u32x4 *>(st.ring + (consumed % (unsigned)kRing) * 1024u)[lane];
+    const int v = kp * 64 + lane;
+    if (v < ge.kv) acc = dot8(x, hv[v], acc);
+    lds_drain();                 // the slot has been read before it is refilled
+    ++consumed;
+    st.issue();
+    if (++kp == ge.ppr || p == hi - 1) {
+      const float s = wave_sum_to63(acc);
+      if (lane == 63) part[row * 8 + st.cw] = s;
+      acc = 0.0f;
+      if (kp == ge.ppr) { kp = 0; ++row; }
+    }
+  }
+  lds_drain();
+  if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
+  if (timed) {
+    st.t_work += now_ticks() - t0;
+    st.pieces += (unsigned long long)(hi - lo);
   }
   return true;
 }
 
-// Chunk shape for a row of kv vectors: CV = 4 vectors per lane when the row
-// fits in 4 per lane, else 8, and as many chunks as needed.
-__device__ __forceinline__ void gemv_shape(int kv, int &cv, int &nc) {
-  const int per_lane = (kv + 63) / 64;
-  cv = per_lane <= 4 ? 4 : 8;
-  nc = (per_lane + cv - 1) / cv;
-}
+// ---------------------------------------------------------------- sync-wave phase pieces
 
-template <class Pre>
-__device__ __forceinline__ bool gemv_dispatch(const void *W, int kv, int nrows, const _Float16 *hl, float *part,
-                                              Pre &&pre) {
-  int cv, nc;
-  gemv_shape(kv, cv, nc);
-  const u32x4 *w = reinterpret_cast<const u32x4 *>(W);
-  const u32x4 *h = reinterpret_cast<const u32x4 *>(hl);
-  if (cv == 4) return gemv_rows<4>(w, kv, nrows, nc, h, part, pre);
-  return gemv_rows<8>(w, kv, nrows, nc, h, part, pre);
-}
-
-// Row sum of the chunk partials (chunk order fixed).
-__device__ __forceinline__ float row_value(const float *part, int row, int nc) {
+// Sum of the stream waves' partials of one row, in wave order.
+__device__ __forceinline__ float row_value(const float *part, const Geo &ge, int row) {
+  const int np = ge.nrows * ge.ppr;
+  const int a = row * ge.ppr, bnd = a + ge.ppr;
   float y = 0.0f;
-  for (int c = 0; c < nc; ++c) y += part[row * nc + c];
+  for (int cw = 0; cw < kNcw; ++cw) {
+    int lo, hi;
+    wave_slice(np, cw, lo, hi);
+    if (lo < hi && lo < bnd && hi > a) y += part[row * 8 + cw];
+  }
   return y;
 }
 
-__device__ __forceinline__ int chunks_for(int kv) {
-  int cv, nc;
-  gemv_shape(kv, cv, nc);
-  return nc;
+// Wave 0: wait until every stream wave finished GEMV phase q.
+__device__ __forceinline__ void wait_streams(const Ctl *ctl, int q) {
+  for (;;) {
+    unsigned mn = 0xffffffffu;
+    if (lane_id() < kNcw) mn = lds_ld(&ctl->done[lane_id()]);
+    mn = wave_min_u32(mn);
+    if (mn >= (unsigned)(q + 1)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
 }
 
-// ------------------------------------------------------------------ attention
+// Wave 0: the input vector of GEMV phase q is in LDS.
+__device__ __forceinline__ void announce_input(Ctl *ctl, int q) {
+  lds_drain();
+  if (lane_id() == 0) lds_st(&ctl->h_ready, (unsigned)(q + 1));
+}
+
+// ---------------------------------------------------------------- attention
 
 __device__ __forceinline__ void attn_split(int n, int G, int Hkv, int &S, int &Lc) {
   int smax = G / Hkv;
+  if (smax > kMaxSplit) smax = kMaxSplit;
   if (smax < 1) smax = 1;
   S = (n + kMinKeysPerUnit - 1) / kMinKeysPerUnit;
   if (S > smax) S = smax;
@@ -303,9 +525,12 @@ __device__ __forceinline__ void attn_split(int n, int G, int Hkv, int &S, int &L
 
 // One split-K unit (KV head g, key chunk c) of layer l at position pos: partial
 // (m, l, o) for the qpg query heads of group g, written to attn_part; the last
-// unit of the group to arrive merges all partials into o16 (wave 0).
+// unit of the group to arrive merges all partials into o16 (wave 0).  These are
+// the pages' three attention stages ("The fused operations, briefly"): per-unit
+// attention over a tile of the cache, cross-unit softmax correction, then the
+// output projection (the next phase).
 __device__ __forceinline__ void attn_unit(const Params &P, int l, int pos, int u, int S, int Lc, unsigned char *lds,
-                          float *red) {
+                                          float *red) {
   const int tid = tid_x(), wave = wave_id(), lane = lane_id();
   const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv;
   const int dpl = dh / 64;
@@ -316,7 +541,7 @@ __device__ __forceinline__ void attn_unit(const Params &P, int l, int pos, int u
   float *qs = reinterpret_cast<float *>(lds);      // [qpg][dh]
   float *sc = qs + qpg * dh;                        // [qpg][kAttnBlock]
   float *ored = sc + qpg * kAttnBlock;              // [kWaves][qpg][dh]
-  for (int i = tid; i < qpg * dh; i += kThreads) qs[i] = P.q[(size_t)g * qpg * dh + i];
+  for (int i = tid; i < qpg * dh; i += kThreads) qs[i] = ld_dev(&P.q[(size_t)g * qpg * dh + i]);
   __syncthreads();
   const size_t lstride = (size_t)P.max_seq * Hkv * dh;
   const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride;
@@ -434,48 +659,68 @@ __device__ __forceinline__ void attn_unit(const Params &P, int l, int pos, int u
       for (int e = lane; e < dh; e += 64) {
         float o = 0.0f;
         for (int w = 0; w < kWaves; ++w) o += ored[(w * qpg + h) * dh + e];
-        dst[h * stride + 2 + e] = o;
+        st_dev(&dst[h * stride + 2 + e], o);
       }
       if (lane == 0) {
-        dst[h * stride + 0] = m_run[h];
-        dst[h * stride + 1] = l_run[h];
+        st_dev(&dst[h * stride + 0], m_run[h]);
+        st_dev(&dst[h * stride + 1], l_run[h]);
       }
     }
     // Arrival ticket of group g: the unit that completes the count merges.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (P.fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
     unsigned old = 0;
     if (lane == 0)
       old = __hip_atomic_fetch_add(&P.tickets[l * Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0, 64);
     if (old == (unsigned)(S - 1)) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (P.fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       const float *src = P.attn_part + (size_t)g * S * qpg * stride;
-      _Float16 *o16 = reinterpret_cast<_Float16 *>(P.o16) + (size_t)g * qpg * dh;
+      float *wgt = red;   // merge weights e^(m_c - M), one per chunk (S <= kMaxSplit = 64)
       for (int h = 0; h < qpg; ++h) {
+        // chunk statistics: lanes over chunks, 64 at a time
         float M = -INFINITY;
-        for (int cc = 0; cc < S; ++cc) M = fmaxf(M, src[(cc * qpg + h) * stride + 0]);
-        float Lsum = 0.0f;
-        for (int cc = 0; cc < S; ++cc) {
-          const float *pp = src + (cc * qpg + h) * stride;
-          Lsum += __expf(pp[0] - M) * pp[1];
+        for (int c0 = 0; c0 < S; c0 += 64) {
+          const int cc = c0 + lane;
+          const float m = cc < S ? ld_dev(&src[(cc * qpg + h) * stride + 0]) : -INFINITY;
+          M = fmaxf(M, wave_max(m));
         }
+        float Lsum = 0.0f;
+        for (int c0 = 0; c0 < S; c0 += 64) {
+          const int cc = c0 + lane;
+          float m = -INFINITY, lc = 0.0f;
+          if (cc < S) {
+            m = ld_dev(&src[(cc * qpg + h) * stride + 0]);
+            lc = ld_dev(&src[(cc * qpg + h) * stride + 1]);
+          }
+          const float w = cc < S ? __expf(m - M) : 0.0f;
+          Lsum += wave_sum(w * lc);
+          if (cc < S) wgt[cc] = w;
+        }
+        lds_drain();
+        const float inv = 1.0f / Lsum;
         for (int e = lane; e < dh; e += 64) {
           float o = 0.0f;
-          for (int cc = 0; cc < S; ++cc) {
-            const float *pp = src + (cc * qpg + h) * stride;
-            o += __expf(pp[0] - M) * pp[2 + e];
+          for (int c0 = 0; c0 < S; c0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              v[j] = c0 + j < S ? ld_dev(&src[((c0 + j) * qpg + h) * stride + 2 + e]) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (c0 + j < S) o += wgt[c0 + j] * v[j];
           }
-          o16[h * dh + e] = (_Float16)(o / Lsum);
+          st_dev_h(P.o16, (size_t)(g * qpg + h) * dh + e, o * inv);
         }
       }
-      if (lane == 0)
-        __hip_atomic_store(&P.tickets[l * Hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) st_dev(&P.tickets[l * Hkv + g], 0u);
     }
   }
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ sampler
+// ---------------------------------------------------------------- sampler
 
 // Defined exponential for x <= 0, bit-identical on any IEEE machine: k = rint(x
 // log2 e); r = x - k ln2 by a two-constant Cody-Waite step with fma; degree-7
@@ -509,6 +754,9 @@ __device__ __forceinline__ void philox4x32_10(unsigned c[4], unsigned k0, unsign
   }
 }
 
+// Plain loads: the caller has taken an agent-scope acquire fence after the
+// logits were published, so this XCD's caches hold no stale copy of them, and
+// the sampler's repeated passes then hit in L2.
 __device__ __forceinline__ float scaled_logit(const float *logits, int i, float inv_temp) {
 #pragma clang fp contract(off)
   float z = logits[i] * inv_temp;
@@ -533,7 +781,7 @@ struct SampLds {
   unsigned long long mass[256];
   unsigned cnt[256];
   unsigned long long wtot[kWaves];
-  unsigned long long sel[4];   // prefix, mask, mass_above, misc
+  unsigned long long sel[4];
   float fred[kWaves];
   int ibc[4];
 };
@@ -554,12 +802,19 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 // reaches ceil(top_p * C_V) in fp64, found by an 8-pass radix select on a 64-bit
 // order key; the Philox draw t = floor(r * C_N / 2^64) with r from counter
 // (pos, 0, 0, 0); the token is the first nucleus member in index order whose
-// running mass exceeds t.
+// running mass exceeds t.  Thread t owns the contiguous indices
+// [t * blk, t * blk + blk) and re-reads their logits in each pass.
 __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv_temp, float top_p,
-                           unsigned long long seed, int pos, SampLds *s) {
+                                           unsigned long long seed, int pos, SampLds *s) {
   const int tid = tid_x();
+  const int blk = (V + kThreads - 1) / kThreads;
+  const int i0 = tid * blk;
+  auto valid = [&](int j) __attribute__((always_inline)) { return i0 + j < V; };
+  auto zval = [&](int j) __attribute__((always_inline)) -> float { return scaled_logit(logits, i0 + j, inv_temp); };
+  const int nj = blk;
   float zm = -INFINITY;
-  for (int i = tid; i < V; i += kThreads) zm = fmaxf(zm, scaled_logit(logits, i, inv_temp));
+  for (int j = 0; j < nj; ++j)
+    if (valid(j)) zm = fmaxf(zm, zval(j));
   zm = wave_max(zm);
   if (lane_id() == 0) s->fred[wave_id()] = zm;
   __syncthreads();
@@ -567,20 +822,23 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
   for (int w = 0; w < kWaves; ++w) zmax = fmaxf(zmax, s->fred[w]);
   __syncthreads();
   unsigned long long part = 0;
-  for (int i = tid; i < V; i += kThreads) part += mass_of(scaled_logit(logits, i, inv_temp), zmax);
+  for (int j = 0; j < nj; ++j)
+    if (valid(j)) part += mass_of(zval(j), zmax);
   const unsigned long long CV = block_sum_u64(part, s);
   const unsigned long long Mstar = (unsigned long long)ceil((double)top_p * (double)CV);
   unsigned long long prefix = 0, pmask = 0, above = 0;
   for (int shift = 56; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kThreads) { s->mass[i] = 0; s->cnt[i] = 0; }
     __syncthreads();
-    for (int i = tid; i < V; i += kThreads) {
-      const float z = scaled_logit(logits, i, inv_temp);
-      const unsigned long long key = order_key(z, i);
-      if ((key & pmask) == prefix) {
-        const int dg = (int)((key >> shift) & 255ull);
-        atomicAdd(&s->mass[dg], mass_of(z, zmax));
-        atomicAdd(&s->cnt[dg], 1u);
+    for (int j = 0; j < nj; ++j) {
+      if (valid(j)) {
+        const float z = zval(j);
+        const unsigned long long key = order_key(z, i0 + j);
+        if ((key & pmask) == prefix) {
+          const int dg = (int)((key >> shift) & 255ull);
+          atomicAdd(&s->mass[dg], mass_of(z, zmax));
+          atomicAdd(&s->cnt[dg], 1u);
+        }
       }
     }
     __syncthreads();
@@ -607,13 +865,12 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
     __syncthreads();
   }
   const unsigned long long kappa = prefix;
-  // nucleus mass; each thread owns a contiguous index block for the final scan
-  const int blk = (V + kThreads - 1) / kThreads;
-  const int i0 = min(V, tid * blk), i1 = min(V, i0 + blk);
   unsigned long long local = 0;
-  for (int i = i0; i < i1; ++i) {
-    const float z = scaled_logit(logits, i, inv_temp);
-    if (order_key(z, i) >= kappa) local += mass_of(z, zmax);
+  for (int j = 0; j < nj; ++j) {
+    if (valid(j)) {
+      const float z = zval(j);
+      if (order_key(z, i0 + j) >= kappa) local += mass_of(z, zmax);
+    }
   }
   const unsigned long long CN = block_sum_u64(local, s);
   unsigned ctr[4] = {(unsigned)pos, 0u, 0u, 0u};
@@ -634,12 +891,17 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
   const unsigned long long excl = base + incl - local;
   if (local > 0 && excl <= t && t < excl + local) {
     unsigned long long run = excl;
-    for (int i = i0; i < i1; ++i) {
-      const float z = scaled_logit(logits, i, inv_temp);
-      if (order_key(z, i) < kappa) continue;
-      run += mass_of(z, zmax);
-      if (run > t) { s->ibc[0] = i; break; }
+    int found = -1;
+    for (int j = 0; j < nj; ++j) {
+      if (found < 0 && valid(j)) {
+        const float z = zval(j);
+        if (order_key(z, i0 + j) >= kappa) {
+          run += mass_of(z, zmax);
+          if (run > t) found = i0 + j;
+        }
+      }
     }
+    s->ibc[0] = found;
   }
   __syncthreads();
   const int tok = s->ibc[0];
@@ -647,7 +909,7 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
   return tok;
 }
 
-// ------------------------------------------------------------------ the kernel
+// ---------------------------------------------------------------- the kernel
 
 // kPrefill: teacher-forced prompt tokens read from in_tokens[], no logits and no
 // sampling; each token's first layer waits for the previous token's last layer.
@@ -656,220 +918,269 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16 *hl = reinterpret_cast<_Float16 *>(smem + P.lds_h);
   float *part = reinterpret_cast<float *>(smem + P.lds_part);
-  float *red = reinterpret_cast<float *>(smem + P.lds_red);   // 64 floats + 16 ints
-  int *ibc = reinterpret_cast<int *>(red + 64);
-  unsigned char *alds = smem + P.lds_attn;
+  float *red = reinterpret_cast<float *>(smem + P.lds_red);   // 64 floats
+  Ctl *ctl = reinterpret_cast<Ctl *>(smem + P.lds_ctl);
+  unsigned char *alds = smem + P.lds_h;                       // attention / sampler scratch
   const int b = blockIdx.x, G = P.G, wave = wave_id(), lane = lane_id();
-  Sync sy{&P, ibc, 0ull, 0ull};
-  const unsigned long long kt0 = now_ticks();
-  const int d = P.d, dh = P.dh;
-  const int kv_d = d / 8;
+  const int L = P.L, d = P.d, dh = P.dh;
+  const bool has_lm = !kPrefill && !P.hidden_io;
+  const int ngp = 4 * L + (has_lm ? 1 : 0);        // GEMV phases per token
   const _Float16 *emb = reinterpret_cast<const _Float16 *>(P.tok_emb);
-  bool ok = true;
 
-  for (int t = 0; t < P.n_tokens && ok; ++t) {
+  // this workgroup's row block of every phase kind
+  if (tid_x() == 0) {
+    const int pairs[K_COUNT] = {P.nqkv / 2, d / 2, P.F, d / 2, P.V / 2};
+    const int kvs[K_COUNT] = {d / 8, P.Hq * dh / 8, d / 8, P.F / 8, d / 8};
+    for (int k = 0; k < K_COUNT; ++k) {
+      int p0, p1;
+      block_range(pairs[k], G, b, p0, p1);
+      ctl->geo[k] = Geo{2 * p0, 2 * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
+    }
+    ctl->h_ready = 0;
+    ctl->abort = 0;
+    for (int w = 0; w < kWaves; ++w) ctl->done[w] = 0;
+    ctl->status = 0;
+  }
+  __syncthreads();
+
+  Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}};
+  const unsigned long long kt0 = now_ticks();
+
+  if (wave > 0) {
+    // ======================= stream waves =======================
+    Streamer st;
+    st.P = &P;
+    st.ctl = ctl;
+    st.cw = wave - 1;
+    st.ring = smem + P.lds_ring + (size_t)st.cw * kRing * 1024;
+    st.ngp = ngp;
+    st.qend = P.n_tokens * ngp;
+    st.issued = 0;
+    st.timed = (P.flags & 4u) && st.cw == 0;
+    st.t_ready = st.t_work = st.pieces = 0;
+    st.locate(0);
+    for (int i = 0; i < kRing; ++i) st.issue();
+    unsigned consumed = 0;
+    for (int t = 0; t < P.n_tokens; ++t) {
+      const int pos = P.pos0 + t;
+      const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
+      for (int l = 0; l < L; ++l) {
+        const int q0 = t * ngp + 4 * l;
+        if (!stream_phase(st, consumed, q0 + 0, K_QKV, ctl, hl, part)) return;
+        // attention: the whole workgroup
+        if (lds_ld(&ctl->abort)) return;
+        if (!wait_all_waves(sy, 0, G, lv0 + (unsigned)(l * PH_PER_LAYER) + PH_QKV)) return;
+        {
+          int S, Lc;
+          attn_split(pos + 1, G, P.Hkv, S, Lc);
+          for (int u = b; u < P.Hkv * S; u += G) attn_unit(P, l, pos, u, S, Lc, alds, red);
+        }
+        if (!stream_phase(st, consumed, q0 + 1, K_O, ctl, hl, part)) return;
+        if (!stream_phase(st, consumed, q0 + 2, K_GU, ctl, hl, part)) return;
+        if (!stream_phase(st, consumed, q0 + 3, K_D, ctl, hl, part)) return;
+      }
+      if (has_lm) {
+        if (!stream_phase(st, consumed, t * ngp + 4 * L, K_LM, ctl, hl, part)) return;
+        if (b == 0 && P.sampling) {
+          const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
+          if (lds_ld(&ctl->abort)) return;
+          if (!wait_all_waves(sy, 0, G, lvl_lm, true)) return;
+          sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds));
+        }
+      }
+    }
+    if (st.timed && lane == 0) {
+      P.stats[b * kStatWords + 9] = st.t_ready;
+      P.stats[b * kStatWords + 10] = st.t_work;
+      P.stats[b * kStatWords + 11] = st.pieces;
+    }
+    return;
+  }
+
+  // ======================= sync wave (wave 0) =======================
+  auto fail = [&]() __attribute__((always_inline)) {
+    if (lane == 0) lds_st(&ctl->abort, 1u);
+  };
+  int token = P.token0;
+  for (int t = 0; t < P.n_tokens; ++t) {
     const int pos = P.pos0 + t;
     const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
-    int token = kPrefill ? P.in_tokens[t] : P.token0;
-    for (int l = 0; l < P.L && ok; ++l) {
-      const LayerW &W = P.layers[l];
+    if (kPrefill) token = P.in_tokens[t];
+    for (int l = 0; l < L; ++l) {
       const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
-      const _Float16 *attn_norm = reinterpret_cast<const _Float16 *>(W.attn_norm);
-      const _Float16 *ffn_norm = reinterpret_cast<const _Float16 *>(W.ffn_norm);
+      const int q0 = t * ngp + 4 * l;
+      const _Float16 *attn_norm = reinterpret_cast<const _Float16 *>(layer_part(P, l, LW_ATTN_NORM));
+      const _Float16 *ffn_norm = reinterpret_cast<const _Float16 *>(layer_part(P, l, LW_FFN_NORM));
 
       // ---------------- QKV + rotary + KV append
       {
-        int p0, p1;
-        block_range(P.nqkv / 2, G, b, p0, p1);
-        const int r0 = 2 * p0, nrows = 2 * (p1 - p0);
-        auto pre = [&]() __attribute__((always_inline)) -> bool {
-          if (l == 0) {
-            if (kPrefill) {
-              if (t > 0 && !wait_level(sy, 0, G, lv0)) return false;
-            } else if (t > 0 && !P.hidden_io) {
-              if (!wait_level(sy, 0, 1, lv0)) return false;
-              token = *P.tok_slot;
-            }
-            if (P.hidden_io)
-              rmsnorm_to_lds(P.x_hidden, nullptr, attn_norm, d, P.eps, hl, red);
-            else
-              rmsnorm_to_lds(nullptr, emb + (size_t)token * d, attn_norm, d, P.eps, hl, red);
-          } else {
-            if (!wait_level(sy, 0, G, lvl)) return false;
-            rmsnorm_to_lds(P.x_out, nullptr, attn_norm, d, P.eps, hl, red);
+        unsigned long long tq = 0;
+        if (l == 0) {
+          if (kPrefill) {
+            if (t > 0 && !poll_level(sy, 0, G, lv0)) { fail(); return; }
+          } else if (t > 0 && !P.hidden_io) {
+            if (!poll_level(sy, 0, 1, lv0)) { fail(); return; }
+            token = ld_dev(P.tok_slot);
           }
-          return true;
-        };
-        const u32x4 *wq = reinterpret_cast<const u32x4 *>(W.wqkv) + (size_t)r0 * kv_d;
-        if (!gemv_dispatch(wq, kv_d, nrows, hl, part, pre)) { ok = false; break; }
-        __syncthreads();
-        if (wave == 0) {
-          const int nc = chunks_for(kv_d);
-          const int half = dh / 2;
-          const int nq = P.Hq * dh, nk = P.Hkv * dh;
-          const size_t kvrow = ((size_t)l * P.max_seq + pos) * (size_t)nk;
-          _Float16 *kc = reinterpret_cast<_Float16 *>(P.kcache) + kvrow;
-          _Float16 *vc = reinterpret_cast<_Float16 *>(P.vcache) + kvrow;
-          for (int i = lane; i < nrows / 2; i += 64) {
-            const float a = row_value(part, 2 * i, nc), bb = row_value(part, 2 * i + 1, nc);
-            const int r = r0 + 2 * i;
-            if (r < nq + nk) {
-              const int rr = r < nq ? r : r - nq;
-              const int hd = rr / dh, k = (rr % dh) / 2;
-              const float cs = P.rope[((size_t)pos * half + k) * 2 + 0];
-              const float sn = P.rope[((size_t)pos * half + k) * 2 + 1];
-              const float y0 = a * cs - bb * sn, y1 = bb * cs + a * sn;
-              if (r < nq) {
-                P.q[hd * dh + k] = y0;
-                P.q[hd * dh + k + half] = y1;
-              } else {
-                kc[hd * dh + k] = (_Float16)y0;
-                kc[hd * dh + k + half] = (_Float16)y1;
-              }
-            } else {
-              const int rv = r - nq - nk;
-              vc[rv] = (_Float16)a;
-              vc[rv + 1] = (_Float16)bb;
-            }
-          }
-          publish(P, lvl + PH_QKV);
+          tq = now_ticks();
+          if (P.hidden_io)
+            stage_rmsnorm(nullptr, P.x_hidden, nullptr, attn_norm, d, P.eps, hl);
+          else
+            stage_rmsnorm(nullptr, nullptr, emb + (size_t)token * d, attn_norm, d, P.eps, hl);
+        } else {
+          if (!poll_level(sy, 0, G, lvl)) { fail(); return; }
+          tq = now_ticks();
+          stage_rmsnorm(P.x_out, nullptr, nullptr, attn_norm, d, P.eps, hl);
         }
+        lap(sy, ST_STAGE, tq);
+        announce_input(ctl, q0);
+        unsigned long long tk = now_ticks();
+        wait_streams(ctl, q0);
+        tk = lap(sy, ST_STREAMS, tk);
+        const Geo ge = ctl->geo[K_QKV];
+        const int half = dh / 2;
+        const int nq = P.Hq * dh, nk = P.Hkv * dh;
+        const size_t kvrow = ((size_t)l * P.max_seq + pos) * (size_t)nk;
+        for (int i = lane; i < ge.nrows / 2; i += 64) {
+          const float a = row_value(part, ge, 2 * i), bb = row_value(part, ge, 2 * i + 1);
+          const int r = ge.r0 + 2 * i;
+          if (r < nq + nk) {
+            const int rr = r < nq ? r : r - nq;
+            const int hd = rr / dh, k = (rr % dh) / 2;
+            const float cs = P.rope[((size_t)pos * half + k) * 2 + 0];
+            const float sn = P.rope[((size_t)pos * half + k) * 2 + 1];
+            const float y0 = a * cs - bb * sn, y1 = bb * cs + a * sn;
+            if (r < nq) {
+              st_dev(&P.q[hd * dh + k], y0);
+              st_dev(&P.q[hd * dh + k + half], y1);
+            } else {
+              st_dev_h(P.kcache, kvrow + hd * dh + k, y0);
+              st_dev_h(P.kcache, kvrow + hd * dh + k + half, y1);
+            }
+          } else {
+            const int rv = r - nq - nk;
+            st_dev_h(P.vcache, kvrow + rv, a);
+            st_dev_h(P.vcache, kvrow + rv + 1, bb);
+          }
+        }
+        publish(P, lvl + PH_QKV);
+        lap(sy, ST_EPI, tk);
       }
 
-      // ---------------- attention (split-K, last arriver merges)
+      // ---------------- attention (all waves; split-K, last arriver merges)
       {
-        if (!wait_level(sy, 0, G, lvl + PH_QKV)) { ok = false; break; }
+        const unsigned long long ta = now_ticks();
+        if (!wait_all_waves(sy, 0, G, lvl + PH_QKV)) { fail(); return; }
         int S, Lc;
         attn_split(pos + 1, G, P.Hkv, S, Lc);
-        const int units = P.Hkv * S;
-        for (int u = b; u < units; u += G) attn_unit(P, l, pos, u, S, Lc, alds, red);
-        if (wave == 0) publish(P, lvl + PH_ATTN);
+        for (int u = b; u < P.Hkv * S; u += G) attn_unit(P, l, pos, u, S, Lc, alds, red);
+        publish(P, lvl + PH_ATTN);
+        lap(sy, ST_ATTN, ta);
       }
 
       // ---------------- output projection + residual
       {
-        int p0, p1;
-        block_range(d / 2, G, b, p0, p1);
-        const int r0 = 2 * p0, nrows = 2 * (p1 - p0);
-        const int kv = P.Hq * dh / 8;
-        auto pre = [&]() __attribute__((always_inline)) -> bool {
-          if (!wait_level(sy, 0, G, lvl + PH_ATTN)) return false;
-          copy16_to_lds(reinterpret_cast<const _Float16 *>(P.o16), P.Hq * dh, hl);
-          return true;
-        };
-        const u32x4 *wo = reinterpret_cast<const u32x4 *>(W.wo) + (size_t)r0 * kv;
-        if (!gemv_dispatch(wo, kv, nrows, hl, part, pre)) { ok = false; break; }
-        __syncthreads();
-        if (wave == 0) {
-          const int nc = chunks_for(kv);
-          for (int i = lane; i < nrows; i += 64) {
-            const int r = r0 + i;
-            float xin;
-            if (l > 0) xin = P.x_out[r];
-            else if (P.hidden_io) xin = P.x_hidden[r];
-            else xin = (float)emb[(size_t)token * d + r];
-            P.x_mid[r] = xin + row_value(part, i, nc);
-          }
-          publish(P, lvl + PH_O);
+        if (!poll_level(sy, 0, G, lvl + PH_ATTN)) { fail(); return; }
+        unsigned long long tk = now_ticks();
+        stage_f16(P.o16, P.Hq * dh, hl);
+        tk = lap(sy, ST_STAGE, tk);
+        announce_input(ctl, q0 + 1);
+        wait_streams(ctl, q0 + 1);
+        tk = lap(sy, ST_STREAMS, tk);
+        const Geo ge = ctl->geo[K_O];
+        for (int i = lane; i < ge.nrows; i += 64) {
+          const int r = ge.r0 + i;
+          float xin;
+          if (l > 0) xin = ld_dev(&P.x_out[r]);
+          else if (P.hidden_io) xin = P.x_hidden[r];
+          else xin = (float)emb[(size_t)token * d + r];
+          st_dev(&P.x_mid[r], xin + row_value(part, ge, i));
         }
+        publish(P, lvl + PH_O);
+        lap(sy, ST_EPI, tk);
       }
 
       // ---------------- FFN norm + gate/up + SwiGLU
       {
-        int p0, p1;
-        block_range(P.F, G, b, p0, p1);
-        const int r0 = 2 * p0, nrows = 2 * (p1 - p0);
-        auto pre = [&]() __attribute__((always_inline)) -> bool {
-          if (!wait_level(sy, 0, G, lvl + PH_O)) return false;
-          rmsnorm_to_lds(P.x_mid, nullptr, ffn_norm, d, P.eps, hl, red);
-          return true;
-        };
-        const u32x4 *wgu = reinterpret_cast<const u32x4 *>(W.wgu) + (size_t)r0 * kv_d;
-        if (!gemv_dispatch(wgu, kv_d, nrows, hl, part, pre)) { ok = false; break; }
-        __syncthreads();
-        if (wave == 0) {
-          const int nc = chunks_for(kv_d);
-          _Float16 *a16 = reinterpret_cast<_Float16 *>(P.a16);
-          for (int i = lane; i < nrows / 2; i += 64) {
-            const float gt = row_value(part, 2 * i, nc), up = row_value(part, 2 * i + 1, nc);
-            const float sg = gt / (1.0f + __expf(-gt));
-            a16[p0 + i] = (_Float16)(sg * up);
-          }
-          publish(P, lvl + PH_GU);
+        if (!poll_level(sy, 0, G, lvl + PH_O)) { fail(); return; }
+        unsigned long long tk = now_ticks();
+        stage_rmsnorm(P.x_mid, nullptr, nullptr, ffn_norm, d, P.eps, hl);
+        tk = lap(sy, ST_STAGE, tk);
+        announce_input(ctl, q0 + 2);
+        wait_streams(ctl, q0 + 2);
+        tk = lap(sy, ST_STREAMS, tk);
+        const Geo ge = ctl->geo[K_GU];
+        for (int i = lane; i < ge.nrows / 2; i += 64) {
+          const float gt = row_value(part, ge, 2 * i), up = row_value(part, ge, 2 * i + 1);
+          const float sg = gt / (1.0f + __expf(-gt));
+          st_dev_h(P.a16, (size_t)(ge.r0 / 2 + i), sg * up);
         }
+        publish(P, lvl + PH_GU);
+        lap(sy, ST_EPI, tk);
       }
 
       // ---------------- down projection + residual
       {
-        int p0, p1;
-        block_range(d / 2, G, b, p0, p1);
-        const int r0 = 2 * p0, nrows = 2 * (p1 - p0);
-        const int kv = P.F / 8;
-        auto pre = [&]() __attribute__((always_inline)) -> bool {
-          if (!wait_level(sy, 0, G, lvl + PH_GU)) return false;
-          copy16_to_lds(reinterpret_cast<const _Float16 *>(P.a16), P.F, hl);
-          return true;
-        };
-        const u32x4 *wd = reinterpret_cast<const u32x4 *>(W.wd) + (size_t)r0 * kv;
-        if (!gemv_dispatch(wd, kv, nrows, hl, part, pre)) { ok = false; break; }
-        __syncthreads();
-        if (wave == 0) {
-          const int nc = chunks_for(kv);
-          for (int i = lane; i < nrows; i += 64) {
-            const int r = r0 + i;
-            P.x_out[r] = P.x_mid[r] + row_value(part, i, nc);
-          }
-          publish(P, lvl + PH_D);
+        if (!poll_level(sy, 0, G, lvl + PH_GU)) { fail(); return; }
+        unsigned long long tk = now_ticks();
+        stage_f16(P.a16, P.F, hl);
+        tk = lap(sy, ST_STAGE, tk);
+        announce_input(ctl, q0 + 3);
+        wait_streams(ctl, q0 + 3);
+        tk = lap(sy, ST_STREAMS, tk);
+        const Geo ge = ctl->geo[K_D];
+        for (int i = lane; i < ge.nrows; i += 64) {
+          const int r = ge.r0 + i;
+          st_dev(&P.x_out[r], ld_dev(&P.x_mid[r]) + row_value(part, ge, i));
         }
+        publish(P, lvl + PH_D);
+        lap(sy, ST_EPI, tk);
       }
     }
-    if (kPrefill || !ok || P.hidden_io) continue;
+    if (!has_lm) continue;
 
     // ---------------- final norm + lm_head + local argmax
-    const unsigned lvl_lm = lv0 + (unsigned)(P.L * PH_PER_LAYER) + 1u;
+    const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
+    const int qlm = t * ngp + 4 * L;
+    const unsigned long long tlm = now_ticks();
     {
-      int p0, p1;
-      block_range(P.V / 2, G, b, p0, p1);
-      const int r0 = 2 * p0, nrows = 2 * (p1 - p0);
-      auto pre = [&]() __attribute__((always_inline)) -> bool {
-        if (!wait_level(sy, 0, G, lvl_lm - 1u)) return false;
-        rmsnorm_to_lds(P.x_out, nullptr, reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl, red);
-        return true;
-      };
-      const u32x4 *wl = reinterpret_cast<const u32x4 *>(P.lm_head) + (size_t)r0 * kv_d;
-      if (!gemv_dispatch(wl, kv_d, nrows, hl, part, pre)) { ok = false; break; }
-      __syncthreads();
-      if (wave == 0) {
-        const int nc = chunks_for(kv_d);
-        float best = -INFINITY;
-        int bi = 0x7fffffff;
-        for (int i = lane; i < nrows; i += 64) {
-          const float y = row_value(part, i, nc);
-          P.logits[r0 + i] = y;
-          if (y > best || (y == best && r0 + i < bi)) { best = y; bi = r0 + i; }
-        }
-        for (int m = 32; m >= 1; m >>= 1) {
-          const float ov = __shfl_xor(best, m, 64);
-          const int oi = __shfl_xor(bi, m, 64);
-          if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-        }
-        if (lane == 0) { P.lm_val[b] = best; P.lm_idx[b] = bi; }
-        publish(P, lvl_lm);
+      if (!poll_level(sy, 0, G, lvl_lm - 1u)) { fail(); return; }
+      stage_rmsnorm(P.x_out, nullptr, nullptr, reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl);
+      announce_input(ctl, qlm);
+      wait_streams(ctl, qlm);
+      const Geo ge = ctl->geo[K_LM];
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int i = lane; i < ge.nrows; i += 64) {
+        const float y = row_value(part, ge, i);
+        st_dev(&P.logits[ge.r0 + i], y);
+        if (y > best || (y == best && ge.r0 + i < bi)) { best = y; bi = ge.r0 + i; }
       }
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(best, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+      }
+      if (lane == 0) {
+        st_dev(&P.lm_val[b], best);
+        st_dev(&P.lm_idx[b], bi);
+      }
+      publish(P, lvl_lm);
     }
 
     // ---------------- next token (workgroup 0)
     if (b == 0) {
-      if (!wait_level(sy, 0, G, lvl_lm)) { ok = false; break; }
       int tok;
       if (P.sampling) {
+        if (!wait_all_waves(sy, 0, G, lvl_lm, true)) { fail(); return; }
         tok = sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds));
       } else {
+        if (!poll_level(sy, 0, G, lvl_lm)) { fail(); return; }
         float best = -INFINITY;
         int bi = 0x7fffffff;
-        for (int i = tid_x(); i < G; i += kThreads) {
-          const float v = P.lm_val[i];
-          const int ix = P.lm_idx[i];
+        for (int i = lane; i < G; i += 64) {
+          const float v = ld_dev(&P.lm_val[i]);
+          const int ix = ld_dev(&P.lm_idx[i]);
           if (v > best || (v == best && ix < bi)) { best = v; bi = ix; }
         }
         for (int m = 32; m >= 1; m >>= 1) {
@@ -877,40 +1188,34 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
           const int oi = __shfl_xor(bi, m, 64);
           if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
         }
-        if (lane == 0) { red[wave] = best; ibc[4 + wave] = bi; }
-        __syncthreads();
-        best = red[0];
-        bi = ibc[4];
-        for (int w = 1; w < kWaves; ++w)
-          if (red[w] > best || (red[w] == best && ibc[4 + w] < bi)) { best = red[w]; bi = ibc[4 + w]; }
-        __syncthreads();
         tok = bi;
       }
       if (tok < 0 || tok >= P.V) {   // never expected; keeps the next embedding read in bounds
-        if (tid_x() == 0) __hip_atomic_store(&P.err[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) st_dev(&P.err[3], 1u);
         tok = 0;
       }
-      if (wave == 0) {
-        if (lane == 0) {
-          *P.tok_slot = tok;
-          P.out_tokens[t] = tok;
-        }
-        publish(P, lvl_lm + 1u);
+      if (lane == 0) {
+        st_dev(P.tok_slot, tok);
+        P.out_tokens[t] = tok;
       }
+      publish(P, lvl_lm + 1u);
     }
+    lap(sy, ST_LM, tlm);
   }
-  if ((P.flags & 4u) && tid_x() == 0) {
+  if ((P.flags & 4u) && lane == 0) {
     unsigned xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    P.stats[b * 4 + 0] = sy.spin;
-    P.stats[b * 4 + 1] = sy.waits;
-    P.stats[b * 4 + 2] = xcc & 0xfu;
-    P.stats[b * 4 + 3] = now_ticks() - kt0;
+    unsigned long long *o = P.stats + (size_t)b * kStatWords;
+    o[0] = sy.spin;
+    o[1] = sy.waits;
+    o[2] = xcc & 0xfu;
+    o[3] = now_ticks() - kt0;
+    for (int k = 0; k < kStatPhases; ++k) o[4 + k] = sy.tm[k];
   }
 }
 
 __global__ void lf_test_expdef_kernel(const float *x, float *y, long long n) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + tid_x(); i < n; i += (long long)gridDim.x * blockDim.x)
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
     y[i] = expdef(x[i]);
 }
 
@@ -920,7 +1225,7 @@ __global__ void __launch_bounds__(kThreads) lf_test_sample_kernel(const float *l
   __shared__ SampLds s;
   const int c = blockIdx.x;
   const int tok = sample_topp(logits + (size_t)c * n, n, inv_temp, top_p, seed, pos[c], &s);
-  if (tid_x() == 0) tokens[c] = tok;
+  if (threadIdx.x == 0) tokens[c] = tok;
 }
 
 }  // namespace
@@ -932,6 +1237,9 @@ const void *monokernel_symbol(bool prefill) {
 
 hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream) {
   void *args[] = {const_cast<Params *>(&p)};
+  if (p.plain_launch)
+    return hipLaunchKernel(monokernel_symbol(prefill), dim3(p.G), dim3(kThreads), args, (size_t)p.lds_bytes,
+                           stream);
   return hipLaunchCooperativeKernel(monokernel_symbol(prefill), dim3(p.G), dim3(kThreads), args,
                                     (unsigned)p.lds_bytes, stream);
 }

@@ -195,7 +195,7 @@ class Engine:
         return x
 
     def stats(self) -> np.ndarray:
-        out = np.zeros((self.grid, 4), dtype=np.uint64)
+        out = np.zeros((self.grid, 16), dtype=np.uint64)
         _check(lib().lf_get_stats(self._st, out.ctypes.data, out.nbytes), self._st)
         return out
 
