@@ -44,6 +44,8 @@ struct lf_state {
   lf::Params P{};
   std::vector<void *> allocs;
   int out_cap = 0, in_cap = 0;
+  void *xbuf = nullptr;        // tagged exchange words (cleared whenever the level numbering restarts)
+  size_t xbuf_bytes = 0;
   unsigned level_base = 0;
   int pending_token = -1, pending_pos = 0;
   bool has_pending = false;
@@ -93,15 +95,25 @@ hipError_t copy_rows_strided(void *dst, size_t dpitch, const void *src, size_t s
   return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToDevice, s);
 }
 
+// Restart the level numbering: progress words, split-K tickets and every tagged
+// exchange word go back to zero (no level is ever zero), level_base to 0.
+hipError_t reset_levels(lf_state *st) {
+  const lf::Params &P = st->P;
+  hipError_t e;
+  if ((e = hipMemsetAsync(P.progress, 0, sizeof(unsigned) * P.G, st->stream)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(P.tickets, 0, sizeof(unsigned) * P.L * P.Hkv, st->stream)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(st->xbuf, 0, st->xbuf_bytes, st->stream)) != hipSuccess) return e;
+  st->level_base = 0;
+  return hipSuccess;
+}
+
 int do_launch(lf_state *st, int token0, int pos0, int n, std::vector<int> *out, bool prefill = false) {
   lf::Params &P = st->P;
   P.levels_per_token = lf::PH_PER_LAYER * P.L + ((P.hidden_io || prefill) ? 0 : 2);
   const unsigned need = (unsigned)(n + 1) * (unsigned)P.levels_per_token;
   hipError_t e;
   if ((unsigned long long)st->level_base + need >= 0x7fffffffull) {
-    if ((e = hipMemsetAsync(P.progress, 0, sizeof(unsigned) * P.G, st->stream)) != hipSuccess)
-      return hip_fail(st, e, "reset progress");
-    st->level_base = 0;
+    if ((e = reset_levels(st)) != hipSuccess) return hip_fail(st, e, "reset levels");
   }
   P.n_tokens = n;
   P.token0 = token0;
@@ -116,10 +128,8 @@ int do_launch(lf_state *st, int token0, int pos0, int n, std::vector<int> *out, 
     return hip_fail(st, e, "read error word");
   if (herr[0]) {
     // a bounded wait expired: the grid drained; restart the level numbering
-    (void)hipMemsetAsync(P.progress, 0, sizeof(unsigned) * P.G, st->stream);
-    (void)hipMemsetAsync(P.tickets, 0, sizeof(unsigned) * P.L * P.Hkv, st->stream);
+    (void)reset_levels(st);
     (void)hipStreamSynchronize(st->stream);
-    st->level_base = 0;
     char buf[160];
     std::snprintf(buf, sizeof buf, "in-kernel wait timed out (workgroup %u, level %u)", herr[1], herr[2]);
     return fail(&st->err, LF_ETIMEOUT, buf);
@@ -291,18 +301,15 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   int smax = G / Hkv;
   if (smax > lf::kMaxSplit) smax = lf::kMaxSplit;
   if (smax < 1) smax = 1;
-  const size_t units_max = (size_t)Hkv * smax;
-  const size_t f_part = units_max * P.qpg * (dh + 2);
-  // one arena for the small buffers, each 256-byte aligned
+  const size_t part_gen = (size_t)Hkv * smax * P.qpg * (dh + 2);
+  // small buffers, each 256-byte aligned, in one arena
   struct Slot { void **dst; size_t bytes; };
-  void *x_hidden, *x_mid, *x_out, *q, *attn_part, *o16, *a16, *logits, *lm_val, *lm_idx, *progress, *tickets,
-      *tok_slot, *errw, *stats;
+  void *x_hidden, *x_out, *logits, *lm_val, *lm_idx, *progress, *tickets, *tok_slot, *errw, *stats;
   Slot slots[] = {
-      {&x_hidden, (size_t)d * 4}, {&x_mid, (size_t)d * 4}, {&x_out, (size_t)d * 4},
-      {&q, (size_t)Hq * dh * 4}, {&attn_part, f_part * 4}, {&o16, (size_t)Hq * dh * 2},
-      {&a16, (size_t)F * 2}, {&logits, (size_t)(V > 0 ? V : 1) * 4}, {&lm_val, (size_t)G * 4},
-      {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4}, {&tickets, (size_t)c.n_layers * Hkv * 4},
-      {&tok_slot, 16}, {&errw, 16}, {&stats, (size_t)G * lf::kStatWords * 8}};
+      {&x_hidden, (size_t)d * 4}, {&x_out, (size_t)d * 4}, {&logits, (size_t)(V > 0 ? V : 1) * 4},
+      {&lm_val, (size_t)G * 4}, {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4},
+      {&tickets, (size_t)c.n_layers * Hkv * 4}, {&tok_slot, 16}, {&errw, 16},
+      {&stats, (size_t)G * lf::kStatWords * 8}};
   size_t arena = 0;
   for (auto &sl : slots) arena += align_up(sl.bytes, 256);
   char *ar = (char *)dev_alloc(st, arena, &e);
@@ -310,11 +317,27 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   (void)hipMemsetAsync(ar, 0, arena, s);
   size_t off = 0;
   for (auto &sl : slots) { *sl.dst = ar + off; off += align_up(sl.bytes, 256); }
-  P.x_hidden = (float *)x_hidden; P.x_mid = (float *)x_mid; P.x_out = (float *)x_out; P.q = (float *)q;
-  P.attn_part = (float *)attn_part; P.o16 = o16; P.a16 = a16; P.logits = (float *)logits;
+  P.x_hidden = (float *)x_hidden; P.x_out = (float *)x_out; P.logits = (float *)logits;
   P.lm_val = (float *)lm_val; P.lm_idx = (int *)lm_idx; P.progress = (unsigned *)progress;
   P.tickets = (unsigned *)tickets; P.tok_slot = (int *)tok_slot; P.err = (unsigned *)errw;
   P.stats = (unsigned long long *)stats;
+  // tagged exchange words, two generations each, in one zeroed allocation
+  {
+    struct TSlot { unsigned long long **dst; size_t words; };
+    TSlot ts[] = {{&P.xmid_t, (size_t)d}, {&P.xout_t, (size_t)d}, {&P.q_t, (size_t)Hq * dh},
+                  {&P.kc_t, (size_t)Hkv * dh / 2}, {&P.vc_t, (size_t)Hkv * dh / 2}, {&P.part_t, part_gen},
+                  {&P.o_t, (size_t)Hq * dh / 2}, {&P.a_t, (size_t)F / 2}};
+    size_t bytes = 0;
+    for (auto &t : ts) bytes += align_up(2 * t.words * 8, 256);
+    char *xb = (char *)dev_alloc(st, bytes, &e);
+    if (!xb) return bail(fail(&st->err, LF_ENOMEM, "exchange buffer allocation failed"));
+    (void)hipMemsetAsync(xb, 0, bytes, s);
+    size_t o2 = 0;
+    for (auto &t : ts) { *t.dst = (unsigned long long *)(xb + o2); o2 += align_up(2 * t.words * 8, 256); }
+    P.part_gen = part_gen;
+    st->xbuf = xb;
+    st->xbuf_bytes = bytes;
+  }
   st->out_cap = 1;
   P.out_tokens = (int *)dev_alloc(st, sizeof(int) * 1, &e);
   st->in_cap = 1;
@@ -324,9 +347,10 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   // ---- LDS layout: [h | part] (also attention / sampler scratch), red, ctl, rings
   int rows_max = 0;
   {
-    const int pairs[5] = {P.nqkv / 2, d / 2, F, d / 2, hidden ? 0 : V / 2};
+    const int units[5] = {P.nqkv / 2, d / 2, F / 2, d / 2, hidden ? 0 : V / 2};
+    const int upr[5] = {2, 2, 4, 2, 2};   // rows per partition unit
     for (int k = 0; k < 5; ++k) {
-      const int r = 2 * ((pairs[k] + G - 1) / G);
+      const int r = upr[k] * ((units[k] + G - 1) / G);
       rows_max = r > rows_max ? r : rows_max;
     }
   }
@@ -335,17 +359,19 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (F > hmax) hmax = F;
   const size_t h_b = align_up((size_t)hmax * 2 + 1024, 16);   // + one piece of slack for masked lanes
   const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);
-  const size_t attn_b = (size_t)P.qpg * dh * 4 + (size_t)P.qpg * lf::kAttnBlock * 4 +
-                        (size_t)lf::kWaves * P.qpg * dh * 4;
+  const size_t attn_sc = (size_t)P.qpg * lf::kAttnBlock * 4, attn_or = (size_t)lf::kWaves * P.qpg * dh * 4;
+  const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (attn_sc > attn_or ? attn_sc : attn_or);
   const size_t samp_b = 4096;
   size_t region_a = h_b + part_b;
+  if ((size_t)d * 4 > region_a) region_a = (size_t)d * 4;   // fp32 staging of a layer input
   if (attn_b > region_a) region_a = attn_b;
   if (samp_b > region_a) region_a = samp_b;
   P.lds_h = 0;
   P.lds_part = (int)h_b;
   P.lds_red = (int)align_up(region_a, 256);
   P.lds_ctl = P.lds_red + 256;
-  P.lds_ring = P.lds_ctl + 256;
+  P.lds_xown = P.lds_ctl + 256;
+  P.lds_ring = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
   P.part_rows = rows_max;
   P.hmax = hmax;
   int lds_limit = 0;
@@ -355,8 +381,8 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (P.lds_ring + rings > lds_limit)
     return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
   P.lds_bytes = P.lds_ring + rings;
-  P.fenced = (std::getenv("LF_FENCED") && std::atoi(std::getenv("LF_FENCED")) != 0) ? 1 : 0;
   P.plain_launch = (std::getenv("LF_PLAIN_LAUNCH") && std::atoi(std::getenv("LF_PLAIN_LAUNCH")) != 0) ? 1 : 0;
+  P.poll_first = (std::getenv("LF_POLL_FIRST") && std::atoi(std::getenv("LF_POLL_FIRST")) != 0) ? 1 : 0;
   for (int pf = 0; pf < 2; ++pf) {
     if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  P.lds_bytes)) != hipSuccess)

@@ -12,7 +12,10 @@ constexpr int kAttnBlock = 512;        // key positions scored per attention sub
 constexpr int kMinKeysPerUnit = 16;    // smallest attention split-K chunk
 constexpr int kMaxSplit = 64;          // most split-K chunks per KV head
 constexpr int kStatWords = 16;         // uint64 statistics per workgroup (LF_STATS)
-constexpr int kRingSlots = 16;         // 1-KB slots of each stream wave's LDS ring
+#ifndef LF_RING_SLOTS
+#define LF_RING_SLOTS 16
+#endif
+constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB slots of each stream wave's LDS ring
 
 // Phases of one layer; each completes one "level" of the dependency chain.
 enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYER = 5 };
@@ -40,11 +43,19 @@ struct Params {
   // state
   void *kcache, *vcache;   // fp16 [L][max_seq][Hkv][dh]
   const float *rope;       // [max_seq][dh/2][2] (cos, sin)
-  float *x_hidden, *x_mid, *x_out;   // fp32 [d]
-  float *q;                // fp32 [Hq*dh] post-rotary queries
-  float *attn_part;        // fp32 [units][qpg][dh+2] split-K partials (m, l, o)
-  void *o16;               // fp16 [Hq*dh] merged attention output
-  void *a16;               // fp16 [F] SwiGLU output
+  float *x_hidden;         // fp32 [d] layer-0 input (LF_HIDDEN_IO, written by the host)
+  float *x_out;            // fp32 [d] residual after the last layer (LF_HIDDEN_IO, read by the host)
+  // Exchange words between workgroups: {payload in bits 0..31, level tag in
+  // bits 32..63}, two generations selected by layer parity.  A consumer accepts
+  // a word only when its tag is the level it waits for.
+  unsigned long long *xmid_t, *xout_t;   // [2][d] fp32 residual after O / after down
+  unsigned long long *q_t;               // [2][Hq*dh] fp32 post-rotary queries
+  unsigned long long *kc_t, *vc_t;       // [2][Hkv*dh/2] fp16 pairs of the current K row
+                                         //   (dims i, i+dh/2) and V row (dims 2j, 2j+1)
+  unsigned long long *part_t;            // [2][part_gen] split-K partials (m, l, o[dh])
+  unsigned long long *o_t;               // [2][Hq*dh/2] fp16 pairs of the merged attention output
+  unsigned long long *a_t;               // [2][F/2] fp16 pairs of the SwiGLU output
+  unsigned long long part_gen;           // words per generation of part_t
   float *logits;           // fp32 [V]
   float *lm_val;           // [G] per-workgroup max logit
   int *lm_idx;             // [G] its index
@@ -59,10 +70,10 @@ struct Params {
   int n_tokens, token0, pos0;
   unsigned level_base;
   unsigned long long timeout_ticks;
-  int fenced;              // 1: agent-scope acquire/release fences around every level
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
+  int poll_first;          // 1: poll the producers' progress words before reading tagged data
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_ctl, lds_ring, lds_bytes;
+  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_ring, lds_bytes;
   int part_rows, hmax;
 };
 

@@ -155,6 +155,26 @@ __device__ __forceinline__ void st_dev_h(void *base, size_t i, float v) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Tagged exchange words: payload in bits 0..31, level tag in bits 32..63.  An
+// aligned 8-byte store / load is single-copy atomic, so a word whose tag is the
+// awaited level carries that level's payload: no fence or store acknowledgement
+// is needed between producing data and announcing it.
+typedef unsigned long long u64;
+__device__ __forceinline__ u64 tag_f(float v, unsigned tag) {
+  return (u64)__float_as_uint(v) | ((u64)tag << 32);
+}
+__device__ __forceinline__ u64 tag_h2(float a, float b, unsigned tag) {
+  f16x2 h;
+  h.x = (_Float16)a;
+  h.y = (_Float16)b;
+  return (u64)__builtin_bit_cast(unsigned, h) | ((u64)tag << 32);
+}
+__device__ __forceinline__ unsigned tag_of(u64 w) { return (unsigned)(w >> 32); }
+__device__ __forceinline__ float pay_f(u64 w) { return __uint_as_float((unsigned)w); }
+__device__ __forceinline__ void st_tag(u64 *p, u64 w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // LDS words shared between the waves of one workgroup.
 __device__ __forceinline__ unsigned lds_ld(const unsigned *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -191,6 +211,7 @@ struct Sync {
   unsigned long long spin;    // ticks spent polling other workgroups
   unsigned long long waits;
   unsigned long long tm[kStatPhases];   // sync-wave time by activity (LF_STATS)
+  unsigned long long rt_sum, rt_n, nfetch;   // tagged-read rounds: total ticks, count; fetches
 };
 
 // Add the ticks since t0 to activity k; returns the current tick.
@@ -200,52 +221,62 @@ __device__ __forceinline__ unsigned long long lap(Sync &s, int k, unsigned long 
   return t1;
 }
 
+// The bound of a wait started at t0 has expired: record the first such event in
+// the error word (any lane may call; one wins).  Also true once another
+// workgroup has recorded an error.
+__device__ __forceinline__ bool expired(const Params &P, unsigned long long t0, unsigned level) {
+  if (now_ticks() - t0 <= P.timeout_ticks) return ld_dev(&P.err[0]) != 0u;
+  unsigned zero = 0u;
+  if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    st_dev(&P.err[1], (unsigned)blockIdx.x);
+    st_dev(&P.err[2], level);
+  }
+  return true;
+}
+
 // Wave 0 only: poll progress[first .. first+count) >= level.  Returns false when
 // the bound expired or another workgroup reported an error.
 __device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsigned level) {
   const Params &P = *s.P;
   const unsigned long long t0 = now_ticks();
   bool ok = false;
-  unsigned it = 0;
   for (;;) {
     unsigned mn = 0xffffffffu;
     for (int i = lane_id(); i < count; i += 64) mn = min(mn, ld_dev(&P.progress[first + i]));
     mn = wave_min_u32(mn);
     if (mn >= level) { ok = true; break; }
-    if ((++it & 15u) == 0 && ld_dev(&P.err[0]) != 0u) break;
-    if (now_ticks() - t0 > P.timeout_ticks) {
-      if (lane_id() == 0) {
-        unsigned zero = 0u;
-        if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)) {
-          st_dev(&P.err[1], (unsigned)blockIdx.x);
-          st_dev(&P.err[2], level);
-        }
-      }
-      break;
-    }
+    if (expired(P, t0, level)) break;
   }
-  if (ok && P.fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   s.spin += now_ticks() - t0;
   s.waits += 1;
   return ok;
 }
 
-// Wave 0 only: publish `level` after wave 0's own stores of the level's data.
-__device__ __forceinline__ void publish(const Params &P, unsigned level) {
-  if (P.fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __builtin_amdgcn_s_waitcnt(0);        // every store of this wave has completed
+// Wave 0 only: announce `level` for this workgroup.  The level's data are tagged
+// words, so the announcement need not wait for them to land: a consumer that
+// sees the progress word early re-reads until the tags match.
+__device__ __forceinline__ void publish_fast(const Params &P, unsigned level) {
+  if (lane_id() == 0) st_dev(&P.progress[blockIdx.x], level);
+}
+
+// Wave 0 only: announce `level` after every store of this wave has completed
+// (for the untagged data of the lm_head and token levels).
+__device__ __forceinline__ void publish_sync(const Params &P, unsigned level) {
+  __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" ::: "memory");
   if (lane_id() == 0) st_dev(&P.progress[blockIdx.x], level);
 }
 
 // All waves: barrier-based wait (wave 0 polls).  Used where the whole workgroup
-// works together (attention, nucleus sampling).
+// works together (attention, nucleus sampling).  With `acquire`, wave 0 takes an
+// agent-scope acquire fence so the workgroup may read untagged data with plain
+// loads.
 __device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, unsigned level,
                                                bool acquire = false) {
   if (wave_id() == 0) {
     const bool ok = poll_level(s, first, count, level);
-    if (ok && acquire && !s.P->fenced) {
+    if (ok && acquire) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __builtin_amdgcn_s_waitcnt(0);
     }
@@ -261,86 +292,119 @@ __device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, un
 
 constexpr int kStageBatch = 32;   // 8-byte loads in flight per lane while staging
 
-// Two consecutive elements of the layer input: fp32 written by other workgroups
-// (device-scope load), fp32 from the host, or an fp16 embedding row.
-__device__ __forceinline__ unsigned long long load_pair_bits(const float *x_dev, const float *x_host,
-                                                             const _Float16 *x16, int i) {
-  if (x_dev) return ld_dev(reinterpret_cast<const unsigned long long *>(x_dev + i));
-  float a, b;
-  if (x_host) {
-    a = x_host[i];
-    b = x_host[i + 1];
-  } else {
-    const f16x2 v = *reinterpret_cast<const f16x2 *>(x16 + i);
-    a = (float)v.x;
-    b = (float)v.y;
+// Wave 0: wait until every word src[0..n) carries `tag`, then hand each payload
+// to use(i, word).  All loads of a batch are issued before any is checked, so a
+// batch costs one memory round trip; a batch with a stale word is re-read.
+template <class F>
+__device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, unsigned tag, F &&use) {
+  const Params &P = *s.P;
+  const int lane = lane_id();
+  if (P.poll_first && !poll_level(s, 0, P.G, tag)) return false;
+  const unsigned long long t0 = now_ticks();
+  s.nfetch += 1;
+  for (int base = 0; base < n; base += 64 * kStageBatch) {
+    for (;;) {
+      const unsigned long long tr = now_ticks();
+      u64 v[kStageBatch];
+#pragma unroll
+      for (int j = 0; j < kStageBatch; ++j) {
+        const int i = base + 64 * j + lane;
+        v[j] = i < n ? ld_dev(src + i) : ((u64)tag << 32);
+      }
+      unsigned bad = 0u;
+#pragma unroll
+      for (int j = 0; j < kStageBatch; ++j) bad |= (unsigned)(tag_of(v[j]) != tag);
+      const unsigned ok = wave_min_u32(1u - bad);
+      s.rt_sum += now_ticks() - tr;
+      s.rt_n += 1;
+      if (ok == 1u) {
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j) {
+          const int i = base + 64 * j + lane;
+          if (i < n) use(i, v[j]);
+        }
+        break;
+      }
+      if (expired(P, t0, tag)) return false;
+    }
   }
-  return (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  return true;
 }
 
-// h = fp16(g * (x / sqrt(mean(x^2) + eps))) into LDS (wave 0).  Every load of a
-// batch is issued before the first is used, so a batch costs one memory round
-// trip (d <= 4096: one batch per pass).
-__device__ __forceinline__ void stage_rmsnorm(const float *x_dev, const float *x_host, const _Float16 *x16,
-                                              const _Float16 *g, int d, float eps, _Float16 *h) {
+// In-place second pass of RMSNorm: xs (fp32 staged in LDS at h's address) ->
+// h = fp16(g * (x / r)).  Iteration k reads fp32 elements [128k, 128k+128) and
+// then writes fp16 elements of the same range, which occupy bytes already read.
+__device__ __forceinline__ void normalize_in_place(const _Float16 *g, int d, float r, _Float16 *h) {
+  const float *xs = reinterpret_cast<const float *>(h);
+  for (int base = 0; base < d; base += 128) {
+    const int i = base + 2 * lane_id();
+    float a = 0.0f, b = 0.0f;
+    if (i < d) {
+      a = xs[i];
+      b = xs[i + 1];
+    }
+    lds_drain();
+    if (i < d) {
+      const f16x2 gg = *reinterpret_cast<const f16x2 *>(g + i);
+      f16x2 o;
+      o.x = (_Float16)((float)gg.x * (a / r));
+      o.y = (_Float16)((float)gg.y * (b / r));
+      *reinterpret_cast<f16x2 *>(h + i) = o;
+    }
+    lds_drain();
+  }
+}
+
+// RMSNorm of a residual published by other workgroups as tagged fp32 words.
+__device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, unsigned tag, const _Float16 *g,
+                                                     int d, float eps, _Float16 *h) {
+  float *xs = reinterpret_cast<float *>(h);
+  float ss = 0.0f;
+  if (!fetch_tagged(s, src, d, tag, [&](int i, u64 w) __attribute__((always_inline)) {
+        const float x = pay_f(w);
+        ss += x * x;
+        xs[i] = x;
+      }))
+    return false;
+  ss = wave_sum(ss);
+  lds_drain();
+  normalize_in_place(g, d, sqrtf(ss / (float)d + eps), h);
+  return true;
+}
+
+// RMSNorm of a layer-0 input: an fp16 embedding row or the host's fp32 vector.
+__device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _Float16 *x16, const _Float16 *g,
+                                                    int d, float eps, _Float16 *h) {
+  float *xs = reinterpret_cast<float *>(h);
   const int lane = lane_id();
   float ss = 0.0f;
-  for (int base = 0; base < d; base += 128 * kStageBatch) {
-    unsigned long long v[kStageBatch];
+  for (int base = 0; base < d; base += 64 * kStageBatch) {
+    float v[kStageBatch];
 #pragma unroll
     for (int j = 0; j < kStageBatch; ++j) {
-      const int i = base + 128 * j + 2 * lane;
-      v[j] = i < d ? load_pair_bits(x_dev, x_host, x16, i) : 0ull;
+      const int i = base + 64 * j + lane;
+      v[j] = i < d ? (x_host ? x_host[i] : (float)x16[i]) : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < kStageBatch; ++j) {
-      const float a = __uint_as_float((unsigned)v[j]), b = __uint_as_float((unsigned)(v[j] >> 32));
-      ss += a * a + b * b;
-    }
-  }
-  ss = wave_sum(ss);
-  const float r = sqrtf(ss / (float)d + eps);
-  for (int base = 0; base < d; base += 128 * kStageBatch) {
-    unsigned long long v[kStageBatch];
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int i = base + 128 * j + 2 * lane;
-      v[j] = i < d ? load_pair_bits(x_dev, x_host, x16, i) : 0ull;
-    }
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int i = base + 128 * j + 2 * lane;
+      const int i = base + 64 * j + lane;
       if (i < d) {
-        const float a = __uint_as_float((unsigned)v[j]), b = __uint_as_float((unsigned)(v[j] >> 32));
-        const f16x2 gg = *reinterpret_cast<const f16x2 *>(g + i);
-        f16x2 o;
-        o.x = (_Float16)((float)gg.x * (a / r));
-        o.y = (_Float16)((float)gg.y * (b / r));
-        *reinterpret_cast<f16x2 *>(h + i) = o;
+        ss += v[j] * v[j];
+        xs[i] = v[j];
       }
     }
   }
+  ss = wave_sum(ss);
+  lds_drain();
+  normalize_in_place(g, d, sqrtf(ss / (float)d + eps), h);
 }
 
-// Copy an fp16 vector written by other workgroups (n % 4 == 0) into LDS (wave 0),
-// one batch of loads per 8192 elements.
-__device__ __forceinline__ void stage_f16(const void *src, int n, _Float16 *h) {
-  const unsigned long long *s = reinterpret_cast<const unsigned long long *>(src);
-  unsigned long long *dst = reinterpret_cast<unsigned long long *>(h);
-  const int n4 = n / 4, lane = lane_id();
-  for (int base = 0; base < n4; base += 64 * kStageBatch) {
-    unsigned long long v[kStageBatch];
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int i = base + 64 * j + lane;
-      v[j] = i < n4 ? ld_dev(s + i) : 0ull;
-    }
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int i = base + 64 * j + lane;
-      if (i < n4) dst[i] = v[j];
-    }
-  }
+// A vector published as tagged fp16 pairs (n_pairs words) into LDS h.
+__device__ __forceinline__ bool stage_pairs_tagged(Sync &s, const u64 *src, int n_pairs, unsigned tag,
+                                                   _Float16 *h) {
+  unsigned *dst = reinterpret_cast<unsigned *>(h);
+  return fetch_tagged(s, src, n_pairs, tag,
+                      [&](int i, u64 w) __attribute__((always_inline)) { dst[i] = (unsigned)w; });
 }
 
 // ---------------------------------------------------------------- stream waves
@@ -523,26 +587,69 @@ __device__ __forceinline__ void attn_split(int n, int G, int Hkv, int &S, int &L
   Lc = (n + S - 1) / S;
 }
 
-// One split-K unit (KV head g, key chunk c) of layer l at position pos: partial
-// (m, l, o) for the qpg query heads of group g, written to attn_part; the last
-// unit of the group to arrive merges all partials into o16 (wave 0).  These are
-// the pages' three attention stages ("The fused operations, briefly"): per-unit
-// attention over a tile of the cache, cross-unit softmax correction, then the
-// output projection (the next phase).
-__device__ __forceinline__ void attn_unit(const Params &P, int l, int pos, int u, int S, int Lc, unsigned char *lds,
+// Wait for one tagged word; on expiry returns it anyway and sets *bad.
+__device__ __forceinline__ u64 ld_tag_wait(const Params &P, const u64 *p, unsigned tag, unsigned long long t0,
+                                           bool &bad) {
+  u64 w = ld_dev(p);
+  while (tag_of(w) != tag) {
+    if (expired(P, t0, tag)) {
+      bad = true;
+      break;
+    }
+    w = ld_dev(p);
+  }
+  return w;
+}
+
+// One split-K unit (KV head g, key chunk c) of layer l at position pos, all
+// waves: partial (m, l, o) for the qpg query heads of group g; the last unit of
+// the group to arrive merges all partials into o_t.  These are the pages' three
+// attention stages ("The fused operations, briefly"): attention over a tile of
+// the cache per unit, cross-unit softmax correction, then the output projection
+// (the next phase).  Queries, the current position's K/V row and the partials
+// arrive as tagged words; earlier cache rows were written in earlier steps.
+// Returns false if a bounded wait expired.
+__device__ __forceinline__ bool attn_unit(const Params &P, Ctl *ctl, int l, int gen, unsigned tag_q,
+                                          unsigned tag_a, int pos, int u, int S, int Lc, unsigned char *lds,
                                           float *red) {
   const int tid = tid_x(), wave = wave_id(), lane = lane_id();
   const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv;
-  const int dpl = dh / 64;
+  const int dpl = dh / 64, half = dh / 2;
   const int g = u / S, c = u - g * S;
   const int n = pos + 1;
   const int j0 = c * Lc;
   const int j1 = min(n, j0 + Lc);
-  float *qs = reinterpret_cast<float *>(lds);      // [qpg][dh]
-  float *sc = qs + qpg * dh;                        // [qpg][kAttnBlock]
-  float *ored = sc + qpg * kAttnBlock;              // [kWaves][qpg][dh]
-  for (int i = tid; i < qpg * dh; i += kThreads) qs[i] = ld_dev(&P.q[(size_t)g * qpg * dh + i]);
+  const bool has_cur = j1 == n && j0 < j1;           // this chunk holds the current position
+  float *qs = reinterpret_cast<float *>(lds);       // [qpg][dh]
+  float *kcur = qs + qpg * dh;                       // [dh]
+  float *vcur = kcur + dh;                           // [dh]
+  float *sc = vcur + dh;                             // [qpg][kAttnBlock] scores, then
+  float *ored = sc;                                  // [kWaves][qpg][dh] after the last block
+  const unsigned long long t0 = now_ticks();
+  bool bad = false;
+  __syncthreads();   // wave 0 may still be reading the phase scratch this unit reuses
+  {
+    const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)g * qpg * dh;
+    for (int i = tid; i < qpg * dh; i += kThreads) qs[i] = pay_f(ld_tag_wait(P, qsrc + i, tag_q, t0, bad));
+    if (has_cur && tid < dh) {
+      const size_t nw = (size_t)Hkv * half;
+      if (tid < half) {
+        const u64 w = ld_tag_wait(P, P.kc_t + gen * nw + (size_t)g * half + tid, tag_q, t0, bad);
+        const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w);
+        kcur[tid] = (float)hv.x;
+        kcur[tid + half] = (float)hv.y;
+      } else {
+        const int jv = tid - half;
+        const u64 w = ld_tag_wait(P, P.vc_t + gen * nw + (size_t)g * half + jv, tag_q, t0, bad);
+        const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w);
+        vcur[2 * jv] = (float)hv.x;
+        vcur[2 * jv + 1] = (float)hv.y;
+      }
+    }
+    if (bad) lds_st(&ctl->abort, 1u);
+  }
   __syncthreads();
+  if (lds_ld(&ctl->abort)) return false;
   const size_t lstride = (size_t)P.max_seq * Hkv * dh;
   const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride;
   const _Float16 *Vl = reinterpret_cast<const _Float16 *>(P.vcache) + (size_t)l * lstride;
@@ -557,18 +664,28 @@ __device__ __forceinline__ void attn_unit(const Params &P, int l, int pos, int u
   for (int sb = j0; sb < j1; sb += kAttnBlock) {
     const int nb = min(kAttnBlock, j1 - sb);
     if (tid < nb) {
-      const u32x4 *kr = reinterpret_cast<const u32x4 *>(Kl + ((size_t)(sb + tid) * Hkv + g) * dh);
+      const int j = sb + tid;
       float s[kMaxQpg];
 #pragma unroll
       for (int h = 0; h < kMaxQpg; ++h) s[h] = 0.0f;
-      for (int e8 = 0; e8 < dh / 8; ++e8) {
-        const f16x8 kv = __builtin_bit_cast(f16x8, kr[e8]);
+      if (j == pos) {
+        for (int e = 0; e < dh; ++e) {
+          const float kv = kcur[e];
 #pragma unroll
-        for (int h = 0; h < kMaxQpg; ++h) {
-          if (h < qpg) {
-            const float *qh = qs + h * dh + e8 * 8;
+          for (int h = 0; h < kMaxQpg; ++h)
+            if (h < qpg) s[h] += qs[h * dh + e] * kv;
+        }
+      } else {
+        const u32x4 *kr = reinterpret_cast<const u32x4 *>(Kl + ((size_t)j * Hkv + g) * dh);
+        for (int e8 = 0; e8 < dh / 8; ++e8) {
+          const f16x8 kv = __builtin_bit_cast(f16x8, kr[e8]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s[h] += qh[i] * (float)kv[i];
+          for (int h = 0; h < kMaxQpg; ++h) {
+            if (h < qpg) {
+              const float *qh = qs + h * dh + e8 * 8;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) s[h] += qh[i] * (float)kv[i];
+            }
           }
         }
       }
@@ -624,14 +741,20 @@ __device__ __forceinline__ void attn_unit(const Params &P, int l, int pos, int u
       m_run[h] = m_new[h];
     }
     for (int jj = wave; jj < nb; jj += kWaves) {
-      const _Float16 *vr = Vl + ((size_t)(sb + jj) * Hkv + g) * dh + lane * dpl;
+      const int j = sb + jj;
       float v0, v1 = 0.0f;
-      if (dpl == 2) {
-        const f16x2 vv = *reinterpret_cast<const f16x2 *>(vr);
-        v0 = (float)vv.x;
-        v1 = (float)vv.y;
+      if (j == pos) {
+        v0 = vcur[lane * dpl];
+        if (dpl == 2) v1 = vcur[lane * dpl + 1];
       } else {
-        v0 = (float)vr[0];
+        const _Float16 *vr = Vl + ((size_t)j * Hkv + g) * dh + lane * dpl;
+        if (dpl == 2) {
+          const f16x2 vv = *reinterpret_cast<const f16x2 *>(vr);
+          v0 = (float)vv.x;
+          v1 = (float)vv.y;
+        } else {
+          v0 = (float)vr[0];
+        }
       }
 #pragma unroll
       for (int h = 0; h < kMaxQpg; ++h) {
@@ -654,70 +777,80 @@ __device__ __forceinline__ void attn_unit(const Params &P, int l, int pos, int u
   __syncthreads();
   if (wave == 0) {
     const int stride = dh + 2;
-    float *dst = P.attn_part + (size_t)u * qpg * stride;
+    u64 *pg = P.part_t + (size_t)gen * P.part_gen;
+    u64 *dst = pg + (size_t)u * qpg * stride;
     for (int h = 0; h < qpg; ++h) {
       for (int e = lane; e < dh; e += 64) {
         float o = 0.0f;
         for (int w = 0; w < kWaves; ++w) o += ored[(w * qpg + h) * dh + e];
-        st_dev(&dst[h * stride + 2 + e], o);
+        st_tag(&dst[h * stride + 2 + e], tag_f(o, tag_a));
       }
       if (lane == 0) {
-        st_dev(&dst[h * stride + 0], m_run[h]);
-        st_dev(&dst[h * stride + 1], l_run[h]);
+        st_tag(&dst[h * stride + 0], tag_f(m_run[h], tag_a));
+        st_tag(&dst[h * stride + 1], tag_f(l_run[h], tag_a));
       }
     }
     // Arrival ticket of group g: the unit that completes the count merges.
-    if (P.fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __builtin_amdgcn_s_waitcnt(0);
-    asm volatile("" ::: "memory");
     unsigned old = 0;
     if (lane == 0)
       old = __hip_atomic_fetch_add(&P.tickets[l * Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0, 64);
     if (old == (unsigned)(S - 1)) {
-      if (P.fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      const float *src = P.attn_part + (size_t)g * S * qpg * stride;
+      const u64 *src = pg + (size_t)g * S * qpg * stride;
       float *wgt = red;   // merge weights e^(m_c - M), one per chunk (S <= kMaxSplit = 64)
+      const int e0 = 2 * lane;
       for (int h = 0; h < qpg; ++h) {
-        // chunk statistics: lanes over chunks, 64 at a time
-        float M = -INFINITY;
-        for (int c0 = 0; c0 < S; c0 += 64) {
-          const int cc = c0 + lane;
-          const float m = cc < S ? ld_dev(&src[(cc * qpg + h) * stride + 0]) : -INFINITY;
-          M = fmaxf(M, wave_max(m));
+        // one batch: this lane's chunk (m, l) and the first 16 chunks' o pairs
+        u64 wm = (u64)tag_a << 32, wl = (u64)tag_a << 32;
+        const u64 *mp = &src[((size_t)lane * qpg + h) * stride];
+        if (lane < S) {
+          wm = ld_dev(mp);
+          wl = ld_dev(mp + 1);
         }
-        float Lsum = 0.0f;
-        for (int c0 = 0; c0 < S; c0 += 64) {
-          const int cc = c0 + lane;
-          float m = -INFINITY, lc = 0.0f;
-          if (cc < S) {
-            m = ld_dev(&src[(cc * qpg + h) * stride + 0]);
-            lc = ld_dev(&src[(cc * qpg + h) * stride + 1]);
-          }
-          const float w = cc < S ? __expf(m - M) : 0.0f;
-          Lsum += wave_sum(w * lc);
-          if (cc < S) wgt[cc] = w;
-        }
-        lds_drain();
-        const float inv = 1.0f / Lsum;
-        for (int e = lane; e < dh; e += 64) {
-          float o = 0.0f;
-          for (int c0 = 0; c0 < S; c0 += 16) {
-            float v[16];
+        float o0 = 0.0f, o1 = 0.0f, inv = 0.0f;
+        for (int c0 = 0; c0 < S; c0 += 16) {
+          u64 v[16][2];
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              v[j] = c0 + j < S ? ld_dev(&src[((c0 + j) * qpg + h) * stride + 2 + e]) : 0.0f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (c0 + j < S) o += wgt[c0 + j] * v[j];
+          for (int j = 0; j < 16; ++j) {
+            const size_t at = ((size_t)(c0 + j) * qpg + h) * stride + 2 + e0;
+            const bool use = c0 + j < S && e0 < dh;
+            v[j][0] = use ? ld_dev(&src[at]) : ((u64)tag_a << 32);
+            v[j][1] = use ? ld_dev(&src[at + 1]) : ((u64)tag_a << 32);
           }
-          st_dev_h(P.o16, (size_t)(g * qpg + h) * dh + e, o * inv);
+          if (c0 == 0) {
+            if (tag_of(wm) != tag_a) wm = ld_tag_wait(P, mp, tag_a, t0, bad);
+            if (tag_of(wl) != tag_a) wl = ld_tag_wait(P, mp + 1, tag_a, t0, bad);
+            const float mc = lane < S ? pay_f(wm) : -INFINITY;
+            const float M = wave_max(mc);
+            const float w = lane < S ? __expf(mc - M) : 0.0f;
+            const float Lsum = wave_sum(w * (lane < S ? pay_f(wl) : 0.0f));
+            if (lane < S) wgt[lane] = w;
+            inv = 1.0f / Lsum;
+            lds_drain();
+          }
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if (c0 + j < S && e0 < dh) {
+              const size_t at = ((size_t)(c0 + j) * qpg + h) * stride + 2 + e0;
+              if (tag_of(v[j][0]) != tag_a) v[j][0] = ld_tag_wait(P, &src[at], tag_a, t0, bad);
+              if (tag_of(v[j][1]) != tag_a) v[j][1] = ld_tag_wait(P, &src[at + 1], tag_a, t0, bad);
+              o0 += wgt[c0 + j] * pay_f(v[j][0]);
+              o1 += wgt[c0 + j] * pay_f(v[j][1]);
+            }
+          }
         }
+        if (e0 < dh) {
+          const size_t ow = (size_t)gen * (P.Hq * dh / 2) + ((size_t)(g * qpg + h) * dh + e0) / 2;
+          st_tag(&P.o_t[ow], tag_h2(o0 * inv, o1 * inv, tag_a));
+        }
+        lds_drain();   // wgt is rewritten for the next head
       }
       if (lane == 0) st_dev(&P.tickets[l * Hkv + g], 0u);
+      if (bad && lane == 0) lds_st(&ctl->abort, 1u);
     }
   }
   __syncthreads();
+  return !lds_ld(&ctl->abort);
 }
 
 // ---------------------------------------------------------------- sampler
@@ -912,7 +1045,16 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
 // ---------------------------------------------------------------- the kernel
 
 // kPrefill: teacher-forced prompt tokens read from in_tokens[], no logits and no
-// sampling; each token's first layer waits for the previous token's last layer.
+// sampling; each token's first layer waits until every workgroup finished the
+// previous token.
+//
+// Dependency levels of token t, layer l (lvl = level of the previous layer's
+// down projection): QKV lvl+1, attention lvl+2, O lvl+3, gate/up lvl+4, down
+// lvl+5; after the last layer, lm_head lvl+1 and the chosen token lvl+2.  The
+// vectors between phases travel as tagged words in generation (t*L + l) & 1.
+// A workgroup reads a phase's input only if it has rows in that phase, so each
+// read is followed by an output that every later phase depends on; a buffer of
+// one generation is rewritten two layers later, after every reader of it.
 template <bool kPrefill>
 __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -920,6 +1062,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
   float *part = reinterpret_cast<float *>(smem + P.lds_part);
   float *red = reinterpret_cast<float *>(smem + P.lds_red);   // 64 floats
   Ctl *ctl = reinterpret_cast<Ctl *>(smem + P.lds_ctl);
+  float *xown = reinterpret_cast<float *>(smem + P.lds_xown); // residual rows of this workgroup
   unsigned char *alds = smem + P.lds_h;                       // attention / sampler scratch
   const int b = blockIdx.x, G = P.G, wave = wave_id(), lane = lane_id();
   const int L = P.L, d = P.d, dh = P.dh;
@@ -927,14 +1070,16 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
   const int ngp = 4 * L + (has_lm ? 1 : 0);        // GEMV phases per token
   const _Float16 *emb = reinterpret_cast<const _Float16 *>(P.tok_emb);
 
-  // this workgroup's row block of every phase kind
+  // this workgroup's row block of every phase kind: contiguous partition units
+  // (row pairs; gate/up in units of two pairs, so one SwiGLU word has one producer)
   if (tid_x() == 0) {
-    const int pairs[K_COUNT] = {P.nqkv / 2, d / 2, P.F, d / 2, P.V / 2};
+    const int units[K_COUNT] = {P.nqkv / 2, d / 2, P.F / 2, d / 2, P.V / 2};
+    const int upr[K_COUNT] = {2, 2, 4, 2, 2};
     const int kvs[K_COUNT] = {d / 8, P.Hq * dh / 8, d / 8, P.F / 8, d / 8};
     for (int k = 0; k < K_COUNT; ++k) {
       int p0, p1;
-      block_range(pairs[k], G, b, p0, p1);
-      ctl->geo[k] = Geo{2 * p0, 2 * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
+      block_range(units[k], G, b, p0, p1);
+      ctl->geo[k] = Geo{upr[k] * p0, upr[k] * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
     }
     ctl->h_ready = 0;
     ctl->abort = 0;
@@ -943,7 +1088,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
   }
   __syncthreads();
 
-  Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}};
+  Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}, 0ull, 0ull, 0ull};
   const unsigned long long kt0 = now_ticks();
 
   if (wave > 0) {
@@ -964,17 +1109,16 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
     for (int t = 0; t < P.n_tokens; ++t) {
       const int pos = P.pos0 + t;
       const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
+      int S, Lc;
+      attn_split(pos + 1, G, P.Hkv, S, Lc);
       for (int l = 0; l < L; ++l) {
         const int q0 = t * ngp + 4 * l;
+        const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
+        const int gen = (t * L + l) & 1;
         if (!stream_phase(st, consumed, q0 + 0, K_QKV, ctl, hl, part)) return;
-        // attention: the whole workgroup
         if (lds_ld(&ctl->abort)) return;
-        if (!wait_all_waves(sy, 0, G, lv0 + (unsigned)(l * PH_PER_LAYER) + PH_QKV)) return;
-        {
-          int S, Lc;
-          attn_split(pos + 1, G, P.Hkv, S, Lc);
-          for (int u = b; u < P.Hkv * S; u += G) attn_unit(P, l, pos, u, S, Lc, alds, red);
-        }
+        for (int u = b; u < P.Hkv * S; u += G)
+          if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
         if (!stream_phase(st, consumed, q0 + 1, K_O, ctl, hl, part)) return;
         if (!stream_phase(st, consumed, q0 + 2, K_GU, ctl, hl, part)) return;
         if (!stream_phase(st, consumed, q0 + 3, K_D, ctl, hl, part)) return;
@@ -1001,139 +1145,171 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
   auto fail = [&]() __attribute__((always_inline)) {
     if (lane == 0) lds_st(&ctl->abort, 1u);
   };
+  const int nq = P.Hq * dh, nk = P.Hkv * dh, half = dh / 2;
+  const size_t nkw = (size_t)P.Hkv * half;   // words per generation of kc_t / vc_t
   int token = P.token0;
   for (int t = 0; t < P.n_tokens; ++t) {
     const int pos = P.pos0 + t;
     const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
     if (kPrefill) token = P.in_tokens[t];
+    int S, Lc;
+    attn_split(pos + 1, G, P.Hkv, S, Lc);
     for (int l = 0; l < L; ++l) {
       const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
       const int q0 = t * ngp + 4 * l;
+      const int gen = (t * L + l) & 1;
       const _Float16 *attn_norm = reinterpret_cast<const _Float16 *>(layer_part(P, l, LW_ATTN_NORM));
       const _Float16 *ffn_norm = reinterpret_cast<const _Float16 *>(layer_part(P, l, LW_FFN_NORM));
 
-      // ---------------- QKV + rotary + KV append
+      // ---------------- attention norm + QKV + rotary + KV append
       {
-        unsigned long long tq = 0;
-        if (l == 0) {
-          if (kPrefill) {
-            if (t > 0 && !poll_level(sy, 0, G, lv0)) { fail(); return; }
-          } else if (t > 0 && !P.hidden_io) {
+        if (l == 0 && t > 0) {
+          if (kPrefill || P.hidden_io) {
+            // the previous token is finished everywhere (its reads included)
+            if (!poll_level(sy, 0, G, lv0)) { fail(); return; }
+          } else {
             if (!poll_level(sy, 0, 1, lv0)) { fail(); return; }
             token = ld_dev(P.tok_slot);
           }
-          tq = now_ticks();
-          if (P.hidden_io)
-            stage_rmsnorm(nullptr, P.x_hidden, nullptr, attn_norm, d, P.eps, hl);
-          else
-            stage_rmsnorm(nullptr, nullptr, emb + (size_t)token * d, attn_norm, d, P.eps, hl);
-        } else {
-          if (!poll_level(sy, 0, G, lvl)) { fail(); return; }
-          tq = now_ticks();
-          stage_rmsnorm(P.x_out, nullptr, nullptr, attn_norm, d, P.eps, hl);
         }
-        lap(sy, ST_STAGE, tq);
-        announce_input(ctl, q0);
-        unsigned long long tk = now_ticks();
-        wait_streams(ctl, q0);
-        tk = lap(sy, ST_STREAMS, tk);
         const Geo ge = ctl->geo[K_QKV];
-        const int half = dh / 2;
-        const int nq = P.Hq * dh, nk = P.Hkv * dh;
+        unsigned long long tq = now_ticks();
+        if (ge.nrows > 0) {
+          if (l > 0) {
+            if (!stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, attn_norm, d, P.eps,
+                                      hl)) { fail(); return; }
+          } else if (P.hidden_io) {
+            stage_rmsnorm_plain(P.x_hidden, nullptr, attn_norm, d, P.eps, hl);
+          } else {
+            stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, attn_norm, d, P.eps, hl);
+          }
+        }
+        tq = lap(sy, ST_STAGE, tq);
+        announce_input(ctl, q0);
+        wait_streams(ctl, q0);
+        tq = lap(sy, ST_STREAMS, tq);
+        const unsigned tag = lvl + PH_QKV;
         const size_t kvrow = ((size_t)l * P.max_seq + pos) * (size_t)nk;
+        _Float16 *kc = reinterpret_cast<_Float16 *>(P.kcache);
+        _Float16 *vc = reinterpret_cast<_Float16 *>(P.vcache);
         for (int i = lane; i < ge.nrows / 2; i += 64) {
           const float a = row_value(part, ge, 2 * i), bb = row_value(part, ge, 2 * i + 1);
           const int r = ge.r0 + 2 * i;
           if (r < nq + nk) {
+            // q / k rows come in rotary pairs (dims k, k + dh/2 of head hd)
             const int rr = r < nq ? r : r - nq;
             const int hd = rr / dh, k = (rr % dh) / 2;
             const float cs = P.rope[((size_t)pos * half + k) * 2 + 0];
             const float sn = P.rope[((size_t)pos * half + k) * 2 + 1];
             const float y0 = a * cs - bb * sn, y1 = bb * cs + a * sn;
             if (r < nq) {
-              st_dev(&P.q[hd * dh + k], y0);
-              st_dev(&P.q[hd * dh + k + half], y1);
+              u64 *qd = P.q_t + (size_t)gen * nq + (size_t)hd * dh;
+              st_tag(qd + k, tag_f(y0, tag));
+              st_tag(qd + k + half, tag_f(y1, tag));
             } else {
-              st_dev_h(P.kcache, kvrow + hd * dh + k, y0);
-              st_dev_h(P.kcache, kvrow + hd * dh + k + half, y1);
+              st_dev_h(kc, kvrow + (size_t)hd * dh + k, y0);
+              st_dev_h(kc, kvrow + (size_t)hd * dh + k + half, y1);
+              st_tag(P.kc_t + gen * nkw + (size_t)hd * half + k, tag_h2(y0, y1, tag));
             }
           } else {
-            const int rv = r - nq - nk;
-            st_dev_h(P.vcache, kvrow + rv, a);
-            st_dev_h(P.vcache, kvrow + rv + 1, bb);
+            const int rv = r - nq - nk;   // V rows in natural order, pairs (rv, rv + 1)
+            const u64 w = tag_h2(a, bb, tag);
+            st_dev(reinterpret_cast<unsigned *>(vc + kvrow + rv), (unsigned)w);
+            st_tag(P.vc_t + gen * nkw + (size_t)(rv / 2), w);
           }
         }
-        publish(P, lvl + PH_QKV);
-        lap(sy, ST_EPI, tk);
+        publish_fast(P, tag);
+        lap(sy, ST_EPI, tq);
       }
 
       // ---------------- attention (all waves; split-K, last arriver merges)
       {
         const unsigned long long ta = now_ticks();
-        if (!wait_all_waves(sy, 0, G, lvl + PH_QKV)) { fail(); return; }
-        int S, Lc;
-        attn_split(pos + 1, G, P.Hkv, S, Lc);
-        for (int u = b; u < P.Hkv * S; u += G) attn_unit(P, l, pos, u, S, Lc, alds, red);
-        publish(P, lvl + PH_ATTN);
+        for (int u = b; u < P.Hkv * S; u += G)
+          if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
+        publish_fast(P, lvl + PH_ATTN);
         lap(sy, ST_ATTN, ta);
       }
 
       // ---------------- output projection + residual
       {
-        if (!poll_level(sy, 0, G, lvl + PH_ATTN)) { fail(); return; }
+        const Geo ge = ctl->geo[K_O];
         unsigned long long tk = now_ticks();
-        stage_f16(P.o16, P.Hq * dh, hl);
+        if (ge.nrows > 0 &&
+            !stage_pairs_tagged(sy, P.o_t + (size_t)gen * (nq / 2), nq / 2, lvl + PH_ATTN, hl)) { fail(); return; }
         tk = lap(sy, ST_STAGE, tk);
         announce_input(ctl, q0 + 1);
         wait_streams(ctl, q0 + 1);
         tk = lap(sy, ST_STREAMS, tk);
-        const Geo ge = ctl->geo[K_O];
+        // Every store this wave made before (KV cache rows, the split-K ticket
+        // reset, tagged words) has completed before anything it publishes from
+        // here on: later steps read the cache rows with plain loads.  They were
+        // issued a whole projection ago, so this wait is short.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        asm volatile("" ::: "memory");
+        const unsigned tag = lvl + PH_O;
+        u64 *xm = P.xmid_t + (size_t)gen * d;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
           float xin;
-          if (l > 0) xin = ld_dev(&P.x_out[r]);
+          if (l > 0) xin = xown[i];
           else if (P.hidden_io) xin = P.x_hidden[r];
           else xin = (float)emb[(size_t)token * d + r];
-          st_dev(&P.x_mid[r], xin + row_value(part, ge, i));
+          const float x = xin + row_value(part, ge, i);
+          xown[i] = x;
+          st_tag(xm + r, tag_f(x, tag));
         }
-        publish(P, lvl + PH_O);
+        publish_fast(P, tag);
         lap(sy, ST_EPI, tk);
       }
 
       // ---------------- FFN norm + gate/up + SwiGLU
       {
-        if (!poll_level(sy, 0, G, lvl + PH_O)) { fail(); return; }
+        const Geo ge = ctl->geo[K_GU];
         unsigned long long tk = now_ticks();
-        stage_rmsnorm(P.x_mid, nullptr, nullptr, ffn_norm, d, P.eps, hl);
+        if (ge.nrows > 0 &&
+            !stage_rmsnorm_tagged(sy, P.xmid_t + (size_t)gen * d, lvl + PH_O, ffn_norm, d, P.eps, hl)) {
+          fail();
+          return;
+        }
         tk = lap(sy, ST_STAGE, tk);
         announce_input(ctl, q0 + 2);
         wait_streams(ctl, q0 + 2);
         tk = lap(sy, ST_STREAMS, tk);
-        const Geo ge = ctl->geo[K_GU];
-        for (int i = lane; i < ge.nrows / 2; i += 64) {
-          const float gt = row_value(part, ge, 2 * i), up = row_value(part, ge, 2 * i + 1);
-          const float sg = gt / (1.0f + __expf(-gt));
-          st_dev_h(P.a16, (size_t)(ge.r0 / 2 + i), sg * up);
+        const unsigned tag = lvl + PH_GU;
+        u64 *ad = P.a_t + (size_t)gen * (P.F / 2);
+        for (int i = lane; i < ge.nrows / 4; i += 64) {
+          // rows 4i..4i+3 = gate j, up j, gate j+1, up j+1 with j = r0/2 + 2i
+          const float g0 = row_value(part, ge, 4 * i), u0 = row_value(part, ge, 4 * i + 1);
+          const float g1 = row_value(part, ge, 4 * i + 2), u1 = row_value(part, ge, 4 * i + 3);
+          const float s0 = g0 / (1.0f + __expf(-g0)), s1 = g1 / (1.0f + __expf(-g1));
+          st_tag(ad + ge.r0 / 4 + i, tag_h2(s0 * u0, s1 * u1, tag));
         }
-        publish(P, lvl + PH_GU);
+        publish_fast(P, tag);
         lap(sy, ST_EPI, tk);
       }
 
       // ---------------- down projection + residual
       {
-        if (!poll_level(sy, 0, G, lvl + PH_GU)) { fail(); return; }
+        const Geo ge = ctl->geo[K_D];
         unsigned long long tk = now_ticks();
-        stage_f16(P.a16, P.F, hl);
+        if (ge.nrows > 0 &&
+            !stage_pairs_tagged(sy, P.a_t + (size_t)gen * (P.F / 2), P.F / 2, lvl + PH_GU, hl)) { fail(); return; }
         tk = lap(sy, ST_STAGE, tk);
         announce_input(ctl, q0 + 3);
         wait_streams(ctl, q0 + 3);
         tk = lap(sy, ST_STREAMS, tk);
-        const Geo ge = ctl->geo[K_D];
+        const unsigned tag = lvl + PH_D;
+        u64 *xo = P.xout_t + (size_t)gen * d;
+        const bool host_out = P.hidden_io && l == L - 1;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
-          st_dev(&P.x_out[r], ld_dev(&P.x_mid[r]) + row_value(part, ge, i));
+          const float x = xown[i] + row_value(part, ge, i);
+          xown[i] = x;
+          st_tag(xo + r, tag_f(x, tag));
+          if (host_out) P.x_out[r] = x;
         }
-        publish(P, lvl + PH_D);
+        publish_fast(P, tag);
         lap(sy, ST_EPI, tk);
       }
     }
@@ -1144,11 +1320,15 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
     const int qlm = t * ngp + 4 * L;
     const unsigned long long tlm = now_ticks();
     {
-      if (!poll_level(sy, 0, G, lvl_lm - 1u)) { fail(); return; }
-      stage_rmsnorm(P.x_out, nullptr, nullptr, reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl);
+      const Geo ge = ctl->geo[K_LM];
+      if (ge.nrows > 0 &&
+          !stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + L - 1) & 1) * d, lvl_lm - 1u,
+                                reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl)) {
+        fail();
+        return;
+      }
       announce_input(ctl, qlm);
       wait_streams(ctl, qlm);
-      const Geo ge = ctl->geo[K_LM];
       float best = -INFINITY;
       int bi = 0x7fffffff;
       for (int i = lane; i < ge.nrows; i += 64) {
@@ -1165,7 +1345,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
         st_dev(&P.lm_val[b], best);
         st_dev(&P.lm_idx[b], bi);
       }
-      publish(P, lvl_lm);
+      publish_sync(P, lvl_lm);
     }
 
     // ---------------- next token (workgroup 0)
@@ -1198,7 +1378,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
         st_dev(P.tok_slot, tok);
         P.out_tokens[t] = tok;
       }
-      publish(P, lvl_lm + 1u);
+      publish_sync(P, lvl_lm + 1u);
     }
     lap(sy, ST_LM, tlm);
   }
@@ -1211,6 +1391,9 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
     o[2] = xcc & 0xfu;
     o[3] = now_ticks() - kt0;
     for (int k = 0; k < kStatPhases; ++k) o[4 + k] = sy.tm[k];
+    o[12] = sy.rt_sum;
+    o[13] = sy.rt_n;
+    o[14] = sy.nfetch;
   }
 }
 

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblf.so")
+# LF_LIB selects another build of the same library (e.g. one compiled with a
+# different LDS ring depth); by default the in-tree build is used.
+LIB_PATH = os.environ.get("LF_LIB") or os.path.join(HERE, "liblf.so")
 
 LF_OK, LF_EINVAL, LF_ENOMEM, LF_EHIP, LF_ERANGE, LF_ETIMEOUT, LF_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 LF_HIDDEN_IO, LF_STATS = 1, 4
