@@ -116,6 +116,7 @@ int do_launch(lf_state *st, int token0, int pos0, int n, std::vector<int> *out, 
     if ((e = reset_levels(st)) != hipSuccess) return hip_fail(st, e, "reset levels");
   }
   P.n_tokens = n;
+  P.trace_token = n / 2;
   P.token0 = token0;
   P.pos0 = pos0;
   P.level_base = st->level_base;
@@ -309,7 +310,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
       {&x_hidden, (size_t)d * 4}, {&x_out, (size_t)d * 4}, {&logits, (size_t)(V > 0 ? V : 1) * 4},
       {&lm_val, (size_t)G * 4}, {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4},
       {&tickets, (size_t)c.n_layers * Hkv * 4}, {&tok_slot, 16}, {&errw, 16},
-      {&stats, (size_t)G * lf::kStatWords * 8}};
+      {&stats, (size_t)G * (lf::kStatWords + (lf::kTrace ? 6 * (5 * c.n_layers + 2) : 0)) * 8}};
   size_t arena = 0;
   for (auto &sl : slots) arena += align_up(sl.bytes, 256);
   char *ar = (char *)dev_alloc(st, arena, &e);
@@ -321,6 +322,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lm_val = (float *)lm_val; P.lm_idx = (int *)lm_idx; P.progress = (unsigned *)progress;
   P.tickets = (unsigned *)tickets; P.tok_slot = (int *)tok_slot; P.err = (unsigned *)errw;
   P.stats = (unsigned long long *)stats;
+  P.stat_stride = lf::kStatWords + (lf::kTrace ? 6 * (5 * c.n_layers + 2) : 0);
   // tagged exchange words, two generations each, in one zeroed allocation
   {
     struct TSlot { unsigned long long **dst; size_t words; };
@@ -359,8 +361,9 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (F > hmax) hmax = F;
   const size_t h_b = align_up((size_t)hmax * 2 + 1024, 16);   // + one piece of slack for masked lanes
   const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);
-  const size_t attn_sc = (size_t)P.qpg * lf::kAttnBlock * 4, attn_or = (size_t)lf::kWaves * P.qpg * dh * 4;
-  const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (attn_sc > attn_or ? attn_sc : attn_or);
+  // attention scratch: queries, current K/V row, per-wave (m, l) and per-wave o
+  const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (size_t)lf::kWaves * 8 * 2 * 4 +
+                        (size_t)lf::kWaves * P.qpg * dh * 4;
   const size_t samp_b = 4096;
   size_t region_a = h_b + part_b;
   if ((size_t)d * 4 > region_a) region_a = (size_t)d * 4;   // fp32 staging of a layer input
@@ -371,7 +374,8 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_red = (int)align_up(region_a, 256);
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + 256;
-  P.lds_ring = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
+  P.lds_gain = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
+  P.lds_ring = (int)align_up((size_t)P.lds_gain + align_up((size_t)d * 2, 1024), 256);
   P.part_rows = rows_max;
   P.hmax = hmax;
   int lds_limit = 0;
@@ -536,7 +540,8 @@ int lf_get_hidden(lf_state *st, float *x) {
 
 int lf_get_stats(lf_state *st, void *dst, size_t bytes) {
   if (!st || !dst) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
-  const size_t need = (size_t)st->P.G * lf::kStatWords * 8;
+  size_t need = (size_t)st->P.G * lf::kStatWords * 8;
+  if (lf::kTrace && bytes >= (size_t)st->P.G * st->P.stat_stride * 8) need = (size_t)st->P.G * st->P.stat_stride * 8;
   if (bytes < need) return fail(&st->err, LF_EINVAL, "stats buffer too small");
   hipError_t e = hipMemcpy(dst, st->P.stats, need, hipMemcpyDeviceToHost);
   return e == hipSuccess ? LF_OK : hip_fail(st, e, "copy stats");

@@ -12,6 +12,13 @@ constexpr int kAttnBlock = 512;        // key positions scored per attention sub
 constexpr int kMinKeysPerUnit = 16;    // smallest attention split-K chunk
 constexpr int kMaxSplit = 64;          // most split-K chunks per KV head
 constexpr int kStatWords = 16;         // uint64 statistics per workgroup (LF_STATS)
+// LF_TRACE builds also record, for one token, three timestamps per phase and
+// workgroup: input staged, stream waves done, published.
+#ifdef LF_TRACE
+constexpr bool kTrace = true;
+#else
+constexpr bool kTrace = false;
+#endif
 #ifndef LF_RING_SLOTS
 #define LF_RING_SLOTS 16
 #endif
@@ -65,7 +72,8 @@ struct Params {
   int *out_tokens;         // [n_tokens]
   const int *in_tokens;    // [n_tokens] teacher-forced tokens (prefill launches)
   unsigned *err;           // [4] {code, workgroup, level, 0}
-  unsigned long long *stats;  // [G][kStatWords]
+  unsigned long long *stats;  // [G][stat_stride]: kStatWords counters, then (LF_TRACE builds) a phase trace
+  int stat_stride, trace_token;
   // this launch
   int n_tokens, token0, pos0;
   unsigned level_base;
@@ -73,7 +81,7 @@ struct Params {
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   int poll_first;          // 1: poll the producers' progress words before reading tagged data
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_ring, lds_bytes;
+  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_gain, lds_ring, lds_bytes;
   int part_rows, hmax;
 };
 

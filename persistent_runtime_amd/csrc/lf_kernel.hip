@@ -50,6 +50,20 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
+// The parameter block as seen by the kernel: in the constant (kernel argument)
+// address space, read with scalar loads.
+typedef const __attribute__((address_space(4))) Params KP;
+
+// The same parameter block through an opaque pointer: field reads after this
+// point cannot be hoisted above it, so a region re-reads the few fields it uses
+// instead of keeping every field of the block live in scalar registers for the
+// whole kernel (they would crowd out the stream loop's state).
+__device__ __forceinline__ KP &fresh(KP &P) {
+  KP *p = &P;
+  asm volatile("" : "+s"(p));
+  return *p;
+}
+
 constexpr int kNcw = kWaves - 1;       // stream waves per workgroup
 constexpr int kRing = kRingSlots;      // 1-KB slots in each stream wave's LDS ring
 constexpr int kMaxQpg = 8;             // query heads per KV head supported
@@ -206,7 +220,7 @@ struct Ctl {
 // ---------------------------------------------------------------- global sync (wave 0)
 
 struct Sync {
-  const Params *P;
+  KP *P;
   Ctl *ctl;
   unsigned long long spin;    // ticks spent polling other workgroups
   unsigned long long waits;
@@ -221,10 +235,18 @@ __device__ __forceinline__ unsigned long long lap(Sync &s, int k, unsigned long 
   return t1;
 }
 
+// LF_TRACE builds: timestamp j (0 input staged, 1 streams done, 2 published;
+// stream wave 1: 3 input seen, 4 first ring's worth consumed, 5 done)
+// of phase k (5l + {QKV, attention, O, gate/up, down}; 5L lm_head; 5L+1 token).
+__device__ __forceinline__ void trace(KP &P, int t, int k, int j) {
+  if (kTrace && t == P.trace_token && lane_id() == 0)
+    P.stats[(size_t)blockIdx.x * P.stat_stride + kStatWords + 6 * k + j] = now_ticks();
+}
+
 // The bound of a wait started at t0 has expired: record the first such event in
 // the error word (any lane may call; one wins).  Also true once another
 // workgroup has recorded an error.
-__device__ __forceinline__ bool expired(const Params &P, unsigned long long t0, unsigned level) {
+__device__ __forceinline__ bool expired(KP &P, unsigned long long t0, unsigned level) {
   if (now_ticks() - t0 <= P.timeout_ticks) return ld_dev(&P.err[0]) != 0u;
   unsigned zero = 0u;
   if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -238,7 +260,7 @@ __device__ __forceinline__ bool expired(const Params &P, unsigned long long t0, 
 // Wave 0 only: poll progress[first .. first+count) >= level.  Returns false when
 // the bound expired or another workgroup reported an error.
 __device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsigned level) {
-  const Params &P = *s.P;
+  KP &P = *s.P;
   const unsigned long long t0 = now_ticks();
   bool ok = false;
   for (;;) {
@@ -256,13 +278,13 @@ __device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsign
 // Wave 0 only: announce `level` for this workgroup.  The level's data are tagged
 // words, so the announcement need not wait for them to land: a consumer that
 // sees the progress word early re-reads until the tags match.
-__device__ __forceinline__ void publish_fast(const Params &P, unsigned level) {
+__device__ __forceinline__ void publish_fast(KP &P, unsigned level) {
   if (lane_id() == 0) st_dev(&P.progress[blockIdx.x], level);
 }
 
 // Wave 0 only: announce `level` after every store of this wave has completed
 // (for the untagged data of the lm_head and token levels).
-__device__ __forceinline__ void publish_sync(const Params &P, unsigned level) {
+__device__ __forceinline__ void publish_sync(KP &P, unsigned level) {
   __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" ::: "memory");
   if (lane_id() == 0) st_dev(&P.progress[blockIdx.x], level);
@@ -297,7 +319,7 @@ constexpr int kStageBatch = 32;   // 8-byte loads in flight per lane while stagi
 // batch costs one memory round trip; a batch with a stale word is re-read.
 template <class F>
 __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, unsigned tag, F &&use) {
-  const Params &P = *s.P;
+  KP &P = *s.P;
   const int lane = lane_id();
   if (P.poll_first && !poll_level(s, 0, P.G, tag)) return false;
   const unsigned long long t0 = now_ticks();
@@ -331,8 +353,24 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
   return true;
 }
 
+// Wave 0: start copying the n fp16 norm gains g[0..n) (n % 8 == 0) into LDS
+// `dst` (rounded up to whole 1-KB pieces) with LDS-DMA.  The copy lands while
+// the wave waits for the vector it normalises; it is complete at vmcnt(0).
+__device__ __forceinline__ void prefetch_gain(const _Float16 *g, int n, unsigned char *dst) {
+  const int nvec = n / 8, lane = lane_id();
+  for (int b = 0; b < nvec; b += 64) {
+    const int v = min(b + lane, nvec - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(g + 8 * v),
+                                     (__attribute__((address_space(3))) void *)(dst + b * 16), 16, 0, 0);
+  }
+}
+__device__ __forceinline__ void gain_ready() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
 // In-place second pass of RMSNorm: xs (fp32 staged in LDS at h's address) ->
-// h = fp16(g * (x / r)).  Iteration k reads fp32 elements [128k, 128k+128) and
+// h = fp16(g * (x / r)), gains g in LDS.  Iteration k reads fp32 elements [128k, 128k+128) and
 // then writes fp16 elements of the same range, which occupy bytes already read.
 __device__ __forceinline__ void normalize_in_place(const _Float16 *g, int d, float r, _Float16 *h) {
   const float *xs = reinterpret_cast<const float *>(h);
@@ -356,9 +394,11 @@ __device__ __forceinline__ void normalize_in_place(const _Float16 *g, int d, flo
 }
 
 // RMSNorm of a residual published by other workgroups as tagged fp32 words.
-__device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, unsigned tag, const _Float16 *g,
-                                                     int d, float eps, _Float16 *h) {
+__device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, unsigned tag, const _Float16 *gain,
+                                                     int d, float eps, _Float16 *h, unsigned char *glds) {
   float *xs = reinterpret_cast<float *>(h);
+  const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
+  prefetch_gain(gain, d, glds);
   float ss = 0.0f;
   if (!fetch_tagged(s, src, d, tag, [&](int i, u64 w) __attribute__((always_inline)) {
         const float x = pay_f(w);
@@ -368,14 +408,17 @@ __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, un
     return false;
   ss = wave_sum(ss);
   lds_drain();
+  gain_ready();
   normalize_in_place(g, d, sqrtf(ss / (float)d + eps), h);
   return true;
 }
 
 // RMSNorm of a layer-0 input: an fp16 embedding row or the host's fp32 vector.
-__device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _Float16 *x16, const _Float16 *g,
-                                                    int d, float eps, _Float16 *h) {
+__device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _Float16 *x16, const _Float16 *gain,
+                                                    int d, float eps, _Float16 *h, unsigned char *glds) {
   float *xs = reinterpret_cast<float *>(h);
+  const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
+  prefetch_gain(gain, d, glds);
   const int lane = lane_id();
   float ss = 0.0f;
   for (int base = 0; base < d; base += 64 * kStageBatch) {
@@ -396,6 +439,7 @@ __device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _
   }
   ss = wave_sum(ss);
   lds_drain();
+  gain_ready();
   normalize_in_place(g, d, sqrtf(ss / (float)d + eps), h);
 }
 
@@ -410,14 +454,14 @@ __device__ __forceinline__ bool stage_pairs_tagged(Sync &s, const u64 *src, int 
 // ---------------------------------------------------------------- stream waves
 
 // Weight rows of phase kind k in layer l for this workgroup: row r0 of its block.
-__device__ __forceinline__ const void *layer_part(const Params &P, int l, int part) {
+__device__ __forceinline__ const void *layer_part(KP &P, int l, int part) {
   return P.wbase + (size_t)l * P.layer_stride + P.part_off[part];
 }
 
 // Weight rows of phase kind k in layer l for this workgroup: row r0 of its block.
 // Pure address arithmetic (no loads), so crossing a phase never drains the
 // stream wave's load pipeline.
-__device__ __forceinline__ const u32x4 *phase_base(const Params &P, const Geo &g, int kind, int l) {
+__device__ __forceinline__ const unsigned char *phase_base(KP &P, const Geo &g, int kind, int l) {
   const void *w;
   switch (kind) {
     case K_QKV: w = layer_part(P, l, LW_QKV); break;
@@ -426,7 +470,14 @@ __device__ __forceinline__ const u32x4 *phase_base(const Params &P, const Geo &g
     case K_D: w = layer_part(P, l, LW_D); break;
     default: w = P.lm_head; break;
   }
-  return reinterpret_cast<const u32x4 *>(w) + (size_t)g.r0 * g.kv;
+  return reinterpret_cast<const unsigned char *>(w) + (size_t)g.r0 * g.kv * 16;
+}
+
+// A phase kind's row block, read from LDS into wave-uniform (scalar) registers.
+__device__ __forceinline__ Geo uniform_geo(const Ctl *ctl, int kind) {
+  const Geo g = ctl->geo[kind];
+  return Geo{__builtin_amdgcn_readfirstlane(g.r0), __builtin_amdgcn_readfirstlane(g.nrows),
+             __builtin_amdgcn_readfirstlane(g.kv), __builtin_amdgcn_readfirstlane(g.ppr)};
 }
 
 // Stream wave cw's share [lo, hi) of the np pieces of a row block (contiguous).
@@ -435,39 +486,47 @@ __device__ __forceinline__ void wave_slice(int np, int cw, int &lo, int &hi) {
   hi = ((cw + 1) * np) / kNcw;
 }
 
+static_assert((kRing & (kRing - 1)) == 0 && kRing <= 32, "ring depth must be a power of two <= 32");
+
 // The issue side of a stream wave: walks GEMV phases q = 0, 1, ... of the launch
 // (token t = q / ngp, phase g = q % ngp; g < 4L is (layer g/4, kind g%4), else
-// the lm_head) and issues one 1-KB piece per call into the wave's LDS ring.
+// the lm_head) and issues one 1-KB piece per call into the wave's LDS ring.  A
+// piece is 64 consecutive 16-byte vectors of one row (the last piece of a row
+// may be partial: its idle lanes re-read the row's last vector).  All cursor
+// state is wave-uniform; the only per-lane value is the lane's byte offset.
 struct Streamer {
-  const Params *P;
+  KP *P;
   const Ctl *ctl;
-  unsigned char *ring;        // this wave's ring: D slots of 1 KB
+  unsigned char *ring;        // this wave's ring: kRing slots of 1 KB
   int cw, ngp, qend;
-  int q, p, phi, row, kp, kv, ppr;
-  const u32x4 *base;
+  int q, left, kp, ppr, tailv;   // phase, pieces left in it, piece in row, pieces per row, vectors in a row's last piece
+  long long adv_last;            // bytes from a row's last piece to the next row
+  const unsigned char *ptr;      // next piece (lane 0's address)
   unsigned issued;
   bool timed;                                 // LF_STATS on stream wave 1
+  int trace_k;                                // LF_TRACE: phase slot of the traced token, else -1
   unsigned long long t_ready, t_work, pieces;
 
   // advance to the first GEMV phase >= q_ in which this wave has pieces
   __device__ __forceinline__ void locate(int q_) {
     q = q_;
+    KP &Q = fresh(*P);
     while (q < qend) {
       const int g = q % ngp;
-      const bool lm = g >= 4 * P->L;
+      const bool lm = g >= 4 * Q.L;
       const int kind = lm ? K_LM : (g & 3);
       const int l = lm ? 0 : (g >> 2);
-      const Geo ge = ctl->geo[kind];
+      const Geo ge = uniform_geo(ctl, kind);
       int lo, hi;
       wave_slice(ge.nrows * ge.ppr, cw, lo, hi);
       if (lo < hi) {
-        p = lo;
-        phi = hi;
-        row = lo / ge.ppr;
+        const int row = lo / ge.ppr;
+        left = hi - lo;
         kp = lo - row * ge.ppr;
-        kv = ge.kv;
         ppr = ge.ppr;
-        base = phase_base(*P, ge, kind, l);
+        tailv = ge.kv - (ge.ppr - 1) * 64;
+        adv_last = (long long)ge.kv * 16 - (long long)(ge.ppr - 1) * 1024;
+        ptr = phase_base(Q, ge, kind, l) + ((size_t)row * ge.kv * 16 + (size_t)kp * 1024);
         return;
       }
       ++q;
@@ -476,16 +535,21 @@ struct Streamer {
 
   __device__ __forceinline__ void issue() {
     if (q >= qend) return;
-    const int v = kp * 64 + lane_id();
-    const int vc = v < kv ? v : kv - 1;      // masked lanes re-read a valid vector
-    const u32x4 *src = base + (size_t)row * kv + vc;
-    unsigned char *dst = ring + (issued % (unsigned)kRing) * 1024u;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
-                                     (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
+    const int lane = lane_id();
+    const bool last = kp == ppr - 1;
+    const int off = (last ? min(lane, tailv - 1) : lane) * 16;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ptr + off),
+                                     (__attribute__((address_space(3))) void *)(ring + (issued & (kRing - 1)) * 1024u),
+                                     16, 0, 0);
     ++issued;
-    ++p;
-    if (++kp == ppr) { kp = 0; ++row; }
-    if (p == phi) locate(q + 1);
+    if (last) {
+      kp = 0;
+      ptr += adv_last;
+    } else {
+      ++kp;
+      ptr += 1024;
+    }
+    if (--left == 0) locate(q + 1);
   }
 };
 
@@ -494,7 +558,7 @@ struct Streamer {
 // in part[row * 8 + cw].  Returns false if the sync wave aborted.
 __device__ __forceinline__ bool stream_phase(Streamer &st, unsigned &consumed, int q, int kind, Ctl *ctl,
                                              const _Float16 *h, float *part) {
-  const Geo ge = ctl->geo[kind];
+  const Geo ge = uniform_geo(ctl, kind);
   int lo, hi;
   wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
   // the dependency wait happens on wave 0; here only its LDS announcement
@@ -510,8 +574,14 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, unsigned &consumed, i
     t0 = t1;
   }
   const int lane = lane_id();
+  const bool tr = kTrace && st.cw == 0 && st.trace_k >= 0;
+  unsigned long long *trp =
+      tr ? st.P->stats + (size_t)blockIdx.x * st.P->stat_stride + kStatWords + 6 * st.trace_k : nullptr;
+  if (tr && lane == 0) trp[3] = now_ticks();
   const u32x4 *hv = reinterpret_cast<const u32x4 *>(h);
-  int row = lo / ge.ppr, kp = lo - row * ge.ppr;
+  const u32x4 *ringv = reinterpret_cast<const u32x4 *>(st.ring);
+  const int ppr = ge.ppr, tailv = ge.kv - (ge.ppr - 1) * 64;
+  int row = lo / ppr, kp = lo - row * ppr;
   float acc = 0.0f;
   for (int p = lo; p < hi; ++p) {
     // in steady state kRing pieces are in flight and the oldest is the one wanted
@@ -520,20 +590,29 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, unsigned &consumed, i
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);
     asm volatile("" ::: "memory");
-    const u32x4 x = reinterpret_cast<const u32x4 *>(st.ring + (consumed % (unsigned)kRing) * 1024u)[lane];
-    const int v = kp * 64 + lane;
-    if (v < ge.kv) acc = dot8(x, hv[v], acc);
+    const bool last = kp == ppr - 1;
+    const u32x4 x = ringv[(consumed & (kRing - 1)) * 64 + lane];
+    const u32x4 hx = hv[kp * 64 + (last ? min(lane, tailv - 1) : lane)];
+    const float a2 = dot8(x, hx, acc);
+    acc = (!last || lane < tailv) ? a2 : acc;
     lds_drain();                 // the slot has been read before it is refilled
     ++consumed;
+    if (tr && lane == 0 && p == lo + kRing - 1) trp[4] = now_ticks();
     st.issue();
-    if (++kp == ge.ppr || p == hi - 1) {
+    if (last || p == hi - 1) {
       const float s = wave_sum_to63(acc);
       if (lane == 63) part[row * 8 + st.cw] = s;
       acc = 0.0f;
-      if (kp == ge.ppr) { kp = 0; ++row; }
+    }
+    if (last) {
+      kp = 0;
+      ++row;
+    } else {
+      ++kp;
     }
   }
   lds_drain();
+  if (tr && lane == 0) trp[5] = now_ticks();
   if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
   if (timed) {
     st.t_work += now_ticks() - t0;
@@ -588,7 +667,7 @@ __device__ __forceinline__ void attn_split(int n, int G, int Hkv, int &S, int &L
 }
 
 // Wait for one tagged word; on expiry returns it anyway and sets *bad.
-__device__ __forceinline__ u64 ld_tag_wait(const Params &P, const u64 *p, unsigned tag, unsigned long long t0,
+__device__ __forceinline__ u64 ld_tag_wait(KP &P, const u64 *p, unsigned tag, unsigned long long t0,
                                            bool &bad) {
   u64 w = ld_dev(p);
   while (tag_of(w) != tag) {
@@ -601,206 +680,192 @@ __device__ __forceinline__ u64 ld_tag_wait(const Params &P, const u64 *p, unsign
   return w;
 }
 
+constexpr int kKeysPerRound = 16;   // keys whose K and V rows one wave loads per round trip
+
 // One split-K unit (KV head g, key chunk c) of layer l at position pos, all
-// waves: partial (m, l, o) for the qpg query heads of group g; the last unit of
-// the group to arrive merges all partials into o_t.  These are the pages' three
-// attention stages ("The fused operations, briefly"): attention over a tile of
-// the cache per unit, cross-unit softmax correction, then the output projection
-// (the next phase).  Queries, the current position's K/V row and the partials
-// arrive as tagged words; earlier cache rows were written in earlier steps.
+// waves of the workgroup.  These are the pages' three attention stages ("The
+// fused operations, briefly"): attention over one tile of the cache per unit,
+// the cross-unit softmax correction, then (next phase) the output projection.
+//
+// Wave w takes keys j0 + w, j0 + w + 8, ...; lane e holds head dims 2e, 2e+1,
+// loads kKeysPerRound K and V rows at once, and keeps an online softmax (m, l,
+// o) per query head.  The eight waves' states are combined into the unit's
+// partial, published as tagged words.  Unit c = 0 of each KV head merges the
+// group's S partials (waiting on their tags) into the fp16 output o_t.  The
+// current position's K/V row comes from the tagged exchange words, not from
+// the cache (whose row for this step may still be in flight).
 // Returns false if a bounded wait expired.
-__device__ __forceinline__ bool attn_unit(const Params &P, Ctl *ctl, int l, int gen, unsigned tag_q,
+__device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsigned tag_q,
                                           unsigned tag_a, int pos, int u, int S, int Lc, unsigned char *lds,
                                           float *red) {
+  KP &P = fresh(P0);
   const int tid = tid_x(), wave = wave_id(), lane = lane_id();
-  const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv;
-  const int dpl = dh / 64, half = dh / 2;
+  const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv, half = dh / 2;
   const int g = u / S, c = u - g * S;
   const int n = pos + 1;
   const int j0 = c * Lc;
   const int j1 = min(n, j0 + Lc);
-  const bool has_cur = j1 == n && j0 < j1;           // this chunk holds the current position
   float *qs = reinterpret_cast<float *>(lds);       // [qpg][dh]
   float *kcur = qs + qpg * dh;                       // [dh]
   float *vcur = kcur + dh;                           // [dh]
-  float *sc = vcur + dh;                             // [qpg][kAttnBlock] scores, then
-  float *ored = sc;                                  // [kWaves][qpg][dh] after the last block
+  float *wml = vcur + dh;                            // [kWaves][qpg][2] per-wave (m, l)
+  float *wo = wml + kWaves * kMaxQpg * 2;            // [kWaves][qpg][dh] per-wave o
   const unsigned long long t0 = now_ticks();
   bool bad = false;
   __syncthreads();   // wave 0 may still be reading the phase scratch this unit reuses
   {
     const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)g * qpg * dh;
-    for (int i = tid; i < qpg * dh; i += kThreads) qs[i] = pay_f(ld_tag_wait(P, qsrc + i, tag_q, t0, bad));
-    if (has_cur && tid < dh) {
-      const size_t nw = (size_t)Hkv * half;
-      if (tid < half) {
-        const u64 w = ld_tag_wait(P, P.kc_t + gen * nw + (size_t)g * half + tid, tag_q, t0, bad);
+    const size_t nw = (size_t)Hkv * half;
+    const bool has_cur = j0 <= pos && pos < j1;
+    // one tagged word per thread: queries, then the current K pairs, then V pairs
+    for (int i = tid; i < qpg * dh + (has_cur ? dh : 0); i += kThreads) {
+      if (i < qpg * dh) {
+        qs[i] = pay_f(ld_tag_wait(P, qsrc + i, tag_q, t0, bad));
+      } else if (i < qpg * dh + half) {
+        const int e = i - qpg * dh;
+        const u64 w = ld_tag_wait(P, P.kc_t + gen * nw + (size_t)g * half + e, tag_q, t0, bad);
         const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w);
-        kcur[tid] = (float)hv.x;
-        kcur[tid + half] = (float)hv.y;
+        kcur[e] = (float)hv.x;
+        kcur[e + half] = (float)hv.y;
       } else {
-        const int jv = tid - half;
-        const u64 w = ld_tag_wait(P, P.vc_t + gen * nw + (size_t)g * half + jv, tag_q, t0, bad);
+        const int e = i - qpg * dh - half;
+        const u64 w = ld_tag_wait(P, P.vc_t + gen * nw + (size_t)g * half + e, tag_q, t0, bad);
         const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w);
-        vcur[2 * jv] = (float)hv.x;
-        vcur[2 * jv + 1] = (float)hv.y;
+        vcur[2 * e] = (float)hv.x;
+        vcur[2 * e + 1] = (float)hv.y;
       }
     }
     if (bad) lds_st(&ctl->abort, 1u);
   }
   __syncthreads();
   if (lds_ld(&ctl->abort)) return false;
-  const size_t lstride = (size_t)P.max_seq * Hkv * dh;
-  const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride;
-  const _Float16 *Vl = reinterpret_cast<const _Float16 *>(P.vcache) + (size_t)l * lstride;
-  float m_run[kMaxQpg], l_run[kMaxQpg], oacc[kMaxQpg][kMaxDpl];
+
+  const bool act = lane < half;                      // lane holds dims 2*lane, 2*lane + 1
+  const int e0 = act ? 2 * lane : 0;
+  float qr[kMaxQpg][2];
 #pragma unroll
   for (int h = 0; h < kMaxQpg; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kMaxDpl; ++e) oacc[h][e] = 0.0f;
+    qr[h][0] = h < qpg && act ? qs[h * dh + e0] : 0.0f;
+    qr[h][1] = h < qpg && act ? qs[h * dh + e0 + 1] : 0.0f;
   }
-  for (int sb = j0; sb < j1; sb += kAttnBlock) {
-    const int nb = min(kAttnBlock, j1 - sb);
-    if (tid < nb) {
-      const int j = sb + tid;
-      float s[kMaxQpg];
+  float m[kMaxQpg], lsum[kMaxQpg], o[kMaxQpg][2];
 #pragma unroll
-      for (int h = 0; h < kMaxQpg; ++h) s[h] = 0.0f;
-      if (j == pos) {
-        for (int e = 0; e < dh; ++e) {
-          const float kv = kcur[e];
+  for (int h = 0; h < kMaxQpg; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.0f;
+    o[h][0] = o[h][1] = 0.0f;
+  }
+  const size_t lstride = (size_t)P.max_seq * Hkv * dh;
+  const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride + (size_t)g * dh + e0;
+  const _Float16 *Vl = reinterpret_cast<const _Float16 *>(P.vcache) + (size_t)l * lstride + (size_t)g * dh + e0;
+  const size_t rstride = (size_t)Hkv * dh;           // elements between positions
+  for (int jb = j0 + wave; jb < j1; jb += kWaves * kKeysPerRound) {
+    unsigned kw[kKeysPerRound], vw[kKeysPerRound];
 #pragma unroll
-          for (int h = 0; h < kMaxQpg; ++h)
-            if (h < qpg) s[h] += qs[h * dh + e] * kv;
-        }
-      } else {
-        const u32x4 *kr = reinterpret_cast<const u32x4 *>(Kl + ((size_t)j * Hkv + g) * dh);
-        for (int e8 = 0; e8 < dh / 8; ++e8) {
-          const f16x8 kv = __builtin_bit_cast(f16x8, kr[e8]);
+    for (int k = 0; k < kKeysPerRound; ++k) {
+      const int j = jb + kWaves * k;
+      kw[k] = vw[k] = 0u;
+      if (j < j1 && j != pos) {
+        kw[k] = *reinterpret_cast<const unsigned *>(Kl + (size_t)j * rstride);
+        vw[k] = *reinterpret_cast<const unsigned *>(Vl + (size_t)j * rstride);
+      }
+    }
+    // per query head: scores of this round's keys, online-softmax rescale, accumulate
 #pragma unroll
-          for (int h = 0; h < kMaxQpg; ++h) {
-            if (h < qpg) {
-              const float *qh = qs + h * dh + e8 * 8;
+    for (int h = 0; h < kMaxQpg; ++h) {
+      if (h < qpg) {
+        float sck[kKeysPerRound];
+        float mb = m[h];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) s[h] += qh[i] * (float)kv[i];
+        for (int k = 0; k < kKeysPerRound; ++k) {
+          const int j = jb + kWaves * k;
+          sck[k] = -INFINITY;
+          if (j < j1) {
+            float k0, k1;
+            if (j == pos) {
+              k0 = kcur[e0];
+              k1 = kcur[e0 + 1];
+            } else {
+              const f16x2 kv = __builtin_bit_cast(f16x2, kw[k]);
+              k0 = (float)kv.x;
+              k1 = (float)kv.y;
             }
+            sck[k] = wave_sum(qr[h][0] * k0 + qr[h][1] * k1) * P.inv_sqrt_dh;
+            mb = fmaxf(mb, sck[k]);
+          }
+        }
+        const float alpha = __expf(m[h] - mb);   // 0 while m is -inf
+        lsum[h] *= alpha;
+        o[h][0] *= alpha;
+        o[h][1] *= alpha;
+        m[h] = mb;
+#pragma unroll
+        for (int k = 0; k < kKeysPerRound; ++k) {
+          const int j = jb + kWaves * k;
+          if (j < j1) {
+            float v0, v1;
+            if (j == pos) {
+              v0 = vcur[e0];
+              v1 = vcur[e0 + 1];
+            } else {
+              const f16x2 vv = __builtin_bit_cast(f16x2, vw[k]);
+              v0 = (float)vv.x;
+              v1 = (float)vv.y;
+            }
+            const float pk = __expf(sck[k] - mb);
+            lsum[h] += pk;
+            o[h][0] += pk * v0;
+            o[h][1] += pk * v1;
           }
         }
       }
-#pragma unroll
-      for (int h = 0; h < kMaxQpg; ++h)
-        if (h < qpg) sc[h * kAttnBlock + tid] = s[h] * P.inv_sqrt_dh;
     }
-    __syncthreads();
-    float m_new[kMaxQpg], alpha[kMaxQpg];
-#pragma unroll
-    for (int h = 0; h < kMaxQpg; ++h) {
-      if (h < qpg) {
-        float v = tid < nb ? sc[h * kAttnBlock + tid] : -INFINITY;
-        v = wave_max(v);
-        if (lane == 0) red[wave * kMaxQpg + h] = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < kMaxQpg; ++h) {
-      m_new[h] = m_run[h];
-      alpha[h] = 0.0f;
-      if (h < qpg) {
-        float mb = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) mb = fmaxf(mb, red[w * kMaxQpg + h]);
-        m_new[h] = fmaxf(m_run[h], mb);
-        alpha[h] = __expf(m_run[h] - m_new[h]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < kMaxQpg; ++h) {
-      if (h < qpg) {
-        float p = 0.0f;
-        if (tid < nb) {
-          p = __expf(sc[h * kAttnBlock + tid] - m_new[h]);
-          sc[h * kAttnBlock + tid] = p;
-        }
-        p = wave_sum(p);
-        if (lane == 0) red[wave * kMaxQpg + h] = p;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < kMaxQpg; ++h) {
-      if (h < qpg) {
-        float lb = 0.0f;
-        for (int w = 0; w < kWaves; ++w) lb += red[w * kMaxQpg + h];
-        l_run[h] = l_run[h] * alpha[h] + lb;
-#pragma unroll
-        for (int e = 0; e < kMaxDpl; ++e) oacc[h][e] *= alpha[h];
-      }
-      m_run[h] = m_new[h];
-    }
-    for (int jj = wave; jj < nb; jj += kWaves) {
-      const int j = sb + jj;
-      float v0, v1 = 0.0f;
-      if (j == pos) {
-        v0 = vcur[lane * dpl];
-        if (dpl == 2) v1 = vcur[lane * dpl + 1];
-      } else {
-        const _Float16 *vr = Vl + ((size_t)j * Hkv + g) * dh + lane * dpl;
-        if (dpl == 2) {
-          const f16x2 vv = *reinterpret_cast<const f16x2 *>(vr);
-          v0 = (float)vv.x;
-          v1 = (float)vv.y;
-        } else {
-          v0 = (float)vr[0];
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < kMaxQpg; ++h) {
-        if (h < qpg) {
-          const float p = sc[h * kAttnBlock + jj];
-          oacc[h][0] += p * v0;
-          oacc[h][1] += p * v1;
-        }
-      }
-    }
-    __syncthreads();
   }
+  // the eight waves' states -> the unit's partial
 #pragma unroll
-  for (int h = 0; h < kMaxQpg; ++h)
+  for (int h = 0; h < kMaxQpg; ++h) {
     if (h < qpg) {
-#pragma unroll
-      for (int e = 0; e < kMaxDpl; ++e)
-        if (e < dpl) ored[(wave * qpg + h) * dh + lane * dpl + e] = oacc[h][e];
+      if (lane == 0) {
+        wml[(wave * kMaxQpg + h) * 2 + 0] = m[h];
+        wml[(wave * kMaxQpg + h) * 2 + 1] = lsum[h];
+      }
+      if (act) {
+        wo[(wave * qpg + h) * dh + e0] = o[h][0];
+        wo[(wave * qpg + h) * dh + e0 + 1] = o[h][1];
+      }
     }
+  }
   __syncthreads();
   if (wave == 0) {
     const int stride = dh + 2;
     u64 *pg = P.part_t + (size_t)gen * P.part_gen;
     u64 *dst = pg + (size_t)u * qpg * stride;
     for (int h = 0; h < qpg; ++h) {
-      for (int e = lane; e < dh; e += 64) {
-        float o = 0.0f;
-        for (int w = 0; w < kWaves; ++w) o += ored[(w * qpg + h) * dh + e];
-        st_tag(&dst[h * stride + 2 + e], tag_f(o, tag_a));
+      float M = -INFINITY;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wml[(w * kMaxQpg + h) * 2]);
+      float Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = wml[(w * kMaxQpg + h) * 2];
+        const float sw = mw == -INFINITY ? 0.0f : __expf(mw - M);
+        Ls += sw * wml[(w * kMaxQpg + h) * 2 + 1];
+        if (act) {
+          a0 += sw * wo[(w * qpg + h) * dh + e0];
+          a1 += sw * wo[(w * qpg + h) * dh + e0 + 1];
+        }
+      }
+      if (act) {
+        st_tag(&dst[h * stride + 2 + e0], tag_f(a0, tag_a));
+        st_tag(&dst[h * stride + 2 + e0 + 1], tag_f(a1, tag_a));
       }
       if (lane == 0) {
-        st_tag(&dst[h * stride + 0], tag_f(m_run[h], tag_a));
-        st_tag(&dst[h * stride + 1], tag_f(l_run[h], tag_a));
+        st_tag(&dst[h * stride + 0], tag_f(M, tag_a));
+        st_tag(&dst[h * stride + 1], tag_f(Ls, tag_a));
       }
     }
-    // Arrival ticket of group g: the unit that completes the count merges.
-    unsigned old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(&P.tickets[l * Hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old == (unsigned)(S - 1)) {
+    if (c == 0) {
+      // the merger: wait for every partial of group g (tags), then combine
       const u64 *src = pg + (size_t)g * S * qpg * stride;
-      float *wgt = red;   // merge weights e^(m_c - M), one per chunk (S <= kMaxSplit = 64)
-      const int e0 = 2 * lane;
       for (int h = 0; h < qpg; ++h) {
-        // one batch: this lane's chunk (m, l) and the first 16 chunks' o pairs
         u64 wm = (u64)tag_a << 32, wl = (u64)tag_a << 32;
         const u64 *mp = &src[((size_t)lane * qpg + h) * stride];
         if (lane < S) {
@@ -808,12 +873,13 @@ __device__ __forceinline__ bool attn_unit(const Params &P, Ctl *ctl, int l, int 
           wl = ld_dev(mp + 1);
         }
         float o0 = 0.0f, o1 = 0.0f, inv = 0.0f;
+        float *wgt = red;   // merge weights e^(m_c - M), one per chunk (S <= kMaxSplit = 64)
         for (int c0 = 0; c0 < S; c0 += 16) {
           u64 v[16][2];
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const size_t at = ((size_t)(c0 + j) * qpg + h) * stride + 2 + e0;
-            const bool use = c0 + j < S && e0 < dh;
+            const bool use = c0 + j < S && act;
             v[j][0] = use ? ld_dev(&src[at]) : ((u64)tag_a << 32);
             v[j][1] = use ? ld_dev(&src[at + 1]) : ((u64)tag_a << 32);
           }
@@ -822,7 +888,7 @@ __device__ __forceinline__ bool attn_unit(const Params &P, Ctl *ctl, int l, int 
             if (tag_of(wl) != tag_a) wl = ld_tag_wait(P, mp + 1, tag_a, t0, bad);
             const float mc = lane < S ? pay_f(wm) : -INFINITY;
             const float M = wave_max(mc);
-            const float w = lane < S ? __expf(mc - M) : 0.0f;
+            const float w = lane < S && mc != -INFINITY ? __expf(mc - M) : 0.0f;
             const float Lsum = wave_sum(w * (lane < S ? pay_f(wl) : 0.0f));
             if (lane < S) wgt[lane] = w;
             inv = 1.0f / Lsum;
@@ -830,7 +896,7 @@ __device__ __forceinline__ bool attn_unit(const Params &P, Ctl *ctl, int l, int 
           }
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            if (c0 + j < S && e0 < dh) {
+            if (c0 + j < S && act) {
               const size_t at = ((size_t)(c0 + j) * qpg + h) * stride + 2 + e0;
               if (tag_of(v[j][0]) != tag_a) v[j][0] = ld_tag_wait(P, &src[at], tag_a, t0, bad);
               if (tag_of(v[j][1]) != tag_a) v[j][1] = ld_tag_wait(P, &src[at + 1], tag_a, t0, bad);
@@ -839,13 +905,12 @@ __device__ __forceinline__ bool attn_unit(const Params &P, Ctl *ctl, int l, int 
             }
           }
         }
-        if (e0 < dh) {
+        if (act) {
           const size_t ow = (size_t)gen * (P.Hq * dh / 2) + ((size_t)(g * qpg + h) * dh + e0) / 2;
           st_tag(&P.o_t[ow], tag_h2(o0 * inv, o1 * inv, tag_a));
         }
         lds_drain();   // wgt is rewritten for the next head
       }
-      if (lane == 0) st_dev(&P.tickets[l * Hkv + g], 0u);
       if (bad && lane == 0) lds_st(&ctl->abort, 1u);
     }
   }
@@ -1056,13 +1121,18 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
 // read is followed by an output that every later phase depends on; a buffer of
 // one generation is rewritten two layers later, after every reader of it.
 template <bool kPrefill>
-__global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
+__global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
+  // Parg is the only argument: read it where the dispatch placed it, at the
+  // start of the kernel-argument segment (never through a copy).
+  (void)Parg;
+  KP &P = *(KP *)(__builtin_amdgcn_kernarg_segment_ptr());
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16 *hl = reinterpret_cast<_Float16 *>(smem + P.lds_h);
   float *part = reinterpret_cast<float *>(smem + P.lds_part);
   float *red = reinterpret_cast<float *>(smem + P.lds_red);   // 64 floats
   Ctl *ctl = reinterpret_cast<Ctl *>(smem + P.lds_ctl);
   float *xown = reinterpret_cast<float *>(smem + P.lds_xown); // residual rows of this workgroup
+  unsigned char *glds = smem + P.lds_gain;                    // norm gains of the phase being staged
   unsigned char *alds = smem + P.lds_h;                       // attention / sampler scratch
   const int b = blockIdx.x, G = P.G, wave = wave_id(), lane = lane_id();
   const int L = P.L, d = P.d, dh = P.dh;
@@ -1103,6 +1173,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
     st.issued = 0;
     st.timed = (P.flags & 4u) && st.cw == 0;
     st.t_ready = st.t_work = st.pieces = 0;
+    st.trace_k = -1;
     st.locate(0);
     for (int i = 0; i < kRing; ++i) st.issue();
     unsigned consumed = 0;
@@ -1115,15 +1186,20 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
         const int q0 = t * ngp + 4 * l;
         const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
         const int gen = (t * L + l) & 1;
+        st.trace_k = t == P.trace_token ? 5 * l + 0 : -1;
         if (!stream_phase(st, consumed, q0 + 0, K_QKV, ctl, hl, part)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
           if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
+        st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
         if (!stream_phase(st, consumed, q0 + 1, K_O, ctl, hl, part)) return;
+        st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
         if (!stream_phase(st, consumed, q0 + 2, K_GU, ctl, hl, part)) return;
+        st.trace_k = t == P.trace_token ? 5 * l + 4 : -1;
         if (!stream_phase(st, consumed, q0 + 3, K_D, ctl, hl, part)) return;
       }
       if (has_lm) {
+        st.trace_k = t == P.trace_token ? 5 * L : -1;
         if (!stream_phase(st, consumed, t * ngp + 4 * L, K_LM, ctl, hl, part)) return;
         if (b == 0 && P.sampling) {
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
@@ -1134,9 +1210,9 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
       }
     }
     if (st.timed && lane == 0) {
-      P.stats[b * kStatWords + 9] = st.t_ready;
-      P.stats[b * kStatWords + 10] = st.t_work;
-      P.stats[b * kStatWords + 11] = st.pieces;
+      P.stats[b * P.stat_stride + 9] = st.t_ready;
+      P.stats[b * P.stat_stride + 10] = st.t_work;
+      P.stats[b * P.stat_stride + 11] = st.pieces;
     }
     return;
   }
@@ -1155,43 +1231,57 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
     int S, Lc;
     attn_split(pos + 1, G, P.Hkv, S, Lc);
     for (int l = 0; l < L; ++l) {
+      KP &Pl = fresh(P);
+      sy.P = &Pl;
       const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
       const int q0 = t * ngp + 4 * l;
       const int gen = (t * L + l) & 1;
-      const _Float16 *attn_norm = reinterpret_cast<const _Float16 *>(layer_part(P, l, LW_ATTN_NORM));
-      const _Float16 *ffn_norm = reinterpret_cast<const _Float16 *>(layer_part(P, l, LW_FFN_NORM));
+      const _Float16 *attn_norm = reinterpret_cast<const _Float16 *>(layer_part(Pl, l, LW_ATTN_NORM));
+      const _Float16 *ffn_norm = reinterpret_cast<const _Float16 *>(layer_part(Pl, l, LW_FFN_NORM));
 
       // ---------------- attention norm + QKV + rotary + KV append
       {
         if (l == 0 && t > 0) {
-          if (kPrefill || P.hidden_io) {
+          if (kPrefill || Pl.hidden_io) {
             // the previous token is finished everywhere (its reads included)
             if (!poll_level(sy, 0, G, lv0)) { fail(); return; }
           } else {
             if (!poll_level(sy, 0, 1, lv0)) { fail(); return; }
-            token = ld_dev(P.tok_slot);
+            token = ld_dev(Pl.tok_slot);
           }
         }
-        const Geo ge = ctl->geo[K_QKV];
+        const Geo ge = uniform_geo(ctl, K_QKV);
+        // rotary factors of this lane's first row pair, loaded before the wait
+        float cs0 = 0.0f, sn0 = 0.0f;
+        if (lane < ge.nrows / 2) {
+          const int r = ge.r0 + 2 * lane;
+          if (r < nq + nk) {
+            const int k = ((r < nq ? r : r - nq) % dh) / 2;
+            cs0 = Pl.rope[((size_t)pos * half + k) * 2 + 0];
+            sn0 = Pl.rope[((size_t)pos * half + k) * 2 + 1];
+          }
+        }
         unsigned long long tq = now_ticks();
         if (ge.nrows > 0) {
           if (l > 0) {
-            if (!stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, attn_norm, d, P.eps,
-                                      hl)) { fail(); return; }
-          } else if (P.hidden_io) {
-            stage_rmsnorm_plain(P.x_hidden, nullptr, attn_norm, d, P.eps, hl);
+            if (!stage_rmsnorm_tagged(sy, Pl.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, attn_norm, d, Pl.eps,
+                                      hl, glds)) { fail(); return; }
+          } else if (Pl.hidden_io) {
+            stage_rmsnorm_plain(Pl.x_hidden, nullptr, attn_norm, d, Pl.eps, hl, glds);
           } else {
-            stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, attn_norm, d, P.eps, hl);
+            stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, attn_norm, d, Pl.eps, hl, glds);
           }
         }
         tq = lap(sy, ST_STAGE, tq);
+        trace(Pl, t, 5 * l + 0, 0);
         announce_input(ctl, q0);
         wait_streams(ctl, q0);
         tq = lap(sy, ST_STREAMS, tq);
+        trace(Pl, t, 5 * l + 0, 1);
         const unsigned tag = lvl + PH_QKV;
-        const size_t kvrow = ((size_t)l * P.max_seq + pos) * (size_t)nk;
-        _Float16 *kc = reinterpret_cast<_Float16 *>(P.kcache);
-        _Float16 *vc = reinterpret_cast<_Float16 *>(P.vcache);
+        const size_t kvrow = ((size_t)l * Pl.max_seq + pos) * (size_t)nk;
+        _Float16 *kc = reinterpret_cast<_Float16 *>(Pl.kcache);
+        _Float16 *vc = reinterpret_cast<_Float16 *>(Pl.vcache);
         for (int i = lane; i < ge.nrows / 2; i += 64) {
           const float a = row_value(part, ge, 2 * i), bb = row_value(part, ge, 2 * i + 1);
           const int r = ge.r0 + 2 * i;
@@ -1199,85 +1289,94 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
             // q / k rows come in rotary pairs (dims k, k + dh/2 of head hd)
             const int rr = r < nq ? r : r - nq;
             const int hd = rr / dh, k = (rr % dh) / 2;
-            const float cs = P.rope[((size_t)pos * half + k) * 2 + 0];
-            const float sn = P.rope[((size_t)pos * half + k) * 2 + 1];
+            const float cs = i == lane ? cs0 : Pl.rope[((size_t)pos * half + k) * 2 + 0];
+            const float sn = i == lane ? sn0 : Pl.rope[((size_t)pos * half + k) * 2 + 1];
             const float y0 = a * cs - bb * sn, y1 = bb * cs + a * sn;
             if (r < nq) {
-              u64 *qd = P.q_t + (size_t)gen * nq + (size_t)hd * dh;
+              u64 *qd = Pl.q_t + (size_t)gen * nq + (size_t)hd * dh;
               st_tag(qd + k, tag_f(y0, tag));
               st_tag(qd + k + half, tag_f(y1, tag));
             } else {
               st_dev_h(kc, kvrow + (size_t)hd * dh + k, y0);
               st_dev_h(kc, kvrow + (size_t)hd * dh + k + half, y1);
-              st_tag(P.kc_t + gen * nkw + (size_t)hd * half + k, tag_h2(y0, y1, tag));
+              st_tag(Pl.kc_t + gen * nkw + (size_t)hd * half + k, tag_h2(y0, y1, tag));
             }
           } else {
             const int rv = r - nq - nk;   // V rows in natural order, pairs (rv, rv + 1)
             const u64 w = tag_h2(a, bb, tag);
             st_dev(reinterpret_cast<unsigned *>(vc + kvrow + rv), (unsigned)w);
-            st_tag(P.vc_t + gen * nkw + (size_t)(rv / 2), w);
+            st_tag(Pl.vc_t + gen * nkw + (size_t)(rv / 2), w);
           }
         }
-        publish_fast(P, tag);
+        publish_fast(Pl, tag);
+        trace(Pl, t, 5 * l + 0, 2);
         lap(sy, ST_EPI, tq);
       }
 
       // ---------------- attention (all waves; split-K, last arriver merges)
       {
         const unsigned long long ta = now_ticks();
-        for (int u = b; u < P.Hkv * S; u += G)
-          if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
-        publish_fast(P, lvl + PH_ATTN);
+        trace(Pl, t, 5 * l + 1, 0);
+        for (int u = b; u < Pl.Hkv * S; u += G)
+          if (!attn_unit(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
+        trace(Pl, t, 5 * l + 1, 1);
+        publish_fast(Pl, lvl + PH_ATTN);
+        trace(Pl, t, 5 * l + 1, 2);
         lap(sy, ST_ATTN, ta);
       }
 
       // ---------------- output projection + residual
       {
-        const Geo ge = ctl->geo[K_O];
+        const Geo ge = uniform_geo(ctl, K_O);
         unsigned long long tk = now_ticks();
         if (ge.nrows > 0 &&
-            !stage_pairs_tagged(sy, P.o_t + (size_t)gen * (nq / 2), nq / 2, lvl + PH_ATTN, hl)) { fail(); return; }
+            !stage_pairs_tagged(sy, Pl.o_t + (size_t)gen * (nq / 2), nq / 2, lvl + PH_ATTN, hl)) { fail(); return; }
         tk = lap(sy, ST_STAGE, tk);
+        trace(Pl, t, 5 * l + 2, 0);
         announce_input(ctl, q0 + 1);
         wait_streams(ctl, q0 + 1);
         tk = lap(sy, ST_STREAMS, tk);
-        // Every store this wave made before (KV cache rows, the split-K ticket
-        // reset, tagged words) has completed before anything it publishes from
-        // here on: later steps read the cache rows with plain loads.  They were
-        // issued a whole projection ago, so this wait is short.
+        trace(Pl, t, 5 * l + 2, 1);
+        // Every store this wave made before (KV cache rows, tagged words) has
+        // completed before anything it publishes from here on: later steps
+        // read the cache rows with plain loads.  They were issued a whole
+        // projection ago, so this wait is short.
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         asm volatile("" ::: "memory");
         const unsigned tag = lvl + PH_O;
-        u64 *xm = P.xmid_t + (size_t)gen * d;
+        u64 *xm = Pl.xmid_t + (size_t)gen * d;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
           float xin;
           if (l > 0) xin = xown[i];
-          else if (P.hidden_io) xin = P.x_hidden[r];
+          else if (Pl.hidden_io) xin = Pl.x_hidden[r];
           else xin = (float)emb[(size_t)token * d + r];
           const float x = xin + row_value(part, ge, i);
           xown[i] = x;
           st_tag(xm + r, tag_f(x, tag));
         }
-        publish_fast(P, tag);
+        publish_fast(Pl, tag);
+        trace(Pl, t, 5 * l + 2, 2);
         lap(sy, ST_EPI, tk);
       }
 
       // ---------------- FFN norm + gate/up + SwiGLU
       {
-        const Geo ge = ctl->geo[K_GU];
+        const Geo ge = uniform_geo(ctl, K_GU);
         unsigned long long tk = now_ticks();
         if (ge.nrows > 0 &&
-            !stage_rmsnorm_tagged(sy, P.xmid_t + (size_t)gen * d, lvl + PH_O, ffn_norm, d, P.eps, hl)) {
+            !stage_rmsnorm_tagged(sy, Pl.xmid_t + (size_t)gen * d, lvl + PH_O, ffn_norm, d, Pl.eps, hl, glds)) {
           fail();
           return;
         }
         tk = lap(sy, ST_STAGE, tk);
+        trace(Pl, t, 5 * l + 3, 0);
         announce_input(ctl, q0 + 2);
         wait_streams(ctl, q0 + 2);
         tk = lap(sy, ST_STREAMS, tk);
+        trace(Pl, t, 5 * l + 3, 1);
         const unsigned tag = lvl + PH_GU;
-        u64 *ad = P.a_t + (size_t)gen * (P.F / 2);
+        u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
         for (int i = lane; i < ge.nrows / 4; i += 64) {
           // rows 4i..4i+3 = gate j, up j, gate j+1, up j+1 with j = r0/2 + 2i
           const float g0 = row_value(part, ge, 4 * i), u0 = row_value(part, ge, 4 * i + 1);
@@ -1285,34 +1384,39 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
           const float s0 = g0 / (1.0f + __expf(-g0)), s1 = g1 / (1.0f + __expf(-g1));
           st_tag(ad + ge.r0 / 4 + i, tag_h2(s0 * u0, s1 * u1, tag));
         }
-        publish_fast(P, tag);
+        publish_fast(Pl, tag);
+        trace(Pl, t, 5 * l + 3, 2);
         lap(sy, ST_EPI, tk);
       }
 
       // ---------------- down projection + residual
       {
-        const Geo ge = ctl->geo[K_D];
+        const Geo ge = uniform_geo(ctl, K_D);
         unsigned long long tk = now_ticks();
         if (ge.nrows > 0 &&
-            !stage_pairs_tagged(sy, P.a_t + (size_t)gen * (P.F / 2), P.F / 2, lvl + PH_GU, hl)) { fail(); return; }
+            !stage_pairs_tagged(sy, Pl.a_t + (size_t)gen * (Pl.F / 2), Pl.F / 2, lvl + PH_GU, hl)) { fail(); return; }
         tk = lap(sy, ST_STAGE, tk);
+        trace(Pl, t, 5 * l + 4, 0);
         announce_input(ctl, q0 + 3);
         wait_streams(ctl, q0 + 3);
         tk = lap(sy, ST_STREAMS, tk);
+        trace(Pl, t, 5 * l + 4, 1);
         const unsigned tag = lvl + PH_D;
-        u64 *xo = P.xout_t + (size_t)gen * d;
-        const bool host_out = P.hidden_io && l == L - 1;
+        u64 *xo = Pl.xout_t + (size_t)gen * d;
+        const bool host_out = Pl.hidden_io && l == L - 1;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
           const float x = xown[i] + row_value(part, ge, i);
           xown[i] = x;
           st_tag(xo + r, tag_f(x, tag));
-          if (host_out) P.x_out[r] = x;
+          if (host_out) Pl.x_out[r] = x;
         }
-        publish_fast(P, tag);
+        publish_fast(Pl, tag);
+        trace(Pl, t, 5 * l + 4, 2);
         lap(sy, ST_EPI, tk);
       }
     }
+    sy.P = &P;
     if (!has_lm) continue;
 
     // ---------------- final norm + lm_head + local argmax
@@ -1320,15 +1424,17 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
     const int qlm = t * ngp + 4 * L;
     const unsigned long long tlm = now_ticks();
     {
-      const Geo ge = ctl->geo[K_LM];
+      const Geo ge = uniform_geo(ctl, K_LM);
       if (ge.nrows > 0 &&
           !stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + L - 1) & 1) * d, lvl_lm - 1u,
-                                reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl)) {
+                                reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl, glds)) {
         fail();
         return;
       }
+      trace(P, t, 5 * L, 0);
       announce_input(ctl, qlm);
       wait_streams(ctl, qlm);
+      trace(P, t, 5 * L, 1);
       float best = -INFINITY;
       int bi = 0x7fffffff;
       for (int i = lane; i < ge.nrows; i += 64) {
@@ -1346,6 +1452,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
         st_dev(&P.lm_idx[b], bi);
       }
       publish_sync(P, lvl_lm);
+      trace(P, t, 5 * L, 2);
     }
 
     // ---------------- next token (workgroup 0)
@@ -1379,13 +1486,14 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params P) {
         P.out_tokens[t] = tok;
       }
       publish_sync(P, lvl_lm + 1u);
+      trace(P, t, 5 * L + 1, 2);
     }
     lap(sy, ST_LM, tlm);
   }
   if ((P.flags & 4u) && lane == 0) {
     unsigned xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    unsigned long long *o = P.stats + (size_t)b * kStatWords;
+    unsigned long long *o = P.stats + (size_t)b * P.stat_stride;
     o[0] = sy.spin;
     o[1] = sy.waits;
     o[2] = xcc & 0xfu;
