@@ -310,7 +310,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
       {&x_hidden, (size_t)d * 4}, {&x_out, (size_t)d * 4}, {&logits, (size_t)(V > 0 ? V : 1) * 4},
       {&lm_val, (size_t)G * 4}, {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4},
       {&tickets, (size_t)c.n_layers * Hkv * 4}, {&tok_slot, 16}, {&errw, 16},
-      {&stats, (size_t)G * (lf::kStatWords + (lf::kTrace ? 6 * (5 * c.n_layers + 2) : 0)) * 8}};
+      {&stats, (size_t)G * (lf::kStatWords + (lf::kTrace ? 8 * (5 * c.n_layers + 2) : 0)) * 8}};
   size_t arena = 0;
   for (auto &sl : slots) arena += align_up(sl.bytes, 256);
   char *ar = (char *)dev_alloc(st, arena, &e);
@@ -322,7 +322,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lm_val = (float *)lm_val; P.lm_idx = (int *)lm_idx; P.progress = (unsigned *)progress;
   P.tickets = (unsigned *)tickets; P.tok_slot = (int *)tok_slot; P.err = (unsigned *)errw;
   P.stats = (unsigned long long *)stats;
-  P.stat_stride = lf::kStatWords + (lf::kTrace ? 6 * (5 * c.n_layers + 2) : 0);
+  P.stat_stride = lf::kStatWords + (lf::kTrace ? 8 * (5 * c.n_layers + 2) : 0);
   // tagged exchange words, two generations each, in one zeroed allocation
   {
     struct TSlot { unsigned long long **dst; size_t words; };
@@ -365,8 +365,8 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (size_t)lf::kWaves * 8 * 2 * 4 +
                         (size_t)lf::kWaves * P.qpg * dh * 4;
   const size_t samp_b = 4096;
-  size_t region_a = h_b + part_b;
-  if ((size_t)d * 4 > region_a) region_a = (size_t)d * 4;   // fp32 staging of a layer input
+  // [h | part]; part also holds the fp32 copy of a vector being normalised
+  size_t region_a = h_b + (part_b > (size_t)d * 4 ? part_b : align_up((size_t)d * 4, 16));
   if (attn_b > region_a) region_a = attn_b;
   if (samp_b > region_a) region_a = samp_b;
   P.lds_h = 0;
@@ -375,16 +375,15 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + 256;
   P.lds_gain = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
-  P.lds_ring = (int)align_up((size_t)P.lds_gain + align_up((size_t)d * 2, 1024), 256);
+  const size_t lds_end = align_up((size_t)P.lds_gain + align_up((size_t)d * 2, 1024), 256);
   P.part_rows = rows_max;
   P.hmax = hmax;
   int lds_limit = 0;
   (void)hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, st->device);
   if (lds_limit <= 0) lds_limit = 65536;
-  const int rings = (lf::kWaves - 1) * lf::kRingSlots * 1024;
-  if (P.lds_ring + rings > lds_limit)
+  if ((long long)lds_end > lds_limit)
     return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
-  P.lds_bytes = P.lds_ring + rings;
+  P.lds_bytes = (int)lds_end;
   P.plain_launch = (std::getenv("LF_PLAIN_LAUNCH") && std::atoi(std::getenv("LF_PLAIN_LAUNCH")) != 0) ? 1 : 0;
   P.poll_first = (std::getenv("LF_POLL_FIRST") && std::atoi(std::getenv("LF_POLL_FIRST")) != 0) ? 1 : 0;
   for (int pf = 0; pf < 2; ++pf) {

@@ -20,9 +20,9 @@ constexpr bool kTrace = true;
 constexpr bool kTrace = false;
 #endif
 #ifndef LF_RING_SLOTS
-#define LF_RING_SLOTS 16
+#define LF_RING_SLOTS 8
 #endif
-constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB slots of each stream wave's LDS ring
+constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB pieces in flight per stream wave (register ring)
 
 // Phases of one layer; each completes one "level" of the dependency chain.
 enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYER = 5 };
@@ -81,7 +81,7 @@ struct Params {
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   int poll_first;          // 1: poll the producers' progress words before reading tagged data
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_gain, lds_ring, lds_bytes;
+  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_gain, lds_bytes;
   int part_rows, hmax;
 };
 

@@ -65,7 +65,7 @@ __device__ __forceinline__ KP &fresh(KP &P) {
 }
 
 constexpr int kNcw = kWaves - 1;       // stream waves per workgroup
-constexpr int kRing = kRingSlots;      // 1-KB slots in each stream wave's LDS ring
+constexpr int kRing = kRingSlots;      // 1-KB pieces each stream wave keeps in flight (registers)
 constexpr int kMaxQpg = 8;             // query heads per KV head supported
 constexpr int kMaxDpl = 2;             // head dims per lane (head_dim <= 128)
 enum Kind { K_QKV = 0, K_O = 1, K_GU = 2, K_D = 3, K_LM = 4, K_COUNT = 5 };
@@ -226,21 +226,28 @@ struct Sync {
   unsigned long long waits;
   unsigned long long tm[kStatPhases];   // sync-wave time by activity (LF_STATS)
   unsigned long long rt_sum, rt_n, nfetch;   // tagged-read rounds: total ticks, count; fetches
+  int trace_k;                               // LF_TRACE: phase slot being staged, else -1
+  bool timed;                                // LF_STATS: activity timers on
 };
 
 // Add the ticks since t0 to activity k; returns the current tick.
 __device__ __forceinline__ unsigned long long lap(Sync &s, int k, unsigned long long t0) {
+  if (!s.timed) return 0ull;
   const unsigned long long t1 = now_ticks();
   s.tm[k] += t1 - t0;
   return t1;
 }
+// The current tick when activity timers are on (LF_STATS), else 0.
+__device__ __forceinline__ unsigned long long stamp(const Sync &s) { return s.timed ? now_ticks() : 0ull; }
 
 // LF_TRACE builds: timestamp j (0 input staged, 1 streams done, 2 published;
-// stream wave 1: 3 input seen, 4 first ring's worth consumed, 5 done)
+// stream wave 1: 3 input seen, 4 first ring's worth consumed, 5 done; wave 0:
+// 6 staging started, 7 tagged input complete; attention: 3 queries staged,
+// 4 keys done, 5 partial stored)
 // of phase k (5l + {QKV, attention, O, gate/up, down}; 5L lm_head; 5L+1 token).
 __device__ __forceinline__ void trace(KP &P, int t, int k, int j) {
   if (kTrace && t == P.trace_token && lane_id() == 0)
-    P.stats[(size_t)blockIdx.x * P.stat_stride + kStatWords + 6 * k + j] = now_ticks();
+    P.stats[(size_t)blockIdx.x * P.stat_stride + kStatWords + 8 * k + j] = now_ticks();
 }
 
 // The bound of a wait started at t0 has expired: record the first such event in
@@ -326,7 +333,7 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
   s.nfetch += 1;
   for (int base = 0; base < n; base += 64 * kStageBatch) {
     for (;;) {
-      const unsigned long long tr = now_ticks();
+      const unsigned long long tr = stamp(s);
       u64 v[kStageBatch];
 #pragma unroll
       for (int j = 0; j < kStageBatch; ++j) {
@@ -337,9 +344,13 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
 #pragma unroll
       for (int j = 0; j < kStageBatch; ++j) bad |= (unsigned)(tag_of(v[j]) != tag);
       const unsigned ok = wave_min_u32(1u - bad);
-      s.rt_sum += now_ticks() - tr;
-      s.rt_n += 1;
+      if (s.timed) {
+        s.rt_sum += now_ticks() - tr;
+        s.rt_n += 1;
+      }
       if (ok == 1u) {
+        if (kTrace && s.trace_k >= 0 && base + 64 * kStageBatch >= n && lane == 0)
+          P.stats[(size_t)blockIdx.x * P.stat_stride + kStatWords + 8 * s.trace_k + 7] = now_ticks();
 #pragma unroll
         for (int j = 0; j < kStageBatch; ++j) {
           const int i = base + 64 * j + lane;
@@ -369,34 +380,31 @@ __device__ __forceinline__ void gain_ready() {
   asm volatile("" ::: "memory");
 }
 
-// In-place second pass of RMSNorm: xs (fp32 staged in LDS at h's address) ->
-// h = fp16(g * (x / r)), gains g in LDS.  Iteration k reads fp32 elements [128k, 128k+128) and
-// then writes fp16 elements of the same range, which occupy bytes already read.
-__device__ __forceinline__ void normalize_in_place(const _Float16 *g, int d, float r, _Float16 *h) {
-  const float *xs = reinterpret_cast<const float *>(h);
-  for (int base = 0; base < d; base += 128) {
-    const int i = base + 2 * lane_id();
-    float a = 0.0f, b = 0.0f;
-    if (i < d) {
-      a = xs[i];
-      b = xs[i + 1];
-    }
-    lds_drain();
-    if (i < d) {
-      const f16x2 gg = *reinterpret_cast<const f16x2 *>(g + i);
-      f16x2 o;
-      o.x = (_Float16)((float)gg.x * (a / r));
-      o.y = (_Float16)((float)gg.y * (b / r));
-      *reinterpret_cast<f16x2 *>(h + i) = o;
-    }
-    lds_drain();
+// Second pass of RMSNorm: h = fp16(g * (x / r)) from the fp32 vector xs, eight
+// elements per lane per step (gains g in LDS).
+__device__ __forceinline__ void normalize(const float *xs, const _Float16 *g, int d, float r, _Float16 *h) {
+  const float4 *x4 = reinterpret_cast<const float4 *>(xs);
+  const f16x8 *g8 = reinterpret_cast<const f16x8 *>(g);
+  f16x8 *h8 = reinterpret_cast<f16x8 *>(h);
+  for (int v = lane_id(); v < d / 8; v += 64) {
+    const float4 a = x4[2 * v], b = x4[2 * v + 1];
+    const f16x8 gg = g8[v];
+    f16x8 o;
+    o[0] = (_Float16)((float)gg[0] * (a.x / r));
+    o[1] = (_Float16)((float)gg[1] * (a.y / r));
+    o[2] = (_Float16)((float)gg[2] * (a.z / r));
+    o[3] = (_Float16)((float)gg[3] * (a.w / r));
+    o[4] = (_Float16)((float)gg[4] * (b.x / r));
+    o[5] = (_Float16)((float)gg[5] * (b.y / r));
+    o[6] = (_Float16)((float)gg[6] * (b.z / r));
+    o[7] = (_Float16)((float)gg[7] * (b.w / r));
+    h8[v] = o;
   }
 }
 
 // RMSNorm of a residual published by other workgroups as tagged fp32 words.
 __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, unsigned tag, const _Float16 *gain,
-                                                     int d, float eps, _Float16 *h, unsigned char *glds) {
-  float *xs = reinterpret_cast<float *>(h);
+                                                     int d, float eps, _Float16 *h, unsigned char *glds, float *xs) {
   const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
   prefetch_gain(gain, d, glds);
   float ss = 0.0f;
@@ -409,14 +417,13 @@ __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, un
   ss = wave_sum(ss);
   lds_drain();
   gain_ready();
-  normalize_in_place(g, d, sqrtf(ss / (float)d + eps), h);
+  normalize(xs, g, d, sqrtf(ss / (float)d + eps), h);
   return true;
 }
 
 // RMSNorm of a layer-0 input: an fp16 embedding row or the host's fp32 vector.
 __device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _Float16 *x16, const _Float16 *gain,
-                                                    int d, float eps, _Float16 *h, unsigned char *glds) {
-  float *xs = reinterpret_cast<float *>(h);
+                                                    int d, float eps, _Float16 *h, unsigned char *glds, float *xs) {
   const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
   prefetch_gain(gain, d, glds);
   const int lane = lane_id();
@@ -440,7 +447,7 @@ __device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _
   ss = wave_sum(ss);
   lds_drain();
   gain_ready();
-  normalize_in_place(g, d, sqrtf(ss / (float)d + eps), h);
+  normalize(xs, g, d, sqrtf(ss / (float)d + eps), h);
 }
 
 // A vector published as tagged fp16 pairs (n_pairs words) into LDS h.
@@ -488,21 +495,29 @@ __device__ __forceinline__ void wave_slice(int np, int cw, int &lo, int &hi) {
 
 static_assert((kRing & (kRing - 1)) == 0 && kRing <= 32, "ring depth must be a power of two <= 32");
 
-// The issue side of a stream wave: walks GEMV phases q = 0, 1, ... of the launch
-// (token t = q / ngp, phase g = q % ngp; g < 4L is (layer g/4, kind g%4), else
-// the lm_head) and issues one 1-KB piece per call into the wave's LDS ring.  A
-// piece is 64 consecutive 16-byte vectors of one row (the last piece of a row
-// may be partial: its idle lanes re-read the row's last vector).  All cursor
-// state is wave-uniform; the only per-lane value is the lane's byte offset.
+// A stream wave's weights in flight: kRing 16-byte vectors per lane (one 1-KB
+// piece per slot), loaded with non-temporal global loads straight into
+// registers.  Each wave's pieces of a phase are padded with dummy pieces (a
+// re-read of one cached vector) to a whole number of rounds of kRing, so a phase
+// always starts at slot 0, every slot is loaded and consumed unconditionally,
+// every register index is a compile-time constant, and the compiler's wait
+// counters (loads complete in order) wait for exactly the oldest slot.
+//
+// The issue side runs one round ahead of the consume side and walks GEMV phases
+// q = 0, 1, ... of the launch (token t = q / ngp, phase g = q % ngp; g < 4L is
+// (layer g/4, kind g%4), else the lm_head).  A piece is 64 consecutive vectors
+// of one row (the last piece of a row may be partial: its idle lanes re-read
+// the row's last vector).  All cursor state is wave-uniform.
 struct Streamer {
   KP *P;
   const Ctl *ctl;
-  unsigned char *ring;        // this wave's ring: kRing slots of 1 KB
   int cw, ngp, qend;
-  int q, left, kp, ppr, tailv;   // phase, pieces left in it, piece in row, pieces per row, vectors in a row's last piece
-  long long adv_last;            // bytes from a row's last piece to the next row
-  const unsigned char *ptr;      // next piece (lane 0's address)
-  unsigned issued;
+  int q, left, pad, kp, ppr, tailv;   // phase, real / dummy pieces left in it, piece in row, pieces per row,
+                                      // vectors in a row's last piece
+  long long adv_last;                 // bytes from a row's last piece to the next row
+  const unsigned char *ptr;           // next real piece (lane 0's address)
+  const unsigned char *dummy;         // the vector dummy pieces re-read
+  u32x4 buf[kRing];
   bool timed;                                 // LF_STATS on stream wave 1
   int trace_k;                                // LF_TRACE: phase slot of the traced token, else -1
   unsigned long long t_ready, t_work, pieces;
@@ -522,6 +537,7 @@ struct Streamer {
       if (lo < hi) {
         const int row = lo / ge.ppr;
         left = hi - lo;
+        pad = (kRing - left % kRing) % kRing;
         kp = lo - row * ge.ppr;
         ppr = ge.ppr;
         tailv = ge.kv - (ge.ppr - 1) * 64;
@@ -533,31 +549,39 @@ struct Streamer {
     }
   }
 
-  __device__ __forceinline__ void issue() {
-    if (q >= qend) return;
+  // load the next piece (real or dummy) into slot k
+  __device__ __forceinline__ void issue(int k) {
     const int lane = lane_id();
+    const bool real = q < qend && left > 0;
     const bool last = kp == ppr - 1;
     const int off = (last ? min(lane, tailv - 1) : lane) * 16;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ptr + off),
-                                     (__attribute__((address_space(3))) void *)(ring + (issued & (kRing - 1)) * 1024u),
-                                     16, 0, 0);
-    ++issued;
-    if (last) {
-      kp = 0;
-      ptr += adv_last;
-    } else {
-      ++kp;
-      ptr += 1024;
+    const unsigned char *src = real ? ptr + off : dummy;
+    buf[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+    if (real) {
+      --left;
+      if (last) {
+        kp = 0;
+        ptr += adv_last;
+      } else {
+        ++kp;
+        ptr += 1024;
+      }
+    } else if (q < qend) {
+      --pad;
     }
-    if (--left == 0) locate(q + 1);
+  }
+  // one round: slots 0 .. kRing-1, then move to the next phase if this one is done
+  __device__ __forceinline__ void next_phase_if_done() {
+    if (q < qend && left == 0 && pad == 0) locate(q + 1);
   }
 };
 
-// A stream wave's share of GEMV phase q: consume its pieces from the ring,
-// refilling the ring as it goes, and leave one partial row sum per (row, wave)
-// in part[row * 8 + cw].  Returns false if the sync wave aborted.
-__device__ __forceinline__ bool stream_phase(Streamer &st, unsigned &consumed, int q, int kind, Ctl *ctl,
-                                             const _Float16 *h, float *part) {
+// A stream wave's share of GEMV phase q: consume its pieces round by round from
+// the register ring, refilling each slot as it is freed, and leave one partial
+// row sum per (row, wave) in part[row * 8 + cw].  Returns false if the sync wave
+// aborted.
+__device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl *ctl, const _Float16 *h,
+                                             float *part) {
   const Geo ge = uniform_geo(ctl, kind);
   int lo, hi;
   wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
@@ -576,47 +600,45 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, unsigned &consumed, i
   const int lane = lane_id();
   const bool tr = kTrace && st.cw == 0 && st.trace_k >= 0;
   unsigned long long *trp =
-      tr ? st.P->stats + (size_t)blockIdx.x * st.P->stat_stride + kStatWords + 6 * st.trace_k : nullptr;
+      tr ? st.P->stats + (size_t)blockIdx.x * st.P->stat_stride + kStatWords + 8 * st.trace_k : nullptr;
   if (tr && lane == 0) trp[3] = now_ticks();
   const u32x4 *hv = reinterpret_cast<const u32x4 *>(h);
-  const u32x4 *ringv = reinterpret_cast<const u32x4 *>(st.ring);
   const int ppr = ge.ppr, tailv = ge.kv - (ge.ppr - 1) * 64;
+  const int n = hi - lo;
   int row = lo / ppr, kp = lo - row * ppr;
   float acc = 0.0f;
-  for (int p = lo; p < hi; ++p) {
-    // in steady state kRing pieces are in flight and the oldest is the one wanted
-    if (st.issued - consumed >= (unsigned)kRing)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | ((kRing - 1) & 15) | (((kRing - 1) >> 4) << 14));
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    asm volatile("" ::: "memory");
-    const bool last = kp == ppr - 1;
-    const u32x4 x = ringv[(consumed & (kRing - 1)) * 64 + lane];
-    const u32x4 hx = hv[kp * 64 + (last ? min(lane, tailv - 1) : lane)];
-    const float a2 = dot8(x, hx, acc);
-    acc = (!last || lane < tailv) ? a2 : acc;
-    lds_drain();                 // the slot has been read before it is refilled
-    ++consumed;
-    if (tr && lane == 0 && p == lo + kRing - 1) trp[4] = now_ticks();
-    st.issue();
-    if (last || p == hi - 1) {
-      const float s = wave_sum_to63(acc);
-      if (lane == 63) part[row * 8 + st.cw] = s;
-      acc = 0.0f;
+  for (int base = 0; base < n; base += kRing) {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) {
+      const int i = base + k;
+      if (i < n) {
+        const bool last = kp == ppr - 1;
+        const u32x4 hx = hv[kp * 64 + (last ? min(lane, tailv - 1) : lane)];
+        const float a2 = dot8(st.buf[k], hx, acc);
+        acc = (!last || lane < tailv) ? a2 : acc;
+        if (last || i == n - 1) {
+          const float s = wave_sum_to63(acc);
+          if (lane == 63) part[row * 8 + st.cw] = s;
+          acc = 0.0f;
+        }
+        if (last) {
+          kp = 0;
+          ++row;
+        } else {
+          ++kp;
+        }
+      }
+      st.issue(k);
     }
-    if (last) {
-      kp = 0;
-      ++row;
-    } else {
-      ++kp;
-    }
+    st.next_phase_if_done();
+    if (tr && lane == 0 && base == 0) trp[4] = now_ticks();
   }
   lds_drain();
   if (tr && lane == 0) trp[5] = now_ticks();
   if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
   if (timed) {
     st.t_work += now_ticks() - t0;
-    st.pieces += (unsigned long long)(hi - lo);
+    st.pieces += (unsigned long long)n;
   }
   return true;
 }
@@ -697,7 +719,7 @@ constexpr int kKeysPerRound = 16;   // keys whose K and V rows one wave loads pe
 // Returns false if a bounded wait expired.
 __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsigned tag_q,
                                           unsigned tag_a, int pos, int u, int S, int Lc, unsigned char *lds,
-                                          float *red) {
+                                          float *red, int trk = -1) {
   KP &P = fresh(P0);
   const int tid = tid_x(), wave = wave_id(), lane = lane_id();
   const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv, half = dh / 2;
@@ -739,6 +761,9 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   }
   __syncthreads();
   if (lds_ld(&ctl->abort)) return false;
+  unsigned long long *trp =
+      kTrace && trk >= 0 && wave == 0 ? P.stats + (size_t)blockIdx.x * P.stat_stride + kStatWords + 8 * trk : nullptr;
+  if (trp && lane == 0) trp[3] = now_ticks();
 
   const bool act = lane < half;                      // lane holds dims 2*lane, 2*lane + 1
   const int e0 = act ? 2 * lane : 0;
@@ -821,6 +846,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       }
     }
   }
+  if (trp && lane == 0) trp[4] = now_ticks();
   // the eight waves' states -> the unit's partial
 #pragma unroll
   for (int h = 0; h < kMaxQpg; ++h) {
@@ -862,6 +888,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
         st_tag(&dst[h * stride + 1], tag_f(Ls, tag_a));
       }
     }
+    if (trp && lane == 0) trp[5] = now_ticks();
     if (c == 0) {
       // the merger: wait for every partial of group g (tags), then combine
       const u64 *src = pg + (size_t)g * S * qpg * stride;
@@ -1158,7 +1185,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
   }
   __syncthreads();
 
-  Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}, 0ull, 0ull, 0ull};
+  Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}, 0ull, 0ull, 0ull, -1, (P.flags & 4u) != 0};
   const unsigned long long kt0 = now_ticks();
 
   if (wave > 0) {
@@ -1167,16 +1194,21 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
     st.P = &P;
     st.ctl = ctl;
     st.cw = wave - 1;
-    st.ring = smem + P.lds_ring + (size_t)st.cw * kRing * 1024;
     st.ngp = ngp;
     st.qend = P.n_tokens * ngp;
-    st.issued = 0;
     st.timed = (P.flags & 4u) && st.cw == 0;
     st.t_ready = st.t_work = st.pieces = 0;
     st.trace_k = -1;
+    st.dummy = reinterpret_cast<const unsigned char *>(P.wbase) + lane * 16;
+    st.left = st.pad = st.kp = 0;
+    st.ppr = 1;
+    st.tailv = 64;
+    st.adv_last = 0;
+    st.ptr = st.dummy;
     st.locate(0);
-    for (int i = 0; i < kRing; ++i) st.issue();
-    unsigned consumed = 0;
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) st.issue(k);
+    st.next_phase_if_done();
     for (int t = 0; t < P.n_tokens; ++t) {
       const int pos = P.pos0 + t;
       const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
@@ -1187,20 +1219,20 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
         const int gen = (t * L + l) & 1;
         st.trace_k = t == P.trace_token ? 5 * l + 0 : -1;
-        if (!stream_phase(st, consumed, q0 + 0, K_QKV, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
           if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
-        if (!stream_phase(st, consumed, q0 + 1, K_O, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
-        if (!stream_phase(st, consumed, q0 + 2, K_GU, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 4 : -1;
-        if (!stream_phase(st, consumed, q0 + 3, K_D, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part)) return;
       }
       if (has_lm) {
         st.trace_k = t == P.trace_token ? 5 * L : -1;
-        if (!stream_phase(st, consumed, t * ngp + 4 * L, K_LM, ctl, hl, part)) return;
+        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part)) return;
         if (b == 0 && P.sampling) {
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
           if (lds_ld(&ctl->abort)) return;
@@ -1261,15 +1293,17 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
             sn0 = Pl.rope[((size_t)pos * half + k) * 2 + 1];
           }
         }
-        unsigned long long tq = now_ticks();
+        unsigned long long tq = stamp(sy);
+        sy.trace_k = t == Pl.trace_token ? 5 * l : -1;
+        trace(Pl, t, 5 * l + 0, 6);
         if (ge.nrows > 0) {
           if (l > 0) {
             if (!stage_rmsnorm_tagged(sy, Pl.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, attn_norm, d, Pl.eps,
-                                      hl, glds)) { fail(); return; }
+                                      hl, glds, part)) { fail(); return; }
           } else if (Pl.hidden_io) {
-            stage_rmsnorm_plain(Pl.x_hidden, nullptr, attn_norm, d, Pl.eps, hl, glds);
+            stage_rmsnorm_plain(Pl.x_hidden, nullptr, attn_norm, d, Pl.eps, hl, glds, part);
           } else {
-            stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, attn_norm, d, Pl.eps, hl, glds);
+            stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, attn_norm, d, Pl.eps, hl, glds, part);
           }
         }
         tq = lap(sy, ST_STAGE, tq);
@@ -1315,10 +1349,11 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
 
       // ---------------- attention (all waves; split-K, last arriver merges)
       {
-        const unsigned long long ta = now_ticks();
+        const unsigned long long ta = stamp(sy);
         trace(Pl, t, 5 * l + 1, 0);
         for (int u = b; u < Pl.Hkv * S; u += G)
-          if (!attn_unit(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
+          if (!attn_unit(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
+                         u == b && t == Pl.trace_token ? 5 * l + 1 : -1)) return;
         trace(Pl, t, 5 * l + 1, 1);
         publish_fast(Pl, lvl + PH_ATTN);
         trace(Pl, t, 5 * l + 1, 2);
@@ -1328,7 +1363,9 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
       // ---------------- output projection + residual
       {
         const Geo ge = uniform_geo(ctl, K_O);
-        unsigned long long tk = now_ticks();
+        unsigned long long tk = stamp(sy);
+        sy.trace_k = t == Pl.trace_token ? 5 * l + 2 : -1;
+        trace(Pl, t, 5 * l + 2, 6);
         if (ge.nrows > 0 &&
             !stage_pairs_tagged(sy, Pl.o_t + (size_t)gen * (nq / 2), nq / 2, lvl + PH_ATTN, hl)) { fail(); return; }
         tk = lap(sy, ST_STAGE, tk);
@@ -1363,9 +1400,11 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
       // ---------------- FFN norm + gate/up + SwiGLU
       {
         const Geo ge = uniform_geo(ctl, K_GU);
-        unsigned long long tk = now_ticks();
+        unsigned long long tk = stamp(sy);
+        sy.trace_k = t == Pl.trace_token ? 5 * l + 3 : -1;
+        trace(Pl, t, 5 * l + 3, 6);
         if (ge.nrows > 0 &&
-            !stage_rmsnorm_tagged(sy, Pl.xmid_t + (size_t)gen * d, lvl + PH_O, ffn_norm, d, Pl.eps, hl, glds)) {
+            !stage_rmsnorm_tagged(sy, Pl.xmid_t + (size_t)gen * d, lvl + PH_O, ffn_norm, d, Pl.eps, hl, glds, part)) {
           fail();
           return;
         }
@@ -1392,7 +1431,9 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
       // ---------------- down projection + residual
       {
         const Geo ge = uniform_geo(ctl, K_D);
-        unsigned long long tk = now_ticks();
+        unsigned long long tk = stamp(sy);
+        sy.trace_k = t == Pl.trace_token ? 5 * l + 4 : -1;
+        trace(Pl, t, 5 * l + 4, 6);
         if (ge.nrows > 0 &&
             !stage_pairs_tagged(sy, Pl.a_t + (size_t)gen * (Pl.F / 2), Pl.F / 2, lvl + PH_GU, hl)) { fail(); return; }
         tk = lap(sy, ST_STAGE, tk);
@@ -1422,12 +1463,12 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
     // ---------------- final norm + lm_head + local argmax
     const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
     const int qlm = t * ngp + 4 * L;
-    const unsigned long long tlm = now_ticks();
+    const unsigned long long tlm = stamp(sy);
     {
       const Geo ge = uniform_geo(ctl, K_LM);
       if (ge.nrows > 0 &&
           !stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + L - 1) & 1) * d, lvl_lm - 1u,
-                                reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl, glds)) {
+                                reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl, glds, part)) {
         fail();
         return;
       }
