@@ -297,6 +297,16 @@ __device__ __forceinline__ void publish_sync(KP &P, unsigned level) {
   if (lane_id() == 0) st_dev(&P.progress[blockIdx.x], level);
 }
 
+// Wave 0: announce a level whose data other workgroups read whole (a staged
+// vector).  With poll-first staging the consumers poll progress words before
+// reading the data once, so the announcement waits for this wave's stores.
+__device__ __forceinline__ void publish_vec(KP &P, unsigned level) {
+  if (P.poll_first)
+    publish_sync(P, level);
+  else
+    publish_fast(P, level);
+}
+
 // All waves: barrier-based wait (wave 0 polls).  Used where the whole workgroup
 // works together (attention, nucleus sampling).  With `acquire`, wave 0 takes an
 // agent-scope acquire fence so the workgroup may read untagged data with plain
@@ -319,7 +329,7 @@ __device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, un
 
 // ---------------------------------------------------------------- staging (wave 0)
 
-constexpr int kStageBatch = 32;   // 8-byte loads in flight per lane while staging
+constexpr int kStageBatch = 40;   // 8-byte loads in flight per lane while staging
 
 // Wave 0: wait until every word src[0..n) carries `tag`, then hand each payload
 // to use(i, word).  All loads of a batch are issued before any is checked, so a
@@ -734,6 +744,27 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   float *wo = wml + kWaves * kMaxQpg * 2;            // [kWaves][qpg][dh] per-wave o
   const unsigned long long t0 = now_ticks();
   bool bad = false;
+  // K/V rows of earlier positions are already in the cache: request this wave's
+  // first round of them before waiting for the queries.
+  const bool act = lane < half;                      // lane holds dims 2*lane, 2*lane + 1
+  const int e0 = act ? 2 * lane : 0;
+  const size_t lstride = (size_t)P.max_seq * Hkv * dh;
+  const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride + (size_t)g * dh + e0;
+  const _Float16 *Vl = reinterpret_cast<const _Float16 *>(P.vcache) + (size_t)l * lstride + (size_t)g * dh + e0;
+  const size_t rstride = (size_t)Hkv * dh;           // elements between positions
+  unsigned kw[kKeysPerRound], vw[kKeysPerRound];
+  auto load_round = [&](int jb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kKeysPerRound; ++k) {
+      const int j = jb + kWaves * k;
+      kw[k] = vw[k] = 0u;
+      if (j < j1 && j != pos) {
+        kw[k] = *reinterpret_cast<const unsigned *>(Kl + (size_t)j * rstride);
+        vw[k] = *reinterpret_cast<const unsigned *>(Vl + (size_t)j * rstride);
+      }
+    }
+  };
+  load_round(j0 + wave);
   __syncthreads();   // wave 0 may still be reading the phase scratch this unit reuses
   {
     const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)g * qpg * dh;
@@ -765,8 +796,6 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       kTrace && trk >= 0 && wave == 0 ? P.stats + (size_t)blockIdx.x * P.stat_stride + kStatWords + 8 * trk : nullptr;
   if (trp && lane == 0) trp[3] = now_ticks();
 
-  const bool act = lane < half;                      // lane holds dims 2*lane, 2*lane + 1
-  const int e0 = act ? 2 * lane : 0;
   float qr[kMaxQpg][2];
 #pragma unroll
   for (int h = 0; h < kMaxQpg; ++h) {
@@ -780,21 +809,8 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     lsum[h] = 0.0f;
     o[h][0] = o[h][1] = 0.0f;
   }
-  const size_t lstride = (size_t)P.max_seq * Hkv * dh;
-  const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride + (size_t)g * dh + e0;
-  const _Float16 *Vl = reinterpret_cast<const _Float16 *>(P.vcache) + (size_t)l * lstride + (size_t)g * dh + e0;
-  const size_t rstride = (size_t)Hkv * dh;           // elements between positions
   for (int jb = j0 + wave; jb < j1; jb += kWaves * kKeysPerRound) {
-    unsigned kw[kKeysPerRound], vw[kKeysPerRound];
-#pragma unroll
-    for (int k = 0; k < kKeysPerRound; ++k) {
-      const int j = jb + kWaves * k;
-      kw[k] = vw[k] = 0u;
-      if (j < j1 && j != pos) {
-        kw[k] = *reinterpret_cast<const unsigned *>(Kl + (size_t)j * rstride);
-        vw[k] = *reinterpret_cast<const unsigned *>(Vl + (size_t)j * rstride);
-      }
-    }
+    if (jb != j0 + wave) load_round(jb);   // the first round was requested before the queries
     // per query head: scores of this round's keys, online-softmax rescale, accumulate
 #pragma unroll
     for (int h = 0; h < kMaxQpg; ++h) {
@@ -1355,7 +1371,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
           if (!attn_unit(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
                          u == b && t == Pl.trace_token ? 5 * l + 1 : -1)) return;
         trace(Pl, t, 5 * l + 1, 1);
-        publish_fast(Pl, lvl + PH_ATTN);
+        publish_vec(Pl, lvl + PH_ATTN);
         trace(Pl, t, 5 * l + 1, 2);
         lap(sy, ST_ATTN, ta);
       }
@@ -1392,7 +1408,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
           xown[i] = x;
           st_tag(xm + r, tag_f(x, tag));
         }
-        publish_fast(Pl, tag);
+        publish_vec(Pl, tag);
         trace(Pl, t, 5 * l + 2, 2);
         lap(sy, ST_EPI, tk);
       }
@@ -1423,7 +1439,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
           const float s0 = g0 / (1.0f + __expf(-g0)), s1 = g1 / (1.0f + __expf(-g1));
           st_tag(ad + ge.r0 / 4 + i, tag_h2(s0 * u0, s1 * u1, tag));
         }
-        publish_fast(Pl, tag);
+        publish_vec(Pl, tag);
         trace(Pl, t, 5 * l + 3, 2);
         lap(sy, ST_EPI, tk);
       }
@@ -1452,7 +1468,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
           st_tag(xo + r, tag_f(x, tag));
           if (host_out) Pl.x_out[r] = x;
         }
-        publish_fast(Pl, tag);
+        publish_vec(Pl, tag);
         trace(Pl, t, 5 * l + 4, 2);
         lap(sy, ST_EPI, tk);
       }
