@@ -4,7 +4,9 @@ Workload (default ``dec2b_25l_greedy``): the synthetic ~2.2B fp16 decoder (25
 layers, d 2560, 20 heads x 128, SwiGLU 6912, vocab 32768 untied, weights
 N(0, 0.02) from seed 0), a 128-token random prompt, greedy decode.  The prompt's
 first 127 tokens go through one teacher-forced launch (untimed); a step is one
-decoded token; W warmup steps run in one launch from position 127, then the
+decoded token.  The W warmup steps run as one more teacher-forced launch of the
+same layer stack from position 127 (so the decode kernel's only dispatch is the
+timed one and a profiler's per-kernel average is the timed launch); then the
 position is reset to 127 and EXACTLY K steps run in ONE lf_generate launch,
 bracketed by device synchronisations and HIP events on the stream the kernel is
 launched on.  Inputs are resident in HBM before timing starts.
@@ -56,6 +58,49 @@ def measured_traffic(workload: str, steps: int):
     return d.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(path: str, counter: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    rows = []
+    with open(files[0], newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+def write_traffic(d: str, workload: str, steps: int) -> int:
+    """HBM bytes of the timed decode launch from counter runs, each counter scaled
+    by its reading for a device copy of 1 GiB (1 GiB read, 1 GiB written)."""
+    kernel = "lf_monokernel<false>"
+    copy_bytes = 1 << 30
+    cal = {}
+    for c, sub in (("FETCH_SIZE", "cfetch"), ("WRITE_SIZE", "cwrite")):
+        copies = [v for _, k, v in _counter_rows(os.path.join(d, sub), c) if "copyBuffer" in k]
+        cal[c] = copy_bytes / max(copies)   # bytes per counted KiB
+    got = {}
+    for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        mine = [v for _, k, v in _counter_rows(os.path.join(d, sub), c) if kernel in k]
+        if not mine:
+            raise SystemExit(f"no {kernel} dispatch in {sub}")
+        got[c] = mine[-1]   # the timed launch is the last (and only) decode dispatch
+    rec = {"workload": workload, "steps": steps, "kernel": kernel, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_counted": got["FETCH_SIZE"], "write_kib_counted": got["WRITE_SIZE"],
+           "fetch_bytes_per_counted_kib": cal["FETCH_SIZE"], "write_bytes_per_counted_kib": cal["WRITE_SIZE"],
+           "hbm_read_bytes_per_launch": int(got["FETCH_SIZE"] * cal["FETCH_SIZE"]),
+           "hbm_write_bytes_per_launch": int(got["WRITE_SIZE"] * cal["WRITE_SIZE"])}
+    rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
 def cpu_baseline(cfg, weights, prompt, seconds: float):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -84,10 +129,16 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--stats", action="store_true", help="build the state with LF_STATS (wait-time counters)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs "
+                         "of this command (DIR/fetch, DIR/write) and of --copy-calibration 1024 (DIR/cfetch, "
+                         "DIR/cwrite), then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (a known-size kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        return write_traffic(args.traffic_from, args.workload, args.steps)
     if args.copy_calibration:
         import torch
         n = args.copy_calibration * (1 << 20) // 4
@@ -130,8 +181,8 @@ def main() -> int:
     eng.prefill(prompt[:pos0], 0)
     torch.cuda.synchronize()
     if W > 0:
-        eng.set_position(int(prompt[pos0]), pos0)
-        eng.generate(W)
+        warm = np.resize(prompt, W).astype(np.int32)   # any in-vocabulary tokens
+        eng.prefill(warm, pos0)
     eng.set_position(int(prompt[pos0]), pos0)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
