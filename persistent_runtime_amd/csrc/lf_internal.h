@@ -81,7 +81,7 @@ struct Params {
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   int poll_first;          // 1: poll the producers' progress words before reading tagged data
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_gain, lds_bytes;
+  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_gain, lds_trace, lds_bytes;
   int part_rows, hmax;
 };
 

@@ -241,13 +241,24 @@ __device__ __forceinline__ unsigned long long lap(Sync &s, int k, unsigned long 
 __device__ __forceinline__ unsigned long long stamp(const Sync &s) { return s.timed ? now_ticks() : 0ull; }
 
 // LF_TRACE builds: timestamp j (0 input staged, 1 streams done, 2 published;
-// stream wave 1: 3 input seen, 4 first ring's worth consumed, 5 done; wave 0:
-// 6 staging started, 7 tagged input complete; attention: 3 queries staged,
-// 4 keys done, 5 partial stored)
+// stream wave 1: 3 input seen, 4 first round done, 5 done; wave 0: 6 staging
+// started, 7 tagged input complete, 8 sum of squares, 9 gains ready, 10
+// normalised; attention: 3 queries staged, 4 keys done, 5 partial stored)
 // of phase k (5l + {QKV, attention, O, gate/up, down}; 5L lm_head; 5L+1 token).
+// Timestamps collect in LDS and are copied out when the kernel ends, so that
+// tracing adds no global stores (and no store waits) to the path it measures.
+typedef __attribute__((address_space(3))) unsigned long long lds_u64;
+constexpr int kTraceSlots = 12;   // timestamps per phase (LF_TRACE builds)
+__device__ __forceinline__ lds_u64 *trace_row(KP &P, int k) {
+  extern __shared__ __align__(16) unsigned char lf_dyn_lds[];
+  return (lds_u64 *)(lf_dyn_lds + P.lds_trace) + kTraceSlots * k;
+}
 __device__ __forceinline__ void trace(KP &P, int t, int k, int j) {
-  if (kTrace && t == P.trace_token && lane_id() == 0)
-    P.stats[(size_t)blockIdx.x * P.stat_stride + kStatWords + 8 * k + j] = now_ticks();
+  if (kTrace && t == P.trace_token && lane_id() == 0) trace_row(P, k)[j] = now_ticks();
+}
+// stamp j of phase slot k, if k >= 0 (lane 0 only)
+__device__ __forceinline__ void trace_at(KP &P, int k, int j) {
+  if (kTrace && k >= 0 && lane_id() == 0) trace_row(P, k)[j] = now_ticks();
 }
 
 // The bound of a wait started at t0 has expired: record the first such event in
@@ -360,7 +371,7 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
       }
       if (ok == 1u) {
         if (kTrace && s.trace_k >= 0 && base + 64 * kStageBatch >= n && lane == 0)
-          P.stats[(size_t)blockIdx.x * P.stat_stride + kStatWords + 8 * s.trace_k + 7] = now_ticks();
+          trace_row(P, s.trace_k)[7] = now_ticks();
 #pragma unroll
         for (int j = 0; j < kStageBatch; ++j) {
           const int i = base + 64 * j + lane;
@@ -390,24 +401,26 @@ __device__ __forceinline__ void gain_ready() {
   asm volatile("" ::: "memory");
 }
 
-// Second pass of RMSNorm: h = fp16(g * (x / r)) from the fp32 vector xs, eight
-// elements per lane per step (gains g in LDS).
+// Second pass of RMSNorm: h = fp16(g * x * (1/r)) from the fp32 vector xs, eight
+// elements per lane per step (gains g in LDS).  The reciprocal is taken once
+// (within an ulp of dividing; the result is rounded to fp16 anyway).
 __device__ __forceinline__ void normalize(const float *xs, const _Float16 *g, int d, float r, _Float16 *h) {
   const float4 *x4 = reinterpret_cast<const float4 *>(xs);
   const f16x8 *g8 = reinterpret_cast<const f16x8 *>(g);
   f16x8 *h8 = reinterpret_cast<f16x8 *>(h);
+  const float inv = 1.0f / r;
   for (int v = lane_id(); v < d / 8; v += 64) {
     const float4 a = x4[2 * v], b = x4[2 * v + 1];
     const f16x8 gg = g8[v];
     f16x8 o;
-    o[0] = (_Float16)((float)gg[0] * (a.x / r));
-    o[1] = (_Float16)((float)gg[1] * (a.y / r));
-    o[2] = (_Float16)((float)gg[2] * (a.z / r));
-    o[3] = (_Float16)((float)gg[3] * (a.w / r));
-    o[4] = (_Float16)((float)gg[4] * (b.x / r));
-    o[5] = (_Float16)((float)gg[5] * (b.y / r));
-    o[6] = (_Float16)((float)gg[6] * (b.z / r));
-    o[7] = (_Float16)((float)gg[7] * (b.w / r));
+    o[0] = (_Float16)((float)gg[0] * (a.x * inv));
+    o[1] = (_Float16)((float)gg[1] * (a.y * inv));
+    o[2] = (_Float16)((float)gg[2] * (a.z * inv));
+    o[3] = (_Float16)((float)gg[3] * (a.w * inv));
+    o[4] = (_Float16)((float)gg[4] * (b.x * inv));
+    o[5] = (_Float16)((float)gg[5] * (b.y * inv));
+    o[6] = (_Float16)((float)gg[6] * (b.z * inv));
+    o[7] = (_Float16)((float)gg[7] * (b.w * inv));
     h8[v] = o;
   }
 }
@@ -425,9 +438,12 @@ __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, un
       }))
     return false;
   ss = wave_sum(ss);
+  if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 8);
   lds_drain();
   gain_ready();
+  if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 9);
   normalize(xs, g, d, sqrtf(ss / (float)d + eps), h);
+  if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 10);
   return true;
 }
 
@@ -608,27 +624,42 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
     t0 = t1;
   }
   const int lane = lane_id();
-  const bool tr = kTrace && st.cw == 0 && st.trace_k >= 0;
-  unsigned long long *trp =
-      tr ? st.P->stats + (size_t)blockIdx.x * st.P->stat_stride + kStatWords + 8 * st.trace_k : nullptr;
-  if (tr && lane == 0) trp[3] = now_ticks();
+  const int trk = kTrace && st.cw == 0 && st.trace_k >= 0 ? st.trace_k : -1;
+  trace_at(*st.P, trk, 3);
   const u32x4 *hv = reinterpret_cast<const u32x4 *>(h);
   const int ppr = ge.ppr, tailv = ge.kv - (ge.ppr - 1) * 64;
   const int n = hi - lo;
   int row = lo / ppr, kp = lo - row * ppr;
   float acc = 0.0f;
-  for (int base = 0; base < n; base += kRing) {
+  // Each round first uses the kRing pieces in the ring, then refills it.  The
+  // first round's pieces landed while the input was pending, and a refill can
+  // stall while every CU refills at once, so consuming first lets a phase start
+  // at register speed; after the last round the phase is finished (done flag)
+  // before its refills, which are the next phase's prefetch, are issued.
+  const int nr = (n + kRing - 1) / kRing;
+  for (int r = 0; r < nr; ++r) {
+    const int base = r * kRing;
+    // the input vectors of this round's pieces, all requested before the first dot
+    u32x4 hx[kRing];
+    {
+      int kq = kp;
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) {
+        const bool last = kq == ppr - 1;
+        hx[k] = hv[kq * 64 + (last ? min(lane, tailv - 1) : lane)];
+        kq = last ? 0 : kq + 1;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kRing; ++k) {
       const int i = base + k;
       if (i < n) {
         const bool last = kp == ppr - 1;
-        const u32x4 hx = hv[kp * 64 + (last ? min(lane, tailv - 1) : lane)];
-        const float a2 = dot8(st.buf[k], hx, acc);
+        const float a2 = dot8(st.buf[k], hx[k], acc);
         acc = (!last || lane < tailv) ? a2 : acc;
         if (last || i == n - 1) {
-          const float s = wave_sum_to63(acc);
-          if (lane == 63) part[row * 8 + st.cw] = s;
+          const float sum = wave_sum_to63(acc);
+          if (lane == 63) part[row * 8 + st.cw] = sum;
           acc = 0.0f;
         }
         if (last) {
@@ -638,14 +669,18 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
           ++kp;
         }
       }
-      st.issue(k);
     }
+    if (r == nr - 1) {
+      lds_drain();
+      trace_at(*st.P, trk, 5);
+      if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
+    }
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) st.issue(k);
     st.next_phase_if_done();
-    if (tr && lane == 0 && base == 0) trp[4] = now_ticks();
+    if (r == 0) trace_at(*st.P, trk, 4);
   }
-  lds_drain();
-  if (tr && lane == 0) trp[5] = now_ticks();
-  if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
+  if (nr == 0 && lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
   if (timed) {
     st.t_work += now_ticks() - t0;
     st.pieces += (unsigned long long)n;
@@ -792,9 +827,8 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   }
   __syncthreads();
   if (lds_ld(&ctl->abort)) return false;
-  unsigned long long *trp =
-      kTrace && trk >= 0 && wave == 0 ? P.stats + (size_t)blockIdx.x * P.stat_stride + kStatWords + 8 * trk : nullptr;
-  if (trp && lane == 0) trp[3] = now_ticks();
+  const int trw = wave == 0 ? trk : -1;
+  trace_at(P, trw, 3);
 
   float qr[kMaxQpg][2];
 #pragma unroll
@@ -862,7 +896,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       }
     }
   }
-  if (trp && lane == 0) trp[4] = now_ticks();
+  trace_at(P, trw, 4);
   // the eight waves' states -> the unit's partial
 #pragma unroll
   for (int h = 0; h < kMaxQpg; ++h) {
@@ -904,7 +938,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
         st_tag(&dst[h * stride + 1], tag_f(Ls, tag_a));
       }
     }
-    if (trp && lane == 0) trp[5] = now_ticks();
+    trace_at(P, trw, 5);
     if (c == 0) {
       // the merger: wait for every partial of group g (tags), then combine
       const u64 *src = pg + (size_t)g * S * qpg * stride;
@@ -1194,6 +1228,8 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
       block_range(units[k], G, b, p0, p1);
       ctl->geo[k] = Geo{upr[k] * p0, upr[k] * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
     }
+    if (kTrace)
+      for (int i = 0; i < kTraceSlots * (5 * L + 2); ++i) trace_row(P, 0)[i] = 0ull;
     ctl->h_ready = 0;
     ctl->abort = 0;
     for (int w = 0; w < kWaves; ++w) ctl->done[w] = 0;
@@ -1436,7 +1472,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
           // rows 4i..4i+3 = gate j, up j, gate j+1, up j+1 with j = r0/2 + 2i
           const float g0 = row_value(part, ge, 4 * i), u0 = row_value(part, ge, 4 * i + 1);
           const float g1 = row_value(part, ge, 4 * i + 2), u1 = row_value(part, ge, 4 * i + 3);
-          const float s0 = g0 / (1.0f + __expf(-g0)), s1 = g1 / (1.0f + __expf(-g1));
+          const float s0 = __fdividef(g0, 1.0f + __expf(-g0)), s1 = __fdividef(g1, 1.0f + __expf(-g1));
           st_tag(ad + ge.r0 / 4 + i, tag_h2(s0 * u0, s1 * u1, tag));
         }
         publish_vec(Pl, tag);
@@ -1547,6 +1583,9 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
     }
     lap(sy, ST_LM, tlm);
   }
+  if (kTrace)
+    for (int i = lane; i < kTraceSlots * (5 * L + 2); i += 64)
+      P.stats[(size_t)b * P.stat_stride + kStatWords + i] = trace_row(P, 0)[i];
   if ((P.flags & 4u) && lane == 0) {
     unsigned xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
