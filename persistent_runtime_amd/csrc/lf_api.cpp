@@ -329,13 +329,15 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     TSlot ts[] = {{&P.xmid_t, (size_t)d}, {&P.xout_t, (size_t)d}, {&P.q_t, (size_t)Hq * dh},
                   {&P.kc_t, (size_t)Hkv * dh / 2}, {&P.vc_t, (size_t)Hkv * dh / 2}, {&P.part_t, part_gen},
                   {&P.o_t, (size_t)Hq * dh / 2}, {&P.a_t, (size_t)F / 2}};
+    // each buffer: two generations, then one staging round of padding (staging
+    // reads whole rounds; the words past a vector's end are ignored)
     size_t bytes = 0;
-    for (auto &t : ts) bytes += align_up(2 * t.words * 8, 256);
+    for (auto &t : ts) bytes += align_up((2 * t.words + lf::kStageRound) * 8, 256);
     char *xb = (char *)dev_alloc(st, bytes, &e);
     if (!xb) return bail(fail(&st->err, LF_ENOMEM, "exchange buffer allocation failed"));
     (void)hipMemsetAsync(xb, 0, bytes, s);
     size_t o2 = 0;
-    for (auto &t : ts) { *t.dst = (unsigned long long *)(xb + o2); o2 += align_up(2 * t.words * 8, 256); }
+    for (auto &t : ts) { *t.dst = (unsigned long long *)(xb + o2); o2 += align_up((2 * t.words + lf::kStageRound) * 8, 256); }
     P.part_gen = part_gen;
     st->xbuf = xb;
     st->xbuf_bytes = bytes;
@@ -359,14 +361,19 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   int hmax = d;
   if (Hq * dh > hmax) hmax = Hq * dh;
   if (F > hmax) hmax = F;
-  const size_t h_b = align_up((size_t)hmax * 2 + 1024, 16);   // + one piece of slack for masked lanes
+  // a staged vector of fp16 pairs is written in whole staging rounds of 32-bit words
+  const size_t round_up_words = [](size_t w) { return (w + lf::kStageRound - 1) / lf::kStageRound * lf::kStageRound; }(
+      (size_t)(Hq * dh / 2 > F / 2 ? Hq * dh / 2 : F / 2));
+  size_t h_b = align_up((size_t)hmax * 2 + 1024, 16);   // + one piece of slack for masked lanes
+  if (round_up_words * 4 > h_b) h_b = align_up(round_up_words * 4, 16);
+  const size_t xs_b = (size_t)(d + lf::kStageRound - 1) / lf::kStageRound * lf::kStageRound * 4;   // fp32 staging
   const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);
   // attention scratch: queries, current K/V row, per-wave (m, l) and per-wave o
   const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (size_t)lf::kWaves * 8 * 2 * 4 +
                         (size_t)lf::kWaves * P.qpg * dh * 4;
   const size_t samp_b = 4096;
   // [h | part]; part also holds the fp32 copy of a vector being normalised
-  size_t region_a = h_b + (part_b > (size_t)d * 4 ? part_b : align_up((size_t)d * 4, 16));
+  size_t region_a = h_b + (part_b > xs_b ? part_b : xs_b);
   if (attn_b > region_a) region_a = attn_b;
   if (samp_b > region_a) region_a = samp_b;
   P.lds_h = 0;

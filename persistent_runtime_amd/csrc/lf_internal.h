@@ -22,6 +22,7 @@ constexpr bool kTrace = false;
 #ifndef LF_RING_SLOTS
 #define LF_RING_SLOTS 8
 #endif
+constexpr int kStageRound = 64 * 40;      // tagged words one staging round reads (buffers are padded to it)
 constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB pieces in flight per stream wave (register ring)
 
 // Phases of one layer; each completes one "level" of the dependency chain.

@@ -340,10 +340,12 @@ __device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, un
 
 // ---------------------------------------------------------------- staging (wave 0)
 
-constexpr int kStageBatch = 40;   // 8-byte loads in flight per lane while staging
+constexpr int kStageBatch = kStageRound / 64;   // 8-byte loads in flight per lane while staging
 
 // Wave 0: wait until every word src[0..n) carries `tag`, then hand each payload
-// to use(i, word).  All loads of a batch are issued before any is checked, so a
+// to use(i, word, real).  src (and use's destination) must be readable
+// (writable) up to n rounded up to whole rounds of 64 * kStageBatch words; the
+// words past n are handed over with real = false.  All loads of a batch are issued before any is checked, so a
 // batch costs one memory round trip; a batch with a stale word is re-read.
 template <class F>
 __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, unsigned tag, F &&use) {
@@ -357,13 +359,10 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
       const unsigned long long tr = stamp(s);
       u64 v[kStageBatch];
 #pragma unroll
-      for (int j = 0; j < kStageBatch; ++j) {
-        const int i = base + 64 * j + lane;
-        v[j] = i < n ? ld_dev(src + i) : ((u64)tag << 32);
-      }
+      for (int j = 0; j < kStageBatch; ++j) v[j] = ld_dev(src + base + 64 * j + lane);   // buffers padded to whole rounds
       unsigned bad = 0u;
 #pragma unroll
-      for (int j = 0; j < kStageBatch; ++j) bad |= (unsigned)(tag_of(v[j]) != tag);
+      for (int j = 0; j < kStageBatch; ++j) bad |= (unsigned)(base + 64 * j + lane < n && tag_of(v[j]) != tag);
       const unsigned ok = wave_min_u32(1u - bad);
       if (s.timed) {
         s.rt_sum += now_ticks() - tr;
@@ -372,10 +371,12 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
       if (ok == 1u) {
         if (kTrace && s.trace_k >= 0 && base + 64 * kStageBatch >= n && lane == 0)
           trace_row(P, s.trace_k)[7] = now_ticks();
+        // Words past the end (padding) are handed over too, flagged: the
+        // destinations are padded as well, so no lane needs a branch.
 #pragma unroll
         for (int j = 0; j < kStageBatch; ++j) {
           const int i = base + 64 * j + lane;
-          if (i < n) use(i, v[j]);
+          use(i, v[j], i < n);
         }
         break;
       }
@@ -431,9 +432,9 @@ __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, un
   const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
   prefetch_gain(gain, d, glds);
   float ss = 0.0f;
-  if (!fetch_tagged(s, src, d, tag, [&](int i, u64 w) __attribute__((always_inline)) {
+  if (!fetch_tagged(s, src, d, tag, [&](int i, u64 w, bool real) __attribute__((always_inline)) {
         const float x = pay_f(w);
-        ss += x * x;
+        ss += real ? x * x : 0.0f;
         xs[i] = x;
       }))
     return false;
@@ -481,7 +482,7 @@ __device__ __forceinline__ bool stage_pairs_tagged(Sync &s, const u64 *src, int 
                                                    _Float16 *h) {
   unsigned *dst = reinterpret_cast<unsigned *>(h);
   return fetch_tagged(s, src, n_pairs, tag,
-                      [&](int i, u64 w) __attribute__((always_inline)) { dst[i] = (unsigned)w; });
+                      [&](int i, u64 w, bool) __attribute__((always_inline)) { dst[i] = (unsigned)w; });
 }
 
 // ---------------------------------------------------------------- stream waves
@@ -690,16 +691,29 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
 
 // ---------------------------------------------------------------- sync-wave phase pieces
 
-// Sum of the stream waves' partials of one row, in wave order.
-__device__ __forceinline__ float row_value(const float *part, const Geo &ge, int row) {
+// The rows each stream wave touches in a phase: [lo[cw], hi[cw]] (empty when
+// lo > hi), computed once per phase (wave-uniform).
+struct RowSpans {
+  int lo[kNcw], hi[kNcw];
+};
+__device__ __forceinline__ RowSpans row_spans(const Geo &ge) {
+  RowSpans rs;
   const int np = ge.nrows * ge.ppr;
-  const int a = row * ge.ppr, bnd = a + ge.ppr;
-  float y = 0.0f;
+#pragma unroll
   for (int cw = 0; cw < kNcw; ++cw) {
     int lo, hi;
     wave_slice(np, cw, lo, hi);
-    if (lo < hi && lo < bnd && hi > a) y += part[row * 8 + cw];
+    rs.lo[cw] = lo < hi ? lo / ge.ppr : 1;
+    rs.hi[cw] = lo < hi ? (hi - 1) / ge.ppr : 0;
   }
+  return rs;
+}
+// Sum of the stream waves' partials of one row, in wave order.
+__device__ __forceinline__ float row_value(const float *part, const RowSpans &rs, int row) {
+  float y = 0.0f;
+#pragma unroll
+  for (int cw = 0; cw < kNcw; ++cw)
+    if (rs.lo[cw] <= row && row <= rs.hi[cw]) y += part[row * 8 + cw];
   return y;
 }
 
@@ -1305,7 +1319,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
   auto fail = [&]() __attribute__((always_inline)) {
     if (lane == 0) lds_st(&ctl->abort, 1u);
   };
-  const int nq = P.Hq * dh, nk = P.Hkv * dh, half = dh / 2;
+  const int nq = P.Hq * dh, nk = P.Hkv * dh, half = dh / 2, dh_log2 = __builtin_ctz((unsigned)dh);
   const size_t nkw = (size_t)P.Hkv * half;   // words per generation of kc_t / vc_t
   int token = P.token0;
   for (int t = 0; t < P.n_tokens; ++t) {
@@ -1340,7 +1354,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         if (lane < ge.nrows / 2) {
           const int r = ge.r0 + 2 * lane;
           if (r < nq + nk) {
-            const int k = ((r < nq ? r : r - nq) % dh) / 2;
+            const int k = ((r < nq ? r : r - nq) & (dh - 1)) >> 1;
             cs0 = Pl.rope[((size_t)pos * half + k) * 2 + 0];
             sn0 = Pl.rope[((size_t)pos * half + k) * 2 + 1];
           }
@@ -1363,18 +1377,19 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0);
         wait_streams(ctl, q0);
         tq = lap(sy, ST_STREAMS, tq);
+        const RowSpans rs = row_spans(ge);
         trace(Pl, t, 5 * l + 0, 1);
         const unsigned tag = lvl + PH_QKV;
         const size_t kvrow = ((size_t)l * Pl.max_seq + pos) * (size_t)nk;
         _Float16 *kc = reinterpret_cast<_Float16 *>(Pl.kcache);
         _Float16 *vc = reinterpret_cast<_Float16 *>(Pl.vcache);
         for (int i = lane; i < ge.nrows / 2; i += 64) {
-          const float a = row_value(part, ge, 2 * i), bb = row_value(part, ge, 2 * i + 1);
+          const float a = row_value(part, rs, 2 * i), bb = row_value(part, rs, 2 * i + 1);
           const int r = ge.r0 + 2 * i;
           if (r < nq + nk) {
             // q / k rows come in rotary pairs (dims k, k + dh/2 of head hd)
             const int rr = r < nq ? r : r - nq;
-            const int hd = rr / dh, k = (rr % dh) / 2;
+            const int hd = rr >> dh_log2, k = (rr & (dh - 1)) >> 1;   // head_dim is 64 or 128
             const float cs = i == lane ? cs0 : Pl.rope[((size_t)pos * half + k) * 2 + 0];
             const float sn = i == lane ? sn0 : Pl.rope[((size_t)pos * half + k) * 2 + 1];
             const float y0 = a * cs - bb * sn, y1 = bb * cs + a * sn;
@@ -1425,6 +1440,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0 + 1);
         wait_streams(ctl, q0 + 1);
         tk = lap(sy, ST_STREAMS, tk);
+        const RowSpans rs = row_spans(ge);
         trace(Pl, t, 5 * l + 2, 1);
         // Every store this wave made before (KV cache rows, tagged words) has
         // completed before anything it publishes from here on: later steps
@@ -1440,7 +1456,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
           if (l > 0) xin = xown[i];
           else if (Pl.hidden_io) xin = Pl.x_hidden[r];
           else xin = (float)emb[(size_t)token * d + r];
-          const float x = xin + row_value(part, ge, i);
+          const float x = xin + row_value(part, rs, i);
           xown[i] = x;
           st_tag(xm + r, tag_f(x, tag));
         }
@@ -1465,13 +1481,14 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0 + 2);
         wait_streams(ctl, q0 + 2);
         tk = lap(sy, ST_STREAMS, tk);
+        const RowSpans rs = row_spans(ge);
         trace(Pl, t, 5 * l + 3, 1);
         const unsigned tag = lvl + PH_GU;
         u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
         for (int i = lane; i < ge.nrows / 4; i += 64) {
           // rows 4i..4i+3 = gate j, up j, gate j+1, up j+1 with j = r0/2 + 2i
-          const float g0 = row_value(part, ge, 4 * i), u0 = row_value(part, ge, 4 * i + 1);
-          const float g1 = row_value(part, ge, 4 * i + 2), u1 = row_value(part, ge, 4 * i + 3);
+          const float g0 = row_value(part, rs, 4 * i), u0 = row_value(part, rs, 4 * i + 1);
+          const float g1 = row_value(part, rs, 4 * i + 2), u1 = row_value(part, rs, 4 * i + 3);
           const float s0 = __fdividef(g0, 1.0f + __expf(-g0)), s1 = __fdividef(g1, 1.0f + __expf(-g1));
           st_tag(ad + ge.r0 / 4 + i, tag_h2(s0 * u0, s1 * u1, tag));
         }
@@ -1493,13 +1510,14 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0 + 3);
         wait_streams(ctl, q0 + 3);
         tk = lap(sy, ST_STREAMS, tk);
+        const RowSpans rs = row_spans(ge);
         trace(Pl, t, 5 * l + 4, 1);
         const unsigned tag = lvl + PH_D;
         u64 *xo = Pl.xout_t + (size_t)gen * d;
         const bool host_out = Pl.hidden_io && l == L - 1;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
-          const float x = xown[i] + row_value(part, ge, i);
+          const float x = xown[i] + row_value(part, rs, i);
           xown[i] = x;
           st_tag(xo + r, tag_f(x, tag));
           if (host_out) Pl.x_out[r] = x;
@@ -1527,11 +1545,12 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
       trace(P, t, 5 * L, 0);
       announce_input(ctl, qlm);
       wait_streams(ctl, qlm);
+      const RowSpans rs = row_spans(ge);
       trace(P, t, 5 * L, 1);
       float best = -INFINITY;
       int bi = 0x7fffffff;
       for (int i = lane; i < ge.nrows; i += 64) {
-        const float y = row_value(part, ge, i);
+        const float y = row_value(part, rs, i);
         st_dev(&P.logits[ge.r0 + i], y);
         if (y > best || (y == best && ge.r0 + i < bi)) { best = y; bi = ge.r0 + i; }
       }
