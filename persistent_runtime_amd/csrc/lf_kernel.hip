@@ -601,14 +601,29 @@ struct Streamer {
   __device__ __forceinline__ void next_phase_if_done() {
     if (q < qend && left == 0 && pad == 0) locate(q + 1);
   }
+  // refill every slot with the next round of pieces
+  __device__ __forceinline__ void refill() {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) issue(k);
+    next_phase_if_done();
+  }
 };
+
+// Whether stream wave st has pieces in phase kind (then stream_phase ends with a
+// round whose refill the caller may defer).
+__device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, const Ctl *ctl) {
+  const Geo ge = uniform_geo(ctl, kind);
+  int lo, hi;
+  wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
+  return hi > lo;
+}
 
 // A stream wave's share of GEMV phase q: consume its pieces round by round from
 // the register ring, refilling each slot as it is freed, and leave one partial
 // row sum per (row, wave) in part[row * 8 + cw].  Returns false if the sync wave
 // aborted.
 __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl *ctl, const _Float16 *h,
-                                             float *part) {
+                                             float *part, bool defer_last_refill = false) {
   const Geo ge = uniform_geo(ctl, kind);
   int lo, hi;
   wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
@@ -675,10 +690,9 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
       lds_drain();
       trace_at(*st.P, trk, 5);
       if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
+      if (defer_last_refill) break;   // the caller refills (st.refill()) later
     }
-#pragma unroll
-    for (int k = 0; k < kRing; ++k) st.issue(k);
-    st.next_phase_if_done();
+    st.refill();
     if (r == 0) trace_at(*st.P, trk, 4);
   }
   if (nr == 0 && lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
@@ -708,12 +722,16 @@ __device__ __forceinline__ RowSpans row_spans(const Geo &ge) {
   }
   return rs;
 }
-// Sum of the stream waves' partials of one row, in wave order.
+// Sum of the stream waves' partials of one row, in wave order: the row's eight
+// partial slots are read at once; slots of waves that did not touch the row
+// hold stale values and are skipped.
 __device__ __forceinline__ float row_value(const float *part, const RowSpans &rs, int row) {
+  const float4 p0 = reinterpret_cast<const float4 *>(part + row * 8)[0];
+  const float4 p1 = reinterpret_cast<const float4 *>(part + row * 8)[1];
+  const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
   float y = 0.0f;
 #pragma unroll
-  for (int cw = 0; cw < kNcw; ++cw)
-    if (rs.lo[cw] <= row && row <= rs.hi[cw]) y += part[row * 8 + cw];
+  for (int cw = 0; cw < kNcw; ++cw) y += (rs.lo[cw] <= row && row <= rs.hi[cw]) ? v[cw] : 0.0f;
   return y;
 }
 
@@ -1285,10 +1303,15 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
         const int gen = (t * L + l) & 1;
         st.trace_k = t == P.trace_token ? 5 * l + 0 : -1;
-        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part)) return;
+        // The refill after the QKV phase (the O phase's first round) waits until
+        // after attention: this wave's loads complete in order, so attention's
+        // K/V loads would otherwise queue behind it.
+        const bool qkv_rounds = st_has_rounds(st, K_QKV, ctl);
+        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, true)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
           if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
+        if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
         if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
