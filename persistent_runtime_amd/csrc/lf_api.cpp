@@ -331,13 +331,14 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
                   {&P.o_t, (size_t)Hq * dh / 2}, {&P.a_t, (size_t)F / 2}};
     // each buffer: two generations, then one staging round of padding (staging
     // reads whole rounds; the words past a vector's end are ignored)
+    const size_t pad_words = lf::kStageRound > lf::kStageRoundWide ? lf::kStageRound : lf::kStageRoundWide;
     size_t bytes = 0;
-    for (auto &t : ts) bytes += align_up((2 * t.words + lf::kStageRound) * 8, 256);
+    for (auto &t : ts) bytes += align_up((2 * t.words + pad_words) * 8, 256);
     char *xb = (char *)dev_alloc(st, bytes, &e);
     if (!xb) return bail(fail(&st->err, LF_ENOMEM, "exchange buffer allocation failed"));
     (void)hipMemsetAsync(xb, 0, bytes, s);
     size_t o2 = 0;
-    for (auto &t : ts) { *t.dst = (unsigned long long *)(xb + o2); o2 += align_up((2 * t.words + lf::kStageRound) * 8, 256); }
+    for (auto &t : ts) { *t.dst = (unsigned long long *)(xb + o2); o2 += align_up((2 * t.words + pad_words) * 8, 256); }
     P.part_gen = part_gen;
     st->xbuf = xb;
     st->xbuf_bytes = bytes;
@@ -362,8 +363,10 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (Hq * dh > hmax) hmax = Hq * dh;
   if (F > hmax) hmax = F;
   // a staged vector of fp16 pairs is written in whole staging rounds of 32-bit words
-  const size_t round_up_words = [](size_t w) { return (w + lf::kStageRound - 1) / lf::kStageRound * lf::kStageRound; }(
-      (size_t)(Hq * dh / 2 > F / 2 ? Hq * dh / 2 : F / 2));
+  const auto round_up = [](size_t w, size_t r) { return (w + r - 1) / r * r; };
+  const size_t o_words = round_up((size_t)Hq * dh / 2, lf::kStageRound);
+  const size_t a_words = round_up((size_t)F / 2, lf::kStageRoundWide);   // the SwiGLU vector's wider rounds
+  const size_t round_up_words = o_words > a_words ? o_words : a_words;
   size_t h_b = align_up((size_t)hmax * 2 + 1024, 16);   // + one piece of slack for masked lanes
   if (round_up_words * 4 > h_b) h_b = align_up(round_up_words * 4, 16);
   const size_t xs_b = (size_t)(d + lf::kStageRound - 1) / lf::kStageRound * lf::kStageRound * 4;   // fp32 staging

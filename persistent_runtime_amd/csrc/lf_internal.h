@@ -23,6 +23,7 @@ constexpr bool kTrace = false;
 #define LF_RING_SLOTS 8
 #endif
 constexpr int kStageRound = 64 * 40;      // tagged words one staging round reads (buffers are padded to it)
+constexpr int kStageRoundWide = 64 * 56;  // the SwiGLU vector's staging round
 constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB pieces in flight per stream wave (register ring)
 
 // Phases of one layer; each completes one "level" of the dependency chain.

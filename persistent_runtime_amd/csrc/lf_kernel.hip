@@ -341,43 +341,50 @@ __device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, un
 // ---------------------------------------------------------------- staging (wave 0)
 
 constexpr int kStageBatch = kStageRound / 64;   // 8-byte loads in flight per lane while staging
+constexpr int kStageBatchWide = kStageRoundWide / 64;   // words per lane in a round of the SwiGLU vector
 
 // Wave 0: wait until every word src[0..n) carries `tag`, then hand each payload
-// to use(i, word, real).  src (and use's destination) must be readable
-// (writable) up to n rounded up to whole rounds of 64 * kStageBatch words; the
-// words past n are handed over with real = false.  All loads of a batch are issued before any is checked, so a
-// batch costs one memory round trip; a batch with a stale word is re-read.
-template <class F>
-__device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, unsigned tag, F &&use) {
+// to use(i, word, real).  The words are read in rounds of 64 * kRound; at most
+// kStageBatch loads per lane are in flight, each later load issued into the
+// registers of a word just handed over, so a round costs one memory round trip.
+// src (and use's destination) must be readable (writable) up to n rounded up to
+// whole rounds; the words past n are handed over with real = false.  Words are
+// handed over as they land, before the round's tags are all known; the round
+// then ends with end(ok), and a round with a stale word (ok = false) is read and
+// handed over afresh.
+template <int kRound = kStageBatch, class F, class E>
+__device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, unsigned tag, F &&use, E &&end) {
+  constexpr int kWin = kRound < kStageBatch ? kRound : kStageBatch;
   KP &P = *s.P;
   const int lane = lane_id();
   if (P.poll_first && !poll_level(s, 0, P.G, tag)) return false;
   const unsigned long long t0 = now_ticks();
   s.nfetch += 1;
-  for (int base = 0; base < n; base += 64 * kStageBatch) {
+  for (int base = 0; base < n; base += 64 * kRound) {
     for (;;) {
       const unsigned long long tr = stamp(s);
-      u64 v[kStageBatch];
+      const u64 *rp = src + base + lane;   // buffers padded to whole rounds
+      u64 v[kWin];
 #pragma unroll
-      for (int j = 0; j < kStageBatch; ++j) v[j] = ld_dev(src + base + 64 * j + lane);   // buffers padded to whole rounds
+      for (int j = 0; j < kWin; ++j) v[j] = ld_dev(rp + 64 * j);
       unsigned bad = 0u;
 #pragma unroll
-      for (int j = 0; j < kStageBatch; ++j) bad |= (unsigned)(base + 64 * j + lane < n && tag_of(v[j]) != tag);
+      for (int j = 0; j < kRound; ++j) {
+        const int i = base + 64 * j + lane;
+        const u64 w = v[j % kWin];
+        bad |= (unsigned)(i < n && tag_of(w) != tag);
+        use(i, w, i < n);
+        if (j + kWin < kRound) v[j % kWin] = ld_dev(rp + 64 * (j + kWin));
+      }
       const unsigned ok = wave_min_u32(1u - bad);
       if (s.timed) {
         s.rt_sum += now_ticks() - tr;
         s.rt_n += 1;
       }
+      end(ok == 1u);
       if (ok == 1u) {
-        if (kTrace && s.trace_k >= 0 && base + 64 * kStageBatch >= n && lane == 0)
+        if (kTrace && s.trace_k >= 0 && base + 64 * kRound >= n && lane == 0)
           trace_row(P, s.trace_k)[7] = now_ticks();
-        // Words past the end (padding) are handed over too, flagged: the
-        // destinations are padded as well, so no lane needs a branch.
-#pragma unroll
-        for (int j = 0; j < kStageBatch; ++j) {
-          const int i = base + 64 * j + lane;
-          use(i, v[j], i < n);
-        }
         break;
       }
       if (expired(P, t0, tag)) return false;
@@ -431,12 +438,18 @@ __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, un
                                                      int d, float eps, _Float16 *h, unsigned char *glds, float *xs) {
   const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
   prefetch_gain(gain, d, glds);
-  float ss = 0.0f;
-  if (!fetch_tagged(s, src, d, tag, [&](int i, u64 w, bool real) __attribute__((always_inline)) {
-        const float x = pay_f(w);
-        ss += real ? x * x : 0.0f;
-        xs[i] = x;
-      }))
+  float ss = 0.0f, ss_round = 0.0f;   // ss_round: the round being read
+  if (!fetch_tagged(
+          s, src, d, tag,
+          [&](int i, u64 w, bool real) __attribute__((always_inline)) {
+            const float x = pay_f(w);
+            ss_round += real ? x * x : 0.0f;
+            xs[i] = x;
+          },
+          [&](bool ok) __attribute__((always_inline)) {
+            ss += ok ? ss_round : 0.0f;
+            ss_round = 0.0f;
+          }))
     return false;
   ss = wave_sum(ss);
   if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 8);
@@ -478,11 +491,13 @@ __device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _
 }
 
 // A vector published as tagged fp16 pairs (n_pairs words) into LDS h.
+template <int kBatch = kStageBatch>
 __device__ __forceinline__ bool stage_pairs_tagged(Sync &s, const u64 *src, int n_pairs, unsigned tag,
                                                    _Float16 *h) {
   unsigned *dst = reinterpret_cast<unsigned *>(h);
-  return fetch_tagged(s, src, n_pairs, tag,
-                      [&](int i, u64 w, bool) __attribute__((always_inline)) { dst[i] = (unsigned)w; });
+  return fetch_tagged<kBatch>(
+      s, src, n_pairs, tag, [&](int i, u64 w, bool) __attribute__((always_inline)) { dst[i] = (unsigned)w; },
+      [](bool) __attribute__((always_inline)) {});
 }
 
 // ---------------------------------------------------------------- stream waves
@@ -1527,7 +1542,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         sy.trace_k = t == Pl.trace_token ? 5 * l + 4 : -1;
         trace(Pl, t, 5 * l + 4, 6);
         if (ge.nrows > 0 &&
-            !stage_pairs_tagged(sy, Pl.a_t + (size_t)gen * (Pl.F / 2), Pl.F / 2, lvl + PH_GU, hl)) { fail(); return; }
+            !stage_pairs_tagged<kStageBatchWide>(sy, Pl.a_t + (size_t)gen * (Pl.F / 2), Pl.F / 2, lvl + PH_GU, hl)) { fail(); return; }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 4, 0);
         announce_input(ctl, q0 + 3);
