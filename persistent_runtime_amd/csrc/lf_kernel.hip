@@ -115,16 +115,38 @@ __device__ __forceinline__ float wave_sum_to63(float v) {
 __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_to63(v)), 63));
 }
+// DPP move whose disabled lanes keep their own value (an identity for max / min).
+#define LF_DPP_KEEP(v, ctrl, rmask) \
+  __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, (v)), __builtin_bit_cast(int, (v)), (ctrl), (rmask), 0xf, false)
+// Wave-wide max / min with the same DPP row steps as wave_sum_to63, the result
+// read back from lane 63 into every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, __builtin_bit_cast(float, LF_DPP_KEEP(v, 0xB1, 0xf)));
+  v = fmaxf(v, __builtin_bit_cast(float, LF_DPP_KEEP(v, 0x4E, 0xf)));
+  v = fmaxf(v, __builtin_bit_cast(float, LF_DPP_KEEP(v, 0x141, 0xf)));
+  v = fmaxf(v, __builtin_bit_cast(float, LF_DPP_KEEP(v, 0x140, 0xf)));
+  v = fmaxf(v, __builtin_bit_cast(float, LF_DPP_KEEP(v, 0x142, 0xa)));
+  v = fmaxf(v, __builtin_bit_cast(float, LF_DPP_KEEP(v, 0x143, 0xc)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ unsigned wave_min_u32(unsigned v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, m, 64));
-  return v;
+  v = min(v, (unsigned)LF_DPP_KEEP(v, 0xB1, 0xf));
+  v = min(v, (unsigned)LF_DPP_KEEP(v, 0x4E, 0xf));
+  v = min(v, (unsigned)LF_DPP_KEEP(v, 0x141, 0xf));
+  v = min(v, (unsigned)LF_DPP_KEEP(v, 0x140, 0xf));
+  v = min(v, (unsigned)LF_DPP_KEEP(v, 0x142, 0xa));
+  v = min(v, (unsigned)LF_DPP_KEEP(v, 0x143, 0xc));
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
 }
+// Wave-wide argmax of (value, index) pairs held one per lane (index >= 0):
+// the largest value, and among lanes holding it the smallest index.
+__device__ __forceinline__ void wave_argmax(float &best, int &bi) {
+  const float m = wave_max(best);
+  bi = (int)wave_min_u32(best == m ? (unsigned)bi : 0xffffffffu);
+  best = m;
+}
+// Whether no active lane has p set (one compare into a scalar lane mask).
+__device__ __forceinline__ bool wave_none(bool p) { return __builtin_amdgcn_ballot_w64(p) == 0ull; }
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += (unsigned long long)__shfl_xor((long long)v, m, 64);
@@ -282,10 +304,9 @@ __device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsign
   const unsigned long long t0 = now_ticks();
   bool ok = false;
   for (;;) {
-    unsigned mn = 0xffffffffu;
-    for (int i = lane_id(); i < count; i += 64) mn = min(mn, ld_dev(&P.progress[first + i]));
-    mn = wave_min_u32(mn);
-    if (mn >= level) { ok = true; break; }
+    bool behind = false;
+    for (int i = lane_id(); i < count; i += 64) behind |= ld_dev(&P.progress[first + i]) < level;
+    if (wave_none(behind)) { ok = true; break; }
     if (expired(P, t0, level)) break;
   }
   s.spin += now_ticks() - t0;
@@ -376,7 +397,7 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
         use(i, w, i < n);
         if (j + kWin < kRound) v[j % kWin] = ld_dev(rp + 64 * (j + kWin));
       }
-      const unsigned ok = wave_min_u32(1u - bad);
+      const unsigned ok = wave_none(bad != 0u) ? 1u : 0u;
       if (s.timed) {
         s.rt_sum += now_ticks() - tr;
         s.rt_n += 1;
@@ -753,10 +774,8 @@ __device__ __forceinline__ float row_value(const float *part, const RowSpans &rs
 // Wave 0: wait until every stream wave finished GEMV phase q.
 __device__ __forceinline__ void wait_streams(const Ctl *ctl, int q) {
   for (;;) {
-    unsigned mn = 0xffffffffu;
-    if (lane_id() < kNcw) mn = lds_ld(&ctl->done[lane_id()]);
-    mn = wave_min_u32(mn);
-    if (mn >= (unsigned)(q + 1)) break;
+    const bool behind = lane_id() < kNcw && lds_ld(&ctl->done[lane_id()]) < (unsigned)(q + 1);
+    if (wave_none(behind)) break;
     __builtin_amdgcn_s_sleep(1);
   }
   asm volatile("" ::: "memory");
@@ -1592,11 +1611,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         st_dev(&P.logits[ge.r0 + i], y);
         if (y > best || (y == best && ge.r0 + i < bi)) { best = y; bi = ge.r0 + i; }
       }
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(best, m, 64);
-        const int oi = __shfl_xor(bi, m, 64);
-        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-      }
+      wave_argmax(best, bi);
       if (lane == 0) {
         st_dev(&P.lm_val[b], best);
         st_dev(&P.lm_idx[b], bi);
@@ -1620,11 +1635,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
           const int ix = ld_dev(&P.lm_idx[i]);
           if (v > best || (v == best && ix < bi)) { best = v; bi = ix; }
         }
-        for (int m = 32; m >= 1; m >>= 1) {
-          const float ov = __shfl_xor(best, m, 64);
-          const int oi = __shfl_xor(bi, m, 64);
-          if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-        }
+        wave_argmax(best, bi);
         tok = bi;
       }
       if (tok < 0 || tok >= P.V) {   // never expected; keeps the next embedding read in bounds
