@@ -235,7 +235,8 @@ struct Ctl {
   unsigned abort;           // the sync wave gave up (the error word is set)
   unsigned done[kWaves];    // per stream wave: last GEMV phase (1-based) it finished
   int status;               // outcome of a barrier-based wait
-  int pad[5];
+  unsigned inv_rms;         // 1 / rms of the vector being normalised (fp32 bits)
+  int pad[4];
   Geo geo[K_COUNT];
 };
 
@@ -430,15 +431,27 @@ __device__ __forceinline__ void gain_ready() {
   asm volatile("" ::: "memory");
 }
 
-// Second pass of RMSNorm: h = fp16(g * x * (1/r)) from the fp32 vector xs, eight
-// elements per lane per step (gains g in LDS).  The reciprocal is taken once
-// (within an ulp of dividing; the result is rounded to fp16 anyway).
-__device__ __forceinline__ void normalize(const float *xs, const _Float16 *g, int d, float r, _Float16 *h) {
+// Workgroup barrier that waits for no memory operation: the stream waves keep
+// their weight loads in flight across it.  A wave that has ended no longer
+// counts, so a sync wave that gives up releases the others.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Second pass of RMSNorm, shared by the workgroup's waves: wave w writes its
+// share of h = fp16(g * x * inv) from the fp32 vector xs, eight elements per
+// lane (gains g in LDS, inv = 1 / rms computed once).  The shares are
+// contiguous runs of 8-element groups, so each wave's LDS reads are sequential.
+__device__ __forceinline__ void normalize_share(const float *xs, const _Float16 *g, int d, float inv, _Float16 *h,
+                                                int w) {
   const float4 *x4 = reinterpret_cast<const float4 *>(xs);
   const f16x8 *g8 = reinterpret_cast<const f16x8 *>(g);
   f16x8 *h8 = reinterpret_cast<f16x8 *>(h);
-  const float inv = 1.0f / r;
-  for (int v = lane_id(); v < d / 8; v += 64) {
+  const int ng = d / 8, per = (ng + kWaves - 1) / kWaves;
+  const int v1 = min(ng, (w + 1) * per);
+  for (int v = w * per + lane_id(); v < v1; v += 64) {
     const float4 a = x4[2 * v], b = x4[2 * v + 1];
     const f16x8 gg = g8[v];
     f16x8 o;
@@ -452,6 +465,22 @@ __device__ __forceinline__ void normalize(const float *xs, const _Float16 *g, in
     o[7] = (_Float16)((float)gg[7] * (b.w * inv));
     h8[v] = o;
   }
+}
+
+// Sync wave, once x (fp32, in xs), the gains and sum(x^2) are in place: publish
+// 1 / rms, release the stream waves (barrier), write its own share of h, and
+// wait until every share is written (second barrier).  The reciprocal is taken
+// once (within an ulp of dividing; the result is rounded to fp16 anyway).
+__device__ __forceinline__ void normalize_shared(Ctl *ctl, const float *xs, const _Float16 *g, int d, float ss,
+                                                 float eps, _Float16 *h) {
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  if (lane_id() == 0) lds_st(&ctl->inv_rms, __float_as_uint(inv));
+  lds_drain();
+  gain_ready();
+  wg_barrier();
+  normalize_share(xs, g, d, inv, h, 0);
+  lds_drain();
+  wg_barrier();
 }
 
 // RMSNorm of a residual published by other workgroups as tagged fp32 words.
@@ -470,21 +499,25 @@ __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, un
           [&](bool ok) __attribute__((always_inline)) {
             ss += ok ? ss_round : 0.0f;
             ss_round = 0.0f;
-          }))
+          })) {
+    // giving up: the stream waves wait at the first barrier; pass it once so
+    // that they see the abort
+    if (lane_id() == 0) lds_st(&s.ctl->abort, 1u);
+    lds_drain();
+    wg_barrier();
     return false;
+  }
   ss = wave_sum(ss);
   if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 8);
-  lds_drain();
-  gain_ready();
-  if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 9);
-  normalize(xs, g, d, sqrtf(ss / (float)d + eps), h);
+  normalize_shared(s.ctl, xs, g, d, ss, eps, h);
   if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 10);
   return true;
 }
 
 // RMSNorm of a layer-0 input: an fp16 embedding row or the host's fp32 vector.
-__device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _Float16 *x16, const _Float16 *gain,
-                                                    int d, float eps, _Float16 *h, unsigned char *glds, float *xs) {
+__device__ __forceinline__ void stage_rmsnorm_plain(Ctl *ctl, const float *x_host, const _Float16 *x16,
+                                                    const _Float16 *gain, int d, float eps, _Float16 *h,
+                                                    unsigned char *glds, float *xs) {
   const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
   prefetch_gain(gain, d, glds);
   const int lane = lane_id();
@@ -505,10 +538,7 @@ __device__ __forceinline__ void stage_rmsnorm_plain(const float *x_host, const _
       }
     }
   }
-  ss = wave_sum(ss);
-  lds_drain();
-  gain_ready();
-  normalize(xs, g, d, sqrtf(ss / (float)d + eps), h);
+  normalize_shared(ctl, xs, g, d, wave_sum(ss), eps, h);
 }
 
 // A vector published as tagged fp16 pairs (n_pairs words) into LDS h.
@@ -658,17 +688,30 @@ __device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, cons
 // the register ring, refilling each slot as it is freed, and leave one partial
 // row sum per (row, wave) in part[row * 8 + cw].  Returns false if the sync wave
 // aborted.
-__device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl *ctl, const _Float16 *h,
-                                             float *part, bool defer_last_refill = false) {
+__device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl *ctl, _Float16 *h, float *part,
+                                             const unsigned char *glds, bool defer_last_refill = false) {
   const Geo ge = uniform_geo(ctl, kind);
   int lo, hi;
   wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
   // the dependency wait happens on wave 0; here only its LDS announcement
   const bool timed = st.timed;
   unsigned long long t0 = timed ? now_ticks() : 0ull;
-  while (lds_ld(&ctl->h_ready) < (unsigned)(q + 1)) {
-    if (lds_ld(&ctl->abort)) return false;
-    __builtin_amdgcn_s_sleep(1);
+  if (kind == K_QKV || kind == K_GU || kind == K_LM) {
+    // an RMSNorm input: every wave writes a share of h between two barriers
+    if (ge.nrows > 0) {
+      wg_barrier();
+      if (lds_ld(&ctl->abort)) return false;
+      normalize_share(part, reinterpret_cast<const _Float16 *>(glds), fresh(*st.P).d,
+                      __uint_as_float(lds_ld(&ctl->inv_rms)), h, st.cw + 1);
+      lds_drain();
+      wg_barrier();
+      if (lds_ld(&ctl->abort)) return false;
+    }
+  } else {
+    while (lds_ld(&ctl->h_ready) < (unsigned)(q + 1)) {
+      if (lds_ld(&ctl->abort)) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
   }
   if (timed) {
     const unsigned long long t1 = now_ticks();
@@ -1341,21 +1384,21 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         // after attention: this wave's loads complete in order, so attention's
         // K/V loads would otherwise queue behind it.
         const bool qkv_rounds = st_has_rounds(st, K_QKV, ctl);
-        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, true)) return;
+        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, glds, true)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
           if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
-        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, glds)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
-        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part, glds)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 4 : -1;
-        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part, glds)) return;
       }
       if (has_lm) {
         st.trace_k = t == P.trace_token ? 5 * L : -1;
-        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part)) return;
+        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part, glds)) return;
         if (b == 0 && P.sampling) {
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
           if (lds_ld(&ctl->abort)) return;
@@ -1375,6 +1418,15 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
   // ======================= sync wave (wave 0) =======================
   auto fail = [&]() __attribute__((always_inline)) {
     if (lane == 0) lds_st(&ctl->abort, 1u);
+  };
+  // Giving up where the stream waves' next step is the first barrier of an
+  // RMSNorm stage: pass that barrier once so that they see the abort and leave.
+  auto fail_release = [&](bool at_barrier) __attribute__((always_inline)) {
+    fail();
+    if (at_barrier) {
+      lds_drain();
+      wg_barrier();
+    }
   };
   const int nq = P.Hq * dh, nk = P.Hkv * dh, half = dh / 2, dh_log2 = __builtin_ctz((unsigned)dh);
   const size_t nkw = (size_t)P.Hkv * half;   // words per generation of kc_t / vc_t
@@ -1396,16 +1448,16 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
 
       // ---------------- attention norm + QKV + rotary + KV append
       {
+        const Geo ge = uniform_geo(ctl, K_QKV);
         if (l == 0 && t > 0) {
           if (kPrefill || Pl.hidden_io) {
             // the previous token is finished everywhere (its reads included)
-            if (!poll_level(sy, 0, G, lv0)) { fail(); return; }
+            if (!poll_level(sy, 0, G, lv0)) { fail_release(ge.nrows > 0); return; }
           } else {
-            if (!poll_level(sy, 0, 1, lv0)) { fail(); return; }
+            if (!poll_level(sy, 0, 1, lv0)) { fail_release(ge.nrows > 0); return; }
             token = ld_dev(Pl.tok_slot);
           }
         }
-        const Geo ge = uniform_geo(ctl, K_QKV);
         // rotary factors of this lane's first row pair, loaded before the wait
         float cs0 = 0.0f, sn0 = 0.0f;
         if (lane < ge.nrows / 2) {
@@ -1424,9 +1476,9 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
             if (!stage_rmsnorm_tagged(sy, Pl.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, attn_norm, d, Pl.eps,
                                       hl, glds, part)) { fail(); return; }
           } else if (Pl.hidden_io) {
-            stage_rmsnorm_plain(Pl.x_hidden, nullptr, attn_norm, d, Pl.eps, hl, glds, part);
+            stage_rmsnorm_plain(ctl, Pl.x_hidden, nullptr, attn_norm, d, Pl.eps, hl, glds, part);
           } else {
-            stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, attn_norm, d, Pl.eps, hl, glds, part);
+            stage_rmsnorm_plain(ctl, nullptr, emb + (size_t)token * d, attn_norm, d, Pl.eps, hl, glds, part);
           }
         }
         tq = lap(sy, ST_STAGE, tq);
@@ -1627,7 +1679,10 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         if (!wait_all_waves(sy, 0, G, lvl_lm, true)) { fail(); return; }
         tok = sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds));
       } else {
-        if (!poll_level(sy, 0, G, lvl_lm)) { fail(); return; }
+        if (!poll_level(sy, 0, G, lvl_lm)) {
+          fail_release(t + 1 < P.n_tokens && uniform_geo(ctl, K_QKV).nrows > 0);
+          return;
+        }
         float best = -INFINITY;
         int bi = 0x7fffffff;
         for (int i = lane; i < G; i += 64) {
