@@ -1360,7 +1360,13 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
     st.timed = (P.flags & 4u) && st.cw == 0;
     st.t_ready = st.t_work = st.pieces = 0;
     st.trace_k = -1;
-    st.dummy = reinterpret_cast<const unsigned char *>(P.wbase) + lane * 16;
+    {
+      // padding pieces re-read 1 KB of layer 0's weights; spread over 64 KB so
+      // that the chip's padding reads do not all queue at one L2 channel
+      const long long nkb = (long long)P.layer_stride / 1024;
+      const long long kb = (long long)((b * kWaves + wave) & 63) % (nkb > 0 ? nkb : 1);
+      st.dummy = reinterpret_cast<const unsigned char *>(P.wbase) + kb * 1024 + lane * 16;
+    }
     st.left = st.pad = st.kp = 0;
     st.ppr = 1;
     st.tailv = 64;
