@@ -310,7 +310,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
       {&x_hidden, (size_t)d * 4}, {&x_out, (size_t)d * 4}, {&logits, (size_t)(V > 0 ? V : 1) * 4},
       {&lm_val, (size_t)G * 4}, {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4},
       {&tickets, (size_t)c.n_layers * Hkv * 4}, {&tok_slot, 16}, {&errw, 16},
-      {&stats, (size_t)G * (lf::kStatWords + (lf::kTrace ? 12 * (5 * c.n_layers + 2) : 0)) * 8}};
+      {&stats, (size_t)G * (lf::kStatWords + (lf::kTrace ? lf::kTraceSlots * (5 * c.n_layers + 2) : 0)) * 8}};
   size_t arena = 0;
   for (auto &sl : slots) arena += align_up(sl.bytes, 256);
   char *ar = (char *)dev_alloc(st, arena, &e);
@@ -322,7 +322,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lm_val = (float *)lm_val; P.lm_idx = (int *)lm_idx; P.progress = (unsigned *)progress;
   P.tickets = (unsigned *)tickets; P.tok_slot = (int *)tok_slot; P.err = (unsigned *)errw;
   P.stats = (unsigned long long *)stats;
-  P.stat_stride = lf::kStatWords + (lf::kTrace ? 12 * (5 * c.n_layers + 2) : 0);
+  P.stat_stride = lf::kStatWords + (lf::kTrace ? lf::kTraceSlots * (5 * c.n_layers + 2) : 0);
   // tagged exchange words, two generations each, in one zeroed allocation
   {
     struct TSlot { unsigned long long **dst; size_t words; };
@@ -383,10 +383,10 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_part = (int)h_b;
   P.lds_red = (int)align_up(region_a, 256);
   P.lds_ctl = P.lds_red + 256;
-  P.lds_xown = P.lds_ctl + 256;
+  P.lds_xown = P.lds_ctl + lf::kCtlBytes;
   P.lds_gain = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
   P.lds_trace = (int)align_up((size_t)P.lds_gain + align_up((size_t)d * 2, 1024), 256);
-  const size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)12 * (5 * c.n_layers + 2) * 8 : 0), 256);
+  const size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
   P.part_rows = rows_max;
   P.hmax = hmax;
   int lds_limit = 0;

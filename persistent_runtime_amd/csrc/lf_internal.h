@@ -22,6 +22,8 @@ constexpr bool kTrace = false;
 #ifndef LF_RING_SLOTS
 #define LF_RING_SLOTS 8
 #endif
+constexpr int kCtlBytes = 1024;           // LDS bytes of a workgroup's control block
+constexpr int kTraceSlots = 16;          // timestamps per phase (LF_TRACE builds)
 constexpr int kStageRound = 64 * 40;      // tagged words one staging round reads (buffers are padded to it)
 constexpr int kStageRoundWide = 64 * 56;  // the SwiGLU vector's staging round
 constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB pieces in flight per stream wave (register ring)

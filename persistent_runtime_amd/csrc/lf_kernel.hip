@@ -230,6 +230,16 @@ struct Geo {            // one phase kind's row block in this workgroup
   int r0, nrows, kv, ppr;   // first row, rows, 16-B vectors per row, 1-KB pieces per row
 };
 
+// The rows each stream wave touches in a phase: [lo[cw], hi[cw]] (empty when
+// lo > hi).
+struct RowSpans {
+  int lo[kNcw], hi[kNcw];
+};
+// A stream wave's pieces of one phase kind: n pieces from piece kp of row `row`.
+struct Slice {
+  int n, row, kp, pad_;
+};
+
 struct Ctl {
   unsigned h_ready;         // last GEMV phase (1-based) whose input vector is staged
   unsigned abort;           // the sync wave gave up (the error word is set)
@@ -238,7 +248,12 @@ struct Ctl {
   unsigned inv_rms;         // 1 / rms of the vector being normalised (fp32 bits)
   int pad[4];
   Geo geo[K_COUNT];
+  // The partition of every phase kind among the stream waves, fixed for the
+  // launch: computed once so that no phase divides by the pieces per row.
+  RowSpans span[K_COUNT];
+  Slice slice[K_COUNT][kNcw];
 };
+static_assert(sizeof(Ctl) <= kCtlBytes, "workgroup control block exceeds its LDS space");
 
 // ---------------------------------------------------------------- global sync (wave 0)
 
@@ -271,7 +286,6 @@ __device__ __forceinline__ unsigned long long stamp(const Sync &s) { return s.ti
 // Timestamps collect in LDS and are copied out when the kernel ends, so that
 // tracing adds no global stores (and no store waits) to the path it measures.
 typedef __attribute__((address_space(3))) unsigned long long lds_u64;
-constexpr int kTraceSlots = 12;   // timestamps per phase (LF_TRACE builds)
 __device__ __forceinline__ lds_u64 *trace_row(KP &P, int k) {
   extern __shared__ __align__(16) unsigned char lf_dyn_lds[];
   return (lds_u64 *)(lf_dyn_lds + P.lds_trace) + kTraceSlots * k;
@@ -580,6 +594,12 @@ __device__ __forceinline__ Geo uniform_geo(const Ctl *ctl, int kind) {
              __builtin_amdgcn_readfirstlane(g.kv), __builtin_amdgcn_readfirstlane(g.ppr)};
 }
 
+__device__ __forceinline__ Slice uniform_slice(const Ctl *ctl, int kind, int cw) {
+  const Slice sl = ctl->slice[kind][cw];
+  return Slice{__builtin_amdgcn_readfirstlane(sl.n), __builtin_amdgcn_readfirstlane(sl.row),
+               __builtin_amdgcn_readfirstlane(sl.kp), 0};
+}
+
 // Stream wave cw's share [lo, hi) of the np pieces of a row block (contiguous).
 __device__ __forceinline__ void wave_slice(int np, int cw, int &lo, int &hi) {
   lo = (cw * np) / kNcw;
@@ -625,13 +645,12 @@ struct Streamer {
       const int kind = lm ? K_LM : (g & 3);
       const int l = lm ? 0 : (g >> 2);
       const Geo ge = uniform_geo(ctl, kind);
-      int lo, hi;
-      wave_slice(ge.nrows * ge.ppr, cw, lo, hi);
-      if (lo < hi) {
-        const int row = lo / ge.ppr;
-        left = hi - lo;
+      const Slice sl = uniform_slice(ctl, kind, cw);
+      if (sl.n > 0) {
+        const int row = sl.row;
+        left = sl.n;
         pad = (kRing - left % kRing) % kRing;
-        kp = lo - row * ge.ppr;
+        kp = sl.kp;
         ppr = ge.ppr;
         tailv = ge.kv - (ge.ppr - 1) * 64;
         adv_last = (long long)ge.kv * 16 - (long long)(ge.ppr - 1) * 1024;
@@ -678,10 +697,7 @@ struct Streamer {
 // Whether stream wave st has pieces in phase kind (then stream_phase ends with a
 // round whose refill the caller may defer).
 __device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, const Ctl *ctl) {
-  const Geo ge = uniform_geo(ctl, kind);
-  int lo, hi;
-  wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
-  return hi > lo;
+  return uniform_slice(ctl, kind, st.cw).n > 0;
 }
 
 // A stream wave's share of GEMV phase q: consume its pieces round by round from
@@ -691,8 +707,7 @@ __device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, cons
 __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl *ctl, _Float16 *h, float *part,
                                              const unsigned char *glds, bool defer_last_refill = false) {
   const Geo ge = uniform_geo(ctl, kind);
-  int lo, hi;
-  wave_slice(ge.nrows * ge.ppr, st.cw, lo, hi);
+  const Slice sl = uniform_slice(ctl, kind, st.cw);
   // the dependency wait happens on wave 0; here only its LDS announcement
   const bool timed = st.timed;
   unsigned long long t0 = timed ? now_ticks() : 0ull;
@@ -723,8 +738,8 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
   trace_at(*st.P, trk, 3);
   const u32x4 *hv = reinterpret_cast<const u32x4 *>(h);
   const int ppr = ge.ppr, tailv = ge.kv - (ge.ppr - 1) * 64;
-  const int n = hi - lo;
-  int row = lo / ppr, kp = lo - row * ppr;
+  const int n = sl.n;
+  int row = sl.row, kp = sl.kp;
   float acc = 0.0f;
   // Each round first uses the kRing pieces in the ring, then refills it.  The
   // first round's pieces landed while the input was pending, and a refill can
@@ -752,6 +767,10 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
         const bool last = kp == ppr - 1;
         const float a2 = dot8(st.buf[k], hx[k], acc);
         acc = (!last || lane < tailv) ? a2 : acc;
+        if (kTrace && r == 0 && k == 0 && trk >= 0) {   // the round's first piece has landed
+          asm volatile("" ::"v"(acc));
+          trace_at(*st.P, trk, 11);
+        }
         if (last || i == n - 1) {
           const float sum = wave_sum_to63(acc);
           if (lane == 63) part[row * 8 + st.cw] = sum;
@@ -764,6 +783,10 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
           ++kp;
         }
       }
+    }
+    if (kTrace && r == 0) {
+      asm volatile("" ::"v"(acc));
+      trace_at(*st.P, trk, 9);   // the first round is used
     }
     if (r == nr - 1) {
       lds_drain();
@@ -784,20 +807,13 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
 
 // ---------------------------------------------------------------- sync-wave phase pieces
 
-// The rows each stream wave touches in a phase: [lo[cw], hi[cw]] (empty when
-// lo > hi), computed once per phase (wave-uniform).
-struct RowSpans {
-  int lo[kNcw], hi[kNcw];
-};
-__device__ __forceinline__ RowSpans row_spans(const Geo &ge) {
+// The rows each stream wave touches in a phase, read from the workgroup's table.
+__device__ __forceinline__ RowSpans row_spans(const Ctl *ctl, int kind) {
   RowSpans rs;
-  const int np = ge.nrows * ge.ppr;
 #pragma unroll
   for (int cw = 0; cw < kNcw; ++cw) {
-    int lo, hi;
-    wave_slice(np, cw, lo, hi);
-    rs.lo[cw] = lo < hi ? lo / ge.ppr : 1;
-    rs.hi[cw] = lo < hi ? (hi - 1) / ge.ppr : 0;
+    rs.lo[cw] = __builtin_amdgcn_readfirstlane(ctl->span[kind].lo[cw]);
+    rs.hi[cw] = __builtin_amdgcn_readfirstlane(ctl->span[kind].hi[cw]);
   }
   return rs;
 }
@@ -1335,7 +1351,16 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
     for (int k = 0; k < K_COUNT; ++k) {
       int p0, p1;
       block_range(units[k], G, b, p0, p1);
-      ctl->geo[k] = Geo{upr[k] * p0, upr[k] * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
+      const Geo ge = Geo{upr[k] * p0, upr[k] * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
+      ctl->geo[k] = ge;
+      for (int cw = 0; cw < kNcw; ++cw) {
+        int lo, hi;
+        wave_slice(ge.nrows * ge.ppr, cw, lo, hi);
+        const int row = lo < hi ? lo / ge.ppr : 0;
+        ctl->slice[k][cw] = Slice{hi - lo, row, lo < hi ? lo - row * ge.ppr : 0, 0};
+        ctl->span[k].lo[cw] = lo < hi ? row : 1;
+        ctl->span[k].hi[cw] = lo < hi ? (hi - 1) / ge.ppr : 0;
+      }
     }
     if (kTrace)
       for (int i = 0; i < kTraceSlots * (5 * L + 2); ++i) trace_row(P, 0)[i] = 0ull;
@@ -1492,7 +1517,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0);
         wait_streams(ctl, q0);
         tq = lap(sy, ST_STREAMS, tq);
-        const RowSpans rs = row_spans(ge);
+        const RowSpans rs = row_spans(ctl, K_QKV);
         trace(Pl, t, 5 * l + 0, 1);
         const unsigned tag = lvl + PH_QKV;
         const size_t kvrow = ((size_t)l * Pl.max_seq + pos) * (size_t)nk;
@@ -1555,7 +1580,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0 + 1);
         wait_streams(ctl, q0 + 1);
         tk = lap(sy, ST_STREAMS, tk);
-        const RowSpans rs = row_spans(ge);
+        const RowSpans rs = row_spans(ctl, K_O);
         trace(Pl, t, 5 * l + 2, 1);
         // Every store this wave made before (KV cache rows, tagged words) has
         // completed before anything it publishes from here on: later steps
@@ -1596,7 +1621,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0 + 2);
         wait_streams(ctl, q0 + 2);
         tk = lap(sy, ST_STREAMS, tk);
-        const RowSpans rs = row_spans(ge);
+        const RowSpans rs = row_spans(ctl, K_GU);
         trace(Pl, t, 5 * l + 3, 1);
         const unsigned tag = lvl + PH_GU;
         u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
@@ -1625,7 +1650,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         announce_input(ctl, q0 + 3);
         wait_streams(ctl, q0 + 3);
         tk = lap(sy, ST_STREAMS, tk);
-        const RowSpans rs = row_spans(ge);
+        const RowSpans rs = row_spans(ctl, K_D);
         trace(Pl, t, 5 * l + 4, 1);
         const unsigned tag = lvl + PH_D;
         u64 *xo = Pl.xout_t + (size_t)gen * d;
@@ -1660,7 +1685,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
       trace(P, t, 5 * L, 0);
       announce_input(ctl, qlm);
       wait_streams(ctl, qlm);
-      const RowSpans rs = row_spans(ge);
+      const RowSpans rs = row_spans(ctl, K_LM);
       trace(P, t, 5 * L, 1);
       float best = -INFINITY;
       int bi = 0x7fffffff;
