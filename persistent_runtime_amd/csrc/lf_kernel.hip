@@ -879,13 +879,16 @@ constexpr int kKeysPerRound = 16;   // keys whose K and V rows one wave loads pe
 // fused operations, briefly"): attention over one tile of the cache per unit,
 // the cross-unit softmax correction, then (next phase) the output projection.
 //
-// Wave w takes keys j0 + w, j0 + w + 8, ...; lane e holds head dims 2e, 2e+1,
-// loads kKeysPerRound K and V rows at once, and keeps an online softmax (m, l,
-// o) per query head.  The eight waves' states are combined into the unit's
-// partial, published as tagged words.  Unit c = 0 of each KV head merges the
-// group's S partials (waiting on their tags) into the fp16 output o_t.  The
-// current position's K/V row comes from the tagged exchange words, not from
-// the cache (whose row for this step may still be in flight).
+// Only the seven stream waves load (the sync wave's loads would complete behind
+// its own epilogue stores, which this wave's memory operations finish in
+// order after).  Stream wave w takes keys j0 + w - 1, j0 + w - 1 + 7, ...;
+// lane e holds head dims 2e, 2e+1, loads kKeysPerRound K and V rows at once,
+// and keeps an online softmax (m, l, o) per query head.  Wave 1 combines the
+// waves' states into the unit's partial, published as tagged words, and in
+// unit c = 0 of each KV head merges the group's S partials (waiting on their
+// tags) into the fp16 output o_t.  The current position's K/V row comes from
+// the tagged exchange words, not from the cache (whose row for this step may
+// still be in flight).
 // Returns false if a bounded wait expired.
 __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsigned tag_q,
                                           unsigned tag_a, int pos, int u, int S, int Lc, unsigned char *lds,
@@ -912,11 +915,15 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride + (size_t)g * dh + e0;
   const _Float16 *Vl = reinterpret_cast<const _Float16 *>(P.vcache) + (size_t)l * lstride + (size_t)g * dh + e0;
   const size_t rstride = (size_t)Hkv * dh;           // elements between positions
+  // The keys and every load of the unit belong to the stream waves (kw = wave - 1):
+  // the sync wave's loads would complete behind its own epilogue stores.
+  constexpr int kKW = kWaves - 1;
+  const int kwv = wave - 1;
   unsigned kw[kKeysPerRound], vw[kKeysPerRound];
   auto load_round = [&](int jb) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kKeysPerRound; ++k) {
-      const int j = jb + kWaves * k;
+      const int j = jb + kKW * k;
       kw[k] = vw[k] = 0u;
       if (j < j1 && j != pos) {
         kw[k] = *reinterpret_cast<const unsigned *>(Kl + (size_t)j * rstride);
@@ -924,14 +931,15 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       }
     }
   };
-  load_round(j0 + wave);
+  if (wave > 0) load_round(j0 + kwv);
   __syncthreads();   // wave 0 may still be reading the phase scratch this unit reuses
   {
     const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)g * qpg * dh;
     const size_t nw = (size_t)Hkv * half;
     const bool has_cur = j0 <= pos && pos < j1;
     // one tagged word per thread: queries, then the current K pairs, then V pairs
-    for (int i = tid; i < qpg * dh + (has_cur ? dh : 0); i += kThreads) {
+    const int nq_words = qpg * dh + (has_cur ? dh : 0);
+    for (int i = wave > 0 ? tid - 64 : nq_words; i < nq_words; i += kThreads - 64) {   // stream waves only
       if (i < qpg * dh) {
         qs[i] = pay_f(ld_tag_wait(P, qsrc + i, tag_q, t0, bad));
       } else if (i < qpg * dh + half) {
@@ -952,7 +960,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   }
   __syncthreads();
   if (lds_ld(&ctl->abort)) return false;
-  const int trw = wave == 0 ? trk : -1;
+  const int trw = wave == 1 ? trk : -1;
   trace_at(P, trw, 3);
 
   float qr[kMaxQpg][2];
@@ -968,8 +976,8 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     lsum[h] = 0.0f;
     o[h][0] = o[h][1] = 0.0f;
   }
-  for (int jb = j0 + wave; jb < j1; jb += kWaves * kKeysPerRound) {
-    if (jb != j0 + wave) load_round(jb);   // the first round was requested before the queries
+  for (int jb = wave > 0 ? j0 + kwv : j1; jb < j1; jb += kKW * kKeysPerRound) {
+    if (jb != j0 + kwv) load_round(jb);   // the first round was requested before the queries
     // per query head: scores of this round's keys, online-softmax rescale, accumulate
 #pragma unroll
     for (int h = 0; h < kMaxQpg; ++h) {
@@ -978,7 +986,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
         float mb = m[h];
 #pragma unroll
         for (int k = 0; k < kKeysPerRound; ++k) {
-          const int j = jb + kWaves * k;
+          const int j = jb + kKW * k;
           sck[k] = -INFINITY;
           if (j < j1) {
             float k0, k1;
@@ -1001,7 +1009,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
         m[h] = mb;
 #pragma unroll
         for (int k = 0; k < kKeysPerRound; ++k) {
-          const int j = jb + kWaves * k;
+          const int j = jb + kKW * k;
           if (j < j1) {
             float v0, v1;
             if (j == pos) {
@@ -1037,7 +1045,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     }
   }
   __syncthreads();
-  if (wave == 0) {
+  if (wave == 1) {
     const int stride = dh + 2;
     u64 *pg = P.part_t + (size_t)gen * P.part_gen;
     u64 *dst = pg + (size_t)u * qpg * stride;
@@ -1418,7 +1426,8 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
         if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, glds, true)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
-          if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red)) return;
+          if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
+                         u == b && t == P.trace_token ? 5 * l + 1 : -1)) return;
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
         if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, glds)) return;
