@@ -486,14 +486,16 @@ __device__ __forceinline__ void normalize_share(const float *xs, const _Float16 
 // wait until every share is written (second barrier).  The reciprocal is taken
 // once (within an ulp of dividing; the result is rounded to fp16 anyway).
 __device__ __forceinline__ void normalize_shared(Ctl *ctl, const float *xs, const _Float16 *g, int d, float ss,
-                                                 float eps, _Float16 *h) {
+                                                 float eps, _Float16 *h, KP *P = nullptr, int trk = -1) {
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   if (lane_id() == 0) lds_st(&ctl->inv_rms, __float_as_uint(inv));
   lds_drain();
   gain_ready();
+  if (kTrace && trk >= 0) trace_at(*P, trk, 14);
   wg_barrier();
   normalize_share(xs, g, d, inv, h, 0);
   lds_drain();
+  if (kTrace && trk >= 0) trace_at(*P, trk, 15);
   wg_barrier();
 }
 
@@ -514,16 +516,17 @@ __device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, un
             ss += ok ? ss_round : 0.0f;
             ss_round = 0.0f;
           })) {
-    // giving up: the stream waves wait at the first barrier; pass it once so
-    // that they see the abort
+    // giving up: the stream waves wait at the first barrier; pass both
+    // barriers so that they see the abort after the second
     if (lane_id() == 0) lds_st(&s.ctl->abort, 1u);
     lds_drain();
+    wg_barrier();
     wg_barrier();
     return false;
   }
   ss = wave_sum(ss);
   if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 8);
-  normalize_shared(s.ctl, xs, g, d, ss, eps, h);
+  normalize_shared(s.ctl, xs, g, d, ss, eps, h, s.P, s.trace_k);
   if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 10);
   return true;
 }
@@ -714,11 +717,15 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
   if (kind == K_QKV || kind == K_GU || kind == K_LM) {
     // an RMSNorm input: every wave writes a share of h between two barriers
     if (ge.nrows > 0) {
+      // (a sync wave that gives up passes both barriers; the share it lets
+      // through reads and writes only this workgroup's LDS)
+      const int trn = kTrace && st.cw == 0 && st.trace_k >= 0 ? st.trace_k : -1;
       wg_barrier();
-      if (lds_ld(&ctl->abort)) return false;
+      trace_at(*st.P, trn, 12);
       normalize_share(part, reinterpret_cast<const _Float16 *>(glds), fresh(*st.P).d,
                       __uint_as_float(lds_ld(&ctl->inv_rms)), h, st.cw + 1);
       lds_drain();
+      trace_at(*st.P, trn, 13);
       wg_barrier();
       if (lds_ld(&ctl->abort)) return false;
     }
@@ -931,8 +938,10 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       }
     }
   };
+  if (kTrace && wave == 1) trace_at(P, trk, 6);
   if (wave > 0) load_round(j0 + kwv);
   __syncthreads();   // wave 0 may still be reading the phase scratch this unit reuses
+  if (kTrace && wave == 1) trace_at(P, trk, 7);
   {
     const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)g * qpg * dh;
     const size_t nw = (size_t)Hkv * half;
@@ -978,6 +987,10 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   }
   for (int jb = wave > 0 ? j0 + kwv : j1; jb < j1; jb += kKW * kKeysPerRound) {
     if (jb != j0 + kwv) load_round(jb);   // the first round was requested before the queries
+    if (kTrace && wave == 1) {
+      asm volatile("" ::"v"(kw[0]), "v"(vw[0]), "v"(kw[kKeysPerRound - 1]), "v"(vw[kKeysPerRound - 1]));
+      trace_at(P, trk, 8);
+    }
     // per query head: scores of this round's keys, online-softmax rescale, accumulate
 #pragma unroll
     for (int h = 0; h < kMaxQpg; ++h) {
@@ -1001,6 +1014,10 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
             sck[k] = wave_sum(qr[h][0] * k0 + qr[h][1] * k1) * P.inv_sqrt_dh;
             mb = fmaxf(mb, sck[k]);
           }
+        }
+        if (kTrace && wave == 1 && h == 0) {
+          asm volatile("" ::"v"(mb));
+          trace_at(P, trk, 10);
         }
         const float alpha = __expf(m[h] - mb);   // 0 while m is -inf
         lsum[h] *= alpha;
@@ -1460,11 +1477,12 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
     if (lane == 0) lds_st(&ctl->abort, 1u);
   };
   // Giving up where the stream waves' next step is the first barrier of an
-  // RMSNorm stage: pass that barrier once so that they see the abort and leave.
+  // RMSNorm stage: pass both of its barriers so that they see the abort and leave.
   auto fail_release = [&](bool at_barrier) __attribute__((always_inline)) {
     fail();
     if (at_barrier) {
       lds_drain();
+      wg_barrier();
       wg_barrier();
     }
   };
