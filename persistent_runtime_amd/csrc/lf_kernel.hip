@@ -376,12 +376,13 @@ __device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, un
 
 // ---------------------------------------------------------------- staging (wave 0)
 
-constexpr int kStageBatch = kStageRound / 64;   // 8-byte loads in flight per lane while staging
+constexpr int kStageBatch = kStageRound / 64;   // words per lane in one staging round
+constexpr int kFetchWindow = 32;                 // 8-byte loads in flight per lane while staging
 constexpr int kStageBatchWide = kStageRoundWide / 64;   // words per lane in a round of the SwiGLU vector
 
 // Wave 0: wait until every word src[0..n) carries `tag`, then hand each payload
 // to use(i, word, real).  The words are read in rounds of 64 * kRound; at most
-// kStageBatch loads per lane are in flight, each later load issued into the
+// kFetchWindow loads per lane are in flight, each later load issued into the
 // registers of a word just handed over, so a round costs one memory round trip.
 // src (and use's destination) must be readable (writable) up to n rounded up to
 // whole rounds; the words past n are handed over with real = false.  Words are
@@ -390,7 +391,7 @@ constexpr int kStageBatchWide = kStageRoundWide / 64;   // words per lane in a r
 // handed over afresh.
 template <int kRound = kStageBatch, class F, class E>
 __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, unsigned tag, F &&use, E &&end) {
-  constexpr int kWin = kRound < kStageBatch ? kRound : kStageBatch;
+  constexpr int kWin = kRound < kFetchWindow ? kRound : kFetchWindow;
   KP &P = *s.P;
   const int lane = lane_id();
   if (P.poll_first && !poll_level(s, 0, P.G, tag)) return false;
@@ -610,6 +611,231 @@ __device__ __forceinline__ void wave_slice(int np, int cw, int &lo, int &hi) {
 }
 
 static_assert((kRing & (kRing - 1)) == 0 && kRing <= 32, "ring depth must be a power of two <= 32");
+static_assert(kRing == 8, "the hand-scheduled stream rounds hold exactly eight pieces");
+
+// ---------------------------------------------------------------- stream rounds in assembly
+//
+// The compiler does not model a load that stays in flight across a loop edge:
+// a ring carried around a loop is moved between registers behind a wait for
+// every load of the round.  The stream waves' ring therefore lives in
+// registers the compiler never allocates (the kernel caps its own allocation
+// at 208 VGPRs): v224..v255 hold the eight pieces in flight (slot k in
+// v[224+4k : 227+4k]), v216..v223 two input-vector buffers, v208..v215
+// temporaries.  Loads into the ring and every use of it are inline assembly
+// with explicit waits; the compiler's own waits stay correct because loads
+// complete in order (an extra ring load only makes them wait longer).
+
+// Every VGPR the ring code owns, named as clobbered so that the kernel's VGPR
+// count includes them (they are outside the compiler's allocation).
+#define LF_RING_VGPRS "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
+
+// Load one 1-KB piece (16 bytes per lane at base + off) into ring slot k.
+#define LF_RING_LOAD(K, R)                                                                           \
+  case K:                                                                                           \
+    asm volatile("global_load_dwordx4 v[" #R "], %0, %1 nt" ::"v"(off), "s"(base)                   \
+                 : "memory", LF_RING_VGPRS);                                                        \
+    break;
+__device__ __forceinline__ void ring_load(int k, const unsigned char *base, unsigned off) {
+  switch (k) {
+    LF_RING_LOAD(0, 224:227)
+    LF_RING_LOAD(1, 228:231)
+    LF_RING_LOAD(2, 232:235)
+    LF_RING_LOAD(3, 236:239)
+    LF_RING_LOAD(4, 240:243)
+    LF_RING_LOAD(5, 244:247)
+    LF_RING_LOAD(6, 248:251)
+    LF_RING_LOAD(7, 252:255)
+    default: break;
+  }
+}
+#undef LF_RING_LOAD
+
+// Request the input vector of the next slot (its piece kp is sQ) from LDS
+// into v[H] and advance sQ to the next piece of the row (0 after the row's
+// last piece, whose lanes past the valid vectors re-read the last one).
+#define LF_HX(H)                                                                                    \
+  "s_cmp_eq_u32 %[sQ], %[ppm1]\n"                                                                   \
+  "s_cselect_b64 vcc, -1, 0\n"                                                                      \
+  "v_cndmask_b32 v214, %[loff], %[toff], vcc\n"                                                     \
+  "s_lshl_b32 %[sT1], %[sQ], 10\n"                                                                  \
+  "s_add_u32 %[sT1], %[sT1], %[hb]\n"                                                               \
+  "v_add_u32 v214, %[sT1], v214\n"                                                                  \
+  "ds_read_b128 v[" #H "], v214\n"                                                                  \
+  "s_add_u32 %[sT1], %[sQ], 1\n"                                                                    \
+  "s_cmp_eq_u32 %[sQ], %[ppm1]\n"                                                                   \
+  "s_cselect_b32 %[sQ], 0, %[sT1]\n"
+
+// Use ring slot K (registers R0..R3, input vector H0..H3) once at most W loads
+// issued after its own are still in flight.  A padding piece (index >= n) is
+// skipped.  The row's last piece is masked to its valid lanes (tm); at a row
+// end (the row's last piece, or the wave's last piece) the wave sum goes to
+// part[pa] from lane 63 and pa advances one row.  The products are summed in
+// the same order as the C dot.
+#define LF_USE(T, K, W, R0, R1, R2, R3, H0, H1, H2, H3)                                                \
+  "s_waitcnt vmcnt(" #W ")\n"                                                                       \
+  "s_add_u32 %[sT1], %[sI], " #K "\n"                                                               \
+  "s_cmp_lt_u32 %[sT1], %[n]\n"                                                                     \
+  "s_cbranch_scc0 .Lu" #T #K "e%=\n"                                                                   \
+  "s_cmp_eq_u32 %[kpc], %[ppm1]\n"                                                                  \
+  "s_cbranch_scc1 .Lu" #T #K "t%=\n"                                                                   \
+  "v_dot2c_f32_f16 %[acc], v" #R0 ", v" #H0 "\n"                                                   \
+  "v_dot2c_f32_f16 %[acc], v" #R1 ", v" #H1 "\n"                                                   \
+  "v_dot2c_f32_f16 %[acc], v" #R2 ", v" #H2 "\n"                                                   \
+  "v_dot2c_f32_f16 %[acc], v" #R3 ", v" #H3 "\n"                                                   \
+  "s_add_u32 %[sT0], %[sT1], 1\n"                                                                   \
+  "s_cmp_eq_u32 %[sT0], %[n]\n"                                                                     \
+  "s_cbranch_scc0 .Lu" #T #K "a%=\n"                                                                   \
+  "s_branch .Lu" #T #K "r%=\n"                                                                         \
+  ".Lu" #T #K "t%=:\n"                                                                                 \
+  "s_mov_b64 %[sE], exec\n"                                                                         \
+  "s_mov_b64 exec, %[tm]\n"                                                                         \
+  "v_dot2c_f32_f16 %[acc], v" #R0 ", v" #H0 "\n"                                                   \
+  "v_dot2c_f32_f16 %[acc], v" #R1 ", v" #H1 "\n"                                                   \
+  "v_dot2c_f32_f16 %[acc], v" #R2 ", v" #H2 "\n"                                                   \
+  "v_dot2c_f32_f16 %[acc], v" #R3 ", v" #H3 "\n"                                                   \
+  "s_mov_b64 exec, %[sE]\n"                                                                         \
+  ".Lu" #T #K "r%=:\n"                                                                                 \
+  "s_nop 4\n"                                                                                       \
+  "v_add_f32_dpp %[acc], %[acc], %[acc] quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+  "s_nop 1\n"                                                                                       \
+  "v_add_f32_dpp %[acc], %[acc], %[acc] quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n" \
+  "s_nop 1\n"                                                                                       \
+  "v_add_f32_dpp %[acc], %[acc], %[acc] row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"  \
+  "s_nop 1\n"                                                                                       \
+  "v_add_f32_dpp %[acc], %[acc], %[acc] row_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"       \
+  "v_mov_b32 v215, 0\n"                                                                             \
+  "s_nop 1\n"                                                                                       \
+  "v_mov_b32_dpp v215, %[acc] row_bcast:15 row_mask:0xa bank_mask:0xf\n"                            \
+  "v_add_f32 %[acc], %[acc], v215\n"                                                                \
+  "v_mov_b32 v215, 0\n"                                                                             \
+  "s_nop 1\n"                                                                                       \
+  "v_mov_b32_dpp v215, %[acc] row_bcast:31 row_mask:0xc bank_mask:0xf\n"                            \
+  "v_add_f32 %[acc], %[acc], v215\n"                                                                \
+  "v_mov_b32 v214, %[pa]\n"                                                                         \
+  "s_mov_b64 %[sE], exec\n"                                                                         \
+  "s_mov_b64 exec, %[m63]\n"                                                                        \
+  "ds_write_b32 v214, %[acc]\n"                                                                     \
+  "s_mov_b64 exec, %[sE]\n"                                                                         \
+  "s_add_u32 %[pa], %[pa], 32\n"                                                                    \
+  "v_mov_b32 %[acc], 0\n"                                                                           \
+  ".Lu" #T #K "a%=:\n"                                                                                 \
+  "s_add_u32 %[sT1], %[kpc], 1\n"                                                                   \
+  "s_cmp_eq_u32 %[kpc], %[ppm1]\n"                                                                  \
+  "s_cselect_b32 %[kpc], 0, %[sT1]\n"                                                               \
+  ".Lu" #T #K "e%=:\n"
+
+// Refill ring slot K (registers RR) with the next piece of the phase (address
+// v[208:209] plus the lane offset; the row's last piece clamps lanes past its
+// valid vectors), or with a padding re-read (v[212:213]) when none is left.
+#define LF_REFILL(K, RR)                                                                            \
+  "s_cmp_eq_u32 %[ileft], 0\n"                                                                      \
+  "s_cbranch_scc1 .Lf" #K "d%=\n"                                                                   \
+  "s_cmp_eq_u32 %[ikp], %[ppm1]\n"                                                                  \
+  "s_cselect_b64 vcc, -1, 0\n"                                                                      \
+  "v_cndmask_b32 v214, %[loff], %[toff], vcc\n"                                                     \
+  "v_add_co_u32 v210, vcc, v208, v214\n"                                                            \
+  "v_addc_co_u32 v211, vcc, 0, v209, vcc\n"                                                         \
+  "global_load_dwordx4 v[" #RR "], v[210:211], off nt\n"                                            \
+  "s_sub_u32 %[ileft], %[ileft], 1\n"                                                               \
+  "s_cmp_eq_u32 %[ikp], %[ppm1]\n"                                                                  \
+  "s_cbranch_scc1 .Lf" #K "n%=\n"                                                                   \
+  "s_add_u32 %[ikp], %[ikp], 1\n"                                                                   \
+  "v_add_co_u32 v208, vcc, 0x400, v208\n"                                                           \
+  "v_addc_co_u32 v209, vcc, 0, v209, vcc\n"                                                         \
+  "s_branch .Lf" #K "e%=\n"                                                                         \
+  ".Lf" #K "n%=:\n"                                                                                 \
+  "s_mov_b32 %[ikp], 0\n"                                                                           \
+  "v_mov_b32 v214, %[adh]\n"                                                                        \
+  "v_add_co_u32 v208, vcc, %[adl], v208\n"                                                          \
+  "v_addc_co_u32 v209, vcc, v214, v209, vcc\n"                                                      \
+  "s_branch .Lf" #K "e%=\n"                                                                         \
+  ".Lf" #K "d%=:\n"                                                                                 \
+  "global_load_dwordx4 v[" #RR "], v[212:213], off nt\n"                                            \
+  ".Lf" #K "e%=:\n"
+
+// Slot K of a round: request the next slot's input vector (NH) unless K is the
+// last slot, wait for this slot's (all LDS accesses but the newest done), use
+// it, and refill the slot if the round is not the phase's last.
+#define LF_SLOT_REFILL(K, NH, R0, R1, R2, R3, H0, H1, H2, H3, RR)                                   \
+  LF_HX(NH) "s_waitcnt lgkmcnt(1)\n" LF_USE(R, K, 7, R0, R1, R2, R3, H0, H1, H2, H3) LF_REFILL(K, RR)
+#define LF_SLOT_LAST(K, W, NH, R0, R1, R2, R3, H0, H1, H2, H3)                                      \
+  LF_HX(NH) "s_waitcnt lgkmcnt(1)\n" LF_USE(L, K, W, R0, R1, R2, R3, H0, H1, H2, H3)
+
+// The LDS byte address of a pointer into this workgroup's LDS.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return (unsigned)(size_t)((const __attribute__((address_space(3))) char *)p);
+}
+
+// One phase of a stream wave: its n pieces (n >= 1) in rounds of eight.  The
+// first round is in the ring on entry (the previous phase's prefetch); every
+// round but the last refills each slot as soon as its piece is used, with the
+// phase's pieces from ip (issue piece kp ikp, ileft real pieces left) and
+// padding re-reads of dummy; the last round only uses its pieces.  No load
+// issued here is in flight on exit.
+struct RoundArgs {
+  unsigned n, nr, kpc, ppm1, hb, pa, ikp, ileft;
+  unsigned long long ip, dummy, adv, tm;
+  unsigned loff, toff;
+};
+__device__ __forceinline__ void stream_rounds(const RoundArgs &a, float &acc) {
+  unsigned kpc = a.kpc, pa = a.pa, ikp = a.ikp, ileft = a.ileft;
+  unsigned sR, sI, sQ, sT0, sT1;
+  unsigned long long sE;
+  const unsigned ipl = (unsigned)a.ip, iph = (unsigned)(a.ip >> 32);
+  const unsigned dml = (unsigned)a.dummy, dmh = (unsigned)(a.dummy >> 32);
+  const unsigned adl = (unsigned)a.adv, adh = (unsigned)(a.adv >> 32);
+  const unsigned long long m63 = 1ull << 63;
+  asm volatile(
+      "v_mov_b32 v208, %[ipl]\n"
+      "v_mov_b32 v209, %[iph]\n"
+      "v_mov_b32 v213, %[dmh]\n"
+      "v_add_co_u32 v212, vcc, %[dml], %[loff]\n"
+      "v_addc_co_u32 v213, vcc, 0, v213, vcc\n"
+      "s_mov_b32 %[sR], 0\n"
+      "s_mov_b32 %[sI], 0\n"
+      ".Lr%=:\n"
+      "s_mov_b32 %[sQ], %[kpc]\n"
+      LF_HX(216:219)
+      "s_add_u32 %[sT1], %[sR], 1\n"
+      "s_cmp_lt_u32 %[sT1], %[nr]\n"
+      "s_cbranch_scc0 .Ll%=\n"
+      LF_SLOT_REFILL(0, 220:223, 224, 225, 226, 227, 216, 217, 218, 219, 224:227)
+      LF_SLOT_REFILL(1, 216:219, 228, 229, 230, 231, 220, 221, 222, 223, 228:231)
+      LF_SLOT_REFILL(2, 220:223, 232, 233, 234, 235, 216, 217, 218, 219, 232:235)
+      LF_SLOT_REFILL(3, 216:219, 236, 237, 238, 239, 220, 221, 222, 223, 236:239)
+      LF_SLOT_REFILL(4, 220:223, 240, 241, 242, 243, 216, 217, 218, 219, 240:243)
+      LF_SLOT_REFILL(5, 216:219, 244, 245, 246, 247, 220, 221, 222, 223, 244:247)
+      LF_SLOT_REFILL(6, 220:223, 248, 249, 250, 251, 216, 217, 218, 219, 248:251)
+      "s_waitcnt lgkmcnt(0)\n"
+      LF_USE(R, 7, 7, 252, 253, 254, 255, 220, 221, 222, 223) LF_REFILL(7, 252:255)
+      "s_add_u32 %[sR], %[sR], 1\n"
+      "s_add_u32 %[sI], %[sI], 8\n"
+      "s_branch .Lr%=\n"
+      ".Ll%=:\n"
+      LF_SLOT_LAST(0, 7, 220:223, 224, 225, 226, 227, 216, 217, 218, 219)
+      LF_SLOT_LAST(1, 6, 216:219, 228, 229, 230, 231, 220, 221, 222, 223)
+      LF_SLOT_LAST(2, 5, 220:223, 232, 233, 234, 235, 216, 217, 218, 219)
+      LF_SLOT_LAST(3, 4, 216:219, 236, 237, 238, 239, 220, 221, 222, 223)
+      LF_SLOT_LAST(4, 3, 220:223, 240, 241, 242, 243, 216, 217, 218, 219)
+      LF_SLOT_LAST(5, 2, 216:219, 244, 245, 246, 247, 220, 221, 222, 223)
+      LF_SLOT_LAST(6, 1, 220:223, 248, 249, 250, 251, 216, 217, 218, 219)
+      "s_waitcnt lgkmcnt(0)\n"
+      LF_USE(L, 7, 0, 252, 253, 254, 255, 220, 221, 222, 223)
+      "s_waitcnt lgkmcnt(0)\n"
+      : [acc] "+v"(acc), [kpc] "+s"(kpc), [pa] "+s"(pa), [ikp] "+s"(ikp), [ileft] "+s"(ileft),
+        [sR] "=&s"(sR), [sI] "=&s"(sI), [sQ] "=&s"(sQ), [sT0] "=&s"(sT0), [sT1] "=&s"(sT1), [sE] "=&s"(sE)
+      : [n] "s"(a.n), [nr] "s"(a.nr), [ppm1] "s"(a.ppm1), [hb] "s"(a.hb), [ipl] "s"(ipl), [iph] "s"(iph),
+        [dml] "s"(dml), [dmh] "s"(dmh), [adl] "s"(adl), [adh] "s"(adh), [tm] "s"(a.tm), [m63] "s"(m63),
+        [loff] "v"(a.loff), [toff] "v"(a.toff)
+      : "vcc", "scc", "memory", LF_RING_VGPRS);
+}
+#undef LF_HX
+#undef LF_USE
+#undef LF_REFILL
+#undef LF_SLOT_REFILL
+#undef LF_SLOT_LAST
+
+
 
 // A stream wave's weights in flight: kRing 16-byte vectors per lane (one 1-KB
 // piece per slot), loaded with non-temporal global loads straight into
@@ -632,8 +858,7 @@ struct Streamer {
                                       // vectors in a row's last piece
   long long adv_last;                 // bytes from a row's last piece to the next row
   const unsigned char *ptr;           // next real piece (lane 0's address)
-  const unsigned char *dummy;         // the vector dummy pieces re-read
-  u32x4 buf[kRing];
+  const unsigned char *dummy;         // the 1 KB that padding pieces re-read
   bool timed;                                 // LF_STATS on stream wave 1
   int trace_k;                                // LF_TRACE: phase slot of the traced token, else -1
   unsigned long long t_ready, t_work, pieces;
@@ -669,9 +894,8 @@ struct Streamer {
     const int lane = lane_id();
     const bool real = q < qend && left > 0;
     const bool last = kp == ppr - 1;
-    const int off = (last ? min(lane, tailv - 1) : lane) * 16;
-    const unsigned char *src = real ? ptr + off : dummy;
-    buf[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+    const unsigned off = (unsigned)((last ? min(lane, tailv - 1) : lane) * 16);
+    ring_load(k, real ? ptr : dummy, off);
     if (real) {
       --left;
       if (last) {
@@ -743,66 +967,40 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
   const int lane = lane_id();
   const int trk = kTrace && st.cw == 0 && st.trace_k >= 0 ? st.trace_k : -1;
   trace_at(*st.P, trk, 3);
-  const u32x4 *hv = reinterpret_cast<const u32x4 *>(h);
   const int ppr = ge.ppr, tailv = ge.kv - (ge.ppr - 1) * 64;
   const int n = sl.n;
-  int row = sl.row, kp = sl.kp;
-  float acc = 0.0f;
-  // Each round first uses the kRing pieces in the ring, then refills it.  The
-  // first round's pieces landed while the input was pending, and a refill can
-  // stall while every CU refills at once, so consuming first lets a phase start
-  // at register speed; after the last round the phase is finished (done flag)
-  // before its refills, which are the next phase's prefetch, are issued.
   const int nr = (n + kRing - 1) / kRing;
-  for (int r = 0; r < nr; ++r) {
-    const int base = r * kRing;
-    // the input vectors of this round's pieces, all requested before the first dot
-    u32x4 hx[kRing];
-    {
-      int kq = kp;
-#pragma unroll
-      for (int k = 0; k < kRing; ++k) {
-        const bool last = kq == ppr - 1;
-        hx[k] = hv[kq * 64 + (last ? min(lane, tailv - 1) : lane)];
-        kq = last ? 0 : kq + 1;
-      }
+  if (nr > 0) {
+    // The ring holds this phase's first round.  If the phase has more pieces
+    // than one round, the streamer still points into this phase: its cursor
+    // (the ninth piece) is where the rounds continue.
+    RoundArgs ra;
+    ra.n = (unsigned)n;
+    ra.nr = (unsigned)nr;
+    ra.kpc = (unsigned)sl.kp;
+    ra.ppm1 = (unsigned)(ppr - 1);
+    ra.hb = lds_addr(h);
+    ra.pa = lds_addr(part + sl.row * 8 + st.cw);
+    const bool more = n > kRing;
+    ra.ikp = more ? (unsigned)st.kp : 0u;
+    ra.ileft = more ? (unsigned)st.left : 0u;
+    ra.ip = reinterpret_cast<unsigned long long>(more ? st.ptr : st.dummy);
+    ra.dummy = reinterpret_cast<unsigned long long>(st.dummy);
+    ra.adv = (unsigned long long)st.adv_last;
+    ra.tm = tailv >= 64 ? ~0ull : ((1ull << tailv) - 1ull);
+    ra.loff = (unsigned)(lane * 16);
+    ra.toff = (unsigned)(min(lane, tailv - 1) * 16);
+    float acc = 0.0f;
+    stream_rounds(ra, acc);
+    if (more) {   // the rounds issued the rest of this phase's pieces
+      st.left = 0;
+      st.pad = 0;
+      st.next_phase_if_done();
     }
-#pragma unroll
-    for (int k = 0; k < kRing; ++k) {
-      const int i = base + k;
-      if (i < n) {
-        const bool last = kp == ppr - 1;
-        const float a2 = dot8(st.buf[k], hx[k], acc);
-        acc = (!last || lane < tailv) ? a2 : acc;
-        if (kTrace && r == 0 && k == 0 && trk >= 0) {   // the round's first piece has landed
-          asm volatile("" ::"v"(acc));
-          trace_at(*st.P, trk, 11);
-        }
-        if (last || i == n - 1) {
-          const float sum = wave_sum_to63(acc);
-          if (lane == 63) part[row * 8 + st.cw] = sum;
-          acc = 0.0f;
-        }
-        if (last) {
-          kp = 0;
-          ++row;
-        } else {
-          ++kp;
-        }
-      }
-    }
-    if (kTrace && r == 0) {
-      asm volatile("" ::"v"(acc));
-      trace_at(*st.P, trk, 9);   // the first round is used
-    }
-    if (r == nr - 1) {
-      lds_drain();
-      trace_at(*st.P, trk, 5);
-      if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
-      if (defer_last_refill) break;   // the caller refills (st.refill()) later
-    }
-    st.refill();
-    if (r == 0) trace_at(*st.P, trk, 4);
+    lds_drain();
+    trace_at(*st.P, trk, 5);
+    if (lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
+    if (!defer_last_refill) st.refill();   // else the caller refills (st.refill()) later
   }
   if (nr == 0 && lane == 0) lds_st(&ctl->done[st.cw], (unsigned)(q + 1));
   if (timed) {
@@ -1348,7 +1546,7 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
 // read is followed by an output that every later phase depends on; a buffer of
 // one generation is rewritten two layers later, after every reader of it.
 template <bool kPrefill>
-__global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))) lf_monokernel(Params Parg) {
   // Parg is the only argument: read it where the dispatch placed it, at the
   // start of the kernel-argument segment (never through a copy).
   (void)Parg;
@@ -1415,7 +1613,7 @@ __global__ void __launch_bounds__(kThreads, 1) lf_monokernel(Params Parg) {
       // that the chip's padding reads do not all queue at one L2 channel
       const long long nkb = (long long)P.layer_stride / 1024;
       const long long kb = (long long)((b * kWaves + wave) & 63) % (nkb > 0 ? nkb : 1);
-      st.dummy = reinterpret_cast<const unsigned char *>(P.wbase) + kb * 1024 + lane * 16;
+      st.dummy = reinterpret_cast<const unsigned char *>(P.wbase) + kb * 1024;
     }
     st.left = st.pad = st.kp = 0;
     st.ppr = 1;
