@@ -1740,9 +1740,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tq = lap(sy, ST_STAGE, tq);
         trace(Pl, t, 5 * l + 0, 0);
         announce_input(ctl, q0);
+        const RowSpans rs = row_spans(ctl, K_QKV);   // (constant: read before the wait)
         wait_streams(ctl, q0);
         tq = lap(sy, ST_STREAMS, tq);
-        const RowSpans rs = row_spans(ctl, K_QKV);
         trace(Pl, t, 5 * l + 0, 1);
         const unsigned tag = lvl + PH_QKV;
         const size_t kvrow = ((size_t)l * Pl.max_seq + pos) * (size_t)nk;
@@ -1803,9 +1803,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 2, 0);
         announce_input(ctl, q0 + 1);
+        const RowSpans rs = row_spans(ctl, K_O);   // (constant: read before the wait)
         wait_streams(ctl, q0 + 1);
         tk = lap(sy, ST_STREAMS, tk);
-        const RowSpans rs = row_spans(ctl, K_O);
         trace(Pl, t, 5 * l + 2, 1);
         // Every store this wave made before (KV cache rows, tagged words) has
         // completed before anything it publishes from here on: later steps
@@ -1844,9 +1844,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 3, 0);
         announce_input(ctl, q0 + 2);
+        const RowSpans rs = row_spans(ctl, K_GU);   // (constant: read before the wait)
         wait_streams(ctl, q0 + 2);
         tk = lap(sy, ST_STREAMS, tk);
-        const RowSpans rs = row_spans(ctl, K_GU);
         trace(Pl, t, 5 * l + 3, 1);
         const unsigned tag = lvl + PH_GU;
         u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
@@ -1873,9 +1873,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 4, 0);
         announce_input(ctl, q0 + 3);
+        const RowSpans rs = row_spans(ctl, K_D);   // (constant: read before the wait)
         wait_streams(ctl, q0 + 3);
         tk = lap(sy, ST_STREAMS, tk);
-        const RowSpans rs = row_spans(ctl, K_D);
         trace(Pl, t, 5 * l + 4, 1);
         const unsigned tag = lvl + PH_D;
         u64 *xo = Pl.xout_t + (size_t)gen * d;
@@ -1909,8 +1909,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       }
       trace(P, t, 5 * L, 0);
       announce_input(ctl, qlm);
+      const RowSpans rs = row_spans(ctl, K_LM);   // (constant: read before the wait)
       wait_streams(ctl, qlm);
-      const RowSpans rs = row_spans(ctl, K_LM);
       trace(P, t, 5 * L, 1);
       float best = -INFINITY;
       int bi = 0x7fffffff;
