@@ -1803,24 +1803,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 2, 0);
         announce_input(ctl, q0 + 1);
-        const RowSpans rs = row_spans(ctl, K_O);   // (constant: read before the wait)
-        wait_streams(ctl, q0 + 1);
-        tk = lap(sy, ST_STREAMS, tk);
-        trace(Pl, t, 5 * l + 2, 1);
+        // Before the wait (none of it depends on the stream waves): the row
+        // spans, the output words, and the residual of this lane's first row.
+        const RowSpans rs = row_spans(ctl, K_O);
+        u64 *xm = Pl.xmid_t + (size_t)gen * d;
+        const int hio = Pl.hidden_io;
+        auto residual = [&](int i) __attribute__((always_inline)) {
+          const int r = ge.r0 + i;
+          return l > 0 ? xown[i] : (hio ? Pl.x_hidden[r] : (float)emb[(size_t)token * d + r]);
+        };
+        const float xin0 = lane < ge.nrows ? residual(lane) : 0.0f;
         // Every store this wave made before (KV cache rows, tagged words) has
         // completed before anything it publishes from here on: later steps
         // read the cache rows with plain loads.  They were issued a whole
         // projection ago, so this wait is short.
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         asm volatile("" ::: "memory");
+        wait_streams(ctl, q0 + 1);
+        tk = lap(sy, ST_STREAMS, tk);
+        trace(Pl, t, 5 * l + 2, 1);
         const unsigned tag = lvl + PH_O;
-        u64 *xm = Pl.xmid_t + (size_t)gen * d;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
-          float xin;
-          if (l > 0) xin = xown[i];
-          else if (Pl.hidden_io) xin = Pl.x_hidden[r];
-          else xin = (float)emb[(size_t)token * d + r];
+          const float xin = i == lane ? xin0 : residual(i);
           const float x = xin + row_value(part, rs, i);
           xown[i] = x;
           st_tag(xm + r, tag_f(x, tag));
@@ -1845,11 +1850,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         trace(Pl, t, 5 * l + 3, 0);
         announce_input(ctl, q0 + 2);
         const RowSpans rs = row_spans(ctl, K_GU);   // (constant: read before the wait)
+        u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
+        asm volatile("" : "+s"(ad));   // computed now, not after the wait
         wait_streams(ctl, q0 + 2);
         tk = lap(sy, ST_STREAMS, tk);
         trace(Pl, t, 5 * l + 3, 1);
         const unsigned tag = lvl + PH_GU;
-        u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
         for (int i = lane; i < ge.nrows / 4; i += 64) {
           // rows 4i..4i+3 = gate j, up j, gate j+1, up j+1 with j = r0/2 + 2i
           const float g0 = row_value(part, rs, 4 * i), u0 = row_value(part, rs, 4 * i + 1);
@@ -1873,16 +1879,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 4, 0);
         announce_input(ctl, q0 + 3);
-        const RowSpans rs = row_spans(ctl, K_D);   // (constant: read before the wait)
+        // before the wait: row spans, output words, this lane's first residual
+        const RowSpans rs = row_spans(ctl, K_D);
+        u64 *xo = Pl.xout_t + (size_t)gen * d;
+        const bool host_out = Pl.hidden_io && l == L - 1;
+        const float xo0 = lane < ge.nrows ? xown[lane] : 0.0f;
         wait_streams(ctl, q0 + 3);
         tk = lap(sy, ST_STREAMS, tk);
         trace(Pl, t, 5 * l + 4, 1);
         const unsigned tag = lvl + PH_D;
-        u64 *xo = Pl.xout_t + (size_t)gen * d;
-        const bool host_out = Pl.hidden_io && l == L - 1;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
-          const float x = xown[i] + row_value(part, rs, i);
+          const float x = (i == lane ? xo0 : xown[i]) + row_value(part, rs, i);
           xown[i] = x;
           st_tag(xo + r, tag_f(x, tag));
           if (host_out) Pl.x_out[r] = x;
