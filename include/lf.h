@@ -76,7 +76,9 @@ typedef struct {
 } lf_weights;
 
 /* Validate the config, repack the weights into library-owned device memory (the
- * caller may free its copies afterwards), allocate the KV cache (zeroed),
+ * caller may free its copies afterwards; each RMSNorm gain vector is folded into
+ * the columns of the projection after it, the weight pre-transform of the
+ * pages' "Weight streaming" section), allocate the KV cache (zeroed),
  * activations and synchronisation words, and build the static work plan.
  * stream: a hipStream_t (NULL = default stream).  On success *out owns all of it.
  * Errors: LF_EINVAL (config, null pointer), LF_EUNSUPPORTED, LF_ENOMEM, LF_EHIP. */

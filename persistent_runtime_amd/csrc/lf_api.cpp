@@ -8,9 +8,11 @@
 // partition" and "Pillar 3"); here the partition is fixed when the state is
 // created: contiguous row blocks of every matrix per workgroup, and
 // (KV head, key chunk) attention units derived from the position.  Weights are
-// repacked once ("Offline, weights are pre-transformed" in "Weight streaming")
-// so the rotary pairs (i, i + head_dim/2) of each head and the SwiGLU pairs
-// (gate j, up j) sit in adjacent rows and every row block holds whole pairs.
+// transformed once, ahead of decoding, as the pages' section "Weight streaming"
+// does it: rows are repacked so the rotary pairs (i, i + head_dim/2) of each
+// head and the SwiGLU pairs (gate j, up j) sit in adjacent rows and every row
+// block holds whole pairs, and each RMSNorm gain vector is folded into the
+// columns of the projection that follows it.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -213,13 +215,12 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
 
   // ---- packed weights
   const size_t rowB_d = (size_t)d * 2;
-  const size_t sz_norm = align_up(rowB_d, 256);
   const size_t sz_qkv = align_up((size_t)P.nqkv * rowB_d, 256);
   const size_t sz_o = align_up((size_t)d * Hq * dh * 2, 256);
   const size_t sz_gu = align_up((size_t)2 * F * rowB_d, 256);
   const size_t sz_d = align_up((size_t)d * F * 2, 256);
-  const size_t per_layer = 2 * sz_norm + sz_qkv + sz_o + sz_gu + sz_d;
-  const size_t sz_head = hidden ? 0 : sz_norm + 2 * align_up((size_t)V * rowB_d, 256);
+  const size_t per_layer = sz_qkv + sz_o + sz_gu + sz_d;
+  const size_t sz_head = hidden ? 0 : 2 * align_up((size_t)V * rowB_d, 256);
   char *wb = (char *)dev_alloc(st, per_layer * c.n_layers + sz_head, &e);
   if (!wb) return bail(fail(&st->err, LF_ENOMEM, "weight buffer allocation failed"));
   hipStream_t s = st->stream;
@@ -227,11 +228,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   for (int l = 0; l < c.n_layers; ++l) {
     const lf_layer_weights &L = w->layers[l];
     char *base = wb + per_layer * l;
-    char *an = base, *fn = base + sz_norm, *qkv = fn + sz_norm, *wo = qkv + sz_qkv, *wgu = wo + sz_o,
-         *wd = wgu + sz_gu;
-    if ((e = hipMemcpyAsync(an, L.attn_norm, rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
-        (e = hipMemcpyAsync(fn, L.ffn_norm, rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess)
-      return bail(hip_fail(st, e, "copy norms"));
+    char *qkv = base, *wo = qkv + sz_qkv, *wgu = wo + sz_o, *wd = wgu + sz_gu;
     // q and k heads: packed row (h*dh + 2i) = source row (h*dh + i), (h*dh + 2i + 1) = (h*dh + i + dh/2)
     for (int part = 0; part < 2; ++part) {
       const char *src = (const char *)(part == 0 ? L.wq : L.wk);
@@ -256,26 +253,29 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
       return bail(hip_fail(st, e, "interleave gate/up rows"));
     if ((e = hipMemcpyAsync(wd, L.w_down, (size_t)d * F * 2, hipMemcpyDeviceToDevice, s)) != hipSuccess)
       return bail(hip_fail(st, e, "copy w_down"));
+    // RMSNorm is g * x / rms(x) and the projection after it is linear, so the
+    // gains are folded into the projection's columns here and the kernel
+    // scales the row sums by 1 / rms.
+    if ((e = lf::launch_scale_columns(qkv, (size_t)P.nqkv, d, L.attn_norm, s)) != hipSuccess ||
+        (e = lf::launch_scale_columns(wgu, (size_t)2 * F, d, L.ffn_norm, s)) != hipSuccess)
+      return bail(hip_fail(st, e, "fold norm gains"));
   }
   if (!hidden) {
     char *base = wb + per_layer * c.n_layers;
-    char *fnorm = base, *lm = base + sz_norm, *emb = lm + align_up((size_t)V * rowB_d, 256);
-    if ((e = hipMemcpyAsync(fnorm, w->final_norm, rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
-        (e = hipMemcpyAsync(lm, w->lm_head, (size_t)V * rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
-        (e = hipMemcpyAsync(emb, w->tok_emb, (size_t)V * rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    char *lm = base, *emb = lm + align_up((size_t)V * rowB_d, 256);
+    if ((e = hipMemcpyAsync(lm, w->lm_head, (size_t)V * rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(emb, w->tok_emb, (size_t)V * rowB_d, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = lf::launch_scale_columns(lm, (size_t)V, d, w->final_norm, s)) != hipSuccess)
       return bail(hip_fail(st, e, "copy embedding / lm_head"));
-    P.final_norm = fnorm;
     P.lm_head = lm;
     P.tok_emb = emb;
   }
   P.wbase = wb;
   P.layer_stride = per_layer;
-  P.part_off[lf::LW_ATTN_NORM] = 0;
-  P.part_off[lf::LW_FFN_NORM] = sz_norm;
-  P.part_off[lf::LW_QKV] = 2 * sz_norm;
-  P.part_off[lf::LW_O] = 2 * sz_norm + sz_qkv;
-  P.part_off[lf::LW_GU] = 2 * sz_norm + sz_qkv + sz_o;
-  P.part_off[lf::LW_D] = 2 * sz_norm + sz_qkv + sz_o + sz_gu;
+  P.part_off[lf::LW_QKV] = 0;
+  P.part_off[lf::LW_O] = sz_qkv;
+  P.part_off[lf::LW_GU] = sz_qkv + sz_o;
+  P.part_off[lf::LW_D] = sz_qkv + sz_o + sz_gu;
 
   // ---- KV cache, rotary table, activations, sync words
   const size_t kv_elems = (size_t)c.n_layers * c.max_seq * Hkv * dh;
@@ -369,14 +369,16 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   const size_t round_up_words = o_words > a_words ? o_words : a_words;
   size_t h_b = align_up((size_t)hmax * 2 + 1024, 16);   // + one piece of slack for masked lanes
   if (round_up_words * 4 > h_b) h_b = align_up(round_up_words * 4, 16);
-  const size_t xs_b = (size_t)(d + lf::kStageRound - 1) / lf::kStageRound * lf::kStageRound * 4;   // fp32 staging
+  // an RMSNorm input is written as fp16 elements in whole rounds of words
+  const size_t d_elems = round_up((size_t)d, lf::kStageRound);
+  if (d_elems * 2 > h_b) h_b = align_up(d_elems * 2, 16);
   const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);
   // attention scratch: queries, current K/V row, per-wave (m, l) and per-wave o
   const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (size_t)lf::kWaves * 8 * 2 * 4 +
                         (size_t)lf::kWaves * P.qpg * dh * 4;
   const size_t samp_b = 4096;
-  // [h | part]; part also holds the fp32 copy of a vector being normalised
-  size_t region_a = h_b + (part_b > xs_b ? part_b : xs_b);
+  // [h | part]
+  size_t region_a = h_b + part_b;
   if (attn_b > region_a) region_a = attn_b;
   if (samp_b > region_a) region_a = samp_b;
   P.lds_h = 0;
@@ -384,8 +386,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_red = (int)align_up(region_a, 256);
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + lf::kCtlBytes;
-  P.lds_gain = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
-  P.lds_trace = (int)align_up((size_t)P.lds_gain + align_up((size_t)d * 2, 1024), 256);
+  P.lds_trace = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
   const size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
   P.part_rows = rows_max;
   P.hmax = hmax;

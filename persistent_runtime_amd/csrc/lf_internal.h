@@ -9,7 +9,10 @@ namespace lf {
 constexpr int kThreads = 512;          // 8 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kAttnBlock = 512;        // key positions scored per attention sub-block
-constexpr int kMinKeysPerUnit = 16;    // smallest attention split-K chunk
+#ifndef LF_MIN_KEYS_PER_UNIT
+#define LF_MIN_KEYS_PER_UNIT 16
+#endif
+constexpr int kMinKeysPerUnit = LF_MIN_KEYS_PER_UNIT;   // smallest attention split-K chunk
 constexpr int kMaxSplit = 64;          // most split-K chunks per KV head
 constexpr int kStatWords = 16;         // uint64 statistics per workgroup (LF_STATS)
 // LF_TRACE builds also record, for one token, three timestamps per phase and
@@ -33,7 +36,7 @@ enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYE
 
 // Offsets (bytes) of one layer's pieces inside the packed weight buffer; layer l
 // starts at wbase + l * layer_stride.
-enum LayerPart { LW_ATTN_NORM = 0, LW_FFN_NORM, LW_QKV, LW_O, LW_GU, LW_D, LW_COUNT };
+enum LayerPart { LW_QKV = 0, LW_O, LW_GU, LW_D, LW_COUNT };
 
 struct Params {
   // shape
@@ -44,13 +47,15 @@ struct Params {
   int hidden_io, sampling;
   int levels_per_token;
   // weights (library-owned, packed)
-  // Per layer: attn_norm [d], ffn_norm [d], Wqkv [(Hq+2Hkv)*dh][d] (q/k rows
-  // pair-interleaved per head: i, i+dh/2), Wo [d][Hq*dh], Wgu [2F][d] (row 2j =
-  // gate j, 2j+1 = up j), Wd [d][F]; all fp16.
+  // Per layer: Wqkv [(Hq+2Hkv)*dh][d] (q/k rows pair-interleaved per head:
+  // i, i+dh/2), Wo [d][Hq*dh], Wgu [2F][d] (row 2j = gate j, 2j+1 = up j),
+  // Wd [d][F]; all fp16.  The RMSNorm gains that precede a projection are
+  // folded into its columns (Wqkv and Wgu by the layer's attention / FFN norm
+  // gains, lm_head by the final norm gain), each product rounded to fp16 once.
   const char *wbase;
   unsigned long long layer_stride;
   unsigned long long part_off[LW_COUNT];
-  const void *tok_emb, *final_norm, *lm_head;
+  const void *tok_emb, *lm_head;
   // state
   void *kcache, *vcache;   // fp16 [L][max_seq][Hkv][dh]
   const float *rope;       // [max_seq][dh/2][2] (cos, sin)
@@ -85,11 +90,14 @@ struct Params {
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   int poll_first;          // 1: poll the producers' progress words before reading tagged data
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_gain, lds_trace, lds_bytes;
+  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_trace, lds_bytes;
   int part_rows, hmax;
 };
 
 hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream);
+// w[r][c] = fp16(w[r][c] * g[c]) for an fp16 matrix of `rows` rows of `cols`
+// elements (cols % 8 == 0, w 16-byte aligned, g 2-byte aligned).
+hipError_t launch_scale_columns(void *w, size_t rows, int cols, const void *g, hipStream_t stream);
 hipError_t launch_test_expdef(const float *x, float *y, int64_t n, hipStream_t stream);
 hipError_t launch_test_sample(const float *logits, int n, float inv_temp, float top_p,
                               unsigned long long seed, const int *pos, int m, int *tokens,

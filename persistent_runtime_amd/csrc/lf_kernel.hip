@@ -245,8 +245,7 @@ struct Ctl {
   unsigned abort;           // the sync wave gave up (the error word is set)
   unsigned done[kWaves];    // per stream wave: last GEMV phase (1-based) it finished
   int status;               // outcome of a barrier-based wait
-  unsigned inv_rms;         // 1 / rms of the vector being normalised (fp32 bits)
-  int pad[4];
+  int pad[5];
   Geo geo[K_COUNT];
   // The partition of every phase kind among the stream waves, fixed for the
   // launch: computed once so that no phase divides by the pieces per row.
@@ -280,8 +279,11 @@ __device__ __forceinline__ unsigned long long stamp(const Sync &s) { return s.ti
 
 // LF_TRACE builds: timestamp j (0 input staged, 1 streams done, 2 published;
 // stream wave 1: 3 input seen, 4 first round done, 5 done; wave 0: 6 staging
-// started, 7 tagged input complete, 8 sum of squares, 9 gains ready, 10
-// normalised; attention: 3 queries staged, 4 keys done, 5 partial stored)
+// started, 7 tagged input complete, 8 sum of squares; attention, wave 1: 6
+// unit start, 7 first barrier passed, 3 queries staged, 8 first keys loaded,
+// 10 first scores, 4 keys done, 9 waves' states in LDS, 5 partial stored, and
+// in a merging unit 11 merge start, 12 chunk weights known, 13 first head
+// merged)
 // of phase k (5l + {QKV, attention, O, gate/up, down}; 5L lm_head; 5L+1 token).
 // Timestamps collect in LDS and are copied out when the kernel ends, so that
 // tracing adds no global stores (and no store waits) to the path it measures.
@@ -300,9 +302,11 @@ __device__ __forceinline__ void trace_at(KP &P, int k, int j) {
 
 // The bound of a wait started at t0 has expired: record the first such event in
 // the error word (any lane may call; one wins).  Also true once another
-// workgroup has recorded an error.
-__device__ __forceinline__ bool expired(KP &P, unsigned long long t0, unsigned level) {
-  if (now_ticks() - t0 <= P.timeout_ticks) return ld_dev(&P.err[0]) != 0u;
+// workgroup has recorded an error: err0 is the error word as read with the
+// polled data, in the same batch of loads, so that checking it adds no memory
+// round trip to a retry.
+__device__ __forceinline__ bool expired(KP &P, unsigned long long t0, unsigned level, unsigned err0) {
+  if (now_ticks() - t0 <= P.timeout_ticks) return err0 != 0u;
   unsigned zero = 0u;
   if (__hip_atomic_compare_exchange_strong(&P.err[0], &zero, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT)) {
@@ -320,9 +324,10 @@ __device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsign
   bool ok = false;
   for (;;) {
     bool behind = false;
+    const unsigned e = ld_dev(&P.err[0]);
     for (int i = lane_id(); i < count; i += 64) behind |= ld_dev(&P.progress[first + i]) < level;
     if (wave_none(behind)) { ok = true; break; }
-    if (expired(P, t0, level)) break;
+    if (expired(P, t0, level, e)) break;
   }
   s.spin += now_ticks() - t0;
   s.waits += 1;
@@ -404,6 +409,7 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
       u64 v[kWin];
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = ld_dev(rp + 64 * j);
+      const unsigned e = ld_dev(&P.err[0]);   // for a retry's give-up check
       unsigned bad = 0u;
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
@@ -424,120 +430,45 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
           trace_row(P, s.trace_k)[7] = now_ticks();
         break;
       }
-      if (expired(P, t0, tag)) return false;
+      if (expired(P, t0, tag, e)) return false;
     }
   }
   return true;
 }
 
-// Wave 0: start copying the n fp16 norm gains g[0..n) (n % 8 == 0) into LDS
-// `dst` (rounded up to whole 1-KB pieces) with LDS-DMA.  The copy lands while
-// the wave waits for the vector it normalises; it is complete at vmcnt(0).
-__device__ __forceinline__ void prefetch_gain(const _Float16 *g, int n, unsigned char *dst) {
-  const int nvec = n / 8, lane = lane_id();
-  for (int b = 0; b < nvec; b += 64) {
-    const int v = min(b + lane, nvec - 1);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(g + 8 * v),
-                                     (__attribute__((address_space(3))) void *)(dst + b * 16), 16, 0, 0);
-  }
-}
-__device__ __forceinline__ void gain_ready() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier that waits for no memory operation: the stream waves keep
-// their weight loads in flight across it.  A wave that has ended no longer
-// counts, so a sync wave that gives up releases the others.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Second pass of RMSNorm, shared by the workgroup's waves: wave w writes its
-// share of h = fp16(g * x * inv) from the fp32 vector xs, eight elements per
-// lane (gains g in LDS, inv = 1 / rms computed once).  The shares are
-// contiguous runs of 8-element groups, so each wave's LDS reads are sequential.
-__device__ __forceinline__ void normalize_share(const float *xs, const _Float16 *g, int d, float inv, _Float16 *h,
-                                                int w) {
-  const float4 *x4 = reinterpret_cast<const float4 *>(xs);
-  const f16x8 *g8 = reinterpret_cast<const f16x8 *>(g);
-  f16x8 *h8 = reinterpret_cast<f16x8 *>(h);
-  const int ng = d / 8, per = (ng + kWaves - 1) / kWaves;
-  const int v1 = min(ng, (w + 1) * per);
-  for (int v = w * per + lane_id(); v < v1; v += 64) {
-    const float4 a = x4[2 * v], b = x4[2 * v + 1];
-    const f16x8 gg = g8[v];
-    f16x8 o;
-    o[0] = (_Float16)((float)gg[0] * (a.x * inv));
-    o[1] = (_Float16)((float)gg[1] * (a.y * inv));
-    o[2] = (_Float16)((float)gg[2] * (a.z * inv));
-    o[3] = (_Float16)((float)gg[3] * (a.w * inv));
-    o[4] = (_Float16)((float)gg[4] * (b.x * inv));
-    o[5] = (_Float16)((float)gg[5] * (b.y * inv));
-    o[6] = (_Float16)((float)gg[6] * (b.z * inv));
-    o[7] = (_Float16)((float)gg[7] * (b.w * inv));
-    h8[v] = o;
-  }
-}
-
-// Sync wave, once x (fp32, in xs), the gains and sum(x^2) are in place: publish
-// 1 / rms, release the stream waves (barrier), write its own share of h, and
-// wait until every share is written (second barrier).  The reciprocal is taken
-// once (within an ulp of dividing; the result is rounded to fp16 anyway).
-__device__ __forceinline__ void normalize_shared(Ctl *ctl, const float *xs, const _Float16 *g, int d, float ss,
-                                                 float eps, _Float16 *h, KP *P = nullptr, int trk = -1) {
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  if (lane_id() == 0) lds_st(&ctl->inv_rms, __float_as_uint(inv));
-  lds_drain();
-  gain_ready();
-  if (kTrace && trk >= 0) trace_at(*P, trk, 14);
-  wg_barrier();
-  normalize_share(xs, g, d, inv, h, 0);
-  lds_drain();
-  if (kTrace && trk >= 0) trace_at(*P, trk, 15);
-  wg_barrier();
-}
-
 // RMSNorm of a residual published by other workgroups as tagged fp32 words.
-__device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, unsigned tag, const _Float16 *gain,
-                                                     int d, float eps, _Float16 *h, unsigned char *glds, float *xs) {
-  const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
-  prefetch_gain(gain, d, glds);
+// The gain vector is folded into the next projection's columns when the
+// weights are packed, and the factor 1 / rms is taken out too: that
+// projection is linear in its input, so h = fp16(x) is written as the words
+// land and the caller scales the row sums by the returned inv.  Nothing runs
+// between the last word's arrival and the stream waves' start but the sum.
+__device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, unsigned tag, int d, float eps,
+                                                     _Float16 *h, float &inv) {
   float ss = 0.0f, ss_round = 0.0f;   // ss_round: the round being read
   if (!fetch_tagged(
           s, src, d, tag,
           [&](int i, u64 w, bool real) __attribute__((always_inline)) {
             const float x = pay_f(w);
             ss_round += real ? x * x : 0.0f;
-            xs[i] = x;
+            h[i] = (_Float16)x;
           },
           [&](bool ok) __attribute__((always_inline)) {
             ss += ok ? ss_round : 0.0f;
             ss_round = 0.0f;
           })) {
-    // giving up: the stream waves wait at the first barrier; pass both
-    // barriers so that they see the abort after the second
     if (lane_id() == 0) lds_st(&s.ctl->abort, 1u);
-    lds_drain();
-    wg_barrier();
-    wg_barrier();
     return false;
   }
-  ss = wave_sum(ss);
+  // one reciprocal (within an ulp of dividing every row sum)
+  inv = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
   if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 8);
-  normalize_shared(s.ctl, xs, g, d, ss, eps, h, s.P, s.trace_k);
-  if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 10);
   return true;
 }
 
-// RMSNorm of a layer-0 input: an fp16 embedding row or the host's fp32 vector.
-__device__ __forceinline__ void stage_rmsnorm_plain(Ctl *ctl, const float *x_host, const _Float16 *x16,
-                                                    const _Float16 *gain, int d, float eps, _Float16 *h,
-                                                    unsigned char *glds, float *xs) {
-  const _Float16 *g = reinterpret_cast<const _Float16 *>(glds);
-  prefetch_gain(gain, d, glds);
+// The same for a layer-0 input: an fp16 embedding row or the host's fp32
+// vector.  Returns 1 / rms.
+__device__ __forceinline__ float stage_rmsnorm_plain(const float *x_host, const _Float16 *x16, int d, float eps,
+                                                     _Float16 *h) {
   const int lane = lane_id();
   float ss = 0.0f;
   for (int base = 0; base < d; base += 64 * kStageBatch) {
@@ -552,11 +483,11 @@ __device__ __forceinline__ void stage_rmsnorm_plain(Ctl *ctl, const float *x_hos
       const int i = base + 64 * j + lane;
       if (i < d) {
         ss += v[j] * v[j];
-        xs[i] = v[j];
+        h[i] = (_Float16)v[j];
       }
     }
   }
-  normalize_shared(ctl, xs, g, d, wave_sum(ss), eps, h);
+  return 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
 }
 
 // A vector published as tagged fp16 pairs (n_pairs words) into LDS h.
@@ -932,32 +863,15 @@ __device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, cons
 // row sum per (row, wave) in part[row * 8 + cw].  Returns false if the sync wave
 // aborted.
 __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl *ctl, _Float16 *h, float *part,
-                                             const unsigned char *glds, bool defer_last_refill = false) {
+                                             bool defer_last_refill = false) {
   const Geo ge = uniform_geo(ctl, kind);
   const Slice sl = uniform_slice(ctl, kind, st.cw);
   // the dependency wait happens on wave 0; here only its LDS announcement
   const bool timed = st.timed;
   unsigned long long t0 = timed ? now_ticks() : 0ull;
-  if (kind == K_QKV || kind == K_GU || kind == K_LM) {
-    // an RMSNorm input: every wave writes a share of h between two barriers
-    if (ge.nrows > 0) {
-      // (a sync wave that gives up passes both barriers; the share it lets
-      // through reads and writes only this workgroup's LDS)
-      const int trn = kTrace && st.cw == 0 && st.trace_k >= 0 ? st.trace_k : -1;
-      wg_barrier();
-      trace_at(*st.P, trn, 12);
-      normalize_share(part, reinterpret_cast<const _Float16 *>(glds), fresh(*st.P).d,
-                      __uint_as_float(lds_ld(&ctl->inv_rms)), h, st.cw + 1);
-      lds_drain();
-      trace_at(*st.P, trn, 13);
-      wg_barrier();
-      if (lds_ld(&ctl->abort)) return false;
-    }
-  } else {
-    while (lds_ld(&ctl->h_ready) < (unsigned)(q + 1)) {
-      if (lds_ld(&ctl->abort)) return false;
-      __builtin_amdgcn_s_sleep(1);
-    }
+  while (lds_ld(&ctl->h_ready) < (unsigned)(q + 1)) {
+    if (lds_ld(&ctl->abort)) return false;
+    __builtin_amdgcn_s_sleep(1);
   }
   if (timed) {
     const unsigned long long t1 = now_ticks();
@@ -1063,16 +977,19 @@ __device__ __forceinline__ void attn_split(int n, int G, int Hkv, int &S, int &L
   Lc = (n + S - 1) / S;
 }
 
-// Wait for one tagged word; on expiry returns it anyway and sets *bad.
+// Wait for one tagged word; on expiry returns it anyway and sets *bad.  Each
+// retry reads the word and the error word together: one round trip.
 __device__ __forceinline__ u64 ld_tag_wait(KP &P, const u64 *p, unsigned tag, unsigned long long t0,
                                            bool &bad) {
   u64 w = ld_dev(p);
   while (tag_of(w) != tag) {
-    if (expired(P, t0, tag)) {
+    const unsigned e = ld_dev(&P.err[0]);
+    w = ld_dev(p);
+    if (tag_of(w) == tag) break;
+    if (expired(P, t0, tag, e)) {
       bad = true;
       break;
     }
-    w = ld_dev(p);
   }
   return w;
 }
@@ -1245,37 +1162,55 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     }
   }
   trace_at(P, trw, 4);
-  // the eight waves' states -> the unit's partial
+  // the stream waves' states -> the unit's partial (wave 0 holds no keys)
 #pragma unroll
   for (int h = 0; h < kMaxQpg; ++h) {
-    if (h < qpg) {
+    if (h < qpg && wave > 0) {
       if (lane == 0) {
         wml[(wave * kMaxQpg + h) * 2 + 0] = m[h];
         wml[(wave * kMaxQpg + h) * 2 + 1] = lsum[h];
       }
-      if (act) {
-        wo[(wave * qpg + h) * dh + e0] = o[h][0];
-        wo[(wave * qpg + h) * dh + e0 + 1] = o[h][1];
-      }
+      if (act) *reinterpret_cast<float2 *>(&wo[(wave * qpg + h) * dh + e0]) = make_float2(o[h][0], o[h][1]);
     }
   }
+  // (taken before the barrier: none of it depends on the other waves)
+  const int stride = dh + 2;
+  u64 *pg = P.part_t + (size_t)gen * P.part_gen;
+  u64 *o_out = P.o_t + (size_t)gen * (P.Hq * dh / 2) + ((size_t)g * qpg * dh + e0) / 2;
+  asm volatile("" : "+s"(pg), "+v"(o_out));
   __syncthreads();
   if (wave == 1) {
-    const int stride = dh + 2;
-    u64 *pg = P.part_t + (size_t)gen * P.part_gen;
+    trace_at(P, trw, 9);
     u64 *dst = pg + (size_t)u * qpg * stride;
     for (int h = 0; h < qpg; ++h) {
-      float M = -INFINITY;
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wml[(w * kMaxQpg + h) * 2]);
+      // every read is in bounds for every lane (e0 = 0 on lanes past the head
+      // dims), so the seven states load together
+      float mw[kKW], lw[kKW];
+      float2 ow[kKW];
+#pragma unroll
+      for (int w = 0; w < kKW; ++w) {
+        mw[w] = wml[((w + 1) * kMaxQpg + h) * 2];
+        lw[w] = wml[((w + 1) * kMaxQpg + h) * 2 + 1];
+        ow[w] = *reinterpret_cast<const float2 *>(&wo[((w + 1) * qpg + h) * dh + e0]);
+      }
+      float M = mw[0];
+#pragma unroll
+      for (int w = 1; w < kKW; ++w) M = fmaxf(M, mw[w]);
       float Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = wml[(w * kMaxQpg + h) * 2];
-        const float sw = mw == -INFINITY ? 0.0f : __expf(mw - M);
-        Ls += sw * wml[(w * kMaxQpg + h) * 2 + 1];
+#pragma unroll
+      for (int w = 0; w < kKW; ++w) {
+        const float sw = mw[w] == -INFINITY ? 0.0f : __expf(mw[w] - M);
+        Ls += sw * lw[w];
+        a0 += sw * ow[w].x;
+        a1 += sw * ow[w].y;
+      }
+      if (S == 1) {
+        // the unit holds every key of the head: its state is the head's output
         if (act) {
-          a0 += sw * wo[(w * qpg + h) * dh + e0];
-          a1 += sw * wo[(w * qpg + h) * dh + e0 + 1];
+          const float il = 1.0f / Ls;
+          st_tag(o_out + (size_t)h * dh / 2, tag_h2(a0 * il, a1 * il, tag_a));
         }
+        continue;
       }
       if (act) {
         st_tag(&dst[h * stride + 2 + e0], tag_f(a0, tag_a));
@@ -1287,8 +1222,12 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       }
     }
     trace_at(P, trw, 5);
-    if (c == 0) {
-      // the merger: wait for every partial of group g (tags), then combine
+    if (c == 0 && S > 1) {
+      trace_at(P, trw, 11);
+      // The merger: wait for every partial of group g (tags), then combine.
+      // Lane c < S polls chunk c's (m, l); every lane polls its two head dims
+      // of 16 chunks at a time.  Each pass re-reads every word still stale at
+      // once, so a pass costs one memory round trip.
       const u64 *src = pg + (size_t)g * S * qpg * stride;
       for (int h = 0; h < qpg; ++h) {
         u64 wm = (u64)tag_a << 32, wl = (u64)tag_a << 32;
@@ -1308,9 +1247,32 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
             v[j][0] = use ? ld_dev(&src[at]) : ((u64)tag_a << 32);
             v[j][1] = use ? ld_dev(&src[at + 1]) : ((u64)tag_a << 32);
           }
+          for (;;) {
+            // (words not read carry the tag already, so they are never stale)
+            bool stale = c0 == 0 && (tag_of(wm) != tag_a || tag_of(wl) != tag_a);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) stale |= tag_of(v[j][0]) != tag_a || tag_of(v[j][1]) != tag_a;
+            if (wave_none(stale)) break;
+            const unsigned e = ld_dev(&P.err[0]);
+            if (c0 == 0) {
+              if (tag_of(wm) != tag_a) wm = ld_dev(mp);
+              if (tag_of(wl) != tag_a) wl = ld_dev(mp + 1);
+            }
+            // (addresses recomputed here, not held across the loop)
+            const u64 *pb = src + ((size_t)c0 * qpg + h) * stride + 2 + e0;
+            asm volatile("" : "+v"(pb));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const u64 *pj = pb + (size_t)j * qpg * stride;
+              if (tag_of(v[j][0]) != tag_a) v[j][0] = ld_dev(pj);
+              if (tag_of(v[j][1]) != tag_a) v[j][1] = ld_dev(pj + 1);
+            }
+            if (expired(P, t0, tag_a, e)) {
+              bad = true;
+              break;
+            }
+          }
           if (c0 == 0) {
-            if (tag_of(wm) != tag_a) wm = ld_tag_wait(P, mp, tag_a, t0, bad);
-            if (tag_of(wl) != tag_a) wl = ld_tag_wait(P, mp + 1, tag_a, t0, bad);
             const float mc = lane < S ? pay_f(wm) : -INFINITY;
             const float M = wave_max(mc);
             const float w = lane < S && mc != -INFINITY ? __expf(mc - M) : 0.0f;
@@ -1318,22 +1280,18 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
             if (lane < S) wgt[lane] = w;
             inv = 1.0f / Lsum;
             lds_drain();
+            if (h == 0) trace_at(P, trw, 12);
           }
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            if (c0 + j < S && act) {
-              const size_t at = ((size_t)(c0 + j) * qpg + h) * stride + 2 + e0;
-              if (tag_of(v[j][0]) != tag_a) v[j][0] = ld_tag_wait(P, &src[at], tag_a, t0, bad);
-              if (tag_of(v[j][1]) != tag_a) v[j][1] = ld_tag_wait(P, &src[at + 1], tag_a, t0, bad);
+            if (c0 + j < S) {
               o0 += wgt[c0 + j] * pay_f(v[j][0]);
               o1 += wgt[c0 + j] * pay_f(v[j][1]);
             }
           }
         }
-        if (act) {
-          const size_t ow = (size_t)gen * (P.Hq * dh / 2) + ((size_t)(g * qpg + h) * dh + e0) / 2;
-          st_tag(&P.o_t[ow], tag_h2(o0 * inv, o1 * inv, tag_a));
-        }
+        if (h == 0) trace_at(P, trw, 13);
+        if (act) st_tag(o_out + (size_t)h * dh / 2, tag_h2(o0 * inv, o1 * inv, tag_a));
         lds_drain();   // wgt is rewritten for the next head
       }
       if (bad && lane == 0) lds_st(&ctl->abort, 1u);
@@ -1557,7 +1515,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
   float *red = reinterpret_cast<float *>(smem + P.lds_red);   // 64 floats
   Ctl *ctl = reinterpret_cast<Ctl *>(smem + P.lds_ctl);
   float *xown = reinterpret_cast<float *>(smem + P.lds_xown); // residual rows of this workgroup
-  unsigned char *glds = smem + P.lds_gain;                    // norm gains of the phase being staged
   unsigned char *alds = smem + P.lds_h;                       // attention / sampler scratch
   const int b = blockIdx.x, G = P.G, wave = wave_id(), lane = lane_id();
   const int L = P.L, d = P.d, dh = P.dh;
@@ -1638,22 +1595,22 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         // after attention: this wave's loads complete in order, so attention's
         // K/V loads would otherwise queue behind it.
         const bool qkv_rounds = st_has_rounds(st, K_QKV, ctl);
-        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, glds, true)) return;
+        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, true)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
           if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
                          u == b && t == P.trace_token ? 5 * l + 1 : -1)) return;
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
-        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, glds)) return;
+        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
-        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part, glds)) return;
+        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part)) return;
         st.trace_k = t == P.trace_token ? 5 * l + 4 : -1;
-        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part, glds)) return;
+        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part)) return;
       }
       if (has_lm) {
         st.trace_k = t == P.trace_token ? 5 * L : -1;
-        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part, glds)) return;
+        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part)) return;
         if (b == 0 && P.sampling) {
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
           if (lds_ld(&ctl->abort)) return;
@@ -1674,16 +1631,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
   auto fail = [&]() __attribute__((always_inline)) {
     if (lane == 0) lds_st(&ctl->abort, 1u);
   };
-  // Giving up where the stream waves' next step is the first barrier of an
-  // RMSNorm stage: pass both of its barriers so that they see the abort and leave.
-  auto fail_release = [&](bool at_barrier) __attribute__((always_inline)) {
-    fail();
-    if (at_barrier) {
-      lds_drain();
-      wg_barrier();
-      wg_barrier();
-    }
-  };
   const int nq = P.Hq * dh, nk = P.Hkv * dh, half = dh / 2, dh_log2 = __builtin_ctz((unsigned)dh);
   const size_t nkw = (size_t)P.Hkv * half;   // words per generation of kc_t / vc_t
   int token = P.token0;
@@ -1699,8 +1646,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
       const int q0 = t * ngp + 4 * l;
       const int gen = (t * L + l) & 1;
-      const _Float16 *attn_norm = reinterpret_cast<const _Float16 *>(layer_part(Pl, l, LW_ATTN_NORM));
-      const _Float16 *ffn_norm = reinterpret_cast<const _Float16 *>(layer_part(Pl, l, LW_FFN_NORM));
 
       // ---------------- attention norm + QKV + rotary + KV append
       {
@@ -1708,9 +1653,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         if (l == 0 && t > 0) {
           if (kPrefill || Pl.hidden_io) {
             // the previous token is finished everywhere (its reads included)
-            if (!poll_level(sy, 0, G, lv0)) { fail_release(ge.nrows > 0); return; }
+            if (!poll_level(sy, 0, G, lv0)) { fail(); return; }
           } else {
-            if (!poll_level(sy, 0, 1, lv0)) { fail_release(ge.nrows > 0); return; }
+            if (!poll_level(sy, 0, 1, lv0)) { fail(); return; }
             token = ld_dev(Pl.tok_slot);
           }
         }
@@ -1727,14 +1672,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         unsigned long long tq = stamp(sy);
         sy.trace_k = t == Pl.trace_token ? 5 * l : -1;
         trace(Pl, t, 5 * l + 0, 6);
+        float inv = 0.0f;   // 1 / rms of the layer input: scales the row sums
         if (ge.nrows > 0) {
           if (l > 0) {
-            if (!stage_rmsnorm_tagged(sy, Pl.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, attn_norm, d, Pl.eps,
-                                      hl, glds, part)) { fail(); return; }
+            if (!stage_rmsnorm_tagged(sy, Pl.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, d, Pl.eps, hl, inv)) {
+              fail();
+              return;
+            }
           } else if (Pl.hidden_io) {
-            stage_rmsnorm_plain(ctl, Pl.x_hidden, nullptr, attn_norm, d, Pl.eps, hl, glds, part);
+            inv = stage_rmsnorm_plain(Pl.x_hidden, nullptr, d, Pl.eps, hl);
           } else {
-            stage_rmsnorm_plain(ctl, nullptr, emb + (size_t)token * d, attn_norm, d, Pl.eps, hl, glds, part);
+            inv = stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, d, Pl.eps, hl);
           }
         }
         tq = lap(sy, ST_STAGE, tq);
@@ -1749,7 +1697,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         _Float16 *kc = reinterpret_cast<_Float16 *>(Pl.kcache);
         _Float16 *vc = reinterpret_cast<_Float16 *>(Pl.vcache);
         for (int i = lane; i < ge.nrows / 2; i += 64) {
-          const float a = row_value(part, rs, 2 * i), bb = row_value(part, rs, 2 * i + 1);
+          const float a = row_value(part, rs, 2 * i) * inv, bb = row_value(part, rs, 2 * i + 1) * inv;
           const int r = ge.r0 + 2 * i;
           if (r < nq + nk) {
             // q / k rows come in rotary pairs (dims k, k + dh/2 of head hd)
@@ -1841,8 +1789,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         unsigned long long tk = stamp(sy);
         sy.trace_k = t == Pl.trace_token ? 5 * l + 3 : -1;
         trace(Pl, t, 5 * l + 3, 6);
+        float inv = 0.0f;
         if (ge.nrows > 0 &&
-            !stage_rmsnorm_tagged(sy, Pl.xmid_t + (size_t)gen * d, lvl + PH_O, ffn_norm, d, Pl.eps, hl, glds, part)) {
+            !stage_rmsnorm_tagged(sy, Pl.xmid_t + (size_t)gen * d, lvl + PH_O, d, Pl.eps, hl, inv)) {
           fail();
           return;
         }
@@ -1858,8 +1807,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         const unsigned tag = lvl + PH_GU;
         for (int i = lane; i < ge.nrows / 4; i += 64) {
           // rows 4i..4i+3 = gate j, up j, gate j+1, up j+1 with j = r0/2 + 2i
-          const float g0 = row_value(part, rs, 4 * i), u0 = row_value(part, rs, 4 * i + 1);
-          const float g1 = row_value(part, rs, 4 * i + 2), u1 = row_value(part, rs, 4 * i + 3);
+          const float g0 = row_value(part, rs, 4 * i) * inv, u0 = row_value(part, rs, 4 * i + 1) * inv;
+          const float g1 = row_value(part, rs, 4 * i + 2) * inv, u1 = row_value(part, rs, 4 * i + 3) * inv;
           const float s0 = __fdividef(g0, 1.0f + __expf(-g0)), s1 = __fdividef(g1, 1.0f + __expf(-g1));
           st_tag(ad + ge.r0 / 4 + i, tag_h2(s0 * u0, s1 * u1, tag));
         }
@@ -1909,9 +1858,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     const unsigned long long tlm = stamp(sy);
     {
       const Geo ge = uniform_geo(ctl, K_LM);
+      float inv = 0.0f;
       if (ge.nrows > 0 &&
-          !stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + L - 1) & 1) * d, lvl_lm - 1u,
-                                reinterpret_cast<const _Float16 *>(P.final_norm), d, P.eps, hl, glds, part)) {
+          !stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + L - 1) & 1) * d, lvl_lm - 1u, d, P.eps, hl, inv)) {
         fail();
         return;
       }
@@ -1923,7 +1872,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       float best = -INFINITY;
       int bi = 0x7fffffff;
       for (int i = lane; i < ge.nrows; i += 64) {
-        const float y = row_value(part, rs, i);
+        const float y = row_value(part, rs, i) * inv;
         st_dev(&P.logits[ge.r0 + i], y);
         if (y > best || (y == best && ge.r0 + i < bi)) { best = y; bi = ge.r0 + i; }
       }
@@ -1944,7 +1893,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tok = sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds));
       } else {
         if (!poll_level(sy, 0, G, lvl_lm)) {
-          fail_release(t + 1 < P.n_tokens && uniform_geo(ctl, K_QKV).nrows > 0);
+          fail();
           return;
         }
         float best = -INFINITY;
@@ -2002,6 +1951,20 @@ __global__ void __launch_bounds__(kThreads) lf_test_sample_kernel(const float *l
   if (threadIdx.x == 0) tokens[c] = tok;
 }
 
+// Weight packing: scale every column of an fp16 matrix (rows x 8*cols8,
+// 16-byte aligned) by the fp16 gain of that column (any 2-byte alignment),
+// eight elements per thread.
+__global__ void __launch_bounds__(256) lf_scale_columns_kernel(f16x8 *w, long long n8, int cols8,
+                                                               const _Float16 *g) {
+  for (long long v = (long long)blockIdx.x * 256 + threadIdx.x; v < n8; v += (long long)gridDim.x * 256) {
+    const _Float16 *gg = g + (v % cols8) * 8;
+    f16x8 x = w[v];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (_Float16)((float)x[k] * (float)gg[k]);
+    w[v] = x;
+  }
+}
+
 }  // namespace
 
 const void *monokernel_symbol(bool prefill) {
@@ -2016,6 +1979,18 @@ hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream) 
                            stream);
   return hipLaunchCooperativeKernel(monokernel_symbol(prefill), dim3(p.G), dim3(kThreads), args,
                                     (unsigned)p.lds_bytes, stream);
+}
+
+hipError_t launch_scale_columns(void *w, size_t rows, int cols, const void *g, hipStream_t stream) {
+  if (cols <= 0 || cols % 8 || reinterpret_cast<uintptr_t>(w) % 16 || reinterpret_cast<uintptr_t>(g) % 2)
+    return hipErrorInvalidValue;
+  const long long n8 = (long long)rows * (cols / 8);
+  if (n8 == 0) return hipSuccess;
+  long long blocks = (n8 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(lf_scale_columns_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<f16x8 *>(w), n8, cols / 8, reinterpret_cast<const _Float16 *>(g));
+  return hipGetLastError();
 }
 
 hipError_t launch_test_expdef(const float *x, float *y, int64_t n, hipStream_t stream) {

@@ -237,6 +237,23 @@ def test_timeout_path_exits_cleanly(lf, tiny, monkeypatch):
     assert ok.decode_step(1, 0) >= 0
 
 
+def test_non_unit_norm_gains(lf, orc):
+    """Gains other than 1: the library folds each RMSNorm gain vector into the
+    columns of the projection after it (QKV, gate/up, lm_head) and scales the row
+    sums by 1/rms; the oracle applies RMSNorm as defined."""
+    cfg = synth.CONFIGS["tiny_2l_d256"]
+    w = synth.model_weights(cfg, seed=5)
+    d = cfg["d_model"]
+
+    def gains(tid):
+        return (1.0 + 0.25 * synth.normal_f32(d, 77, tid)).astype(np.float16)
+
+    for l, lw in enumerate(w["layers"]):
+        lw["attn_norm"], lw["ffn_norm"] = gains(2 * l), gains(2 * l + 1)
+    w["final_norm"] = gains(99)
+    teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 12))
+
+
 # ---------------------------------------------------------------- full-size shapes
 
 def test_single_layer_2b_shape_hidden_io(lf, orc):
