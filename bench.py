@@ -204,9 +204,7 @@ def main() -> int:
                                         "epilogue": frac(6), "attention": frac(7), "lm_sample": frac(8)},
                  "stream_wave1_fraction": {"wait_input": frac(9), "consume": frac(10)},
                  "stream_wave1_ns_per_piece": round(float((s[:, 10] * 10.0 / np.maximum(s[:, 11], 1)).mean()), 1),
-                 "xcd_ids": sorted(set(int(x) for x in s[:, 2])),
-                 "tagged_read_round_us": round(float(s[:, 12].sum() / max(s[:, 13].sum(), 1)) * 0.01, 3),
-                 "tagged_read_rounds_per_fetch": round(float(s[:, 13].sum() / max(s[:, 14].sum(), 1)), 3)}
+                 "xcd_ids": sorted(set(int(x) for x in s[:, 2]))}
         log(f"stats: {stats}")
 
     nbytes = roofline.bytes_for_steps(cfg, pos0, K)

@@ -397,7 +397,6 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
   P.lds_bytes = (int)lds_end;
   P.plain_launch = (std::getenv("LF_PLAIN_LAUNCH") && std::atoi(std::getenv("LF_PLAIN_LAUNCH")) != 0) ? 1 : 0;
-  P.poll_first = (std::getenv("LF_POLL_FIRST") && std::atoi(std::getenv("LF_POLL_FIRST")) != 0) ? 1 : 0;
   for (int pf = 0; pf < 2; ++pf) {
     if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  P.lds_bytes)) != hipSuccess)

@@ -88,7 +88,6 @@ struct Params {
   unsigned level_base;
   unsigned long long timeout_ticks;
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
-  int poll_first;          // 1: poll the producers' progress words before reading tagged data
   // LDS layout (byte offsets into dynamic shared memory)
   int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_trace, lds_bytes;
   int part_rows, hmax;

@@ -241,11 +241,11 @@ struct Slice {
 };
 
 struct Ctl {
-  unsigned h_ready;         // last GEMV phase (1-based) whose input vector is staged
   unsigned abort;           // the sync wave gave up (the error word is set)
   unsigned done[kWaves];    // per stream wave: last GEMV phase (1-based) it finished
   int status;               // outcome of a barrier-based wait
-  int pad[5];
+  int pad[6];
+  float ssw[kWaves];        // per wave: sum of squares of its share of an RMSNorm input
   Geo geo[K_COUNT];
   // The partition of every phase kind among the stream waves, fixed for the
   // launch: computed once so that no phase divides by the pieces per row.
@@ -262,7 +262,6 @@ struct Sync {
   unsigned long long spin;    // ticks spent polling other workgroups
   unsigned long long waits;
   unsigned long long tm[kStatPhases];   // sync-wave time by activity (LF_STATS)
-  unsigned long long rt_sum, rt_n, nfetch;   // tagged-read rounds: total ticks, count; fetches
   int trace_k;                               // LF_TRACE: phase slot being staged, else -1
   bool timed;                                // LF_STATS: activity timers on
 };
@@ -349,15 +348,8 @@ __device__ __forceinline__ void publish_sync(KP &P, unsigned level) {
   if (lane_id() == 0) st_dev(&P.progress[blockIdx.x], level);
 }
 
-// Wave 0: announce a level whose data other workgroups read whole (a staged
-// vector).  With poll-first staging the consumers poll progress words before
-// reading the data once, so the announcement waits for this wave's stores.
-__device__ __forceinline__ void publish_vec(KP &P, unsigned level) {
-  if (P.poll_first)
-    publish_sync(P, level);
-  else
-    publish_fast(P, level);
-}
+// Wave 0: announce a level whose data other workgroups read as tagged words.
+__device__ __forceinline__ void publish_vec(KP &P, unsigned level) { publish_fast(P, level); }
 
 // All waves: barrier-based wait (wave 0 polls).  Used where the whole workgroup
 // works together (attention, nucleus sampling).  With `acquire`, wave 0 takes an
@@ -382,52 +374,60 @@ __device__ __forceinline__ bool wait_all_waves(Sync &s, int first, int count, un
 // ---------------------------------------------------------------- staging (wave 0)
 
 constexpr int kStageBatch = kStageRound / 64;   // words per lane in one staging round
-constexpr int kFetchWindow = 32;                 // 8-byte loads in flight per lane while staging
-constexpr int kStageBatchWide = kStageRoundWide / 64;   // words per lane in a round of the SwiGLU vector
 
-// Wave 0: wait until every word src[0..n) carries `tag`, then hand each payload
-// to use(i, word, real).  The words are read in rounds of 64 * kRound; at most
-// kFetchWindow loads per lane are in flight, each later load issued into the
-// registers of a word just handed over, so a round costs one memory round trip.
-// src (and use's destination) must be readable (writable) up to n rounded up to
-// whole rounds; the words past n are handed over with real = false.  Words are
-// handed over as they land, before the round's tags are all known; the round
-// then ends with end(ok), and a round with a stale word (ok = false) is read and
-// handed over afresh.
-template <int kRound = kStageBatch, class F, class E>
-__device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, unsigned tag, F &&use, E &&end) {
-  constexpr int kWin = kRound < kFetchWindow ? kRound : kFetchWindow;
-  KP &P = *s.P;
+// ---- cooperative staging (all waves)
+
+// Workgroup barrier that waits for no memory operation: the stream waves keep
+// their ring loads in flight across it.  A wave that has ended no longer
+// counts, so a wave that gives up releases the others.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// How a GEMV phase's input vector reaches LDS: a tagged residual to normalise
+// (RMS: fp32 words -> fp16 h, sum of squares), tagged fp16 pairs (PAIRS: 32-bit
+// words -> h), or, for the first layer's input, plain memory read by the sync
+// wave alone (PLAIN).  n words at src, each carrying `tag` once valid.
+enum StageMode { SM_RMS = 0, SM_PAIRS = 1, SM_PLAIN = 2 };
+struct StageSpec {
+  const u64 *src;
+  int n, mode;
+  unsigned tag;
+};
+
+// One wave's share of a tagged vector src[0..n): the 64-word slots
+// [w ns / 8, (w + 1) ns / 8) of the vector's ns slots, read up to kCoopChunk
+// slots at once and re-read until every word carries `tag`; then use(i, word,
+// real) for every word of the share (real: i < n).  Only the pass that finds
+// the words valid hands them over, so a retry costs one bare round trip, and
+// the eight waves' passes run side by side.  The buffer must be readable up to
+// n rounded up to whole slots.  Each pass reads the error word with the data.
+constexpr int kCoopChunk = 8;
+template <class F>
+__device__ __forceinline__ bool coop_fetch(KP &P, const u64 *src, int n, unsigned tag, int wave, F &&use) {
   const int lane = lane_id();
-  if (P.poll_first && !poll_level(s, 0, P.G, tag)) return false;
   const unsigned long long t0 = now_ticks();
-  s.nfetch += 1;
-  for (int base = 0; base < n; base += 64 * kRound) {
+  const int ns = (n + 63) >> 6;
+  const int s0 = wave * ns / kWaves, s1 = (wave + 1) * ns / kWaves;
+  for (int c0 = s0; c0 < s1; c0 += kCoopChunk) {
+    const int m = min(kCoopChunk, s1 - c0);
+    const u64 *rp = src + 64 * c0 + lane;
     for (;;) {
-      const unsigned long long tr = stamp(s);
-      const u64 *rp = src + base + lane;   // buffers padded to whole rounds
-      u64 v[kWin];
+      u64 v[kCoopChunk];
 #pragma unroll
-      for (int j = 0; j < kWin; ++j) v[j] = ld_dev(rp + 64 * j);
-      const unsigned e = ld_dev(&P.err[0]);   // for a retry's give-up check
-      unsigned bad = 0u;
+      for (int k = 0; k < kCoopChunk; ++k) v[k] = k < m ? ld_dev(rp + 64 * k) : ((u64)tag << 32);
+      const unsigned e = ld_dev(&P.err[0]);
+      bool bad = false;
 #pragma unroll
-      for (int j = 0; j < kRound; ++j) {
-        const int i = base + 64 * j + lane;
-        const u64 w = v[j % kWin];
-        bad |= (unsigned)(i < n && tag_of(w) != tag);
-        use(i, w, i < n);
-        if (j + kWin < kRound) v[j % kWin] = ld_dev(rp + 64 * (j + kWin));
-      }
-      const unsigned ok = wave_none(bad != 0u) ? 1u : 0u;
-      if (s.timed) {
-        s.rt_sum += now_ticks() - tr;
-        s.rt_n += 1;
-      }
-      end(ok == 1u);
-      if (ok == 1u) {
-        if (kTrace && s.trace_k >= 0 && base + 64 * kRound >= n && lane == 0)
-          trace_row(P, s.trace_k)[7] = now_ticks();
+      for (int k = 0; k < kCoopChunk; ++k) bad |= 64 * (c0 + k) + lane < n && tag_of(v[k]) != tag;
+      if (wave_none(bad)) {
+#pragma unroll
+        for (int k = 0; k < kCoopChunk; ++k) {
+          const int i = 64 * (c0 + k) + lane;
+          if (k < m) use(i, v[k], i < n);
+        }
         break;
       }
       if (expired(P, t0, tag, e)) return false;
@@ -436,33 +436,77 @@ __device__ __forceinline__ bool fetch_tagged(Sync &s, const u64 *src, int n, uns
   return true;
 }
 
-// RMSNorm of a residual published by other workgroups as tagged fp32 words.
-// The gain vector is folded into the next projection's columns when the
-// weights are packed, and the factor 1 / rms is taken out too: that
-// projection is linear in its input, so h = fp16(x) is written as the words
-// land and the caller scales the row sums by the returned inv.  Nothing runs
-// between the last word's arrival and the stream waves' start but the sum.
-__device__ __forceinline__ bool stage_rmsnorm_tagged(Sync &s, const u64 *src, unsigned tag, int d, float eps,
-                                                     _Float16 *h, float &inv) {
-  float ss = 0.0f, ss_round = 0.0f;   // ss_round: the round being read
-  if (!fetch_tagged(
-          s, src, d, tag,
-          [&](int i, u64 w, bool real) __attribute__((always_inline)) {
-            const float x = pay_f(w);
-            ss_round += real ? x * x : 0.0f;
-            h[i] = (_Float16)x;
-          },
-          [&](bool ok) __attribute__((always_inline)) {
-            ss += ok ? ss_round : 0.0f;
-            ss_round = 0.0f;
-          })) {
-    if (lane_id() == 0) lds_st(&s.ctl->abort, 1u);
-    return false;
+// All waves (of a workgroup with rows in the phase): stage the phase's input
+// vector into LDS h.  Tagged inputs are split over the eight waves; a plain
+// input is read by the sync wave alone.  For RMSNorm inputs each wave leaves
+// the sum of squares of its share in ctl->ssw.  On a timeout the wave sets the
+// abort flag.  The caller then meets the other waves at wg_barrier().
+__device__ __forceinline__ void coop_stage(KP &P, Ctl *ctl, const StageSpec &sp, int wave, _Float16 *h) {
+  const int lane = lane_id();
+  bool ok = true;
+  if (sp.mode == SM_RMS) {
+    float ss = 0.0f;
+    ok = coop_fetch(P, sp.src, sp.n, sp.tag, wave, [&](int i, u64 w, bool real) __attribute__((always_inline)) {
+      const float x = pay_f(w);
+      ss += real ? x * x : 0.0f;
+      h[i] = (_Float16)x;
+    });
+    ss = wave_sum(ss);
+    if (lane == 0) ctl->ssw[wave] = ss;
+  } else if (sp.mode == SM_PAIRS) {
+    unsigned *dst = reinterpret_cast<unsigned *>(h);
+    ok = coop_fetch(P, sp.src, sp.n, sp.tag, wave,
+                    [&](int i, u64 w, bool) __attribute__((always_inline)) { dst[i] = (unsigned)w; });
   }
-  // one reciprocal (within an ulp of dividing every row sum)
-  inv = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
-  if (kTrace && s.trace_k >= 0) trace_at(*s.P, s.trace_k, 8);
-  return true;
+  if (!ok && lane == 0) lds_st(&ctl->abort, 1u);
+  lds_drain();
+}
+
+// Sync wave, after the barrier of an RMSNorm stage: 1 / rms from the waves'
+// sums of squares (added in wave order).
+__device__ __forceinline__ float coop_inv_rms(const Ctl *ctl, int d, float eps) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) ss += ctl->ssw[w];
+  return 1.0f / sqrtf(ss / (float)d + eps);
+}
+
+// The input of GEMV phase `kind` of layer l of token t (gen: the layer's buffer
+// generation, lvl: the layer's base level; for K_LM, lvl is the level of the
+// last layer's down projection).
+__device__ __forceinline__ StageSpec stage_spec(const KP &P, int kind, int t, int l, int gen, unsigned lvl) {
+  StageSpec sp;
+  const int L = P.L, d = P.d;
+  sp.src = nullptr;
+  sp.n = d;
+  sp.mode = SM_RMS;
+  sp.tag = lvl;
+  switch (kind) {
+    case K_QKV:
+      if (l > 0) sp.src = P.xout_t + (size_t)((t * L + l - 1) & 1) * d;
+      else sp.mode = SM_PLAIN;
+      break;
+    case K_O:
+      sp.src = P.o_t + (size_t)gen * (P.Hq * P.dh / 2);
+      sp.n = P.Hq * P.dh / 2;
+      sp.mode = SM_PAIRS;
+      sp.tag = lvl + PH_ATTN;
+      break;
+    case K_GU:
+      sp.src = P.xmid_t + (size_t)gen * d;
+      sp.tag = lvl + PH_O;
+      break;
+    case K_D:
+      sp.src = P.a_t + (size_t)gen * (P.F / 2);
+      sp.n = P.F / 2;
+      sp.mode = SM_PAIRS;
+      sp.tag = lvl + PH_GU;
+      break;
+    default:   // K_LM
+      sp.src = P.xout_t + (size_t)((t * L + L - 1) & 1) * d;
+      break;
+  }
+  return sp;
 }
 
 // The same for a layer-0 input: an fp16 embedding row or the host's fp32
@@ -488,16 +532,6 @@ __device__ __forceinline__ float stage_rmsnorm_plain(const float *x_host, const 
     }
   }
   return 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
-}
-
-// A vector published as tagged fp16 pairs (n_pairs words) into LDS h.
-template <int kBatch = kStageBatch>
-__device__ __forceinline__ bool stage_pairs_tagged(Sync &s, const u64 *src, int n_pairs, unsigned tag,
-                                                   _Float16 *h) {
-  unsigned *dst = reinterpret_cast<unsigned *>(h);
-  return fetch_tagged<kBatch>(
-      s, src, n_pairs, tag, [&](int i, u64 w, bool) __attribute__((always_inline)) { dst[i] = (unsigned)w; },
-      [](bool) __attribute__((always_inline)) {});
 }
 
 // ---------------------------------------------------------------- stream waves
@@ -863,15 +897,17 @@ __device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, cons
 // row sum per (row, wave) in part[row * 8 + cw].  Returns false if the sync wave
 // aborted.
 __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl *ctl, _Float16 *h, float *part,
-                                             bool defer_last_refill = false) {
+                                             const StageSpec &sp, bool defer_last_refill = false) {
   const Geo ge = uniform_geo(ctl, kind);
   const Slice sl = uniform_slice(ctl, kind, st.cw);
   // the dependency wait happens on wave 0; here only its LDS announcement
   const bool timed = st.timed;
   unsigned long long t0 = timed ? now_ticks() : 0ull;
-  while (lds_ld(&ctl->h_ready) < (unsigned)(q + 1)) {
+  if (ge.nrows > 0) {
+    // this wave's share of the input vector, then the workgroup barrier
+    coop_stage(*st.P, ctl, sp, st.cw + 1, h);
+    wg_barrier();
     if (lds_ld(&ctl->abort)) return false;
-    __builtin_amdgcn_s_sleep(1);
   }
   if (timed) {
     const unsigned long long t1 = now_ticks();
@@ -959,11 +995,6 @@ __device__ __forceinline__ void wait_streams(const Ctl *ctl, int q) {
   asm volatile("" ::: "memory");
 }
 
-// Wave 0: the input vector of GEMV phase q is in LDS.
-__device__ __forceinline__ void announce_input(Ctl *ctl, int q) {
-  lds_drain();
-  if (lane_id() == 0) lds_st(&ctl->h_ready, (unsigned)(q + 1));
-}
 
 // ---------------------------------------------------------------- attention
 
@@ -1544,14 +1575,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     }
     if (kTrace)
       for (int i = 0; i < kTraceSlots * (5 * L + 2); ++i) trace_row(P, 0)[i] = 0ull;
-    ctl->h_ready = 0;
     ctl->abort = 0;
     for (int w = 0; w < kWaves; ++w) ctl->done[w] = 0;
     ctl->status = 0;
   }
   __syncthreads();
 
-  Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}, 0ull, 0ull, 0ull, -1, (P.flags & 4u) != 0};
+  Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}, -1, (P.flags & 4u) != 0};
   const unsigned long long kt0 = now_ticks();
 
   if (wave > 0) {
@@ -1595,22 +1625,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         // after attention: this wave's loads complete in order, so attention's
         // K/V loads would otherwise queue behind it.
         const bool qkv_rounds = st_has_rounds(st, K_QKV, ctl);
-        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, true)) return;
+        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, stage_spec(P, K_QKV, t, l, gen, lvl), true)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
           if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
                          u == b && t == P.trace_token ? 5 * l + 1 : -1)) return;
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
-        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, stage_spec(P, K_O, t, l, gen, lvl))) return;
         st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
-        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part, stage_spec(P, K_GU, t, l, gen, lvl))) return;
         st.trace_k = t == P.trace_token ? 5 * l + 4 : -1;
-        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part)) return;
+        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part, stage_spec(P, K_D, t, l, gen, lvl))) return;
       }
       if (has_lm) {
         st.trace_k = t == P.trace_token ? 5 * L : -1;
-        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part)) return;
+        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part,
+                          stage_spec(P, K_LM, t, L, 0, lv0 + (unsigned)(L * PH_PER_LAYER))))
+          return;
         if (b == 0 && P.sampling) {
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
           if (lds_ld(&ctl->abort)) return;
@@ -1675,19 +1707,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         float inv = 0.0f;   // 1 / rms of the layer input: scales the row sums
         if (ge.nrows > 0) {
           if (l > 0) {
-            if (!stage_rmsnorm_tagged(sy, Pl.xout_t + (size_t)((t * L + l - 1) & 1) * d, lvl, d, Pl.eps, hl, inv)) {
-              fail();
-              return;
-            }
-          } else if (Pl.hidden_io) {
-            inv = stage_rmsnorm_plain(Pl.x_hidden, nullptr, d, Pl.eps, hl);
+            coop_stage(Pl, ctl, stage_spec(Pl, K_QKV, t, l, gen, lvl), 0, hl);
           } else {
-            inv = stage_rmsnorm_plain(nullptr, emb + (size_t)token * d, d, Pl.eps, hl);
+            inv = stage_rmsnorm_plain(Pl.hidden_io ? Pl.x_hidden : nullptr,
+                                      Pl.hidden_io ? nullptr : emb + (size_t)token * d, d, Pl.eps, hl);
+            lds_drain();
           }
+          trace(Pl, t, 5 * l + 0, 7);
+          wg_barrier();
+          if (lds_ld(&ctl->abort)) return;
+          if (l > 0) inv = coop_inv_rms(ctl, d, Pl.eps);
         }
         tq = lap(sy, ST_STAGE, tq);
         trace(Pl, t, 5 * l + 0, 0);
-        announce_input(ctl, q0);
         const RowSpans rs = row_spans(ctl, K_QKV);   // (constant: read before the wait)
         wait_streams(ctl, q0);
         tq = lap(sy, ST_STREAMS, tq);
@@ -1746,11 +1778,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         unsigned long long tk = stamp(sy);
         sy.trace_k = t == Pl.trace_token ? 5 * l + 2 : -1;
         trace(Pl, t, 5 * l + 2, 6);
-        if (ge.nrows > 0 &&
-            !stage_pairs_tagged(sy, Pl.o_t + (size_t)gen * (nq / 2), nq / 2, lvl + PH_ATTN, hl)) { fail(); return; }
+        if (ge.nrows > 0) {
+          coop_stage(Pl, ctl, stage_spec(Pl, K_O, t, l, gen, lvl), 0, hl);
+          trace(Pl, t, 5 * l + 2, 7);
+          wg_barrier();
+          if (lds_ld(&ctl->abort)) return;
+        }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 2, 0);
-        announce_input(ctl, q0 + 1);
         // Before the wait (none of it depends on the stream waves): the row
         // spans, the output words, and the residual of this lane's first row.
         const RowSpans rs = row_spans(ctl, K_O);
@@ -1790,14 +1825,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         sy.trace_k = t == Pl.trace_token ? 5 * l + 3 : -1;
         trace(Pl, t, 5 * l + 3, 6);
         float inv = 0.0f;
-        if (ge.nrows > 0 &&
-            !stage_rmsnorm_tagged(sy, Pl.xmid_t + (size_t)gen * d, lvl + PH_O, d, Pl.eps, hl, inv)) {
-          fail();
-          return;
+        if (ge.nrows > 0) {
+          coop_stage(Pl, ctl, stage_spec(Pl, K_GU, t, l, gen, lvl), 0, hl);
+          trace(Pl, t, 5 * l + 3, 7);
+          wg_barrier();
+          if (lds_ld(&ctl->abort)) return;
+          inv = coop_inv_rms(ctl, d, Pl.eps);
         }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 3, 0);
-        announce_input(ctl, q0 + 2);
         const RowSpans rs = row_spans(ctl, K_GU);   // (constant: read before the wait)
         u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
         asm volatile("" : "+s"(ad));   // computed now, not after the wait
@@ -1823,11 +1859,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         unsigned long long tk = stamp(sy);
         sy.trace_k = t == Pl.trace_token ? 5 * l + 4 : -1;
         trace(Pl, t, 5 * l + 4, 6);
-        if (ge.nrows > 0 &&
-            !stage_pairs_tagged<kStageBatchWide>(sy, Pl.a_t + (size_t)gen * (Pl.F / 2), Pl.F / 2, lvl + PH_GU, hl)) { fail(); return; }
+        if (ge.nrows > 0) {
+          coop_stage(Pl, ctl, stage_spec(Pl, K_D, t, l, gen, lvl), 0, hl);
+          trace(Pl, t, 5 * l + 4, 7);
+          wg_barrier();
+          if (lds_ld(&ctl->abort)) return;
+        }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 4, 0);
-        announce_input(ctl, q0 + 3);
         // before the wait: row spans, output words, this lane's first residual
         const RowSpans rs = row_spans(ctl, K_D);
         u64 *xo = Pl.xout_t + (size_t)gen * d;
@@ -1859,13 +1898,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     {
       const Geo ge = uniform_geo(ctl, K_LM);
       float inv = 0.0f;
-      if (ge.nrows > 0 &&
-          !stage_rmsnorm_tagged(sy, P.xout_t + (size_t)((t * L + L - 1) & 1) * d, lvl_lm - 1u, d, P.eps, hl, inv)) {
-        fail();
-        return;
+      if (ge.nrows > 0) {
+        coop_stage(P, ctl, stage_spec(P, K_LM, t, L, 0, lvl_lm - 1u), 0, hl);
+        trace(P, t, 5 * L, 7);
+        wg_barrier();
+        if (lds_ld(&ctl->abort)) return;
+        inv = coop_inv_rms(ctl, d, P.eps);
       }
       trace(P, t, 5 * L, 0);
-      announce_input(ctl, qlm);
       const RowSpans rs = row_spans(ctl, K_LM);   // (constant: read before the wait)
       wait_streams(ctl, qlm);
       trace(P, t, 5 * L, 1);
@@ -1931,9 +1971,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     o[2] = xcc & 0xfu;
     o[3] = now_ticks() - kt0;
     for (int k = 0; k < kStatPhases; ++k) o[4 + k] = sy.tm[k];
-    o[12] = sy.rt_sum;
-    o[13] = sy.rt_n;
-    o[14] = sy.nfetch;
   }
 }
 
