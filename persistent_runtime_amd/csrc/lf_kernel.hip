@@ -281,8 +281,8 @@ __device__ __forceinline__ unsigned long long stamp(const Sync &s) { return s.ti
 // started, 7 tagged input complete, 8 sum of squares; attention, wave 1: 6
 // unit start, 7 first barrier passed, 3 queries staged, 8 first keys loaded,
 // 10 first scores, 4 keys done, 9 waves' states in LDS, 5 partial stored, and
-// in a merging unit 11 merge start, 12 chunk weights known, 13 first head
-// merged)
+// in a merging unit 11 merge start, 12 the waves' folded states in LDS, 13
+// heads merged and stored)
 // of phase k (5l + {QKV, attention, O, gate/up, down}; 5L lm_head; 5L+1 token).
 // Timestamps collect in LDS and are copied out when the kernel ends, so that
 // tracing adds no global stores (and no store waits) to the path it measures.
@@ -1209,32 +1209,37 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   u64 *pg = P.part_t + (size_t)gen * P.part_gen;
   u64 *o_out = P.o_t + (size_t)gen * (P.Hq * dh / 2) + ((size_t)g * qpg * dh + e0) / 2;
   asm volatile("" : "+s"(pg), "+v"(o_out));
+  // Wave 1: combine the stream waves' states of head h (m, l, o for this lane's
+  // two dims) left in wml / wo.  Every read is in bounds for every lane (e0 = 0
+  // on lanes past the head dims), so the seven states load together.
+  auto combine = [&](int h, float &M, float &Ls, float &a0, float &a1) __attribute__((always_inline)) {
+    float mw[kKW], lw[kKW];
+    float2 ow[kKW];
+#pragma unroll
+    for (int w = 0; w < kKW; ++w) {
+      mw[w] = wml[((w + 1) * kMaxQpg + h) * 2];
+      lw[w] = wml[((w + 1) * kMaxQpg + h) * 2 + 1];
+      ow[w] = *reinterpret_cast<const float2 *>(&wo[((w + 1) * qpg + h) * dh + e0]);
+    }
+    M = mw[0];
+#pragma unroll
+    for (int w = 1; w < kKW; ++w) M = fmaxf(M, mw[w]);
+    Ls = a0 = a1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kKW; ++w) {
+      const float sw = mw[w] == -INFINITY ? 0.0f : __expf(mw[w] - M);
+      Ls += sw * lw[w];
+      a0 += sw * ow[w].x;
+      a1 += sw * ow[w].y;
+    }
+  };
   __syncthreads();
   if (wave == 1) {
     trace_at(P, trw, 9);
     u64 *dst = pg + (size_t)u * qpg * stride;
     for (int h = 0; h < qpg; ++h) {
-      // every read is in bounds for every lane (e0 = 0 on lanes past the head
-      // dims), so the seven states load together
-      float mw[kKW], lw[kKW];
-      float2 ow[kKW];
-#pragma unroll
-      for (int w = 0; w < kKW; ++w) {
-        mw[w] = wml[((w + 1) * kMaxQpg + h) * 2];
-        lw[w] = wml[((w + 1) * kMaxQpg + h) * 2 + 1];
-        ow[w] = *reinterpret_cast<const float2 *>(&wo[((w + 1) * qpg + h) * dh + e0]);
-      }
-      float M = mw[0];
-#pragma unroll
-      for (int w = 1; w < kKW; ++w) M = fmaxf(M, mw[w]);
-      float Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kKW; ++w) {
-        const float sw = mw[w] == -INFINITY ? 0.0f : __expf(mw[w] - M);
-        Ls += sw * lw[w];
-        a0 += sw * ow[w].x;
-        a1 += sw * ow[w].y;
-      }
+      float M, Ls, a0, a1;
+      combine(h, M, Ls, a0, a1);
       if (S == 1) {
         // the unit holds every key of the head: its state is the head's output
         if (act) {
@@ -1253,79 +1258,91 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       }
     }
     trace_at(P, trw, 5);
-    if (c == 0 && S > 1) {
-      trace_at(P, trw, 11);
-      // The merger: wait for every partial of group g (tags), then combine.
-      // Lane c < S polls chunk c's (m, l); every lane polls its two head dims
-      // of 16 chunks at a time.  Each pass re-reads every word still stale at
-      // once, so a pass costs one memory round trip.
+  }
+  if (c == 0 && S > 1) {
+    // The merging unit (c = 0 of each KV head), all waves.  Stream wave w polls
+    // chunks w - 1, w + 6, ... of the group (their (m, l) and this lane's two o
+    // dims, up to four chunks' words in flight at once, each pass re-reading
+    // every stale word: one round trip per pass), folds them into one online
+    // softmax state per head and leaves it in wml / wo; wave 1 then combines
+    // the seven states into the head's output.
+    __syncthreads();   // wave 1 has read the unit's own states: wml / wo are free
+    if (wave == 1) trace_at(P, trw, 11);
+    if (wave > 0) {
       const u64 *src = pg + (size_t)g * S * qpg * stride;
+      const u64 tagw = (u64)tag_a << 32;
       for (int h = 0; h < qpg; ++h) {
-        u64 wm = (u64)tag_a << 32, wl = (u64)tag_a << 32;
-        const u64 *mp = &src[((size_t)lane * qpg + h) * stride];
-        if (lane < S) {
-          wm = ld_dev(mp);
-          wl = ld_dev(mp + 1);
-        }
-        float o0 = 0.0f, o1 = 0.0f, inv = 0.0f;
-        float *wgt = red;   // merge weights e^(m_c - M), one per chunk (S <= kMaxSplit = 64)
-        for (int c0 = 0; c0 < S; c0 += 16) {
-          u64 v[16][2];
+        float M = -INFINITY, Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
+        for (int cb = kwv; cb < S; cb += 4 * kKW) {
+          u64 w[4][4];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const size_t at = ((size_t)(c0 + j) * qpg + h) * stride + 2 + e0;
-            const bool use = c0 + j < S && act;
-            v[j][0] = use ? ld_dev(&src[at]) : ((u64)tag_a << 32);
-            v[j][1] = use ? ld_dev(&src[at + 1]) : ((u64)tag_a << 32);
+          for (int i = 0; i < 4; ++i) {
+            const bool use = cb + kKW * i < S;
+            const u64 *q = src + ((size_t)(cb + kKW * i) * qpg + h) * stride;
+            w[i][0] = use ? ld_dev(q) : tagw;
+            w[i][1] = use ? ld_dev(q + 1) : tagw;
+            w[i][2] = use ? ld_dev(q + 2 + e0) : tagw;
+            w[i][3] = use ? ld_dev(q + 3 + e0) : tagw;
           }
           for (;;) {
             // (words not read carry the tag already, so they are never stale)
-            bool stale = c0 == 0 && (tag_of(wm) != tag_a || tag_of(wl) != tag_a);
+            bool stale = false;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) stale |= tag_of(v[j][0]) != tag_a || tag_of(v[j][1]) != tag_a;
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) stale |= tag_of(w[i][k]) != tag_a;
             if (wave_none(stale)) break;
             const unsigned e = ld_dev(&P.err[0]);
-            if (c0 == 0) {
-              if (tag_of(wm) != tag_a) wm = ld_dev(mp);
-              if (tag_of(wl) != tag_a) wl = ld_dev(mp + 1);
-            }
             // (addresses recomputed here, not held across the loop)
-            const u64 *pb = src + ((size_t)c0 * qpg + h) * stride + 2 + e0;
+            const u64 *pb = src + ((size_t)cb * qpg + h) * stride;
             asm volatile("" : "+v"(pb));
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const u64 *pj = pb + (size_t)j * qpg * stride;
-              if (tag_of(v[j][0]) != tag_a) v[j][0] = ld_dev(pj);
-              if (tag_of(v[j][1]) != tag_a) v[j][1] = ld_dev(pj + 1);
+            for (int i = 0; i < 4; ++i) {
+              const u64 *q = pb + (size_t)kKW * i * qpg * stride;
+              if (tag_of(w[i][0]) != tag_a) w[i][0] = ld_dev(q);
+              if (tag_of(w[i][1]) != tag_a) w[i][1] = ld_dev(q + 1);
+              if (tag_of(w[i][2]) != tag_a) w[i][2] = ld_dev(q + 2 + e0);
+              if (tag_of(w[i][3]) != tag_a) w[i][3] = ld_dev(q + 3 + e0);
             }
             if (expired(P, t0, tag_a, e)) {
               bad = true;
               break;
             }
           }
-          if (c0 == 0) {
-            const float mc = lane < S ? pay_f(wm) : -INFINITY;
-            const float M = wave_max(mc);
-            const float w = lane < S && mc != -INFINITY ? __expf(mc - M) : 0.0f;
-            const float Lsum = wave_sum(w * (lane < S ? pay_f(wl) : 0.0f));
-            if (lane < S) wgt[lane] = w;
-            inv = 1.0f / Lsum;
-            lds_drain();
-            if (h == 0) trace_at(P, trw, 12);
-          }
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            if (c0 + j < S) {
-              o0 += wgt[c0 + j] * pay_f(v[j][0]);
-              o1 += wgt[c0 + j] * pay_f(v[j][1]);
+          for (int i = 0; i < 4; ++i) {
+            if (cb + kKW * i < S) {
+              const float mc = pay_f(w[i][0]);
+              const float Mn = fmaxf(M, mc);
+              const float sa = M == -INFINITY ? 0.0f : __expf(M - Mn);
+              const float sb = mc == -INFINITY ? 0.0f : __expf(mc - Mn);
+              Ls = Ls * sa + pay_f(w[i][1]) * sb;
+              a0 = a0 * sa + pay_f(w[i][2]) * sb;
+              a1 = a1 * sa + pay_f(w[i][3]) * sb;
+              M = Mn;
             }
           }
         }
-        if (h == 0) trace_at(P, trw, 13);
-        if (act) st_tag(o_out + (size_t)h * dh / 2, tag_h2(o0 * inv, o1 * inv, tag_a));
-        lds_drain();   // wgt is rewritten for the next head
+        if (lane == 0) {
+          wml[(wave * kMaxQpg + h) * 2 + 0] = M;
+          wml[(wave * kMaxQpg + h) * 2 + 1] = Ls;
+        }
+        if (act) *reinterpret_cast<float2 *>(&wo[(wave * qpg + h) * dh + e0]) = make_float2(a0, a1);
       }
       if (bad && lane == 0) lds_st(&ctl->abort, 1u);
+    }
+    __syncthreads();
+    if (wave == 1) {
+      if (trw >= 0) trace_at(P, trw, 12);
+      for (int h = 0; h < qpg; ++h) {
+        float M, Ls, a0, a1;
+        combine(h, M, Ls, a0, a1);
+        if (act) {
+          const float il = 1.0f / Ls;
+          st_tag(o_out + (size_t)h * dh / 2, tag_h2(a0 * il, a1 * il, tag_a));
+        }
+      }
+      trace_at(P, trw, 13);
     }
   }
   __syncthreads();
