@@ -1131,34 +1131,48 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     lsum[h] = 0.0f;
     o[h][0] = o[h][1] = 0.0f;
   }
+  // The current position's K/V row comes from the tagged words staged in LDS
+  // (the cache row may still be in flight): this lane's two dims, repacked to
+  // fp16 (exact: they were fp16) and patched into the round's registers, so the
+  // key loops below treat every key alike.
+  const unsigned kcw = __builtin_bit_cast(unsigned, f16x2{(_Float16)kcur[e0], (_Float16)kcur[e0 + 1]});
+  const unsigned vcw = __builtin_bit_cast(unsigned, f16x2{(_Float16)vcur[e0], (_Float16)vcur[e0 + 1]});
   for (int jb = wave > 0 ? j0 + kwv : j1; jb < j1; jb += kKW * kKeysPerRound) {
     if (jb != j0 + kwv) load_round(jb);   // the first round was requested before the queries
+    // (only inside the chunk: a unit whose chunk ends before pos staged no
+    // current row, and its keys past the chunk must stay zero)
+#pragma unroll
+    for (int k = 0; k < kKeysPerRound; ++k) {
+      const bool cur = jb + kKW * k == pos && pos < j1;
+      kw[k] = cur ? kcw : kw[k];
+      vw[k] = cur ? vcw : vw[k];
+    }
     if (kTrace && wave == 1) {
       asm volatile("" ::"v"(kw[0]), "v"(vw[0]), "v"(kw[kKeysPerRound - 1]), "v"(vw[kKeysPerRound - 1]));
       trace_at(P, trk, 8);
     }
-    // per query head: scores of this round's keys, online-softmax rescale, accumulate
+    // Per query head: scores of this round's keys, online-softmax rescale,
+    // accumulate.  Keys go in groups of four under one (uniform) check, so a
+    // group's four reductions are independent; a key past the chunk (its K/V
+    // registers are zero) scores -inf.
 #pragma unroll
     for (int h = 0; h < kMaxQpg; ++h) {
       if (h < qpg) {
         float sck[kKeysPerRound];
         float mb = m[h];
 #pragma unroll
-        for (int k = 0; k < kKeysPerRound; ++k) {
-          const int j = jb + kKW * k;
-          sck[k] = -INFINITY;
-          if (j < j1) {
-            float k0, k1;
-            if (j == pos) {
-              k0 = kcur[e0];
-              k1 = kcur[e0 + 1];
-            } else {
+        for (int kg = 0; kg < kKeysPerRound; kg += 4) {
+          if (jb + kKW * kg < j1) {
+#pragma unroll
+            for (int k = kg; k < kg + 4; ++k) {
               const f16x2 kv = __builtin_bit_cast(f16x2, kw[k]);
-              k0 = (float)kv.x;
-              k1 = (float)kv.y;
+              const float sc = wave_sum(qr[h][0] * (float)kv.x + qr[h][1] * (float)kv.y) * P.inv_sqrt_dh;
+              sck[k] = jb + kKW * k < j1 ? sc : -INFINITY;
+              mb = fmaxf(mb, sck[k]);
             }
-            sck[k] = wave_sum(qr[h][0] * k0 + qr[h][1] * k1) * P.inv_sqrt_dh;
-            mb = fmaxf(mb, sck[k]);
+          } else {
+#pragma unroll
+            for (int k = kg; k < kg + 4; ++k) sck[k] = -INFINITY;
           }
         }
         if (kTrace && wave == 1 && h == 0) {
@@ -1171,22 +1185,16 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
         o[h][1] *= alpha;
         m[h] = mb;
 #pragma unroll
-        for (int k = 0; k < kKeysPerRound; ++k) {
-          const int j = jb + kKW * k;
-          if (j < j1) {
-            float v0, v1;
-            if (j == pos) {
-              v0 = vcur[e0];
-              v1 = vcur[e0 + 1];
-            } else {
+        for (int kg = 0; kg < kKeysPerRound; kg += 4) {
+          if (jb + kKW * kg < j1) {
+#pragma unroll
+            for (int k = kg; k < kg + 4; ++k) {
               const f16x2 vv = __builtin_bit_cast(f16x2, vw[k]);
-              v0 = (float)vv.x;
-              v1 = (float)vv.y;
+              const float pk = __expf(sck[k] - mb);   // 0 past the chunk
+              lsum[h] += pk;
+              o[h][0] += pk * (float)vv.x;
+              o[h][1] += pk * (float)vv.y;
             }
-            const float pk = __expf(sck[k] - mb);
-            lsum[h] += pk;
-            o[h][0] += pk * v0;
-            o[h][1] += pk * v1;
           }
         }
       }

@@ -254,6 +254,17 @@ def test_non_unit_norm_gains(lf, orc):
     teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 12))
 
 
+def test_large_activations_across_chunks(lf, orc):
+    """Weights at 5x the usual scale give residual and SwiGLU values well above
+    1, which the kernel stages unnormalised as fp16; positions up to 40 split the
+    attention over several chunks, whose keys past the chunk must contribute
+    nothing (regression: a current-row patch past the chunk produced NaN)."""
+    cfg = synth.CONFIGS["tiny_2l_d256"]
+    w = synth.model_weights(cfg, seed=9, scale=0.1)
+    eng, m, worst = teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 40))
+    assert np.isfinite(eng.logits().cpu().numpy()).all()
+
+
 # ---------------------------------------------------------------- full-size shapes
 
 def test_single_layer_2b_shape_hidden_io(lf, orc):
