@@ -210,6 +210,18 @@ __device__ __forceinline__ float pay_f(u64 w) { return __uint_as_float((unsigned
 __device__ __forceinline__ void st_tag(u64 *p, u64 w) {
   __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Exchange words through a pointer typed as global memory.  A pointer passed
+// through an empty asm statement (to fix where its address is computed) loses
+// what the compiler knew of its address space, and a generic pointer's accesses
+// become FLAT instructions, which also count in lgkmcnt: every later wait for an
+// LDS access would then wait for them too.  This type keeps them global.
+typedef __attribute__((address_space(1))) u64 gu64;
+__device__ __forceinline__ void st_tag(gu64 *p, u64 w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 ld_dev(const gu64 *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // LDS words shared between the waves of one workgroup.
 __device__ __forceinline__ unsigned lds_ld(const unsigned *p) {
@@ -1214,8 +1226,8 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   }
   // (taken before the barrier: none of it depends on the other waves)
   const int stride = dh + 2;
-  u64 *pg = P.part_t + (size_t)gen * P.part_gen;
-  u64 *o_out = P.o_t + (size_t)gen * (P.Hq * dh / 2) + ((size_t)g * qpg * dh + e0) / 2;
+  gu64 *pg = (gu64 *)(P.part_t + (size_t)gen * P.part_gen);
+  gu64 *o_out = (gu64 *)(P.o_t + (size_t)gen * (P.Hq * dh / 2) + ((size_t)g * qpg * dh + e0) / 2);
   asm volatile("" : "+s"(pg), "+v"(o_out));
   // Wave 1: combine the stream waves' states of head h (m, l, o for this lane's
   // two dims) left in wml / wo.  Every read is in bounds for every lane (e0 = 0
@@ -1244,7 +1256,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   __syncthreads();
   if (wave == 1) {
     trace_at(P, trw, 9);
-    u64 *dst = pg + (size_t)u * qpg * stride;
+    gu64 *dst = pg + (size_t)u * qpg * stride;
     for (int h = 0; h < qpg; ++h) {
       float M, Ls, a0, a1;
       combine(h, M, Ls, a0, a1);
@@ -1277,7 +1289,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     __syncthreads();   // wave 1 has read the unit's own states: wml / wo are free
     if (wave == 1) trace_at(P, trw, 11);
     if (wave > 0) {
-      const u64 *src = pg + (size_t)g * S * qpg * stride;
+      const gu64 *src = pg + (size_t)g * S * qpg * stride;
       const u64 tagw = (u64)tag_a << 32;
       for (int h = 0; h < qpg; ++h) {
         float M = -INFINITY, Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
@@ -1286,7 +1298,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const bool use = cb + kKW * i < S;
-            const u64 *q = src + ((size_t)(cb + kKW * i) * qpg + h) * stride;
+            const gu64 *q = src + ((size_t)(cb + kKW * i) * qpg + h) * stride;
             w[i][0] = use ? ld_dev(q) : tagw;
             w[i][1] = use ? ld_dev(q + 1) : tagw;
             w[i][2] = use ? ld_dev(q + 2 + e0) : tagw;
@@ -1302,11 +1314,11 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
             if (wave_none(stale)) break;
             const unsigned e = ld_dev(&P.err[0]);
             // (addresses recomputed here, not held across the loop)
-            const u64 *pb = src + ((size_t)cb * qpg + h) * stride;
+            const gu64 *pb = src + ((size_t)cb * qpg + h) * stride;
             asm volatile("" : "+v"(pb));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const u64 *q = pb + (size_t)kKW * i * qpg * stride;
+              const gu64 *q = pb + (size_t)kKW * i * qpg * stride;
               if (tag_of(w[i][0]) != tag_a) w[i][0] = ld_dev(q);
               if (tag_of(w[i][1]) != tag_a) w[i][1] = ld_dev(q + 1);
               if (tag_of(w[i][2]) != tag_a) w[i][2] = ld_dev(q + 2 + e0);
@@ -1860,7 +1872,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 3, 0);
         const RowSpans rs = row_spans(ctl, K_GU);   // (constant: read before the wait)
-        u64 *ad = Pl.a_t + (size_t)gen * (Pl.F / 2);
+        gu64 *ad = (gu64 *)(Pl.a_t + (size_t)gen * (Pl.F / 2));
         asm volatile("" : "+s"(ad));   // computed now, not after the wait
         wait_streams(ctl, q0 + 2);
         tk = lap(sy, ST_STREAMS, tk);
