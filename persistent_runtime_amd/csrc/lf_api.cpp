@@ -372,21 +372,21 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   // an RMSNorm input is written as fp16 elements in whole rounds of words
   const size_t d_elems = round_up((size_t)d, lf::kStageRound);
   if (d_elems * 2 > h_b) h_b = align_up(d_elems * 2, 16);
-  const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);
+  const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);   // one phase kind's partial row sums
   // attention scratch: queries, current K/V row, per-wave (m, l) and per-wave o
   const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (size_t)lf::kWaves * 8 * 2 * 4 +
                         (size_t)lf::kWaves * P.qpg * dh * 4;
   const size_t samp_b = 4096;
-  // [h | part]
-  size_t region_a = h_b + part_b;
+  // h, overlaid by the attention / sampler scratch between GEMV phases
+  size_t region_a = h_b;
   if (attn_b > region_a) region_a = attn_b;
   if (samp_b > region_a) region_a = samp_b;
   P.lds_h = 0;
-  P.lds_part = (int)h_b;
   P.lds_red = (int)align_up(region_a, 256);
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + lf::kCtlBytes;
-  P.lds_trace = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);
+  P.lds_part = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);   // [kind][rows][8]
+  P.lds_trace = (int)align_up((size_t)P.lds_part + 5 * part_b, 256);
   const size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
   P.part_rows = rows_max;
   P.hmax = hmax;

@@ -242,11 +242,6 @@ struct Geo {            // one phase kind's row block in this workgroup
   int r0, nrows, kv, ppr;   // first row, rows, 16-B vectors per row, 1-KB pieces per row
 };
 
-// The rows each stream wave touches in a phase: [lo[cw], hi[cw]] (empty when
-// lo > hi).
-struct RowSpans {
-  int lo[kNcw], hi[kNcw];
-};
 // A stream wave's pieces of one phase kind: n pieces from piece kp of row `row`.
 struct Slice {
   int n, row, kp, pad_;
@@ -261,7 +256,6 @@ struct Ctl {
   Geo geo[K_COUNT];
   // The partition of every phase kind among the stream waves, fixed for the
   // launch: computed once so that no phase divides by the pieces per row.
-  RowSpans span[K_COUNT];
   Slice slice[K_COUNT][kNcw];
 };
 static_assert(sizeof(Ctl) <= kCtlBytes, "workgroup control block exceeds its LDS space");
@@ -567,6 +561,9 @@ __device__ __forceinline__ const unsigned char *phase_base(KP &P, const Geo &g, 
   }
   return reinterpret_cast<const unsigned char *>(w) + (size_t)g.r0 * g.kv * 16;
 }
+
+// A phase kind's partial row sums in LDS: [rows][8], slot 7 unused.
+__device__ __forceinline__ float *kind_part(float *part, int kind, int rows) { return part + kind * rows * 8; }
 
 // A phase kind's row block, read from LDS into wave-uniform (scalar) registers.
 __device__ __forceinline__ Geo uniform_geo(const Ctl *ctl, int kind) {
@@ -942,7 +939,7 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
     ra.kpc = (unsigned)sl.kp;
     ra.ppm1 = (unsigned)(ppr - 1);
     ra.hb = lds_addr(h);
-    ra.pa = lds_addr(part + sl.row * 8 + st.cw);
+    ra.pa = lds_addr(kind_part(part, kind, fresh(*st.P).part_rows) + sl.row * 8 + st.cw);
     const bool more = n > kRing;
     ra.ikp = more ? (unsigned)st.kp : 0u;
     ra.ileft = more ? (unsigned)st.left : 0u;
@@ -974,28 +971,17 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
 
 // ---------------------------------------------------------------- sync-wave phase pieces
 
-// The rows each stream wave touches in a phase, read from the workgroup's table.
-__device__ __forceinline__ RowSpans row_spans(const Ctl *ctl, int kind) {
-  RowSpans rs;
-#pragma unroll
-  for (int cw = 0; cw < kNcw; ++cw) {
-    rs.lo[cw] = __builtin_amdgcn_readfirstlane(ctl->span[kind].lo[cw]);
-    rs.hi[cw] = __builtin_amdgcn_readfirstlane(ctl->span[kind].hi[cw]);
-  }
-  return rs;
-}
 // Sum of the stream waves' partials of one row, in wave order: the row's eight
-// partial slots are read at once; slots of waves that did not touch the row
-// hold stale values and are skipped.
-__device__ __forceinline__ float row_value(const float *part, const RowSpans &rs, int row) {
+// partial slots are read at once.  Each phase kind has its own slots, zeroed
+// when the kernel starts, and the partition of a kind among the stream waves
+// is fixed for the launch: a slot of a wave that does not touch the row is
+// never written and stays zero, so no slot needs a check.
+__device__ __forceinline__ float row_value(const float *part, int row) {
   const float4 p0 = reinterpret_cast<const float4 *>(part + row * 8)[0];
   const float4 p1 = reinterpret_cast<const float4 *>(part + row * 8)[1];
-  const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-  float y = 0.0f;
-#pragma unroll
-  for (int cw = 0; cw < kNcw; ++cw) y += (rs.lo[cw] <= row && row <= rs.hi[cw]) ? v[cw] : 0.0f;
-  return y;
+  return ((((((p0.x + p0.y) + p0.z) + p0.w) + p1.x) + p1.y) + p1.z);
 }
+
 
 // Wave 0: wait until every stream wave finished GEMV phase q.
 __device__ __forceinline__ void wait_streams(const Ctl *ctl, int q) {
@@ -1606,8 +1592,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         wave_slice(ge.nrows * ge.ppr, cw, lo, hi);
         const int row = lo < hi ? lo / ge.ppr : 0;
         ctl->slice[k][cw] = Slice{hi - lo, row, lo < hi ? lo - row * ge.ppr : 0, 0};
-        ctl->span[k].lo[cw] = lo < hi ? row : 1;
-        ctl->span[k].hi[cw] = lo < hi ? (hi - 1) / ge.ppr : 0;
       }
     }
     if (kTrace)
@@ -1616,6 +1600,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     for (int w = 0; w < kWaves; ++w) ctl->done[w] = 0;
     ctl->status = 0;
   }
+  for (int i = tid_x(); i < K_COUNT * P.part_rows * 8; i += kThreads) part[i] = 0.0f;
   __syncthreads();
 
   Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}, -1, (P.flags & 4u) != 0};
@@ -1757,7 +1742,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         }
         tq = lap(sy, ST_STAGE, tq);
         trace(Pl, t, 5 * l + 0, 0);
-        const RowSpans rs = row_spans(ctl, K_QKV);   // (constant: read before the wait)
+        const float *pk = kind_part(part, K_QKV, Pl.part_rows);
         wait_streams(ctl, q0);
         tq = lap(sy, ST_STREAMS, tq);
         trace(Pl, t, 5 * l + 0, 1);
@@ -1766,7 +1751,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         _Float16 *kc = reinterpret_cast<_Float16 *>(Pl.kcache);
         _Float16 *vc = reinterpret_cast<_Float16 *>(Pl.vcache);
         for (int i = lane; i < ge.nrows / 2; i += 64) {
-          const float a = row_value(part, rs, 2 * i) * inv, bb = row_value(part, rs, 2 * i + 1) * inv;
+          const float a = row_value(pk, 2 * i) * inv, bb = row_value(pk, 2 * i + 1) * inv;
           const int r = ge.r0 + 2 * i;
           if (r < nq + nk) {
             // q / k rows come in rotary pairs (dims k, k + dh/2 of head hd)
@@ -1823,9 +1808,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 2, 0);
-        // Before the wait (none of it depends on the stream waves): the row
-        // spans, the output words, and the residual of this lane's first row.
-        const RowSpans rs = row_spans(ctl, K_O);
+        // Before the wait (none of it depends on the stream waves): the output
+        // words and the residual of this lane's first row.
+        const float *pk = kind_part(part, K_O, Pl.part_rows);
         u64 *xm = Pl.xmid_t + (size_t)gen * d;
         const int hio = Pl.hidden_io;
         auto residual = [&](int i) __attribute__((always_inline)) {
@@ -1846,7 +1831,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
           const float xin = i == lane ? xin0 : residual(i);
-          const float x = xin + row_value(part, rs, i);
+          const float x = xin + row_value(pk, i);
           xown[i] = x;
           st_tag(xm + r, tag_f(x, tag));
         }
@@ -1871,7 +1856,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 3, 0);
-        const RowSpans rs = row_spans(ctl, K_GU);   // (constant: read before the wait)
+        const float *pk = kind_part(part, K_GU, Pl.part_rows);
         gu64 *ad = (gu64 *)(Pl.a_t + (size_t)gen * (Pl.F / 2));
         asm volatile("" : "+s"(ad));   // computed now, not after the wait
         wait_streams(ctl, q0 + 2);
@@ -1880,8 +1865,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         const unsigned tag = lvl + PH_GU;
         for (int i = lane; i < ge.nrows / 4; i += 64) {
           // rows 4i..4i+3 = gate j, up j, gate j+1, up j+1 with j = r0/2 + 2i
-          const float g0 = row_value(part, rs, 4 * i) * inv, u0 = row_value(part, rs, 4 * i + 1) * inv;
-          const float g1 = row_value(part, rs, 4 * i + 2) * inv, u1 = row_value(part, rs, 4 * i + 3) * inv;
+          const float g0 = row_value(pk, 4 * i) * inv, u0 = row_value(pk, 4 * i + 1) * inv;
+          const float g1 = row_value(pk, 4 * i + 2) * inv, u1 = row_value(pk, 4 * i + 3) * inv;
           const float s0 = __fdividef(g0, 1.0f + __expf(-g0)), s1 = __fdividef(g1, 1.0f + __expf(-g1));
           st_tag(ad + ge.r0 / 4 + i, tag_h2(s0 * u0, s1 * u1, tag));
         }
@@ -1904,8 +1889,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 4, 0);
-        // before the wait: row spans, output words, this lane's first residual
-        const RowSpans rs = row_spans(ctl, K_D);
+        // before the wait: output words, this lane's first residual
+        const float *pk = kind_part(part, K_D, Pl.part_rows);
         u64 *xo = Pl.xout_t + (size_t)gen * d;
         const bool host_out = Pl.hidden_io && l == L - 1;
         const float xo0 = lane < ge.nrows ? xown[lane] : 0.0f;
@@ -1915,7 +1900,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         const unsigned tag = lvl + PH_D;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
-          const float x = (i == lane ? xo0 : xown[i]) + row_value(part, rs, i);
+          const float x = (i == lane ? xo0 : xown[i]) + row_value(pk, i);
           xown[i] = x;
           st_tag(xo + r, tag_f(x, tag));
           if (host_out) Pl.x_out[r] = x;
@@ -1943,13 +1928,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         inv = coop_inv_rms(ctl, d, P.eps);
       }
       trace(P, t, 5 * L, 0);
-      const RowSpans rs = row_spans(ctl, K_LM);   // (constant: read before the wait)
+      const float *pk = kind_part(part, K_LM, P.part_rows);
       wait_streams(ctl, qlm);
       trace(P, t, 5 * L, 1);
       float best = -INFINITY;
       int bi = 0x7fffffff;
       for (int i = lane; i < ge.nrows; i += 64) {
-        const float y = row_value(part, rs, i) * inv;
+        const float y = row_value(pk, i) * inv;
         st_dev(&P.logits[ge.r0 + i], y);
         if (y > best || (y == best && ge.r0 + i < bi)) { best = y; bi = ge.r0 + i; }
       }
