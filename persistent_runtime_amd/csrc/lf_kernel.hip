@@ -1139,11 +1139,13 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     if (jb != j0 + kwv) load_round(jb);   // the first round was requested before the queries
     // (only inside the chunk: a unit whose chunk ends before pos staged no
     // current row, and its keys past the chunk must stay zero)
+    if (pos < j1 && jb <= pos) {
 #pragma unroll
-    for (int k = 0; k < kKeysPerRound; ++k) {
-      const bool cur = jb + kKW * k == pos && pos < j1;
-      kw[k] = cur ? kcw : kw[k];
-      vw[k] = cur ? vcw : vw[k];
+      for (int k = 0; k < kKeysPerRound; ++k) {
+        const bool cur = jb + kKW * k == pos;
+        kw[k] = cur ? kcw : kw[k];
+        vw[k] = cur ? vcw : vw[k];
+      }
     }
     if (kTrace && wave == 1) {
       asm volatile("" ::"v"(kw[0]), "v"(vw[0]), "v"(kw[kKeysPerRound - 1]), "v"(vw[kKeysPerRound - 1]));
