@@ -1041,9 +1041,13 @@ constexpr int kKeysPerRound = 16;   // keys whose K and V rows one wave loads pe
 // the tagged exchange words, not from the cache (whose row for this step may
 // still be in flight).
 // Returns false if a bounded wait expired.
+// kQ: a bound on the query heads per KV head (qpg <= kQ), so that an MHA
+// model's unit keeps one head's state in registers and no loop over heads.
+template <int kQ>
 __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsigned tag_q,
                                           unsigned tag_a, int pos, int u, int S, int Lc, unsigned char *lds,
                                           float *red, int trk = -1) {
+  static_assert(kQ <= kMaxQpg, "query heads per KV head");
   KP &P = fresh(P0);
   const int tid = tid_x(), wave = wave_id(), lane = lane_id();
   const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv, half = dh / 2;
@@ -1116,15 +1120,15 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   const int trw = wave == 1 ? trk : -1;
   trace_at(P, trw, 3);
 
-  float qr[kMaxQpg][2];
+  float qr[kQ][2];
 #pragma unroll
-  for (int h = 0; h < kMaxQpg; ++h) {
+  for (int h = 0; h < kQ; ++h) {
     qr[h][0] = h < qpg && act ? qs[h * dh + e0] : 0.0f;
     qr[h][1] = h < qpg && act ? qs[h * dh + e0 + 1] : 0.0f;
   }
-  float m[kMaxQpg], lsum[kMaxQpg], o[kMaxQpg][2];
+  float m[kQ], lsum[kQ], o[kQ][2];
 #pragma unroll
-  for (int h = 0; h < kMaxQpg; ++h) {
+  for (int h = 0; h < kQ; ++h) {
     m[h] = -INFINITY;
     lsum[h] = 0.0f;
     o[h][0] = o[h][1] = 0.0f;
@@ -1156,7 +1160,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     // group's four reductions are independent; a key past the chunk (its K/V
     // registers are zero) scores -inf.
 #pragma unroll
-    for (int h = 0; h < kMaxQpg; ++h) {
+    for (int h = 0; h < kQ; ++h) {
       if (h < qpg) {
         float sck[kKeysPerRound];
         float mb = m[h];
@@ -1203,7 +1207,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   trace_at(P, trw, 4);
   // the stream waves' states -> the unit's partial (wave 0 holds no keys)
 #pragma unroll
-  for (int h = 0; h < kMaxQpg; ++h) {
+  for (int h = 0; h < kQ; ++h) {
     if (h < qpg && wave > 0) {
       if (lane == 0) {
         wml[(wave * kMaxQpg + h) * 2 + 0] = m[h];
@@ -1652,8 +1656,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, stage_spec(P, K_QKV, t, l, gen, lvl), true)) return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
-          if (!attn_unit(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
-                         u == b && t == P.trace_token ? 5 * l + 1 : -1)) return;
+          if (!(P.qpg == 1 ? attn_unit<1>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
+                                          u == b && t == P.trace_token ? 5 * l + 1 : -1)
+                           : attn_unit<kMaxQpg>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds,
+                                                red, u == b && t == P.trace_token ? 5 * l + 1 : -1)))
+            return;
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
         if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, stage_spec(P, K_O, t, l, gen, lvl))) return;
@@ -1788,8 +1795,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         const unsigned long long ta = stamp(sy);
         trace(Pl, t, 5 * l + 1, 0);
         for (int u = b; u < Pl.Hkv * S; u += G)
-          if (!attn_unit(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
-                         u == b && t == Pl.trace_token ? 5 * l + 1 : -1)) return;
+          if (!(Pl.qpg == 1 ? attn_unit<1>(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
+                                           u == b && t == Pl.trace_token ? 5 * l + 1 : -1)
+                            : attn_unit<kMaxQpg>(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc,
+                                                 alds, red, u == b && t == Pl.trace_token ? 5 * l + 1 : -1)))
+            return;
         trace(Pl, t, 5 * l + 1, 1);
         publish_vec(Pl, lvl + PH_ATTN);
         trace(Pl, t, 5 * l + 1, 2);
