@@ -352,10 +352,11 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   // ---- LDS layout: [h | part] (also attention / sampler scratch), red, ctl, rings
   int rows_max = 0;
   {
-    const int units[5] = {P.nqkv / 2, d / 2, F / 2, d / 2, hidden ? 0 : V / 2};
-    const int upr[5] = {2, 2, 4, 2, 2};   // rows per partition unit
+    const int units[5] = {P.nqkv / 2, d, F / 2, d / 2, hidden ? 0 : V / 2};
+    const int upr[5] = {2, 1, 4, 2, 2};   // rows per partition unit (as in the kernel)
     for (int k = 0; k < 5; ++k) {
-      const int r = upr[k] * ((units[k] + G - 1) / G);
+      const int g = k == 1 ? G - lf::o_rows_skip(G, Hkv) : G;   // the output projection's workgroups
+      const int r = upr[k] * ((units[k] + g - 1) / g);
       rows_max = r > rows_max ? r : rows_max;
     }
   }
@@ -385,7 +386,8 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_red = (int)align_up(region_a, 256);
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + lf::kCtlBytes;
-  P.lds_part = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 256);   // [kind][rows][8]
+  P.lds_xres = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 16);
+  P.lds_part = (int)align_up((size_t)P.lds_xres + (size_t)rows_max * 4, 256);   // [kind][rows][8]
   P.lds_trace = (int)align_up((size_t)P.lds_part + 5 * part_b, 256);
   const size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
   P.part_rows = rows_max;

@@ -14,6 +14,10 @@ constexpr int kAttnBlock = 512;        // key positions scored per attention sub
 #endif
 constexpr int kMinKeysPerUnit = LF_MIN_KEYS_PER_UNIT;   // smallest attention split-K chunk
 constexpr int kMaxSplit = 64;          // most split-K chunks per KV head
+// Workgroups 0 .. n-1 merge the attention heads' split-K partials (unit c = 0
+// of head g runs on workgroup g); they are the last to finish attention, so
+// with enough workgroups they get no rows of the output projection.
+__host__ __device__ constexpr int o_rows_skip(int G, int Hkv) { return G > 2 * Hkv ? Hkv : 0; }
 constexpr int kStatWords = 16;         // uint64 statistics per workgroup (LF_STATS)
 // LF_TRACE builds also record, for one token, three timestamps per phase and
 // workgroup: input staged, stream waves done, published.
@@ -89,7 +93,7 @@ struct Params {
   unsigned long long timeout_ticks;
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_trace, lds_bytes;
+  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_bytes;
   int part_rows, hmax;
 };
 

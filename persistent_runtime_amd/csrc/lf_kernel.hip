@@ -401,6 +401,8 @@ struct StageSpec {
   const u64 *src;
   int n, mode;
   unsigned tag;
+  int cap0, capn;   // RMS: words [cap0, cap0 + capn) are also kept in fp32, in cap[0 .. capn)
+  float *cap;
 };
 
 // One wave's share of a tagged vector src[0..n): the 64-word slots
@@ -456,6 +458,7 @@ __device__ __forceinline__ void coop_stage(KP &P, Ctl *ctl, const StageSpec &sp,
       const float x = pay_f(w);
       ss += real ? x * x : 0.0f;
       h[i] = (_Float16)x;
+      if ((unsigned)(i - sp.cap0) < (unsigned)sp.capn) sp.cap[i - sp.cap0] = x;
     });
     ss = wave_sum(ss);
     if (lane == 0) ctl->ssw[wave] = ss;
@@ -479,18 +482,30 @@ __device__ __forceinline__ float coop_inv_rms(const Ctl *ctl, int d, float eps) 
 
 // The input of GEMV phase `kind` of layer l of token t (gen: the layer's buffer
 // generation, lvl: the layer's base level; for K_LM, lvl is the level of the
-// last layer's down projection).
-__device__ __forceinline__ StageSpec stage_spec(const KP &P, int kind, int t, int l, int gen, unsigned lvl) {
+// last layer's down projection).  The residual stream's rows that this
+// workgroup's epilogues add to are kept in fp32 as they arrive: its
+// output-projection rows of the layer input in xo, its down-projection rows of
+// x after attention in xd (two buffers: a workgroup may still read xd for the
+// previous layer's down projection while its waves fetch the next layer input).
+__device__ __forceinline__ StageSpec stage_spec(const KP &P, const Ctl *ctl, int kind, int t, int l, int gen,
+                                                unsigned lvl, float *xo, float *xd) {
   StageSpec sp;
   const int L = P.L, d = P.d;
   sp.src = nullptr;
   sp.n = d;
   sp.mode = SM_RMS;
   sp.tag = lvl;
+  sp.cap0 = sp.capn = 0;
+  sp.cap = xo;
   switch (kind) {
     case K_QKV:
-      if (l > 0) sp.src = P.xout_t + (size_t)((t * L + l - 1) & 1) * d;
-      else sp.mode = SM_PLAIN;
+      if (l > 0) {
+        sp.src = P.xout_t + (size_t)((t * L + l - 1) & 1) * d;
+        sp.cap0 = __builtin_amdgcn_readfirstlane(ctl->geo[K_O].r0);
+        sp.capn = __builtin_amdgcn_readfirstlane(ctl->geo[K_O].nrows);
+      } else {
+        sp.mode = SM_PLAIN;
+      }
       break;
     case K_O:
       sp.src = P.o_t + (size_t)gen * (P.Hq * P.dh / 2);
@@ -501,6 +516,9 @@ __device__ __forceinline__ StageSpec stage_spec(const KP &P, int kind, int t, in
     case K_GU:
       sp.src = P.xmid_t + (size_t)gen * d;
       sp.tag = lvl + PH_O;
+      sp.cap0 = __builtin_amdgcn_readfirstlane(ctl->geo[K_D].r0);
+      sp.capn = __builtin_amdgcn_readfirstlane(ctl->geo[K_D].nrows);
+      sp.cap = xd;
       break;
     case K_D:
       sp.src = P.a_t + (size_t)gen * (P.F / 2);
@@ -912,7 +930,7 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
   // the dependency wait happens on wave 0; here only its LDS announcement
   const bool timed = st.timed;
   unsigned long long t0 = timed ? now_ticks() : 0ull;
-  if (ge.nrows > 0) {
+  if (ge.nrows > 0 || sp.capn > 0) {
     // this wave's share of the input vector, then the workgroup barrier
     coop_stage(*st.P, ctl, sp, st.cw + 1, h);
     wg_barrier();
@@ -1051,7 +1069,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   KP &P = fresh(P0);
   const int tid = tid_x(), wave = wave_id(), lane = lane_id();
   const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv, half = dh / 2;
-  const int g = u / S, c = u - g * S;
+  const int g = u % Hkv, c = u / Hkv;   // chunk c = 0 of head g runs on workgroup g
   const int n = pos + 1;
   const int j0 = c * Lc;
   const int j1 = min(n, j0 + Lc);
@@ -1248,7 +1266,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   __syncthreads();
   if (wave == 1) {
     trace_at(P, trw, 9);
-    gu64 *dst = pg + (size_t)u * qpg * stride;
+    gu64 *dst = pg + (size_t)(g * S + c) * qpg * stride;   // partials of head g in chunk order
     for (int h = 0; h < qpg; ++h) {
       float M, Ls, a0, a1;
       combine(h, M, Ls, a0, a1);
@@ -1574,7 +1592,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
   float *part = reinterpret_cast<float *>(smem + P.lds_part);
   float *red = reinterpret_cast<float *>(smem + P.lds_red);   // 64 floats
   Ctl *ctl = reinterpret_cast<Ctl *>(smem + P.lds_ctl);
-  float *xown = reinterpret_cast<float *>(smem + P.lds_xown); // residual rows of this workgroup
+  float *xown = reinterpret_cast<float *>(smem + P.lds_xown); // residual rows: output projection
+  float *xres = reinterpret_cast<float *>(smem + P.lds_xres); // residual rows: down projection
   unsigned char *alds = smem + P.lds_h;                       // attention / sampler scratch
   const int b = blockIdx.x, G = P.G, wave = wave_id(), lane = lane_id();
   const int L = P.L, d = P.d, dh = P.dh;
@@ -1583,14 +1602,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
   const _Float16 *emb = reinterpret_cast<const _Float16 *>(P.tok_emb);
 
   // this workgroup's row block of every phase kind: contiguous partition units
-  // (row pairs; gate/up in units of two pairs, so one SwiGLU word has one producer)
+  // (row pairs, so each rotary pair has one producer; gate/up in units of two
+  // pairs, so one SwiGLU word has one producer; the output projection in single
+  // rows, over the workgroups that merge no attention head)
   if (tid_x() == 0) {
-    const int units[K_COUNT] = {P.nqkv / 2, d / 2, P.F / 2, d / 2, P.V / 2};
-    const int upr[K_COUNT] = {2, 2, 4, 2, 2};
+    const int units[K_COUNT] = {P.nqkv / 2, d, P.F / 2, d / 2, P.V / 2};
+    const int upr[K_COUNT] = {2, 1, 4, 2, 2};
     const int kvs[K_COUNT] = {d / 8, P.Hq * dh / 8, d / 8, P.F / 8, d / 8};
+    const int nskip = o_rows_skip(G, P.Hkv);
     for (int k = 0; k < K_COUNT; ++k) {
-      int p0, p1;
-      block_range(units[k], G, b, p0, p1);
+      int p0 = 0, p1 = 0;
+      if (k != K_O) block_range(units[k], G, b, p0, p1);
+      else if (b >= nskip) block_range(units[k], G - nskip, b - nskip, p0, p1);
       const Geo ge = Geo{upr[k] * p0, upr[k] * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
       ctl->geo[k] = ge;
       for (int cw = 0; cw < kNcw; ++cw) {
@@ -1653,7 +1676,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         // after attention: this wave's loads complete in order, so attention's
         // K/V loads would otherwise queue behind it.
         const bool qkv_rounds = st_has_rounds(st, K_QKV, ctl);
-        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, stage_spec(P, K_QKV, t, l, gen, lvl), true)) return;
+        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, stage_spec(P, ctl, K_QKV, t, l, gen, lvl, xown, xres),
+                          true))
+          return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
           if (!(P.qpg == 1 ? attn_unit<1>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
@@ -1663,16 +1688,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
             return;
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
-        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, stage_spec(P, K_O, t, l, gen, lvl))) return;
+        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, stage_spec(P, ctl, K_O, t, l, gen, lvl, xown, xres))) return;
         st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
-        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part, stage_spec(P, K_GU, t, l, gen, lvl))) return;
+        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part, stage_spec(P, ctl, K_GU, t, l, gen, lvl, xown, xres))) return;
         st.trace_k = t == P.trace_token ? 5 * l + 4 : -1;
-        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part, stage_spec(P, K_D, t, l, gen, lvl))) return;
+        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part, stage_spec(P, ctl, K_D, t, l, gen, lvl, xown, xres))) return;
       }
       if (has_lm) {
         st.trace_k = t == P.trace_token ? 5 * L : -1;
         if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part,
-                          stage_spec(P, K_LM, t, L, 0, lv0 + (unsigned)(L * PH_PER_LAYER))))
+                          stage_spec(P, ctl, K_LM, t, L, 0, lv0 + (unsigned)(L * PH_PER_LAYER), xown, xres)))
           return;
         if (b == 0 && P.sampling) {
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
@@ -1736,9 +1761,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         sy.trace_k = t == Pl.trace_token ? 5 * l : -1;
         trace(Pl, t, 5 * l + 0, 6);
         float inv = 0.0f;   // 1 / rms of the layer input: scales the row sums
-        if (ge.nrows > 0) {
+        const StageSpec sp = stage_spec(Pl, ctl, K_QKV, t, l, gen, lvl, xown, xres);
+        if (ge.nrows > 0 || sp.capn > 0) {
           if (l > 0) {
-            coop_stage(Pl, ctl, stage_spec(Pl, K_QKV, t, l, gen, lvl), 0, hl);
+            coop_stage(Pl, ctl, sp, 0, hl);
           } else {
             inv = stage_rmsnorm_plain(Pl.hidden_io ? Pl.x_hidden : nullptr,
                                       Pl.hidden_io ? nullptr : emb + (size_t)token * d, d, Pl.eps, hl);
@@ -1813,7 +1839,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         sy.trace_k = t == Pl.trace_token ? 5 * l + 2 : -1;
         trace(Pl, t, 5 * l + 2, 6);
         if (ge.nrows > 0) {
-          coop_stage(Pl, ctl, stage_spec(Pl, K_O, t, l, gen, lvl), 0, hl);
+          coop_stage(Pl, ctl, stage_spec(Pl, ctl, K_O, t, l, gen, lvl, xown, xres), 0, hl);
           trace(Pl, t, 5 * l + 2, 7);
           wg_barrier();
           if (lds_ld(&ctl->abort)) return;
@@ -1844,7 +1870,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           const int r = ge.r0 + i;
           const float xin = i == lane ? xin0 : residual(i);
           const float x = xin + row_value(pk, i);
-          xown[i] = x;
           st_tag(xm + r, tag_f(x, tag));
         }
         publish_vec(Pl, tag);
@@ -1859,8 +1884,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         sy.trace_k = t == Pl.trace_token ? 5 * l + 3 : -1;
         trace(Pl, t, 5 * l + 3, 6);
         float inv = 0.0f;
-        if (ge.nrows > 0) {
-          coop_stage(Pl, ctl, stage_spec(Pl, K_GU, t, l, gen, lvl), 0, hl);
+        const StageSpec sp = stage_spec(Pl, ctl, K_GU, t, l, gen, lvl, xown, xres);
+        if (ge.nrows > 0 || sp.capn > 0) {
+          coop_stage(Pl, ctl, sp, 0, hl);
           trace(Pl, t, 5 * l + 3, 7);
           wg_barrier();
           if (lds_ld(&ctl->abort)) return;
@@ -1894,7 +1920,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         sy.trace_k = t == Pl.trace_token ? 5 * l + 4 : -1;
         trace(Pl, t, 5 * l + 4, 6);
         if (ge.nrows > 0) {
-          coop_stage(Pl, ctl, stage_spec(Pl, K_D, t, l, gen, lvl), 0, hl);
+          coop_stage(Pl, ctl, stage_spec(Pl, ctl, K_D, t, l, gen, lvl, xown, xres), 0, hl);
           trace(Pl, t, 5 * l + 4, 7);
           wg_barrier();
           if (lds_ld(&ctl->abort)) return;
@@ -1905,15 +1931,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         const float *pk = kind_part(part, K_D, Pl.part_rows);
         u64 *xo = Pl.xout_t + (size_t)gen * d;
         const bool host_out = Pl.hidden_io && l == L - 1;
-        const float xo0 = lane < ge.nrows ? xown[lane] : 0.0f;
+        const float xo0 = lane < ge.nrows ? xres[lane] : 0.0f;
         wait_streams(ctl, q0 + 3);
         tk = lap(sy, ST_STREAMS, tk);
         trace(Pl, t, 5 * l + 4, 1);
         const unsigned tag = lvl + PH_D;
         for (int i = lane; i < ge.nrows; i += 64) {
           const int r = ge.r0 + i;
-          const float x = (i == lane ? xo0 : xown[i]) + row_value(pk, i);
-          xown[i] = x;
+          const float x = (i == lane ? xo0 : xres[i]) + row_value(pk, i);
           st_tag(xo + r, tag_f(x, tag));
           if (host_out) Pl.x_out[r] = x;
         }
@@ -1933,7 +1958,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       const Geo ge = uniform_geo(ctl, K_LM);
       float inv = 0.0f;
       if (ge.nrows > 0) {
-        coop_stage(P, ctl, stage_spec(P, K_LM, t, L, 0, lvl_lm - 1u), 0, hl);
+        coop_stage(P, ctl, stage_spec(P, ctl, K_LM, t, L, 0, lvl_lm - 1u, xown, xres), 0, hl);
         trace(P, t, 5 * L, 7);
         wg_barrier();
         if (lds_ld(&ctl->abort)) return;
