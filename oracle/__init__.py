@@ -70,6 +70,13 @@ def lib():
         L.orc_expdef_constants.argtypes = [P]
         L.orc_expdef_n.argtypes = [P, P, C.c_size_t]
         L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_logdef.restype = C.c_float
+        L.orc_logdef.argtypes = [C.c_float]
+        L.orc_logdef_n.argtypes = [P, P, C.c_size_t]
+        L.orc_gumbel_noise.restype = C.c_float
+        L.orc_gumbel_noise.argtypes = [C.c_uint64, C.c_int32, C.c_int32]
+        L.orc_sample_gumbel.restype = C.c_int32
+        L.orc_sample_gumbel.argtypes = [P, C.c_int32, C.c_float, C.c_uint64, C.c_int32]
         L.orc_sample.restype = C.c_int32
         L.orc_sample.argtypes = [P, C.c_int32, C.c_float, C.c_float, C.c_uint64, C.c_int32]
         L.orc_sample_detail.restype = C.c_int32
@@ -170,6 +177,22 @@ def philox4x32_10(ctr, key) -> np.ndarray:
     out = np.zeros(4, dtype=np.uint32)
     lib().orc_philox4x32_10(_p(c), _p(k), _p(out))
     return out
+
+
+def logdef(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.atleast_1d(np.asarray(x, dtype=np.float32)))
+    y = np.empty_like(x)
+    lib().orc_logdef_n(_p(x), _p(y), x.size)
+    return y
+
+
+def gumbel_noise(seed: int, pos: int, i: int) -> float:
+    return lib().orc_gumbel_noise(seed, pos, i)
+
+
+def sample_gumbel(logits: np.ndarray, temperature: float, seed: int, pos: int) -> int:
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    return lib().orc_sample_gumbel(_p(logits), logits.size, temperature, seed, pos)
 
 
 def sample(logits: np.ndarray, temperature: float, top_p: float, seed: int, pos: int) -> int:

@@ -415,6 +415,73 @@ extern "C" int32_t orc_sample(const float *logits, int32_t n, float temperature,
                            nullptr, nullptr, nullptr);
 }
 
+/* Defined natural logarithm L(x) for positive normal binary32 x, identical on any
+ * IEEE-754 machine (every step one correctly rounded operation or one fma):
+ *   x = m 2^e with m in [sqrt(1/2), sqrt(2)) (read from the bits);  f = m - 1 (exact);
+ *   s = f / (2 + f);  ln(1 + f) = 2 atanh(s) = 2s + 2s R(s^2) with
+ *   R(w) = w/3 + w^2/5 + ... + w^6/13 in Horner form;  L = e ln2_hi + (e ln2_lo + ln(1+f)).
+ * Constants are the nearest binary32 values of ln 2 (split hi / lo) and 1/(2k+1). */
+static const float LOG_SQRT2 = 0x1.6a09e6p+0f;     /* sqrt(2) rounded */
+static const float LOG_LN2_HI = 0x1.62e430p-1f;    /* ln 2 rounded to binary32 */
+static const float LOG_LN2_LO = -0x1.05c610p-29f;  /* ln 2 - LOG_LN2_HI, rounded */
+static const float LOG_C[6] = {0x1.555556p-2f, 0x1.99999ap-3f, 0x1.24924ap-3f,
+                               0x1.c71c72p-4f, 0x1.745d18p-4f, 0x1.3b13b2p-4f}; /* 1/3 .. 1/13 */
+
+extern "C" float orc_logdef(float x) {
+  uint32_t bits;
+  memcpy(&bits, &x, 4);
+  int e = (int)(bits >> 23) - 127;
+  const uint32_t mb = (bits & 0x7fffffu) | 0x3f800000u;
+  float m;
+  memcpy(&m, &mb, 4);
+  if (m > LOG_SQRT2) { m = m * 0.5f; e += 1; }
+  const float f = m - 1.0f;
+  const float s = f / (2.0f + f);
+  const float w = s * s;
+  float r = LOG_C[5];
+  for (int k = 4; k >= 0; --k) r = fmaf(r, w, LOG_C[k]);
+  r = r * w;
+  const float s2 = s + s;
+  const float l1p = fmaf(s2, r, s2);
+  const float ef = (float)e;
+  return fmaf(ef, LOG_LN2_HI, fmaf(ef, LOG_LN2_LO, l1p));
+}
+
+extern "C" void orc_logdef_n(const float *x, float *y, size_t n) {
+  for (size_t i = 0; i < n; ++i) y[i] = orc_logdef(x[i]);
+}
+
+/* Gumbel noise of vocabulary entry i at RNG counter pos (reading of the pages'
+ * Gumbel-max sampling, made bit-reproducible): Philox4x32-10 with key (seed lo,
+ * seed hi) and counter (pos, i, 1, 0) gives x0; u = (2 (x0 >> 9) + 1) 2^-24, a
+ * binary32 value strictly inside (0, 1); g = -L(-L(u)). */
+extern "C" float orc_gumbel_noise(uint64_t seed, int32_t pos, int32_t i) {
+  const uint32_t ctr[4] = {(uint32_t)pos, (uint32_t)i, 1u, 0u};
+  const uint32_t key[2] = {(uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+  uint32_t x[4];
+  orc_philox4x32_10(ctr, key, x);
+  const float u = (float)(2u * (x[0] >> 9) + 1u) * 0x1.0p-24f;
+  return -orc_logdef(-orc_logdef(u));
+}
+
+/* Gumbel-max sampling ("KOG LaneFormer-2B & the monokernel", "The fused
+ * operations, briefly"): the token is argmax_i (z_i + g_i) with z_i = logit_i *
+ * (float)(1/T) and g_i the noise above, the lowest index among equal maxima.
+ * The sum is one binary32 addition.  Returns -1 for n <= 0; T <= 0 is greedy. */
+extern "C" int32_t orc_sample_gumbel(const float *logits, int32_t n, float temperature, uint64_t seed,
+                                     int32_t pos) {
+  if (n <= 0) return -1;
+  if (!(temperature > 0.0f)) return orc_argmax(logits, n);
+  const float invT = (float)(1.0 / (double)temperature);
+  int32_t best = 0;
+  float bv = -INFINITY;
+  for (int32_t i = 0; i < n; ++i) {
+    const float y = logits[i] * invT + orc_gumbel_noise(seed, pos, i);
+    if (y > bv) { bv = y; best = i; }
+  }
+  return best;
+}
+
 extern "C" int orc_generate(const orc_config *c, const orc_weights *w, uint16_t *kcache,
                             uint16_t *vcache, int32_t token, int32_t pos, int32_t n,
                             float temperature, float top_p, uint64_t seed, int32_t *out,

@@ -91,6 +91,11 @@ float    orc_expdef(float x);                                  /* defined exp, x
 void     orc_expdef_constants(float out[11]);
 void     orc_expdef_n(const float *x, float *y, size_t n);
 void     orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+float    orc_logdef(float x);                                  /* defined ln, x > 0 normal */
+void     orc_logdef_n(const float *x, float *y, size_t n);
+float    orc_gumbel_noise(uint64_t seed, int32_t pos, int32_t i);  /* -L(-L(u_i)) */
+int32_t  orc_sample_gumbel(const float *logits, int32_t n, float temperature, uint64_t seed,
+                           int32_t pos);                       /* argmax(z + g) */
 /* temperature == 0 -> argmax; else nucleus sampling keyed by (seed, pos). */
 int32_t  orc_sample(const float *logits, int32_t n, float temperature, float top_p,
                     uint64_t seed, int32_t pos);

@@ -8,6 +8,11 @@
 * The nucleus draw equals a brute-force re-derivation with Python integers on
   tiny vocabularies; top-p -> 0 reduces to argmax; with T = 1 and top-p = 1 the
   draws follow softmax(logits) (chi-square test).
+* The defined log L is within two ulps of fp64 log over the inputs the Gumbel
+  noise feeds it; the noise follows the standard Gumbel law (Kolmogorov-Smirnov
+  against exp(-exp(-g))); Gumbel-max equals a brute-force re-derivation from
+  Philox words and fp64 logs on tiny vocabularies, reduces to argmax for large
+  logit gaps and T = 0, and its draws follow softmax(logits / T) (chi-square).
 """
 import math
 import os
@@ -153,5 +158,90 @@ def test_draws_follow_softmax(orc):
     counts = np.zeros(len(logits))
     for pos in range(N):
         counts[orc.sample(logits, 1.0, 1.0, 42, pos)] += 1
+    chi2 = float(((counts - N * p) ** 2 / (N * p)).sum())
+    assert chi2 < 30.0, (chi2, counts / N, p)        # 7 dof: P(chi2 > 30) ~ 1e-4
+
+
+# ---------------------------------------------------------------- Gumbel-max
+
+def test_logdef_within_two_ulp_of_log(orc):
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        (2 * np.arange(0, 2 ** 23, 97, dtype=np.float64) + 1) * 2.0 ** -24,    # the u grid
+        np.linspace(1e-7, 17.0, 400_001),                                     # -L(u) range
+        rng.random(200_000) * 2.0 ** rng.integers(-126, 127, 200_000),        # all exponents
+        2.0 ** np.arange(-126, 128, dtype=np.float64),
+        [1.0, 1.0 - 2.0 ** -24, 1.0 + 2.0 ** -23, float.fromhex("0x1.6a09e6p+0"), float.fromhex("0x1.6a09e8p+0"), 0.5, 2.0]])
+    x = x.astype(np.float32)
+    x = x[(x > 0) & np.isfinite(x) & (x >= np.float32(2.0 ** -126))]
+    y = orc.logdef(x).astype(np.float64)
+    ref = np.log(x.astype(np.float64))
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    ulp = np.maximum(ulp, np.float64(2.0 ** -149))
+    err = np.abs(y - ref) / ulp
+    assert err.max() <= 2.0, (err.max(), x[np.argmax(err)])
+    assert orc.logdef([1.0])[0] == 0.0
+
+
+def test_gumbel_noise_follows_gumbel_law(orc):
+    """Kolmogorov-Smirnov: 2*10^5 noise values against F(g) = exp(-exp(-g))."""
+    g = np.array([orc.gumbel_noise(99, pos, i) for pos in range(2000) for i in range(100)])
+    assert np.isfinite(g).all()
+    g.sort()
+    n = g.size
+    F = np.exp(-np.exp(-g))
+    ks = max(np.max(np.arange(1, n + 1) / n - F), np.max(F - np.arange(n) / n))
+    assert ks < 1.95 / math.sqrt(n), ks            # P(D > 1.95/sqrt(n)) ~ 1e-3
+    assert abs(g.mean() - 0.5772156649) < 0.01      # Euler-Mascheroni constant
+
+
+def _gumbel_brute(orc, logits, T, seed, pos):
+    """argmax(z + g) with g from the Philox words and fp64 logs; also the gap
+    between the two largest scores."""
+    key = np.uint32([seed & 0xFFFFFFFF, seed >> 32])
+    invT = np.float32(1.0 / T)
+    y = []
+    for i, l in enumerate(logits):
+        x0 = int(orc.philox4x32_10(np.uint32([pos, i, 1, 0]), key)[0])
+        u = (2 * (x0 >> 9) + 1) * 2.0 ** -24
+        y.append(float(np.float32(l) * invT) - math.log(-math.log(u)))
+    y = np.array(y)
+    top = np.sort(y)[-2:]
+    return int(np.argmax(y)), (top[1] - top[0]) if len(y) > 1 else math.inf
+
+
+def test_gumbel_brute_force_tiny_vocab(orc):
+    rng = np.random.default_rng(8)
+    checked = 0
+    for case in range(300):
+        V = int(rng.integers(1, 12))
+        logits = (rng.standard_normal(V) * 2).astype(np.float32)
+        T, seed, pos = float(rng.choice([0.5, 0.8, 1.0, 1.7])), int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 31))
+        tok = orc.sample_gumbel(logits, T, seed, pos)
+        ref, gap = _gumbel_brute(orc, logits, T, seed, pos)
+        if gap > 1e-4:
+            assert tok == ref, (case, tok, ref, gap)
+            checked += 1
+    assert checked > 250
+
+
+def test_gumbel_greedy_limits(orc):
+    logits = np.float32([0.0, 3.0, -1.0, 2.5])
+    assert all(orc.sample_gumbel(logits, 0.0, 7, pos) == 1 for pos in range(50))
+    logits = np.float32([0.0, 100.0, -1.0, 2.5])   # gap beyond any noise difference (< 40)
+    assert all(orc.sample_gumbel(logits, 1.0, 7, pos) == 1 for pos in range(500))
+    assert orc.sample_gumbel(np.float32([]), 1.0, 7, 0) == -1
+
+
+def test_gumbel_draws_follow_softmax(orc):
+    """T = 0.7: frequencies over 10^5 counters match softmax(logits / T) (chi-square)."""
+    logits = np.float32([1.0, 0.0, -0.5, 2.0, 0.25, -3.0, 1.5, 0.9])
+    z = logits.astype(np.float64) * float(np.float32(1.0 / 0.7))
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    N = 100_000
+    counts = np.zeros(len(logits))
+    for pos in range(N):
+        counts[orc.sample_gumbel(logits, 0.7, 42, pos)] += 1
     chi2 = float(((counts - N * p) ** 2 / (N * p)).sum())
     assert chi2 < 30.0, (chi2, counts / N, p)        # 7 dof: P(chi2 > 30) ~ 1e-4
