@@ -47,6 +47,16 @@ enum {
 #define LF_HIDDEN_IO 1u  /* no embedding / lm_head: the layers run on a hidden vector
                             set with lf_set_hidden and read with lf_get_hidden */
 #define LF_STATS 4u      /* record per-workgroup wait time (lf_get_stats) */
+#define LF_GUMBEL 8u     /* with temperature > 0: Gumbel-max sampling instead of the
+                            nucleus (top_p unused).  "KOG LaneFormer-2B & the
+                            monokernel", "The fused operations, briefly": the token
+                            is argmax_i(logit_i / T + g_i), g_i = -ln(-ln u_i),
+                            u_i = (2 (x0 >> 9) + 1) 2^-24 from the first word of
+                            the Philox4x32-10 block with key (seed lo, seed hi) and
+                            counter (pos, i, 1, 0); ln is the library's defined
+                            logarithm (lf_test_logdef); lowest index on ties.  Each
+                            lm_head workgroup publishes its best score, so no
+                            workgroup reads the whole logit vector. */
 
 typedef struct lf_state lf_state;
 
@@ -54,10 +64,10 @@ typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_seq;
   float rms_eps;       /* RMSNorm epsilon, inside the square root (1e-5) */
   float rope_base;     /* rotary base (10000) */
-  float temperature;   /* 0: greedy argmax; > 0: nucleus sampling */
-  float top_p;         /* nucleus mass fraction in (0, 1] when temperature > 0 */
+  float temperature;   /* 0: greedy argmax; > 0: nucleus (or, with LF_GUMBEL, Gumbel-max) sampling */
+  float top_p;         /* nucleus mass fraction in (0, 1] when temperature > 0 (not LF_GUMBEL) */
   uint64_t seed;       /* Philox4x32-10 key of the sampler */
-  uint32_t flags;      /* LF_HIDDEN_IO | LF_STATS */
+  uint32_t flags;      /* LF_HIDDEN_IO | LF_STATS | LF_GUMBEL */
 } lf_config;
 
 /* One layer's weights: fp16 device pointers, row-major [out][in]:
@@ -151,6 +161,15 @@ int lf_query(const lf_state *st, int32_t what);
  * from logits_dev[c*n .. c*n+n) with (temperature, top_p, seed) and RNG counter
  * pos_dev[c]; tokens_dev[c] receives it. */
 int lf_test_expdef(const float *x_dev, float *y_dev, int64_t n, void *stream);
+/* lf_test_logdef: y[i] = L(x[i]), the library's defined natural logarithm, for
+ * positive normal x (the Gumbel noise's only use; other inputs are not defined).
+ * lf_test_sample_gumbel: for each case c < m, the LF_GUMBEL token of
+ * logits_dev[c*n .. c*n+n) at temperature T and RNG counter pos_dev[c].
+ * All return LF_EINVAL on NULL pointers, n < 1 or T <= 0, LF_EHIP on a HIP error,
+ * and wait for the stream. */
+int lf_test_logdef(const float *x_dev, float *y_dev, int64_t n, void *stream);
+int lf_test_sample_gumbel(const float *logits_dev, int32_t n, float temperature, uint64_t seed,
+                          const int32_t *pos_dev, int32_t m, int32_t *tokens_dev, void *stream);
 int lf_test_sample(const float *logits_dev, int32_t n, float temperature, float top_p,
                    uint64_t seed, const int32_t *pos_dev, int32_t m, int32_t *tokens_dev,
                    void *stream);

@@ -86,8 +86,9 @@ int validate(const lf_config *c) {
     return fail(nullptr, LF_EINVAL, "vocab must be even and at least 2");
   if (!(c->rms_eps >= 0.0f) || !(c->rope_base > 0.0f)) return fail(nullptr, LF_EINVAL, "bad rms_eps or rope_base");
   if (!(c->temperature >= 0.0f)) return fail(nullptr, LF_EINVAL, "temperature must be >= 0");
-  if (c->temperature > 0.0f && !(c->top_p > 0.0f)) return fail(nullptr, LF_EINVAL, "top_p must be > 0");
-  if (c->flags & ~(LF_HIDDEN_IO | LF_STATS)) return fail(nullptr, LF_EINVAL, "unknown flag bits");
+  if (c->temperature > 0.0f && !(c->flags & LF_GUMBEL) && !(c->top_p > 0.0f))
+    return fail(nullptr, LF_EINVAL, "top_p must be > 0");
+  if (c->flags & ~(LF_HIDDEN_IO | LF_STATS | LF_GUMBEL)) return fail(nullptr, LF_EINVAL, "unknown flag bits");
   return LF_OK;
 }
 
@@ -202,7 +203,9 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.max_seq = c.max_seq; P.G = G; P.qpg = Hq / Hkv; P.nqkv = (Hq + 2 * Hkv) * dh;
   P.eps = c.rms_eps;
   P.inv_sqrt_dh = 1.0f / std::sqrt((float)dh);
-  P.sampling = (!hidden && c.temperature > 0.0f) ? 1 : 0;
+  P.sampling = (hidden || !(c.temperature > 0.0f)) ? lf::SAMPLE_GREEDY
+               : (c.flags & LF_GUMBEL)              ? lf::SAMPLE_GUMBEL
+                                                    : lf::SAMPLE_NUCLEUS;
   P.inv_temp = P.sampling ? (float)(1.0 / (double)c.temperature) : 0.0f;
   P.top_p = c.top_p;
   P.seed = c.seed;
@@ -575,6 +578,25 @@ int lf_test_expdef(const float *x, float *y, int64_t n, void *stream) {
   hipError_t e = lf::launch_test_expdef(x, y, n, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   return e == hipSuccess ? LF_OK : hip_fail(nullptr, e, "lf_test_expdef");
+}
+
+int lf_test_logdef(const float *x, float *y, int64_t n, void *stream) {
+  if ((!x || !y) && n > 0) return fail(nullptr, LF_EINVAL, "NULL argument");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = lf::launch_test_logdef(x, y, n, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? LF_OK : hip_fail(nullptr, e, "lf_test_logdef");
+}
+
+int lf_test_sample_gumbel(const float *logits, int32_t n, float temperature, uint64_t seed, const int32_t *pos,
+                          int32_t m, int32_t *tokens, void *stream) {
+  if (!logits || !pos || !tokens || n < 1 || m < 0) return fail(nullptr, LF_EINVAL, "bad argument");
+  if (!(temperature > 0.0f)) return fail(nullptr, LF_EINVAL, "temperature must be > 0");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const float inv_temp = (float)(1.0 / (double)temperature);
+  hipError_t e = lf::launch_test_gumbel(logits, n, inv_temp, seed, pos, m, tokens, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? LF_OK : hip_fail(nullptr, e, "lf_test_sample_gumbel");
 }
 
 int lf_test_sample(const float *logits, int32_t n, float temperature, float top_p, uint64_t seed,

@@ -42,13 +42,17 @@ enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYE
 // starts at wbase + l * layer_stride.
 enum LayerPart { LW_QKV = 0, LW_O, LW_GU, LW_D, LW_COUNT };
 
+// Next-token choice: argmax, nucleus draw by workgroup 0, or Gumbel-max (every
+// lm_head workgroup publishes its best noised score, workgroup 0 reduces them).
+enum SampleMode { SAMPLE_GREEDY = 0, SAMPLE_NUCLEUS = 1, SAMPLE_GUMBEL = 2 };
+
 struct Params {
   // shape
   int L, d, Hq, Hkv, dh, F, V, max_seq, G, qpg, nqkv;
   float eps, inv_sqrt_dh, inv_temp, top_p;
   unsigned long long seed;
   unsigned flags;
-  int hidden_io, sampling;
+  int hidden_io, sampling;   // sampling: a SampleMode
   int levels_per_token;
   // weights (library-owned, packed)
   // Per layer: Wqkv [(Hq+2Hkv)*dh][d] (q/k rows pair-interleaved per head:
@@ -102,6 +106,9 @@ hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream);
 // elements (cols % 8 == 0, w 16-byte aligned, g 2-byte aligned).
 hipError_t launch_scale_columns(void *w, size_t rows, int cols, const void *g, hipStream_t stream);
 hipError_t launch_test_expdef(const float *x, float *y, int64_t n, hipStream_t stream);
+hipError_t launch_test_logdef(const float *x, float *y, int64_t n, hipStream_t stream);
+hipError_t launch_test_gumbel(const float *logits, int n, float inv_temp, unsigned long long seed, const int *pos,
+                              int m, int *tokens, hipStream_t stream);
 hipError_t launch_test_sample(const float *logits, int n, float inv_temp, float top_p,
                               unsigned long long seed, const int *pos, int m, int *tokens,
                               hipStream_t stream);

@@ -1413,6 +1413,57 @@ __device__ __forceinline__ void philox4x32_10(unsigned c[4], unsigned k0, unsign
   }
 }
 
+// Defined natural logarithm of a positive normal x, the same bits on any
+// IEEE-754 machine (each step one correctly rounded operation or one fma):
+// x = m 2^e with m in [sqrt(1/2), sqrt(2)), f = m - 1 (exact), s = f / (2 + f),
+// ln(1 + f) = 2 atanh(s) = 2s + 2s (w/3 + w^2/5 + ... + w^6/13) with w = s^2,
+// plus e ln 2 split into a binary32 high part and the rounded remainder.
+__device__ __forceinline__ float logdef(float x) {
+#pragma clang fp contract(off)
+  const unsigned bits = __float_as_uint(x);
+  int e = (int)(bits >> 23) - 127;
+  float m = __uint_as_float((bits & 0x7fffffu) | 0x3f800000u);
+  if (m > 0x1.6a09e6p+0f) {
+    m = m * 0.5f;
+    e += 1;
+  }
+  const float f = m - 1.0f;
+  const float s = __fdiv_rn(f, 2.0f + f);
+  const float w = s * s;
+  float r = 0x1.3b13b2p-4f;                  // 1/13
+  r = __builtin_fmaf(r, w, 0x1.745d18p-4f);  // 1/11
+  r = __builtin_fmaf(r, w, 0x1.c71c72p-4f);  // 1/9
+  r = __builtin_fmaf(r, w, 0x1.24924ap-3f);  // 1/7
+  r = __builtin_fmaf(r, w, 0x1.99999ap-3f);  // 1/5
+  r = __builtin_fmaf(r, w, 0x1.555556p-2f);  // 1/3
+  r = r * w;
+  const float s2 = s + s;
+  const float ef = (float)e;
+  return __builtin_fmaf(ef, 0x1.62e430p-1f, __builtin_fmaf(ef, -0x1.05c610p-29f, __builtin_fmaf(s2, r, s2)));
+}
+
+// Gumbel noise of vocabulary entry i at RNG counter pos: the first word x0 of
+// the Philox4x32-10 block with counter (pos, i, 1, 0) (the nucleus draw uses
+// (pos, 0, 0, 0)), u = (2 (x0 >> 9) + 1) 2^-24 strictly inside (0, 1) and exact
+// in binary32, g = -ln(-ln u) with the defined logarithm.
+__device__ __forceinline__ float gumbel_noise(unsigned long long seed, int pos, int i) {
+  unsigned c[4] = {(unsigned)pos, (unsigned)i, 1u, 0u};
+  philox4x32_10(c, (unsigned)(seed & 0xffffffffull), (unsigned)(seed >> 32));
+  const float u = (float)(2u * (c[0] >> 9) + 1u) * 0x1.0p-24f;
+  return -logdef(-logdef(u));
+}
+
+// Gumbel-max score of one logit ("KOG LaneFormer-2B & the monokernel", "The
+// fused operations, briefly"): z + g with z = logit * (1/T), one rounded
+// product and one rounded sum.  The token is the argmax of the scores (lowest
+// index among equal maxima): a draw from softmax(z) without normalising it.
+__device__ __forceinline__ float gumbel_score(float logit, float inv_temp, unsigned long long seed, int pos,
+                                              int i) {
+#pragma clang fp contract(off)
+  const float z = logit * inv_temp;
+  return z + gumbel_noise(seed, pos, i);
+}
+
 // Plain loads: the caller has taken an agent-scope acquire fence after the
 // logits were published, so this XCD's caches hold no stale copy of them, and
 // the sampler's repeated passes then hit in L2.
@@ -1699,7 +1750,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part,
                           stage_spec(P, ctl, K_LM, t, L, 0, lv0 + (unsigned)(L * PH_PER_LAYER), xown, xres)))
           return;
-        if (b == 0 && P.sampling) {
+        if (b == 0 && P.sampling == SAMPLE_NUCLEUS) {
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
           if (lds_ld(&ctl->abort)) return;
           if (!wait_all_waves(sy, 0, G, lvl_lm, true)) return;
@@ -1970,10 +2021,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       trace(P, t, 5 * L, 1);
       float best = -INFINITY;
       int bi = 0x7fffffff;
+      const bool gumbel = P.sampling == SAMPLE_GUMBEL;
       for (int i = lane; i < ge.nrows; i += 64) {
         const float y = row_value(pk, i) * inv;
         st_dev(&P.logits[ge.r0 + i], y);
-        if (y > best || (y == best && ge.r0 + i < bi)) { best = y; bi = ge.r0 + i; }
+        // Gumbel-max: this workgroup's best score z + g instead of its best logit
+        const float sc = gumbel ? gumbel_score(y, P.inv_temp, P.seed, pos, ge.r0 + i) : y;
+        if (sc > best || (sc == best && ge.r0 + i < bi)) { best = sc; bi = ge.r0 + i; }
       }
       wave_argmax(best, bi);
       if (lane == 0) {
@@ -1987,7 +2041,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     // ---------------- next token (workgroup 0)
     if (b == 0) {
       int tok;
-      if (P.sampling) {
+      if (P.sampling == SAMPLE_NUCLEUS) {
         if (!wait_all_waves(sy, 0, G, lvl_lm, true)) { fail(); return; }
         tok = sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds));
       } else {
@@ -2047,6 +2101,39 @@ __global__ void __launch_bounds__(kThreads) lf_test_sample_kernel(const float *l
   if (threadIdx.x == 0) tokens[c] = tok;
 }
 
+__global__ void lf_test_logdef_kernel(const float *x, float *y, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    y[i] = logdef(x[i]);
+}
+
+// One case per workgroup: the Gumbel-max token of logits[c*n .. c*n+n) at
+// counter pos[c], from the same score function as the decode kernel.
+__global__ void __launch_bounds__(kThreads) lf_test_gumbel_kernel(const float *logits, int n, float inv_temp,
+                                                                 unsigned long long seed, const int *pos,
+                                                                 int *tokens) {
+  __shared__ float wbest[kWaves];
+  __shared__ int wbi[kWaves];
+  const int c = blockIdx.x;
+  const float *lg = logits + (size_t)c * n;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const float sc = gumbel_score(lg[i], inv_temp, seed, pos[c], i);
+    if (sc > best || (sc == best && i < bi)) { best = sc; bi = i; }
+  }
+  wave_argmax(best, bi);
+  if (lane_id() == 0) {
+    wbest[wave_id()] = best;
+    wbi[wave_id()] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWaves; ++w)
+      if (wbest[w] > best || (wbest[w] == best && wbi[w] < bi)) { best = wbest[w]; bi = wbi[w]; }
+    tokens[c] = bi;
+  }
+}
+
 // Weight packing: scale every column of an fp16 matrix (rows x 8*cols8,
 // 16-byte aligned) by the fp16 gain of that column (any 2-byte alignment),
 // eight elements per thread.
@@ -2094,6 +2181,22 @@ hipError_t launch_test_expdef(const float *x, float *y, int64_t n, hipStream_t s
   long long blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(lf_test_expdef_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, (long long)n);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_logdef(const float *x, float *y, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(lf_test_logdef_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, (long long)n);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_gumbel(const float *logits, int n, float inv_temp, unsigned long long seed, const int *pos,
+                              int m, int *tokens, hipStream_t stream) {
+  if (m <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lf_test_gumbel_kernel, dim3(m), dim3(kThreads), 0, stream, logits, n, inv_temp, seed, pos,
+                     tokens);
   return hipGetLastError();
 }
 

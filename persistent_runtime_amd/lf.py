@@ -18,14 +18,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("LF_LIB") or os.path.join(HERE, "liblf.so")
 
 LF_OK, LF_EINVAL, LF_ENOMEM, LF_EHIP, LF_ERANGE, LF_ETIMEOUT, LF_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-LF_HIDDEN_IO, LF_STATS = 1, 4
+LF_HIDDEN_IO, LF_STATS, LF_GUMBEL = 1, 4, 8
 LF_Q_GRID, LF_Q_THREADS, LF_Q_LDS_BYTES = 0, 1, 2
 LAYER_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 
 # every symbol include/lf.h declares
 EXPORTS = ("lf_model_create", "lf_model_destroy", "lf_decode_step", "lf_generate", "lf_prefill", "lf_set_position",
            "lf_last_error", "lf_get_logits", "lf_kv_fill", "lf_kv_read", "lf_set_hidden", "lf_get_hidden",
-           "lf_get_stats", "lf_query", "lf_test_expdef", "lf_test_sample")
+           "lf_get_stats", "lf_query", "lf_test_expdef", "lf_test_sample",
+           "lf_test_logdef", "lf_test_sample_gumbel")
 
 
 class LfError(RuntimeError):
@@ -79,6 +80,8 @@ def lib():
         L.lf_query.argtypes = [P, I32]
         L.lf_test_expdef.argtypes = [P, P, C.c_int64, P]
         L.lf_test_sample.argtypes = [P, I32, C.c_float, C.c_float, U64, P, I32, P, P]
+        L.lf_test_logdef.argtypes = [P, P, C.c_int64, P]
+        L.lf_test_sample_gumbel.argtypes = [P, I32, C.c_float, U64, P, I32, P, P]
         _lib = L
     return _lib
 
@@ -99,7 +102,8 @@ def make_config(cfg: dict, flags: int = 0) -> LfConfig:
     return LfConfig(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
                     cfg["ffn_dim"], cfg.get("vocab", 0), cfg["max_seq"], cfg.get("rms_eps", 1e-5),
                     cfg.get("rope_base", 10000.0), cfg.get("temperature", 0.0), cfg.get("top_p", 1.0),
-                    cfg.get("seed", 1234), flags | (LF_HIDDEN_IO if cfg.get("vocab", 0) == 0 else 0))
+                    cfg.get("seed", 1234), flags | (LF_HIDDEN_IO if cfg.get("vocab", 0) == 0 else 0)
+                    | (LF_GUMBEL if cfg.get("sampler", "nucleus") == "gumbel" else 0))
 
 
 def upload_weights(weights: dict, device="cuda") -> dict:
@@ -217,4 +221,22 @@ def test_sample(logits, temperature: float, top_p: float, seed: int, pos):
     tokens = torch.empty(m, dtype=torch.int32, device=logits.device)
     _check(lib().lf_test_sample(logits.data_ptr(), n, temperature, top_p, seed, pos.data_ptr(), m,
                                 tokens.data_ptr(), _stream_handle(None)))
+    return tokens
+
+
+def test_logdef(x):
+    """Defined natural logarithm on the GPU (test hook); x: positive fp32 cuda tensor."""
+    import torch
+    y = torch.empty_like(x)
+    _check(lib().lf_test_logdef(x.data_ptr(), y.data_ptr(), x.numel(), _stream_handle(None)))
+    return y
+
+
+def test_sample_gumbel(logits, temperature: float, seed: int, pos):
+    """In-kernel Gumbel-max choice on m cases (test hook): logits [m, n] fp32 cuda, pos [m] int32 cuda."""
+    import torch
+    m, n = logits.shape
+    tokens = torch.empty(m, dtype=torch.int32, device=logits.device)
+    _check(lib().lf_test_sample_gumbel(logits.data_ptr(), n, temperature, seed, pos.data_ptr(), m,
+                                       tokens.data_ptr(), _stream_handle(None)))
     return tokens

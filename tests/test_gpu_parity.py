@@ -94,6 +94,39 @@ def test_sampler_bit_exact_against_oracle(lf, orc, V, scale, top_p, T):
         assert tok[c] == orc.sample(logits[c], T, top_p, 1234, int(pos[c])), c
 
 
+def test_logdef_bit_exact_against_oracle(lf, orc):
+    import torch
+    # every 37th binary32 from the smallest normal up to 17 (the Gumbel noise's
+    # inputs lie in [2^-24, 1) and (0, 16.7]), plus edges: ~29M values
+    lo, hi = np.float32(2.0 ** -126).view(np.uint32), np.float32(17.0).view(np.uint32)
+    bits = np.arange(lo, hi + 1, 37, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([bits.view(np.float32),
+                        np.float32([1.0, 2.0 ** -24, 1.0 - 2.0 ** -24, 0.5, 2.0, 1.4142135, 1.4142137])])
+    y_gpu = lf.test_logdef(torch.from_numpy(x).cuda()).cpu().numpy()
+    y_cpu = orc.logdef(x)
+    assert np.array_equal(y_gpu.view(np.uint32), y_cpu.view(np.uint32))
+
+
+@pytest.mark.parametrize("V,scale,T", [(32768, 1.0, 0.8), (32768, 4.0, 1.0), (128256, 1.0, 0.7),
+                                       (37, 2.0, 1.3), (2, 1.0, 0.8), (1000, 0.05, 0.25)])
+def test_gumbel_sampler_bit_exact_against_oracle(lf, orc, V, scale, T):
+    import torch
+    rng = np.random.default_rng(V + int(scale * 100))
+    m = 24
+    logits = (rng.standard_normal((m, V)) * scale).astype(np.float32)
+    logits[1] = np.round(logits[1])                  # many exact ties
+    logits[2] = 0.0                                   # all equal: the noise alone decides
+    logits[3, :] = -40.0
+    logits[3, V // 2] = 0.0                           # one token far ahead
+    pos = np.concatenate([np.arange(16384, 16384 + m - 2), [0, 2 ** 31 - 1]]).astype(np.int32)
+    seed = 0x9E3779B97F4A7C15
+    tok = lf.test_sample_gumbel(torch.from_numpy(logits).cuda(), T, seed,
+                                torch.from_numpy(pos).cuda()).cpu().numpy()
+    for c in range(m):
+        assert tok[c] == orc.sample_gumbel(logits[c], T, seed, int(pos[c])), c
+    assert tok[3] == V // 2
+
+
 # ---------------------------------------------------------------- tiny decoder
 
 @pytest.fixture(scope="module")
@@ -185,6 +218,27 @@ def test_sampling_model_tokens_match_oracle_sampler(lf, orc, tiny):
         logits = eng.logits().cpu().numpy()
         assert nxt == orc.sample(logits, 0.8, 0.9, 1234, pos)
         tok, pos = nxt, pos + 1
+
+
+def test_gumbel_model_tokens_match_oracle_sampler(lf, orc, tiny):
+    """Gumbel-max in the decode kernel (each lm_head workgroup publishes its best
+    noised score): for the GPU's own logits and counters the oracle's Gumbel-max
+    picks the same token at every step, stepwise and in one multi-token launch."""
+    cfg, w = tiny
+    cfg = dict(cfg, temperature=0.8, top_p=0.0, seed=987654321, sampler="gumbel")
+    dw = lf.upload_weights(w)
+    eng = lf.Engine(cfg, dw)
+    tok, pos, steps = 7, 0, []
+    for _ in range(20):
+        nxt = eng.decode_step(tok, pos)
+        logits = eng.logits().cpu().numpy()
+        assert nxt == orc.sample_gumbel(logits, 0.8, 987654321, pos), pos
+        steps.append(nxt)
+        tok, pos = nxt, pos + 1
+    other = lf.Engine(cfg, dw)
+    other.decode_step(7, 0)
+    assert list(other.generate(19)) == steps[1:]
+    del dw
 
 
 # ---------------------------------------------------------------- edges
@@ -343,6 +397,25 @@ def test_dec2b_long_context_sampling(lf, orc, dec2b):
         ok, err = close(got, ref)
         assert ok, (pos, err)
         assert nxt == orc.sample(got, 0.8, 0.9, 1234, pos)
+        tok = nxt
+
+
+def test_dec2b_gumbel_sampling(lf, orc, dec2b):
+    """The ~2.2B decoder with Gumbel-max sampling (V = 32000 over 256 lm_head
+    workgroups): GPU logits within tolerance of the oracle's, and the sampled
+    token equals the oracle's Gumbel-max on the GPU's own logits."""
+    cfg, w = dec2b
+    cfg = dict(cfg, temperature=0.8, sampler="gumbel", seed=4242)
+    orc.set_threads(min(16, os.cpu_count() or 1))
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    m = orc.Model(cfg, w)
+    tok = int(synth.prompt(cfg, 1)[0])
+    for pos in range(4):
+        nxt = eng.decode_step(tok, pos)
+        got = eng.logits().cpu().numpy()
+        ok, err = close(got, m.decode_step(tok, pos))
+        assert ok, (pos, err)
+        assert nxt == orc.sample_gumbel(got, 0.8, 4242, pos), pos
         tok = nxt
 
 
