@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "liblf_oracle.so")
 class OrcConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "d_model", "n_heads", "n_kv_heads",
                                          "head_dim", "ffn_dim", "vocab", "max_seq")] + \
-               [("rms_eps", C.c_float), ("rope_base", C.c_float)]
+               [("rms_eps", C.c_float), ("rope_base", C.c_float), ("sliding_window", C.c_int32),
+                ("reserved", C.c_int32), ("window_layers", C.c_uint64)]
 
 
 _LAYER_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
@@ -57,10 +58,10 @@ def lib():
         L.orc_gemv.argtypes = [P, P, C.c_int32, C.c_int32, P]
         L.orc_rmsnorm.argtypes = [P, P, C.c_int32, C.c_float, P]
         L.orc_rope.argtypes = [P, C.c_int32, C.c_int32, C.c_float]
-        L.orc_attention.argtypes = [P, P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, P]
+        L.orc_attention.argtypes = [P, P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, P]
         L.orc_silu.restype = C.c_float
         L.orc_silu.argtypes = [C.c_float]
-        L.orc_layer_forward.argtypes = [P, P, P, P, P, C.c_int32]
+        L.orc_layer_forward.argtypes = [P, P, P, P, P, C.c_int32, C.c_int32]
         L.orc_decode_step.argtypes = [P, P, P, P, C.c_int32, C.c_int32, P]
         L.orc_forward_nocache.argtypes = [P, P, P, C.c_int32, P]
         L.orc_argmax.restype = C.c_int32
@@ -137,15 +138,16 @@ def rope(v: np.ndarray, pos: int, base: float = 10000.0) -> np.ndarray:
     return v
 
 
-def attention(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, pos: int) -> np.ndarray:
-    """q [Hq][dh] fp32; kc, vc [max_seq][Hkv][dh] fp16 (one layer)."""
+def attention(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, pos: int, window: int = 0) -> np.ndarray:
+    """q [Hq][dh] fp32; kc, vc [max_seq][Hkv][dh] fp16 (one layer); window > 0: the last
+    `window` positions only."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     kc = np.ascontiguousarray(kc, dtype=np.float16)
     vc = np.ascontiguousarray(vc, dtype=np.float16)
     hq, dh = q.shape
     hkv = kc.shape[1]
     o = np.empty_like(q)
-    lib().orc_attention(_p(q), _p(kc), _p(vc), pos, hq, hkv, dh, _p(o))
+    lib().orc_attention(_p(q), _p(kc), _p(vc), pos, hq, hkv, dh, window, _p(o))
     return o
 
 
@@ -220,7 +222,8 @@ def sample_detail(logits: np.ndarray, temperature: float, top_p: float, seed: in
 def _cfg_struct(cfg: dict) -> OrcConfig:
     return OrcConfig(cfg["n_layers"], cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"],
                      cfg["head_dim"], cfg["ffn_dim"], cfg.get("vocab", 0), cfg["max_seq"],
-                     cfg.get("rms_eps", 1e-5), cfg.get("rope_base", 10000.0))
+                     cfg.get("rms_eps", 1e-5), cfg.get("rope_base", 10000.0),
+                     cfg.get("sliding_window", 0), 0, cfg.get("window_layers", 0))
 
 
 class Model:
@@ -270,7 +273,8 @@ class Model:
     def layer_forward(self, layer: int, x: np.ndarray, pos: int) -> np.ndarray:
         x = np.array(x, dtype=np.float32, copy=True)
         rc = lib().orc_layer_forward(C.byref(self._c), C.byref(self._layers[layer]),
-                                     _p(self.kcache[layer]), _p(self.vcache[layer]), _p(x), int(pos))
+                                     _p(self.kcache[layer]), _p(self.vcache[layer]), _p(x), int(pos),
+                                     int(layer))
         if rc:
             raise ValueError(f"orc_layer_forward failed ({rc})")
         return x

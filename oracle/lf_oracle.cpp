@@ -129,15 +129,21 @@ extern "C" void orc_rope(float *v, int32_t dh, int32_t pos, float base) {
   }
 }
 
-/* Causal attention of one position over cache rows 0..pos.  Query head h uses
+/* Causal attention of one position over cache rows 0..pos, or with window > 0
+ * over the last `window` of them, rows max(0, pos - window + 1)..pos (sliding-
+ * window attention, "KOG LaneFormer-2B & the monokernel", "Pillar 1": it bounds
+ * the KV rows a step reads).  Query head h uses
  * KV head h / (n_heads / n_kv_heads) (contiguous groups).  Scores scaled by
  * 1/sqrt(dh), softmax with max subtraction, o = sum_j a_j v_j.  A split over
  * the sequence merged by online-softmax correction is the same quantity, so one
  * pass is used. */
 extern "C" void orc_attention(const float *q, const uint16_t *kc, const uint16_t *vc, int32_t pos,
-                              int32_t n_heads, int32_t n_kv_heads, int32_t dh, float *o) {
+                              int32_t n_heads, int32_t n_kv_heads, int32_t dh, int32_t window, float *o) {
   const int32_t group = n_heads / n_kv_heads;
-  const int32_t n = pos + 1;
+  const int32_t j_lo = window > 0 && pos + 1 > window ? pos + 1 - window : 0;
+  kc += (size_t)j_lo * n_kv_heads * dh;   /* the rows the window keeps, renumbered from 0 */
+  vc += (size_t)j_lo * n_kv_heads * dh;
+  const int32_t n = pos + 1 - j_lo;
   const float scale = 1.0f / sqrtf((float)dh);
   std::vector<float> s(n);
   for (int32_t h = 0; h < n_heads; ++h) {
@@ -172,8 +178,13 @@ static bool cfg_ok(const orc_config *c) {
 }
 
 /* One pre-norm decoder layer at position pos (Llama-2 lineage, "Pillar 1"). */
+extern "C" int32_t orc_layer_window(const orc_config *c, int32_t layer) {
+  const bool on = c->sliding_window > 0 && layer >= 0 && layer < 64 && ((c->window_layers >> layer) & 1u);
+  return on ? c->sliding_window : 0;
+}
+
 extern "C" int orc_layer_forward(const orc_config *c, const orc_layer *w, uint16_t *kc,
-                                 uint16_t *vc, float *x, int32_t pos) {
+                                 uint16_t *vc, float *x, int32_t pos, int32_t layer) {
   if (!cfg_ok(c) || !w || !kc || !vc || !x || pos < 0 || pos >= c->max_seq) return -1;
   const int32_t d = c->d_model, hq = c->n_heads, hkv = c->n_kv_heads, dh = c->head_dim,
                 f = c->ffn_dim;
@@ -187,7 +198,7 @@ extern "C" int orc_layer_forward(const orc_config *c, const orc_layer *w, uint16
   for (int32_t i = 0; i < hkv; ++i) orc_rope(k.data() + (size_t)i * dh, dh, pos, c->rope_base);
   uint16_t *krow = kc + (size_t)pos * hkv * dh, *vrow = vc + (size_t)pos * hkv * dh;
   for (int32_t i = 0; i < hkv * dh; ++i) { krow[i] = orc_f32_to_f16(k[i]); vrow[i] = orc_f32_to_f16(v[i]); }
-  orc_attention(q.data(), kc, vc, pos, hq, hkv, dh, o.data());
+  orc_attention(q.data(), kc, vc, pos, hq, hkv, dh, orc_layer_window(c, layer), o.data());
   orc_gemv(w->wo, o.data(), d, hq * dh, y.data());
   for (int32_t i = 0; i < d; ++i) x[i] = x[i] + y[i];
   orc_rmsnorm(x, w->ffn_norm, d, c->rms_eps, h.data());
@@ -209,7 +220,7 @@ extern "C" int orc_decode_step(const orc_config *c, const orc_weights *w, uint16
   orc_f16_to_f32_n(w->tok_emb + (size_t)token * d, x.data(), d);
   for (int32_t l = 0; l < c->n_layers; ++l) {
     int rc = orc_layer_forward(c, &w->layers[l], kcache + l * layer_stride,
-                               vcache + l * layer_stride, x.data(), pos);
+                               vcache + l * layer_stride, x.data(), pos, l);
     if (rc) return rc;
   }
   orc_rmsnorm(x.data(), w->final_norm, d, c->rms_eps, h.data());
@@ -251,23 +262,25 @@ extern "C" int orc_forward_nocache(const orc_config *c, const orc_weights *w, co
         vi[e] = orc_f16_to_f32(orc_f32_to_f16(vi[e]));
       }
     }
+    const int32_t win = orc_layer_window(c, l);
     for (int32_t i = 0; i < n; ++i) {
+      const int32_t jl = win > 0 && i + 1 > win ? i + 1 - win : 0;   /* first key in the window */
       for (int32_t t = 0; t < hq; ++t) {
         const int32_t gk = t / group;
         const float *qt = Q.data() + ((size_t)i * hq + t) * dh;
-        for (int32_t j = 0; j <= i; ++j) {
+        for (int32_t j = jl; j <= i; ++j) {
           const float *kj = Kf.data() + ((size_t)j * hkv + gk) * dh;
           float acc = 0.0f;
           for (int32_t e = 0; e < dh; ++e) acc += qt[e] * kj[e];
           s[j] = acc * scale;
         }
-        float m = s[0];
-        for (int32_t j = 1; j <= i; ++j) m = s[j] > m ? s[j] : m;
+        float m = s[jl];
+        for (int32_t j = jl + 1; j <= i; ++j) m = s[j] > m ? s[j] : m;
         float lsum = 0.0f;
-        for (int32_t j = 0; j <= i; ++j) { s[j] = expf(s[j] - m); lsum += s[j]; }
+        for (int32_t j = jl; j <= i; ++j) { s[j] = expf(s[j] - m); lsum += s[j]; }
         float *ot = o.data() + (size_t)t * dh;
         for (int32_t e = 0; e < dh; ++e) ot[e] = 0.0f;
-        for (int32_t j = 0; j <= i; ++j) {
+        for (int32_t j = jl; j <= i; ++j) {
           const float p = s[j] / lsum;
           const float *vj = Vf.data() + ((size_t)j * hkv + gk) * dh;
           for (int32_t e = 0; e < dh; ++e) ot[e] += p * vj[e];

@@ -43,6 +43,9 @@ extern "C" {
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_seq;
   float rms_eps, rope_base;
+  int32_t sliding_window;   /* 0: every layer attends to all earlier positions */
+  int32_t reserved;
+  uint64_t window_layers;   /* bit l set: layer l attends to the last sliding_window positions */
 } orc_config;
 
 typedef struct {
@@ -66,16 +69,19 @@ void orc_gemv(const uint16_t *W, const float *x, int32_t rows, int32_t cols, flo
 void orc_rmsnorm(const float *x, const uint16_t *g, int32_t d, float eps, float *y);
 /* in-place rotate-half RoPE of one head vector of length dh at position pos */
 void orc_rope(float *v, int32_t dh, int32_t pos, float base);
-/* attention of n_heads query heads at position pos over cache rows 0..pos of one layer.
+/* attention of n_heads query heads at position pos over cache rows 0..pos of one layer
+ * (rows pos-window+1..pos when window > 0).
  * q: [n_heads][dh] fp32; kc, vc: layer base of the cache [max_seq][n_kv][dh]; o: [n_heads][dh]. */
 void orc_attention(const float *q, const uint16_t *kc, const uint16_t *vc, int32_t pos,
-                   int32_t n_heads, int32_t n_kv_heads, int32_t dh, float *o);
+                   int32_t n_heads, int32_t n_kv_heads, int32_t dh, int32_t window, float *o);
 float orc_silu(float z);
 
 /* ---- the decoder ---- */
 /* one layer at position pos on the fp32 residual x (in place); writes K/V at pos. */
 int orc_layer_forward(const orc_config *c, const orc_layer *w, uint16_t *kc_layer,
-                      uint16_t *vc_layer, float *x, int32_t pos);
+                      uint16_t *vc_layer, float *x, int32_t pos, int32_t layer);
+/* the window layer l attends over: c->sliding_window if bit l of c->window_layers is set, else 0 */
+int32_t orc_layer_window(const orc_config *c, int32_t layer);
 /* full decode step: embed token, all layers, final norm, lm_head -> logits[V]. */
 int orc_decode_step(const orc_config *c, const orc_weights *w, uint16_t *kcache,
                     uint16_t *vcache, int32_t token, int32_t pos, float *logits);

@@ -199,3 +199,35 @@ def test_argmax_lowest_index_on_ties(orc):
     x = np.zeros(4096, np.float32)
     x[4095] = 1e-30
     assert orc.argmax(x) == 4095
+
+
+def test_attention_window_weights_match_fp64_softmax(orc):
+    """Sliding window: one-hot value rows expose the weights; rows before
+    pos - window + 1 get none, the rest equal an fp64 softmax over the window."""
+    rng = np.random.default_rng(18)
+    n, dh, hq, hkv = 48, 96, 4, 2
+    k = (rng.standard_normal((n, hkv, dh)) * 0.5).astype(np.float16)
+    v = np.zeros((n, hkv, dh), np.float16)
+    for j in range(n):
+        v[j, :, j] = 1.0
+    q = rng.standard_normal((hq, dh)).astype(np.float32)
+    for pos, W in ((0, 4), (3, 4), (4, 4), (30, 7), (n - 1, 16), (n - 1, 1)):
+        o = orc.attention(q, k, v, pos, W).astype(np.float64)
+        lo = max(0, pos - W + 1)
+        for h in range(hq):
+            g = h // (hq // hkv)
+            s = (k[lo: pos + 1, g].astype(np.float64) @ q[h].astype(np.float64)) / math.sqrt(dh)
+            a = np.exp(s - s.max())
+            a /= a.sum()
+            assert np.all(o[h, :lo] == 0) and np.all(o[h, pos + 1:] == 0), (pos, W)
+            assert np.allclose(o[h, lo: pos + 1], a, rtol=1e-5, atol=1e-7), (pos, W)
+
+
+def test_attention_window_one_returns_current_value_row(orc):
+    rng = np.random.default_rng(19)
+    k, v = _cache(rng, 10, 2, 96)
+    q = rng.standard_normal((4, 96)).astype(np.float32)
+    o = orc.attention(q, k, v, 7, 1)
+    assert np.array_equal(o, v[7][[0, 0, 1, 1]].astype(np.float32))
+    # a window that covers every row is full attention
+    assert np.array_equal(orc.attention(q, k, v, 7, 8), orc.attention(q, k, v, 7))

@@ -146,3 +146,19 @@ def test_decode_rejects_bad_arguments(orc, tiny_weights):
         m.decode_step(0, TINY["max_seq"])
     with pytest.raises(ValueError):
         m.decode_step(-1, 0)
+
+
+def test_sliding_window_cached_equals_nocache_and_matters(orc, tiny_weights):
+    """Window 4 on layer 0 only: the cached decode equals the no-cache recompute
+    (two separate code paths) past the window, and differs from full attention."""
+    cfg = dict(TINY, sliding_window=4, window_layers=0b01)
+    m, full = orc.Model(cfg, tiny_weights), orc.Model(TINY, tiny_weights)
+    toks = synth.prompt(TINY, 10)
+    for pos, t in enumerate(toks):
+        got, ref_full = m.decode_step(int(t), pos), full.decode_step(int(t), pos)
+        if pos in (2, 3, 4, 9):
+            ref = m.forward_nocache(toks[: pos + 1])
+            assert np.allclose(got, ref, rtol=0, atol=1e-6 * np.abs(ref).max()), pos
+        if pos < 4:
+            assert np.array_equal(got, ref_full), pos
+    assert not np.allclose(got, ref_full, rtol=0, atol=1e-4)
