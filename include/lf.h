@@ -61,13 +61,18 @@ enum {
 typedef struct lf_state lf_state;
 
 typedef struct {
-  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_seq;
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, max_seq;   /* head_dim 64, 96 or 128 */
   float rms_eps;       /* RMSNorm epsilon, inside the square root (1e-5) */
   float rope_base;     /* rotary base (10000) */
   float temperature;   /* 0: greedy argmax; > 0: nucleus (or, with LF_GUMBEL, Gumbel-max) sampling */
   float top_p;         /* nucleus mass fraction in (0, 1] when temperature > 0 (not LF_GUMBEL) */
   uint64_t seed;       /* Philox4x32-10 key of the sampler */
   uint32_t flags;      /* LF_HIDDEN_IO | LF_STATS | LF_GUMBEL */
+  int32_t sliding_window;   /* > 0: the layers in window_layers attend to the last
+                               sliding_window positions only (rows pos-W+1..pos);
+                               0: every layer attends to all earlier positions.
+                               "KOG LaneFormer-2B & the monokernel", "Pillar 1". */
+  uint64_t window_layers;   /* bit l set: layer l (< 64) uses the window */
 } lf_config;
 
 /* One layer's weights: fp16 device pointers, row-major [out][in]:

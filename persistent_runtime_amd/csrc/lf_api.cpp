@@ -81,7 +81,9 @@ int validate(const lf_config *c) {
   if (c->n_heads % c->n_kv_heads)
     return fail(nullptr, LF_EINVAL, "n_heads must be a multiple of n_kv_heads");
   if (c->n_heads / c->n_kv_heads > 8) return fail(nullptr, LF_EUNSUPPORTED, "more than 8 query heads per KV head");
-  if (c->head_dim != 64 && c->head_dim != 128) return fail(nullptr, LF_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->head_dim != 64 && c->head_dim != 96 && c->head_dim != 128)
+    return fail(nullptr, LF_EUNSUPPORTED, "head_dim must be 64, 96 or 128");
+  if (c->sliding_window < 0) return fail(nullptr, LF_EINVAL, "sliding_window must be >= 0");
   if (!hidden && (c->vocab < 2 || c->vocab % 2))
     return fail(nullptr, LF_EINVAL, "vocab must be even and at least 2");
   if (!(c->rms_eps >= 0.0f) || !(c->rope_base > 0.0f)) return fail(nullptr, LF_EINVAL, "bad rms_eps or rope_base");
@@ -211,6 +213,8 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.seed = c.seed;
   P.flags = c.flags;
   P.hidden_io = hidden ? 1 : 0;
+  P.window = c.sliding_window;
+  P.window_layers = c.sliding_window > 0 ? c.window_layers : 0ull;
   P.levels_per_token = lf::PH_PER_LAYER * c.n_layers + (hidden ? 0 : 2);
   double tmo_ms = 2000.0;
   if (const char *s = std::getenv("LF_TIMEOUT_MS")) tmo_ms = std::atof(s);

@@ -53,6 +53,8 @@ struct Params {
   unsigned long long seed;
   unsigned flags;
   int hidden_io, sampling;   // sampling: a SampleMode
+  int window;                          // sliding-window length (0: none)
+  unsigned long long window_layers;    // bit l: layer l attends over the window
   int levels_per_token;
   // weights (library-owned, packed)
   // Per layer: Wqkv [(Hq+2Hkv)*dh][d] (q/k rows pair-interleaved per head:

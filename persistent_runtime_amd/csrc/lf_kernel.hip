@@ -1024,6 +1024,36 @@ __device__ __forceinline__ void attn_split(int n, int G, int Hkv, int &S, int &L
   Lc = (n + S - 1) / S;
 }
 
+// r = hd * dh + rem: shifts and masks when dh is a power of two (a uniform
+// branch), a division otherwise (head_dim 96).
+__device__ __forceinline__ void head_split(int r, int dh, int &hd, int &rem) {
+  if ((dh & (dh - 1)) == 0) {
+    hd = r >> __builtin_ctz((unsigned)dh);
+    rem = r & (dh - 1);
+  } else {
+    hd = r / dh;
+    rem = r - hd * dh;
+  }
+}
+
+// Whether layer l attends over a sliding window (bit l of the window mask).
+__device__ __forceinline__ bool layer_windowed(const KP &P, int l) {
+  return P.window > 0 && l < 64 && ((P.window_layers >> l) & 1ull);
+}
+
+// The attention split of one position for full layers ([0]) and windowed layers
+// ([1]): units per head S, keys per unit Lc, first key kb.
+struct AttnSplit {
+  int S[2], Lc[2], kb[2];
+  __device__ __forceinline__ AttnSplit(int pos, int G, int Hkv, int window) {
+    const int n = pos + 1, nw = window > 0 && n > window ? window : n;
+    attn_split(n, G, Hkv, S[0], Lc[0]);
+    attn_split(nw, G, Hkv, S[1], Lc[1]);
+    kb[0] = 0;
+    kb[1] = n - nw;
+  }
+};
+
 // Wait for one tagged word; on expiry returns it anyway and sets *bad.  Each
 // retry reads the word and the error word together: one round trip.
 __device__ __forceinline__ u64 ld_tag_wait(KP &P, const u64 *p, unsigned tag, unsigned long long t0,
@@ -1063,7 +1093,7 @@ constexpr int kKeysPerRound = 16;   // keys whose K and V rows one wave loads pe
 // model's unit keeps one head's state in registers and no loop over heads.
 template <int kQ>
 __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsigned tag_q,
-                                          unsigned tag_a, int pos, int u, int S, int Lc, unsigned char *lds,
+                                          unsigned tag_a, int pos, int u, int S, int Lc, int kb, unsigned char *lds,
                                           float *red, int trk = -1) {
   static_assert(kQ <= kMaxQpg, "query heads per KV head");
   KP &P = fresh(P0);
@@ -1071,7 +1101,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv, half = dh / 2;
   const int g = u % Hkv, c = u / Hkv;   // chunk c = 0 of head g runs on workgroup g
   const int n = pos + 1;
-  const int j0 = c * Lc;
+  const int j0 = kb + c * Lc;   // kb: the first key (0, or pos - window + 1 in a windowed layer)
   const int j1 = min(n, j0 + Lc);
   float *qs = reinterpret_cast<float *>(lds);       // [qpg][dh]
   float *kcur = qs + qpg * dh;                       // [dh]
@@ -1716,10 +1746,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     for (int t = 0; t < P.n_tokens; ++t) {
       const int pos = P.pos0 + t;
       const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
-      int S, Lc;
-      attn_split(pos + 1, G, P.Hkv, S, Lc);
+      AttnSplit asp(pos, G, P.Hkv, P.window);
       for (int l = 0; l < L; ++l) {
         const int q0 = t * ngp + 4 * l;
+        const bool win = layer_windowed(P, l);
+        const int S = asp.S[win], Lc = asp.Lc[win], kb = asp.kb[win];
         const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
         const int gen = (t * L + l) & 1;
         st.trace_k = t == P.trace_token ? 5 * l + 0 : -1;
@@ -1732,9 +1763,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           return;
         if (lds_ld(&ctl->abort)) return;
         for (int u = b; u < P.Hkv * S; u += G)
-          if (!(P.qpg == 1 ? attn_unit<1>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
+          if (!(P.qpg == 1 ? attn_unit<1>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, kb, alds, red,
                                           u == b && t == P.trace_token ? 5 * l + 1 : -1)
-                           : attn_unit<kMaxQpg>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds,
+                           : attn_unit<kMaxQpg>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, kb, alds,
                                                 red, u == b && t == P.trace_token ? 5 * l + 1 : -1)))
             return;
         if (qkv_rounds) st.refill();
@@ -1770,15 +1801,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
   auto fail = [&]() __attribute__((always_inline)) {
     if (lane == 0) lds_st(&ctl->abort, 1u);
   };
-  const int nq = P.Hq * dh, nk = P.Hkv * dh, half = dh / 2, dh_log2 = __builtin_ctz((unsigned)dh);
+  const int nq = P.Hq * dh, nk = P.Hkv * dh, half = dh / 2;
   const size_t nkw = (size_t)P.Hkv * half;   // words per generation of kc_t / vc_t
   int token = P.token0;
   for (int t = 0; t < P.n_tokens; ++t) {
     const int pos = P.pos0 + t;
     const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
     if (kPrefill) token = P.in_tokens[t];
-    int S, Lc;
-    attn_split(pos + 1, G, P.Hkv, S, Lc);
+    const AttnSplit asp(pos, G, P.Hkv, P.window);
     for (int l = 0; l < L; ++l) {
       KP &Pl = fresh(P);
       sy.P = &Pl;
@@ -1803,7 +1833,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         if (lane < ge.nrows / 2) {
           const int r = ge.r0 + 2 * lane;
           if (r < nq + nk) {
-            const int k = ((r < nq ? r : r - nq) & (dh - 1)) >> 1;
+            int hd, rem;
+            head_split(r < nq ? r : r - nq, dh, hd, rem);
+            const int k = rem >> 1;
             cs0 = Pl.rope[((size_t)pos * half + k) * 2 + 0];
             sn0 = Pl.rope[((size_t)pos * half + k) * 2 + 1];
           }
@@ -1842,7 +1874,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           if (r < nq + nk) {
             // q / k rows come in rotary pairs (dims k, k + dh/2 of head hd)
             const int rr = r < nq ? r : r - nq;
-            const int hd = rr >> dh_log2, k = (rr & (dh - 1)) >> 1;   // head_dim is 64 or 128
+            int hd, rem;
+            head_split(rr, dh, hd, rem);
+            const int k = rem >> 1;
             const float cs = i == lane ? cs0 : Pl.rope[((size_t)pos * half + k) * 2 + 0];
             const float sn = i == lane ? sn0 : Pl.rope[((size_t)pos * half + k) * 2 + 1];
             const float y0 = a * cs - bb * sn, y1 = bb * cs + a * sn;
@@ -1871,11 +1905,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       {
         const unsigned long long ta = stamp(sy);
         trace(Pl, t, 5 * l + 1, 0);
+        const bool win = layer_windowed(Pl, l);
+        const int S = asp.S[win], Lc = asp.Lc[win], kb = asp.kb[win];
         for (int u = b; u < Pl.Hkv * S; u += G)
-          if (!(Pl.qpg == 1 ? attn_unit<1>(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, alds, red,
+          if (!(Pl.qpg == 1 ? attn_unit<1>(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, kb, alds, red,
                                            u == b && t == Pl.trace_token ? 5 * l + 1 : -1)
                             : attn_unit<kMaxQpg>(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc,
-                                                 alds, red, u == b && t == Pl.trace_token ? 5 * l + 1 : -1)))
+                                                 kb, alds, red, u == b && t == Pl.trace_token ? 5 * l + 1 : -1)))
             return;
         trace(Pl, t, 5 * l + 1, 1);
         publish_vec(Pl, lvl + PH_ATTN);

@@ -39,7 +39,8 @@ class LfConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "d_model", "n_heads", "n_kv_heads", "head_dim",
                                          "ffn_dim", "vocab", "max_seq")] + \
                [("rms_eps", C.c_float), ("rope_base", C.c_float), ("temperature", C.c_float),
-                ("top_p", C.c_float), ("seed", C.c_uint64), ("flags", C.c_uint32)]
+                ("top_p", C.c_float), ("seed", C.c_uint64), ("flags", C.c_uint32),
+                ("sliding_window", C.c_int32), ("window_layers", C.c_uint64)]
 
 
 class LfLayerWeights(C.Structure):
@@ -103,7 +104,8 @@ def make_config(cfg: dict, flags: int = 0) -> LfConfig:
                     cfg["ffn_dim"], cfg.get("vocab", 0), cfg["max_seq"], cfg.get("rms_eps", 1e-5),
                     cfg.get("rope_base", 10000.0), cfg.get("temperature", 0.0), cfg.get("top_p", 1.0),
                     cfg.get("seed", 1234), flags | (LF_HIDDEN_IO if cfg.get("vocab", 0) == 0 else 0)
-                    | (LF_GUMBEL if cfg.get("sampler", "nucleus") == "gumbel" else 0))
+                    | (LF_GUMBEL if cfg.get("sampler", "nucleus") == "gumbel" else 0),
+                    cfg.get("sliding_window", 0), cfg.get("window_layers", 0))
 
 
 def upload_weights(weights: dict, device="cuda") -> dict:

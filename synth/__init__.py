@@ -48,6 +48,13 @@ CONFIGS = {
     "dec2b_25l_kv16k_topp": dict(n_layers=25, d_model=2560, n_heads=20, n_kv_heads=20, head_dim=128,
                                  ffn_dim=6912, vocab=32768, max_seq=16512,
                                  kv_prefill=16384, n_decode=128, temperature=0.8, top_p=0.9),
+    # LaneFormer-2B-shaped decoder: 15 layers, GQA 32 query / 16 KV heads of dim 96,
+    # sliding window in 10 of the 15 layers (every third layer attends globally),
+    # 4096-token context; d_model, ffn_dim, window and vocabulary are readings
+    "laneformer_15l_swa": dict(n_layers=15, d_model=3072, n_heads=32, n_kv_heads=16, head_dim=96,
+                               ffn_dim=12288, vocab=32000, max_seq=4096, sliding_window=1024,
+                               window_layers=sum(1 << l for l in range(15) if l % 3 != 2),
+                               kv_prefill=2048, n_decode=128, temperature=0.0, top_p=1.0),
     # ~8B dense GQA decoder
     "dec8b_32l_gqa": dict(n_layers=32, d_model=4096, n_heads=32, n_kv_heads=8, head_dim=128,
                           ffn_dim=14336, vocab=128256, max_seq=768,

@@ -57,7 +57,8 @@ def _create(lf, cfg, weights_ptr_ok=True):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n_heads=4, n_kv_heads=3), -1),           # heads not a multiple of KV heads
-    (dict(head_dim=96), -6),                        # unsupported head size
+    (dict(head_dim=80), -6),                        # unsupported head size
+    (dict(sliding_window=-1), -1),
     (dict(d_model=250), -1),                        # d_model not a multiple of 8
     (dict(vocab=4095), -1),                         # odd vocabulary
     (dict(n_layers=0), -1),

@@ -401,7 +401,7 @@ def test_dec2b_long_context_sampling(lf, orc, dec2b):
 
 
 def test_dec2b_gumbel_sampling(lf, orc, dec2b):
-    """The ~2.2B decoder with Gumbel-max sampling (V = 32000 over 256 lm_head
+    """The ~2.2B decoder with Gumbel-max sampling (V = 32768 over 256 lm_head
     workgroups): GPU logits within tolerance of the oracle's, and the sampled
     token equals the oracle's Gumbel-max on the GPU's own logits."""
     cfg, w = dec2b
@@ -417,6 +417,46 @@ def test_dec2b_gumbel_sampling(lf, orc, dec2b):
         assert ok, (pos, err)
         assert nxt == orc.sample_gumbel(got, 0.8, 4242, pos), pos
         tok = nxt
+
+
+def test_sliding_window_gqa_head96_teacher_forced(lf, orc):
+    """Sliding-window attention on layers 0 and 2 of three (window 36: the windowed
+    layers split 3 ways, the full layer 4 ways at the end), GQA 4/2 heads of dim 96:
+    logits against the oracle at every position, most of them past the window."""
+    cfg = synth.scaled_config("tiny_2l_d256", n_layers=3, d_model=384, n_heads=4, n_kv_heads=2,
+                              head_dim=96, ffn_dim=1024, vocab=2000, max_seq=64,
+                              sliding_window=36, window_layers=0b101)
+    w = synth.model_weights(cfg, seed=5)
+    teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 60))
+
+
+def test_laneformer_shape_sliding_window_long_context(lf, orc):
+    """The LaneFormer-2B-shaped decoder (15 layers, 32/16 heads of dim 96, window
+    1024 in 10 layers) with its cache prefilled to 2048: GPU logits within
+    tolerance of the oracle's and the greedy token equal where the margin allows."""
+    import torch
+    cfg = synth.CONFIGS["laneformer_15l_swa"]
+    w = synth.model_weights(cfg)
+    orc.set_threads(min(16, os.cpu_count() or 1))
+    P = cfg["kv_prefill"]
+    k, v = synth.kv_prefill(cfg, P)
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    for l in range(cfg["n_layers"]):
+        eng.kv_fill(l, 0, torch.from_numpy(k[l]).cuda(), torch.from_numpy(v[l]).cuda())
+    m = orc.Model(cfg, w)
+    m.kv_fill(k, v, 0)
+    del k, v
+    tok = int(synth.prompt(dict(cfg, prompt_len=1), 1)[0])
+    for i in range(3):
+        pos = P + i
+        nxt = eng.decode_step(tok, pos)
+        got = eng.logits().cpu().numpy()
+        ref = m.decode_step(tok, pos)
+        ok, err = close(got, ref)
+        assert ok, (pos, err)
+        if margin(ref) >= 1e-2:
+            assert nxt == int(np.argmax(ref)), pos
+        tok = int(np.argmax(ref))
 
 
 def test_prefill_one_launch_matches_oracle(lf, orc, tiny):
