@@ -9,7 +9,8 @@ Bytes counted per token at position ``pos`` (algorithmic, not measured):
   * every layer matrix and RMSNorm gain, the final gain and the lm_head (fp16);
   * one embedding row (the table is gathered, not streamed);
   * K and V of positions 0..pos for every layer (attention reads them all,
-    the current one included), and the K/V row written at ``pos``.
+    the current one included; a sliding-window layer reads the last W only),
+    and the K/V row written at ``pos``.
 Activations (a few KB per phase, cache resident) are not counted.
 """
 from __future__ import annotations
@@ -37,9 +38,15 @@ def weight_bytes(cfg: dict) -> int:
 
 
 def kv_bytes(cfg: dict, pos: int) -> int:
-    """K/V read over positions 0..pos plus the row written at pos, all layers."""
+    """K/V read over positions 0..pos (the last ``sliding_window`` of them in the
+    layers of ``window_layers``) plus the row written at pos, all layers."""
     row = cfg["n_kv_heads"] * cfg["head_dim"] * FP16
-    return cfg["n_layers"] * 2 * row * ((pos + 1) + 1)
+    W, mask = cfg.get("sliding_window", 0), cfg.get("window_layers", 0)
+    rows = 0
+    for l in range(cfg["n_layers"]):
+        keys = min(pos + 1, W) if W > 0 and l < 64 and (mask >> l) & 1 else pos + 1
+        rows += keys + 1
+    return 2 * row * rows
 
 
 def bytes_per_token(cfg: dict, pos: int) -> int:
