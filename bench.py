@@ -161,29 +161,40 @@ def main() -> int:
     from persistent_runtime_amd import lf, roofline
 
     cfg = dict(synth.CONFIGS[args.workload])
-    if cfg.get("vocab", 0) == 0 or "prompt_len" not in cfg:
-        log(f"workload {args.workload} is not a prompt + decode workload")
+    if cfg.get("vocab", 0) == 0 or ("prompt_len" not in cfg and "kv_prefill" not in cfg):
+        log(f"workload {args.workload} is not a prompt + decode or prefilled-cache decode workload")
         return 2
-    P = cfg["prompt_len"]
-    pos0 = P - 1
+    # prompt workloads decode after a teacher-forced prompt; prefilled-cache
+    # workloads (long context) start at position kv_prefill over synthetic K/V rows
+    kv_pre = "prompt_len" not in cfg
+    P = cfg["kv_prefill"] if kv_pre else cfg["prompt_len"]
+    pos0 = P if kv_pre else P - 1
     K, W = args.steps, args.warmup
     cfg["max_seq"] = max(cfg["max_seq"], pos0 + max(K, W) + 1)
     torch.cuda.set_device(0)
     t0 = time.time()
     weights = synth.model_weights(cfg)
-    prompt = synth.prompt(cfg, P)
+    prompt = synth.prompt(dict(cfg, prompt_len=1), 1) if kv_pre else synth.prompt(cfg, P)
     log(f"weights generated in {time.time() - t0:.1f}s")
     dev = lf.upload_weights(weights)
     eng = lf.Engine(cfg, dev, flags=lf.LF_STATS if args.stats else 0)
     del dev
     torch.cuda.empty_cache()
     log(f"engine: grid={eng.grid} lds={eng.lds_bytes}")
-    eng.prefill(prompt[:pos0], 0)
+    if kv_pre:
+        k, v = synth.kv_prefill(cfg, P)
+        for l in range(cfg["n_layers"]):
+            eng.kv_fill(l, 0, torch.from_numpy(k[l]).cuda(), torch.from_numpy(v[l]).cuda())
+        del k, v
+        first = int(prompt[0])
+    else:
+        eng.prefill(prompt[:pos0], 0)
+        first = int(prompt[pos0])
     torch.cuda.synchronize()
     if W > 0:
         warm = np.resize(prompt, W).astype(np.int32)   # any in-vocabulary tokens
         eng.prefill(warm, pos0)
-    eng.set_position(int(prompt[pos0]), pos0)
+    eng.set_position(first, pos0)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -225,7 +236,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "n_layers": cfg["n_layers"], "d_model": cfg["d_model"],
                    "n_heads": cfg["n_heads"], "n_kv_heads": cfg["n_kv_heads"], "head_dim": cfg["head_dim"],
-                   "ffn_dim": cfg["ffn_dim"], "vocab": cfg["vocab"], "batch": 1, "prompt_len": P,
+                   "ffn_dim": cfg["ffn_dim"], "vocab": cfg["vocab"], "batch": 1, ("kv_prefill" if kv_pre else "prompt_len"): P,
+                   "sliding_window": cfg.get("sliding_window", 0),
+                   "window_layers": bin(cfg.get("window_layers", 0)),
                    "positions": f"{pos0}..{pos0 + K - 1}", "sampling": "greedy" if cfg["temperature"] == 0 else
                    f"T={cfg['temperature']} top_p={cfg['top_p']}", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
@@ -236,7 +249,8 @@ def main() -> int:
     if stats:
         res["wait_stats"] = stats
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(cfg, weights, prompt, args.cpu_seconds)
+        sample = synth.prompt(dict(cfg, prompt_len=64), 64) if kv_pre else prompt
+        res["cpu_baseline"] = cpu_baseline(cfg, weights, sample, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     eng.close()
     return 0
