@@ -427,7 +427,13 @@ def test_sliding_window_gqa_head96_teacher_forced(lf, orc):
                               head_dim=96, ffn_dim=1024, vocab=2000, max_seq=64,
                               sliding_window=36, window_layers=0b101)
     w = synth.model_weights(cfg, seed=5)
-    teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 60))
+    prompt = synth.prompt(cfg, 60)
+    teacher_forced(lf, orc, cfg, w, prompt)
+    # the check is decisive: full attention in every layer misses the tolerance
+    a, b = orc.Model(cfg, w), orc.Model(dict(cfg, sliding_window=0, window_layers=0), w)
+    for pos, t in enumerate(prompt):
+        la, lb = a.decode_step(int(t), pos), b.decode_step(int(t), pos)
+    assert not close(la, lb)[0]
 
 
 def test_laneformer_shape_sliding_window_long_context(lf, orc):
