@@ -40,7 +40,7 @@ enum {
   LF_EHIP = -3,        /* HIP runtime or launch failure (incl. co-residency refused) */
   LF_ERANGE = -4,      /* pos >= max_seq, token outside [0, vocab), n out of range */
   LF_ETIMEOUT = -5,    /* a bounded in-kernel wait expired; the kernel exited cleanly */
-  LF_EUNSUPPORTED = -6 /* valid but not implemented (e.g. head_dim not 64 or 128) */
+  LF_EUNSUPPORTED = -6 /* valid but not implemented (e.g. head_dim not 64, 96 or 128) */
 };
 
 /* config.flags */

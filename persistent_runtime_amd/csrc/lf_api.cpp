@@ -84,6 +84,12 @@ int validate(const lf_config *c) {
   if (c->head_dim != 64 && c->head_dim != 96 && c->head_dim != 128)
     return fail(nullptr, LF_EUNSUPPORTED, "head_dim must be 64, 96 or 128");
   if (c->sliding_window < 0) return fail(nullptr, LF_EINVAL, "sliding_window must be >= 0");
+  if (c->sliding_window > 0) {
+    // the layer mask is one 64-bit word: bit l selects layer l
+    if (c->n_layers > 64) return fail(nullptr, LF_EUNSUPPORTED, "sliding windows need n_layers <= 64");
+    if (c->n_layers < 64 && (c->window_layers >> c->n_layers) != 0)
+      return fail(nullptr, LF_EINVAL, "window_layers has bits at or above n_layers");
+  }
   if (!hidden && (c->vocab < 2 || c->vocab % 2))
     return fail(nullptr, LF_EINVAL, "vocab must be even and at least 2");
   if (!(c->rms_eps >= 0.0f) || !(c->rope_base > 0.0f)) return fail(nullptr, LF_EINVAL, "bad rms_eps or rope_base");
@@ -100,13 +106,12 @@ hipError_t copy_rows_strided(void *dst, size_t dpitch, const void *src, size_t s
   return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToDevice, s);
 }
 
-// Restart the level numbering: progress words, split-K tickets and every tagged
+// Restart the level numbering: progress words and every tagged
 // exchange word go back to zero (no level is ever zero), level_base to 0.
 hipError_t reset_levels(lf_state *st) {
   const lf::Params &P = st->P;
   hipError_t e;
   if ((e = hipMemsetAsync(P.progress, 0, sizeof(unsigned) * P.G, st->stream)) != hipSuccess) return e;
-  if ((e = hipMemsetAsync(P.tickets, 0, sizeof(unsigned) * P.L * P.Hkv, st->stream)) != hipSuccess) return e;
   if ((e = hipMemsetAsync(st->xbuf, 0, st->xbuf_bytes, st->stream)) != hipSuccess) return e;
   st->level_base = 0;
   return hipSuccess;
@@ -312,11 +317,11 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   const size_t part_gen = (size_t)Hkv * smax * P.qpg * (dh + 2);
   // small buffers, each 256-byte aligned, in one arena
   struct Slot { void **dst; size_t bytes; };
-  void *x_hidden, *x_out, *logits, *lm_val, *lm_idx, *progress, *tickets, *tok_slot, *errw, *stats;
+  void *x_hidden, *x_out, *logits, *lm_val, *lm_idx, *progress, *tok_slot, *errw, *stats;
   Slot slots[] = {
       {&x_hidden, (size_t)d * 4}, {&x_out, (size_t)d * 4}, {&logits, (size_t)(V > 0 ? V : 1) * 4},
       {&lm_val, (size_t)G * 4}, {&lm_idx, (size_t)G * 4}, {&progress, (size_t)G * 4},
-      {&tickets, (size_t)c.n_layers * Hkv * 4}, {&tok_slot, 16}, {&errw, 16},
+      {&tok_slot, 16}, {&errw, 16},
       {&stats, (size_t)G * (lf::kStatWords + (lf::kTrace ? lf::kTraceSlots * (5 * c.n_layers + 2) : 0)) * 8}};
   size_t arena = 0;
   for (auto &sl : slots) arena += align_up(sl.bytes, 256);
@@ -327,7 +332,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   for (auto &sl : slots) { *sl.dst = ar + off; off += align_up(sl.bytes, 256); }
   P.x_hidden = (float *)x_hidden; P.x_out = (float *)x_out; P.logits = (float *)logits;
   P.lm_val = (float *)lm_val; P.lm_idx = (int *)lm_idx; P.progress = (unsigned *)progress;
-  P.tickets = (unsigned *)tickets; P.tok_slot = (int *)tok_slot; P.err = (unsigned *)errw;
+  P.tok_slot = (int *)tok_slot; P.err = (unsigned *)errw;
   P.stats = (unsigned long long *)stats;
   P.stat_stride = lf::kStatWords + (lf::kTrace ? lf::kTraceSlots * (5 * c.n_layers + 2) : 0);
   // tagged exchange words, two generations each, in one zeroed allocation

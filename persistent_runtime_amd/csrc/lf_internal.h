@@ -86,7 +86,6 @@ struct Params {
   float *lm_val;           // [G] per-workgroup max logit
   int *lm_idx;             // [G] its index
   unsigned *progress;      // [G] last completed level of each workgroup
-  unsigned *tickets;       // [L][Hkv] split-K arrival counters
   int *tok_slot;           // [1] token chosen by the last step
   int *out_tokens;         // [n_tokens]
   const int *in_tokens;    // [n_tokens] teacher-forced tokens (prefill launches)

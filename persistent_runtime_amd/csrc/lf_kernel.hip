@@ -7,32 +7,34 @@
 // matrix is cut into contiguous row blocks, one per workgroup, fixed for the
 // life of the state; attention is cut into (KV head, key chunk) units.
 //
-// Roles inside a workgroup.  Wave 0 is the SYNC wave: it polls the producers a
-// phase depends on, stages the phase's input vector in LDS (RMSNorm folded in),
-// and after the phase writes the outputs and publishes them.  Waves 1..7 are
-// STREAM waves: each walks its own contiguous slice of the workgroup's weight
-// rows, phase after phase, layer after layer, token after token, and copies it
-// into a private LDS ring with global_load_lds_dwordx4 (16 B per lane, 1 KB per
-// instruction).  A stream wave issues up to D pieces ahead of the piece it
-// consumes, across dependency waits and phase boundaries, and never waits on
-// another workgroup: it only waits on an LDS word the sync wave sets when the
-// phase's input vector is ready ("Weight streaming - keeping HBM saturated":
-// weights are prefetched while earlier stages still wait, and the LDS path keeps
-// registers free).  Keeping every dependency-sensitive load on wave 0 keeps the
-// stream waves' vmcnt pipeline free of anything but weights, so their waits are
-// exact.
+// Roles inside a workgroup.  Wave 0 is the SYNC wave: after each phase it adds
+// the stream waves' partial row sums and runs the phase's epilogue (rotary
+// embedding and the KV-cache append, the residual add, SiLU(gate) * up, the
+// lm_head's local argmax), stores the outputs as tagged exchange words and
+// stores its progress word.  Waves 1..7 are STREAM waves: each walks its own
+// contiguous slice of the workgroup's weight rows, phase after phase, layer
+// after layer, token after token, through a ring of eight 1-KB pieces held in
+// registers the compiler never allocates (v224..v255), loaded with
+// non-temporal 16-byte global loads; the loop that consumes a phase's rounds
+// and refills each slot as it is freed is inline assembly, and the first
+// round of the next phase is issued as soon as a phase is done, so those loads
+// are in flight while its input is still being produced ("Weight streaming -
+// keeping HBM saturated").  All eight waves stage each phase's input vector
+// into LDS together, and the stream waves also run the attention units.
 //
-// Synchronisation between workgroups.  No grid barrier.  Each workgroup owns
-// one 32-bit progress word = the last dependency level it completed (one level
-// per phase per layer per token, numbered across launches).  A consumer polls
-// the words of the producers it needs ("Cross-GPU synchronization without
-// atomics": consumers poll memory the producer writes, instead of an
-// atomic-counter barrier).  All data exchanged between workgroups is written
-// and read with device-scope (sc1) accesses; the producer waits for its stores
-// to complete before storing its progress word.  Split-K attention partials are
-// merged by the last-arriving unit of each KV head (an atomic ticket).  Every
-// wait is bounded: on expiry the workgroup writes the error word and returns,
-// every other wait sees it and returns too, so the grid always drains.
+// Synchronisation between workgroups.  No grid barrier and no counter.  The
+// vectors passed between phases are 64-bit words that carry their payload and
+// the dependency level that produced it, and an aligned 8-byte store is
+// single-copy atomic: a consumer re-reads a vector until every word carries
+// the level it waits for, so the data are their own flag and a producer never
+// waits for its stores before announcing them ("Cross-GPU synchronization
+// without atomics": consumers poll the memory the producer writes).  Split-K
+// attention partials are merged by a fixed unit per KV head that waits on the
+// partials' tags.  Untagged data (logits, the per-workgroup argmax partials,
+// the chosen token) use the per-workgroup progress words, stored after the
+// producer's stores complete.  Every wait is bounded: on expiry the workgroup
+// writes the error word and returns, every other wait sees it and returns too,
+// so the grid always drains.
 //
 // Matrix-vector products run on the vector ALUs with v_dot2_f32_f16 (fp16 x
 // fp16 products, fp32 accumulation) and cross-lane sums, not on MFMA: at batch 1

@@ -64,6 +64,8 @@ def _create(lf, cfg, weights_ptr_ok=True):
     (dict(n_layers=0), -1),
     (dict(temperature=0.8, top_p=0.0), -1),
     (dict(n_heads=36, n_kv_heads=4), -6),           # 9 query heads per KV head
+    (dict(sliding_window=16, window_layers=0b100), -1),   # mask bit at or above n_layers (2)
+    (dict(sliding_window=16, n_layers=65, window_layers=1), -6),   # the mask word covers 64 layers
 ])
 def test_create_rejects_bad_config_without_device(lf, kw, code):
     rc, msg = _create(lf, _cfg(**kw))

@@ -372,6 +372,102 @@ def test_dec2b_teacher_forced_and_generate_launch(lf, orc, dec2b):
     del dw
 
 
+@pytest.mark.timeout(900)
+def test_dec2b_timed_positions_prefill_and_generate(lf, orc, dec2b):
+    """The benchmark's own path at the ~2.2B shape: the 127-token prompt in one
+    teacher-forced launch, then steps at the timed positions 127.. against the
+    oracle (logits within tolerance every step), then one generate launch from
+    position 127 against the oracle's greedy continuation up to the first step
+    whose top-2 margin is below 1e-2."""
+    cfg, w = dec2b
+    orc.set_threads(min(16, os.cpu_count() or 1))
+    prompt = synth.prompt(cfg, cfg["prompt_len"])
+    P = len(prompt) - 1
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    eng.prefill(prompt[:P], 0)
+    m = orc.Model(cfg, w)
+    for p in range(P):
+        m.decode_step(int(prompt[p]), p)
+    # snapshot the oracle's cache so that the generate check restarts from pos P
+    kc, vc = m.kcache.copy(), m.vcache.copy()
+    tok = int(prompt[P])
+    for i in range(3):
+        pos = P + i
+        nxt = eng.decode_step(tok, pos)
+        ref = m.decode_step(tok, pos)
+        ok, err = close(eng.logits().cpu().numpy(), ref)
+        assert ok, (pos, err)
+        if margin(ref) >= 1e-2:
+            assert nxt == orc.argmax(ref), pos
+        tok = orc.argmax(ref)
+    n = 8
+    eng.set_position(int(prompt[P]), P)
+    got = eng.generate(n)
+    m.kcache[...] = kc
+    m.vcache[...] = vc
+    ref, hist = m.generate(int(prompt[P]), P, n, keep_logits=True)
+    for i in range(n):
+        if margin(hist[i]) < 1e-2:
+            break
+        assert got[i] == ref[i], i
+
+
+@pytest.fixture(scope="module")
+def dec8b():
+    cfg = synth.CONFIGS["dec8b_32l_gqa"]
+    return cfg, synth.model_weights(cfg)
+
+
+@pytest.mark.timeout(900)
+def test_dec8b_gqa_full_shape(lf, orc, dec8b):
+    """The ~8B GQA decoder at full size (32 layers, d 4096, 32 query / 8 KV heads of
+    dim 128, F 14336, untied vocabulary of 128,256 over the lm_head workgroups):
+    teacher-forced steps from position 0; then the cache is filled with 255
+    synthetic rows and the steps at positions 255.. attend over them split across
+    several workgroups per KV head (4 query heads each); then one generate launch
+    against the oracle's greedy continuation.  Logits within tolerance at every
+    step, greedy tokens equal where the oracle's top-2 margin is at least 1e-2."""
+    import torch
+    cfg, w = dec8b
+    orc.set_threads(min(16, os.cpu_count() or 1))
+    dw = lf.upload_weights(w)
+    eng = lf.Engine(cfg, dw)
+    del dw
+    torch.cuda.empty_cache()
+    m = orc.Model(cfg, w)
+    prompt = synth.prompt(cfg, 3)
+    teacher_forced(lf, orc, cfg, w, prompt, engine=eng, model=m)
+    P = 255
+    k, v = synth.kv_prefill(cfg, P)
+    for l in range(cfg["n_layers"]):
+        eng.kv_fill(l, 0, torch.from_numpy(k[l]).cuda(), torch.from_numpy(v[l]).cuda())
+    m.kv_fill(k, v, 0)
+    del k, v
+    kc, vc = m.kcache.copy(), m.vcache.copy()
+    tok0 = int(synth.prompt(cfg, 4)[3])
+    tok = tok0
+    for i in range(3):
+        pos = P + i
+        nxt = eng.decode_step(tok, pos)
+        ref = m.decode_step(tok, pos)
+        got = eng.logits().cpu().numpy()
+        ok, err = close(got, ref)
+        assert ok, (pos, err, np.abs(ref).max())
+        if margin(ref) >= 1e-2:
+            assert nxt == orc.argmax(ref), pos
+        tok = orc.argmax(ref)
+    n = 6
+    eng.set_position(tok0, P)
+    got = eng.generate(n)
+    m.kcache[...] = kc
+    m.vcache[...] = vc
+    ref, hist = m.generate(tok0, P, n, keep_logits=True)
+    for i in range(n):
+        if margin(hist[i]) < 1e-2:
+            break
+        assert got[i] == ref[i], i
+
+
 def test_dec2b_long_context_sampling(lf, orc, dec2b):
     """16K prefilled cache, temperature 0.8 / top-p 0.9 Philox sampling at pos 16384..:
     GPU logits within tolerance of the oracle's, and the token the kernel samples

@@ -56,3 +56,18 @@ def test_flops_about_one_per_byte():
     c3 = synth.CONFIGS["dec2b_25l_greedy"]
     ratio = rf.flops_per_token(c3, 255) / rf.bytes_per_token(c3, 255)
     assert 0.95 < ratio < 1.05
+
+
+def test_windowed_kv_bytes_closed_form():
+    """Sliding-window layers read min(pos+1, W) cached rows (plus the row written),
+    the other layers pos+1: the LaneFormer-shaped workload at position 2048 has
+    10 windowed layers of 1024 + 1 rows and 5 full layers of 2049 + 1 rows of
+    2 x 16 heads x 96 dims x 2 bytes each."""
+    lfm = synth.CONFIGS["laneformer_15l_swa"]
+    row = 2 * 16 * 96 * 2
+    assert rf.kv_bytes(lfm, 2048) == row * (10 * (1024 + 1) + 5 * (2049 + 1))
+    # before the window fills, windowed and full layers read the same rows
+    assert rf.kv_bytes(lfm, 100) == row * 15 * (101 + 1)
+    # an all-zero mask is the unwindowed count, whatever the window
+    assert rf.kv_bytes(dict(lfm, window_layers=0), 2048) == rf.kv_bytes(dict(lfm, sliding_window=0), 2048)
+    assert rf.kv_bytes(dict(lfm, window_layers=0), 2048) == row * 15 * (2049 + 1)
