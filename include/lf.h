@@ -118,6 +118,22 @@ int lf_decode_step(lf_state *st, int32_t token, int32_t pos, int32_t *next_token
  * LF_ETIMEOUT, LF_EHIP. */
 int lf_generate(lf_state *st, int32_t n, int32_t *out_tokens);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same n
+ * decode steps in ONE launch as lf_generate, with the same kernel and results,
+ * that allocates nothing -- no hipMalloc, hipFree or allocating library call.
+ * The per-launch scratch (exchange words, progress and error words, argmax
+ * partials, the token slot; lf_query(st, LF_Q_SCRATCH_BYTES) bytes) lives in
+ * the library's static device array of LF_Q_SCRATCH_MAX bytes (4 MiB), one per
+ * GPU, held until the process ends; it is cleared by a fill kernel at each
+ * call.  Every state on a GPU shares that GPU's array: calls that overlap on
+ * one GPU race.  out_tokens_dev (device, n int32 entries, caller-owned)
+ * receives the sampled tokens; the pending (token, pos) advances as with
+ * lf_generate.  Errors: LF_EINVAL (NULL, LF_HIDDEN_IO), LF_ERANGE (no pending
+ * token, n < 1, pos + n > max_seq), LF_EUNSUPPORTED (the state needs more
+ * scratch than the array holds), LF_ETIMEOUT, LF_EHIP. */
+int lf_generate_noalloc(lf_state *st, int32_t n, int32_t *out_tokens_dev);
+
 /* Teacher-forced prompt in ONE launch: tokens[i] (host array) is consumed at
  * position pos0 + i and its K/V written; no logits, no sampling, and the pending
  * token is cleared (follow with lf_set_position or lf_decode_step).
@@ -159,6 +175,8 @@ int lf_query(const lf_state *st, int32_t what);
 #define LF_Q_GRID 0
 #define LF_Q_THREADS 1
 #define LF_Q_LDS_BYTES 2
+#define LF_Q_SCRATCH_BYTES 3   /* scratch lf_generate_noalloc uses for this state */
+#define LF_Q_SCRATCH_MAX 4     /* bytes of the static scratch array */
 
 /* Test hooks, device pointers, on `stream`:
  * lf_test_expdef: y[i] = E(x[i]) with the library's defined exponential.

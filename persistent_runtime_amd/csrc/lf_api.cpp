@@ -155,6 +155,44 @@ int do_launch(lf_state *st, int token0, int pos0, int n, std::vector<int> *out, 
   return LF_OK;
 }
 
+// Where lf_generate_noalloc puts the per-launch scratch inside the static
+// array: the exchange words at the same offsets as in the state's own buffer,
+// then the progress words, the error words, the argmax partials and the token
+// slot.  Returns the bytes used; with base != null also fills P's pointers.
+size_t noalloc_layout(const lf_state *st, char *base, lf::Params *P) {
+  const lf::Params &S = st->P;
+  auto rel = [&](const void *p) -> unsigned long long * {
+    return reinterpret_cast<unsigned long long *>(base + ((const char *)p - (const char *)st->xbuf));
+  };
+  size_t off = align_up(st->xbuf_bytes, 256);
+  const size_t prog = off;
+  off += align_up((size_t)S.G * 4, 256);
+  const size_t errw = off;
+  off += 256;
+  const size_t lmv = off;
+  off += align_up((size_t)S.G * 4, 256);
+  const size_t lmi = off;
+  off += align_up((size_t)S.G * 4, 256);
+  const size_t tok = off;
+  off += 256;
+  if (base && P) {
+    P->xmid_t = rel(S.xmid_t);
+    P->xout_t = rel(S.xout_t);
+    P->q_t = rel(S.q_t);
+    P->kc_t = rel(S.kc_t);
+    P->vc_t = rel(S.vc_t);
+    P->part_t = rel(S.part_t);
+    P->o_t = rel(S.o_t);
+    P->a_t = rel(S.a_t);
+    P->progress = reinterpret_cast<unsigned *>(base + prog);
+    P->err = reinterpret_cast<unsigned *>(base + errw);
+    P->lm_val = reinterpret_cast<float *>(base + lmv);
+    P->lm_idx = reinterpret_cast<int *>(base + lmi);
+    P->tok_slot = reinterpret_cast<int *>(base + tok);
+  }
+  return off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,6 +231,9 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     return code;
   };
   if ((e = hipGetDevice(&st->device)) != hipSuccess) return bail(hip_fail(st, e, "hipGetDevice"));
+  // the device address of lf_generate_noalloc's static scratch on this device
+  if ((e = lf::noalloc_scratch_init(st->device)) != hipSuccess)
+    return bail(hip_fail(st, e, "hipGetSymbolAddress(scratch)"));
   int ncu = 0, coop = 0;
   (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, st->device);
   (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, st->device);
@@ -486,6 +527,54 @@ int lf_generate(lf_state *st, int32_t n, int32_t *out_tokens) {
   return LF_OK;
 }
 
+int lf_generate_noalloc(lf_state *st, int32_t n, int32_t *out_tokens_dev) {
+  if (!st) return fail(nullptr, LF_EINVAL, "state is NULL");
+  if (st->P.hidden_io) return fail(&st->err, LF_EINVAL, "lf_generate_noalloc needs a vocabulary");
+  if (!out_tokens_dev) return fail(&st->err, LF_EINVAL, "out_tokens_dev is NULL");
+  if (!st->has_pending) return fail(&st->err, LF_ERANGE, "no pending token: call lf_decode_step or lf_set_position");
+  if (n < 1 || st->pending_pos + n > st->cfg.max_seq)
+    return fail(&st->err, LF_ERANGE, "n < 1 or pos + n > max_seq");
+  char *base = static_cast<char *>(lf::noalloc_scratch(st->device));
+  if (!base) return fail(&st->err, LF_EHIP, "the static scratch of this device was never looked up");
+  const size_t need = noalloc_layout(st, nullptr, nullptr);
+  if (need > lf::kNoallocScratchBytes) {
+    char buf[200];
+    std::snprintf(buf, sizeof buf, "this state needs %zu bytes of launch scratch; the static array holds %zu",
+                  need, lf::kNoallocScratchBytes);
+    return fail(&st->err, LF_EUNSUPPORTED, buf);
+  }
+  lf::Params P = st->P;
+  noalloc_layout(st, base, &P);
+  P.out_tokens = out_tokens_dev;
+  P.levels_per_token = lf::PH_PER_LAYER * P.L + 2;
+  P.n_tokens = n;
+  P.trace_token = n / 2;
+  P.token0 = st->pending_token;
+  P.pos0 = st->pending_pos;
+  P.level_base = 0;   // the words are cleared below: the numbering restarts at every call
+  hipError_t e;
+  // a fill kernel (not a memset node, so the sequence may be captured in a graph)
+  if ((e = lf::launch_zero(base, need, st->stream)) != hipSuccess) return hip_fail(st, e, "clear scratch");
+  if ((e = lf::launch_monokernel(P, false, st->stream)) != hipSuccess) return hip_fail(st, e, "cooperative launch");
+  if ((e = hipStreamSynchronize(st->stream)) != hipSuccess) return hip_fail(st, e, "kernel execution");
+  unsigned herr[4];
+  if ((e = hipMemcpy(herr, P.err, sizeof(herr), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(st, e, "read error word");
+  if (herr[0]) {
+    char buf[160];
+    std::snprintf(buf, sizeof buf, "in-kernel wait timed out (workgroup %u, level %u)", herr[1], herr[2]);
+    return fail(&st->err, LF_ETIMEOUT, buf);
+  }
+  if (herr[3]) return fail(&st->err, LF_EHIP, "the token choice produced no valid token (non-finite logits?)");
+  int last = 0;
+  if ((e = hipMemcpy(&last, out_tokens_dev + (n - 1), sizeof(int), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(st, e, "read last token");
+  st->pending_pos += n;
+  st->pending_token = last;
+  st->has_pending = st->pending_pos < st->cfg.max_seq;
+  return LF_OK;
+}
+
 int lf_prefill(lf_state *st, const int32_t *tokens, int32_t n, int32_t pos0) {
   if (!st) return fail(nullptr, LF_EINVAL, "state is NULL");
   if (st->P.hidden_io) return fail(&st->err, LF_EINVAL, "lf_prefill needs a vocabulary");
@@ -577,6 +666,8 @@ int lf_query(const lf_state *st, int32_t what) {
     case LF_Q_GRID: return st->P.G;
     case LF_Q_THREADS: return lf::kThreads;
     case LF_Q_LDS_BYTES: return st->P.lds_bytes;
+    case LF_Q_SCRATCH_BYTES: return (int)noalloc_layout(st, nullptr, nullptr);
+    case LF_Q_SCRATCH_MAX: return (int)lf::kNoallocScratchBytes;
     default: return LF_EINVAL;
   }
 }

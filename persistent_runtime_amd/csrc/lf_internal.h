@@ -103,6 +103,15 @@ struct Params {
 };
 
 hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream);
+// The entry point that allocates nothing keeps its per-launch scratch in a
+// static device array of this many bytes (one per GPU).
+constexpr size_t kNoallocScratchBytes = (size_t)4 << 20;
+// Look up the array's device address on `device` (current) once; later calls
+// return at once.  noalloc_scratch: that address, or null before the lookup.
+hipError_t noalloc_scratch_init(int device);
+void *noalloc_scratch(int device);
+// Zero `bytes` (a multiple of 8) at p with a fill kernel on `stream`.
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 // w[r][c] = fp16(w[r][c] * g[c]) for an fp16 matrix of `rows` rows of `cols`
 // elements (cols % 8 == 0, w 16-byte aligned, g 2-byte aligned).
 hipError_t launch_scale_columns(void *w, size_t rows, int cols, const void *g, hipStream_t stream);

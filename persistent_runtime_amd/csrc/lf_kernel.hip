@@ -43,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lf_internal.h"
 
 namespace lf {
@@ -2186,7 +2188,52 @@ __global__ void __launch_bounds__(256) lf_scale_columns_kernel(f16x8 *w, long lo
   }
 }
 
+// Clears n 64-bit words (the scratch of the entry point that allocates nothing).
+__global__ void __launch_bounds__(256) lf_zero_kernel(unsigned long long *p, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = 0ull;
+}
+
 }  // namespace
+
+// Device memory of lf_generate_noalloc: one array per GPU (every device that
+// loads this code object holds its own copy until the process ends).  Host code
+// never names it directly: the array's host-side symbol is not a device
+// address, so kernels and copies use the address hipGetSymbolAddress returns
+// for the current device, kept per device in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = p;
+  return hipSuccess;
+}
+
+void *noalloc_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {
+  const long long n = (long long)(bytes / 8);
+  if (n == 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(lf_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<unsigned long long *>(p), n);
+  return hipGetLastError();
+}
 
 const void *monokernel_symbol(bool prefill) {
   return prefill ? reinterpret_cast<const void *>(&lf_monokernel<true>)

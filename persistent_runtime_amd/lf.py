@@ -19,11 +19,12 @@ LIB_PATH = os.environ.get("LF_LIB") or os.path.join(HERE, "liblf.so")
 
 LF_OK, LF_EINVAL, LF_ENOMEM, LF_EHIP, LF_ERANGE, LF_ETIMEOUT, LF_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 LF_HIDDEN_IO, LF_STATS, LF_GUMBEL = 1, 4, 8
-LF_Q_GRID, LF_Q_THREADS, LF_Q_LDS_BYTES = 0, 1, 2
+LF_Q_GRID, LF_Q_THREADS, LF_Q_LDS_BYTES, LF_Q_SCRATCH_BYTES, LF_Q_SCRATCH_MAX = 0, 1, 2, 3, 4
 LAYER_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 
 # every symbol include/lf.h declares
-EXPORTS = ("lf_model_create", "lf_model_destroy", "lf_decode_step", "lf_generate", "lf_prefill", "lf_set_position",
+EXPORTS = ("lf_model_create", "lf_model_destroy", "lf_decode_step", "lf_generate", "lf_generate_noalloc",
+           "lf_prefill", "lf_set_position",
            "lf_last_error", "lf_get_logits", "lf_kv_fill", "lf_kv_read", "lf_set_hidden", "lf_get_hidden",
            "lf_get_stats", "lf_query", "lf_test_expdef", "lf_test_sample",
            "lf_test_logdef", "lf_test_sample_gumbel")
@@ -68,6 +69,7 @@ def lib():
         L.lf_model_destroy.restype = None
         L.lf_decode_step.argtypes = [P, I32, I32, C.POINTER(I32)]
         L.lf_generate.argtypes = [P, I32, P]
+        L.lf_generate_noalloc.argtypes = [P, I32, P]
         L.lf_set_position.argtypes = [P, I32, I32]
         L.lf_prefill.argtypes = [P, P, I32, I32]
         L.lf_last_error.argtypes = [P]
@@ -174,6 +176,19 @@ class Engine:
         out = np.zeros(n, dtype=np.int32)
         _check(lib().lf_generate(self._st, int(n), out.ctypes.data), self._st)
         return out
+
+    def generate_noalloc(self, n: int, out=None):
+        """lf_generate_noalloc: tokens into a caller-owned int32 device tensor (allocated
+        here, on the caller's side, when `out` is None)."""
+        import torch
+        if out is None:
+            out = torch.empty(n, dtype=torch.int32, device="cuda")
+        assert out.is_cuda and out.dtype == torch.int32 and out.is_contiguous() and out.numel() >= n
+        _check(lib().lf_generate_noalloc(self._st, int(n), out.data_ptr()), self._st)
+        return out
+
+    def query(self, what: int) -> int:
+        return lib().lf_query(self._st, int(what))
 
     def logits(self):
         import torch
