@@ -260,6 +260,11 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.flags = c.flags;
   P.hidden_io = hidden ? 1 : 0;
   P.window = c.sliding_window;
+  P.attn_unit_tiles = lf::kWaves - 1;   // one tile per stream wave
+  if (const char *s = std::getenv("LF_ATTN_UNIT_TILES")) {
+    const int v = std::atoi(s);
+    if (v >= 1 && v <= lf::kWaves - 1) P.attn_unit_tiles = v;
+  }
   P.window_layers = c.sliding_window > 0 ? c.window_layers : 0ull;
   P.levels_per_token = lf::PH_PER_LAYER * c.n_layers + (hidden ? 0 : 2);
   double tmo_ms = 2000.0;
@@ -331,7 +336,8 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.part_off[lf::LW_D] = sz_qkv + sz_o + sz_gu;
 
   // ---- KV cache, rotary table, activations, sync words
-  const size_t kv_elems = (size_t)c.n_layers * c.max_seq * Hkv * dh;
+  P.kv_tiles = (c.max_seq + lf::kKvTile - 1) / lf::kKvTile;
+  const size_t kv_elems = (size_t)c.n_layers * Hkv * P.kv_tiles * lf::kKvTile * dh;
   P.kcache = dev_alloc(st, kv_elems * 2, &e);
   P.vcache = P.kcache ? dev_alloc(st, kv_elems * 2, &e) : nullptr;
   if (!P.vcache) return bail(fail(&st->err, LF_ENOMEM, "KV cache allocation failed"));
@@ -428,15 +434,14 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (d_elems * 2 > h_b) h_b = align_up(d_elems * 2, 16);
   const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);   // one phase kind's partial row sums
   // attention scratch: queries, current K/V row, per-wave (m, l) and per-wave o
-  const size_t attn_b = (size_t)P.qpg * dh * 4 + 2 * (size_t)dh * 4 + (size_t)lf::kWaves * 8 * 2 * 4 +
-                        (size_t)lf::kWaves * P.qpg * dh * 4;
+  const size_t attn_b = (size_t)lf::attn_lds(P.qpg, dh).bytes;
   const size_t samp_b = 4096;
-  // h, overlaid by the attention / sampler scratch between GEMV phases
+  // h, overlaid by the sampler scratch after the last layer; attention has an area of its own
   size_t region_a = h_b;
-  if (attn_b > region_a) region_a = attn_b;
   if (samp_b > region_a) region_a = samp_b;
   P.lds_h = 0;
-  P.lds_red = (int)align_up(region_a, 256);
+  P.lds_attn = (int)align_up(region_a, 256);
+  P.lds_red = (int)align_up((size_t)P.lds_attn + attn_b, 256);
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + lf::kCtlBytes;
   P.lds_xres = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 16);
@@ -612,19 +617,8 @@ static int kv_copy(lf_state *st, int32_t layer, int32_t pos0, int32_t n, void *k
   if (!st || !k || !v) return fail(st ? &st->err : nullptr, LF_EINVAL, "NULL argument");
   if (layer < 0 || layer >= st->cfg.n_layers || pos0 < 0 || n < 0 || pos0 + n > st->cfg.max_seq)
     return fail(&st->err, LF_ERANGE, "layer / position range outside the cache");
-  const size_t row = (size_t)st->P.Hkv * st->P.dh * 2;
-  const size_t off = ((size_t)layer * st->cfg.max_seq + pos0) * row;
-  char *kc = (char *)st->P.kcache + off, *vc = (char *)st->P.vcache + off;
-  hipError_t e;
-  if (fill) {
-    if ((e = hipMemcpyAsync(kc, k, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess ||
-        (e = hipMemcpyAsync(vc, v, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess)
-      return hip_fail(st, e, "kv fill");
-  } else {
-    if ((e = hipMemcpyAsync(k, kc, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess ||
-        (e = hipMemcpyAsync(v, vc, row * n, hipMemcpyDeviceToDevice, st->stream)) != hipSuccess)
-      return hip_fail(st, e, "kv read");
-  }
+  hipError_t e = lf::launch_kv_copy(st->P, layer, pos0, n, k, v, fill, st->stream);
+  if (e != hipSuccess) return hip_fail(st, e, fill ? "kv fill" : "kv read");
   e = hipStreamSynchronize(st->stream);
   return e == hipSuccess ? LF_OK : hip_fail(st, e, "kv copy");
 }

@@ -8,12 +8,24 @@ namespace lf {
 
 constexpr int kThreads = 512;          // 8 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kAttnBlock = 512;        // key positions scored per attention sub-block
-#ifndef LF_MIN_KEYS_PER_UNIT
-#define LF_MIN_KEYS_PER_UNIT 16
-#endif
-constexpr int kMinKeysPerUnit = LF_MIN_KEYS_PER_UNIT;   // smallest attention split-K chunk
 constexpr int kMaxSplit = 64;          // most split-K chunks per KV head
+// The KV cache of one (layer, KV head) is a run of tiles of kKvTile positions,
+// each 128 * head_dim bytes for K and for V:
+//   K tile [head_dim / 8][64 keys][8 dims]: one 16-byte vector is 8 dims of one
+//     key, and a 1-KB piece is the same 8 dims of all 64 keys, so a wave64 load
+//     puts one key in each lane;
+//   V tile [8 key groups][head_dim][8 keys]: one 16-byte vector is one dim of 8
+//     consecutive keys, and a 1-KB piece is 64 dims of one key group, so a wave64
+//     load puts one dim in each lane.
+// Both make every load of a tile a contiguous 1-KB piece.
+constexpr int kKvTile = 64;
+// Element (position j, dim e) of a K / V tile run, in fp16 elements from its start.
+__host__ __device__ constexpr size_t k_elem(int dh, int j, int e) {
+  return (size_t)(j >> 6) * (size_t)(64 * dh) + (size_t)((e >> 3) * 512 + (j & 63) * 8 + (e & 7));
+}
+__host__ __device__ constexpr size_t v_elem(int dh, int j, int e) {
+  return (size_t)(j >> 6) * (size_t)(64 * dh) + (size_t)(((j & 63) >> 3) * dh * 8 + e * 8 + (j & 7));
+}
 // Workgroups 0 .. n-1 merge the attention heads' split-K partials (unit c = 0
 // of head g runs on workgroup g); they are the last to finish attention, so
 // with enough workgroups they get no rows of the output projection.
@@ -35,6 +47,25 @@ constexpr int kStageRound = 64 * 40;      // tagged words one staging round read
 constexpr int kStageRoundWide = 64 * 56;  // the SwiGLU vector's staging round
 constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB pieces in flight per stream wave (register ring)
 
+// Attention scratch in LDS (an area of its own, so the sync wave may stage the
+// next phase's input while the stream waves run attention): fp16 queries [qpg][dh], fp32 current K and V rows [dh] each, fp16
+// softmax weights [kWaves][8][64], per-wave (m, l) [kWaves][8][2] and per-wave
+// o [kWaves][qpg][dh].  Byte offsets.
+struct AttnLds {
+  int q16, kcur, vcur, p16, wml, wo, bytes;
+};
+__host__ __device__ inline AttnLds attn_lds(int qpg, int dh) {
+  AttnLds a{};
+  a.q16 = 0;
+  a.kcur = (qpg * dh * 2 + 15) & ~15;
+  a.vcur = a.kcur + dh * 4;
+  a.p16 = (a.vcur + dh * 4 + 15) & ~15;
+  a.wml = a.p16 + kWaves * 8 * kKvTile * 2;
+  a.wo = a.wml + kWaves * 8 * 2 * 4;
+  a.bytes = a.wo + kWaves * qpg * dh * 4;
+  return a;
+}
+
 // Phases of one layer; each completes one "level" of the dependency chain.
 enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYER = 5 };
 
@@ -54,6 +85,7 @@ struct Params {
   unsigned flags;
   int hidden_io, sampling;   // sampling: a SampleMode
   int window;                          // sliding-window length (0: none)
+  int attn_unit_tiles;                 // most KV tiles per attention unit (1 .. 7)
   unsigned long long window_layers;    // bit l: layer l attends over the window
   int levels_per_token;
   // weights (library-owned, packed)
@@ -67,7 +99,8 @@ struct Params {
   unsigned long long part_off[LW_COUNT];
   const void *tok_emb, *lm_head;
   // state
-  void *kcache, *vcache;   // fp16 [L][max_seq][Hkv][dh]
+  void *kcache, *vcache;   // fp16 [L][Hkv][kv_tiles] tiles of kKvTile positions (k_elem / v_elem)
+  int kv_tiles;            // tiles per (layer, KV head): ceil(max_seq / kKvTile)
   const float *rope;       // [max_seq][dh/2][2] (cos, sin)
   float *x_hidden;         // fp32 [d] layer-0 input (LF_HIDDEN_IO, written by the host)
   float *x_out;            // fp32 [d] residual after the last layer (LF_HIDDEN_IO, read by the host)
@@ -98,7 +131,7 @@ struct Params {
   unsigned long long timeout_ticks;
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_bytes;
+  int lds_h, lds_attn, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_bytes;
   int part_rows, hmax;
 };
 
@@ -115,6 +148,10 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 // w[r][c] = fp16(w[r][c] * g[c]) for an fp16 matrix of `rows` rows of `cols`
 // elements (cols % 8 == 0, w 16-byte aligned, g 2-byte aligned).
 hipError_t launch_scale_columns(void *w, size_t rows, int cols, const void *g, hipStream_t stream);
+// Copy n cache positions pos0.. of layer l between natural [n][Hkv][dh] fp16
+// buffers k, v and the tiled cache (to_cache: into the cache, else out of it).
+hipError_t launch_kv_copy(const Params &p, int l, int pos0, int n, void *k, void *v, bool to_cache,
+                          hipStream_t stream);
 hipError_t launch_test_expdef(const float *x, float *y, int64_t n, hipStream_t stream);
 hipError_t launch_test_logdef(const float *x, float *y, int64_t n, hipStream_t stream);
 hipError_t launch_test_gumbel(const float *logits, int n, float inv_temp, unsigned long long seed, const int *pos,

@@ -71,7 +71,6 @@ __device__ __forceinline__ KP &fresh(KP &P) {
 constexpr int kNcw = kWaves - 1;       // stream waves per workgroup
 constexpr int kRing = kRingSlots;      // 1-KB pieces each stream wave keeps in flight (registers)
 constexpr int kMaxQpg = 8;             // query heads per KV head supported
-constexpr int kMaxDpl = 2;             // head dims per lane (head_dim <= 128)
 enum Kind { K_QKV = 0, K_O = 1, K_GU = 2, K_D = 3, K_LM = 4, K_COUNT = 5 };
 // sync-wave activities timed with LF_STATS: staging, waiting for the stream
 // waves, epilogue + publish, attention, lm_head + token choice
@@ -255,7 +254,8 @@ struct Ctl {
   unsigned abort;           // the sync wave gave up (the error word is set)
   unsigned done[kWaves];    // per stream wave: last GEMV phase (1-based) it finished
   int status;               // outcome of a barrier-based wait
-  int pad[6];
+  unsigned abar;            // arrivals at the stream waves' barrier (kNcw per barrier)
+  int pad[5];
   float ssw[kWaves];        // per wave: sum of squares of its share of an RMSNorm input
   Geo geo[K_COUNT];
   // The partition of every phase kind among the stream waves, fixed for the
@@ -1005,27 +1005,52 @@ __device__ __forceinline__ float row_value(const float *part, int row) {
 }
 
 
-// Wave 0: wait until every stream wave finished GEMV phase q.
-__device__ __forceinline__ void wait_streams(const Ctl *ctl, int q) {
+// Wave 0: wait until every stream wave finished GEMV phase q.  Returns false
+// if the abort flag is set instead: a stream wave leaves the kernel only after
+// setting or seeing it (a bounded wait of its own expired), so it may never
+// report the phase done.
+__device__ __forceinline__ bool wait_streams(const Ctl *ctl, int q) {
   for (;;) {
     const bool behind = lane_id() < kNcw && lds_ld(&ctl->done[lane_id()]) < (unsigned)(q + 1);
     if (wave_none(behind)) break;
+    if (lds_ld(&ctl->abort)) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   asm volatile("" ::: "memory");
+  return true;
 }
 
 
 // ---------------------------------------------------------------- attention
 
-__device__ __forceinline__ void attn_split(int n, int G, int Hkv, int &S, int &Lc) {
+// The cached keys attended at position pos are [kb, pos) (kb = 0, or the
+// window's first key pos - W + 1); the key at pos itself comes from the QKV
+// phase's tagged words.  The cached keys lie in tiles t0 .. t0 + nt - 1 of
+// kKvTile positions, split into S units of at most tpu consecutive tiles (unit
+// c takes tiles from t0 + c tpu): ceil(nt / ut) units per KV head, at most
+// G / Hkv and kMaxSplit, where ut (at most kNcw: one tile per stream wave) is
+// the plan's tile count per unit.  Unit 0 also takes the current key.
+struct AttnPart {
+  int S, tpu, t0, nt, kb;
+};
+__device__ __forceinline__ AttnPart attn_part(int kb, int pos, int G, int Hkv, int ut) {
+  AttnPart a;
+  a.kb = kb;
   int smax = G / Hkv;
   if (smax > kMaxSplit) smax = kMaxSplit;
   if (smax < 1) smax = 1;
-  S = (n + kMinKeysPerUnit - 1) / kMinKeysPerUnit;
-  if (S > smax) S = smax;
-  if (S < 1) S = 1;
-  Lc = (n + S - 1) / S;
+  if (pos > kb) {
+    a.t0 = kb / kKvTile;
+    a.nt = (pos - 1) / kKvTile - a.t0 + 1;
+    int S = (a.nt + ut - 1) / ut;
+    if (S > smax) S = smax;
+    a.tpu = (a.nt + S - 1) / S;
+    a.S = (a.nt + a.tpu - 1) / a.tpu;   // no unit is left without tiles
+  } else {
+    a.t0 = a.nt = a.tpu = 0;
+    a.S = 1;
+  }
+  return a;
 }
 
 // r = hd * dh + rem: shifts and masks when dh is a power of two (a uniform
@@ -1045,16 +1070,14 @@ __device__ __forceinline__ bool layer_windowed(const KP &P, int l) {
   return P.window > 0 && l < 64 && ((P.window_layers >> l) & 1ull);
 }
 
-// The attention split of one position for full layers ([0]) and windowed layers
-// ([1]): units per head S, keys per unit Lc, first key kb.
+// The attention split of one position for full layers ([0]) and windowed
+// layers ([1]).
 struct AttnSplit {
-  int S[2], Lc[2], kb[2];
-  __device__ __forceinline__ AttnSplit(int pos, int G, int Hkv, int window) {
-    const int n = pos + 1, nw = window > 0 && n > window ? window : n;
-    attn_split(n, G, Hkv, S[0], Lc[0]);
-    attn_split(nw, G, Hkv, S[1], Lc[1]);
-    kb[0] = 0;
-    kb[1] = n - nw;
+  AttnPart a[2];
+  __device__ __forceinline__ AttnSplit(int pos, int G, int Hkv, int window, int ut) {
+    const int n = pos + 1;
+    a[0] = attn_part(0, pos, G, Hkv, ut);
+    a[1] = attn_part(window > 0 && n > window ? n - window : 0, pos, G, Hkv, ut);
   }
 };
 
@@ -1075,200 +1098,300 @@ __device__ __forceinline__ u64 ld_tag_wait(KP &P, const u64 *p, unsigned tag, un
   return w;
 }
 
-constexpr int kKeysPerRound = 16;   // keys whose K and V rows one wave loads per round trip
+// A buffer resource over `bytes` bytes from p: loads past the end return zero.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes of a KV tile run at byte offset off, device-scope (sc1) and
+// non-temporal (nt).  A line of a tile also holds positions that are written
+// after an earlier step has read the line, so the load must not be served from
+// a copy this XCD's L2 kept from that earlier read.
+#ifndef LF_KV_AUX
+#define LF_KV_AUX (16 | 2)
+#endif
+__device__ __forceinline__ u32x4 kv_load(Rsrc r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, LF_KV_AUX);
+}
 
-// One split-K unit (KV head g, key chunk c) of layer l at position pos, all
-// waves of the workgroup.  These are the pages' three attention stages ("The
-// fused operations, briefly"): attention over one tile of the cache per unit,
+// Barrier of the seven stream waves (the sync wave takes no part in attention):
+// each wave completes its LDS accesses, counts itself in, and waits until the
+// count reaches the next multiple of kNcw.  No wave waits for its global stores.
+__device__ __forceinline__ void stream_barrier(Ctl *ctl) {
+  lds_drain();
+  unsigned old = 0u;
+  if (lane_id() == 0)
+    old = __hip_atomic_fetch_add(&ctl->abar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  old = __builtin_amdgcn_readfirstlane(old);
+  const unsigned target = (old / kNcw + 1u) * kNcw;
+  while (lds_ld(&ctl->abar) < target && !lds_ld(&ctl->abort)) __builtin_amdgcn_s_sleep(0);
+  asm volatile("" ::: "memory");
+}
+
+// Lanes 2i of the result hold the fp16 pair (x of lane 2i, x of lane 2i + 1).
+__device__ __forceinline__ unsigned pair_up(_Float16 x) {
+  const unsigned lo = (unsigned)__builtin_bit_cast(unsigned short, x);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)lo, 0xF5, 0xf, 0xf, false);   // quad_perm [1,1,3,3]
+  return lo | (hi << 16);
+}
+
+// fp16 pair m (elements 2m, 2m + 1) of a 16-byte vector.
+__device__ __forceinline__ f16x2 pair_of(u32x4 w, int m) {
+  const f16x8 a = __builtin_bit_cast(f16x8, w);
+  switch (m) {
+    case 0: return __builtin_shufflevector(a, a, 0, 1);
+    case 1: return __builtin_shufflevector(a, a, 2, 3);
+    case 2: return __builtin_shufflevector(a, a, 4, 5);
+    default: return __builtin_shufflevector(a, a, 6, 7);
+  }
+}
+
+// One split-K unit (KV head g, tile chunk c) of layer l at position pos, run by
+// the seven stream waves.  These are the pages' three attention stages ("The
+// fused operations, briefly"): attention over one run of cache tiles per unit,
 // the cross-unit softmax correction, then (next phase) the output projection.
 //
-// Only the seven stream waves load (the sync wave's loads would complete behind
-// its own epilogue stores, which this wave's memory operations finish in
-// order after).  Stream wave w takes keys j0 + w - 1, j0 + w - 1 + 7, ...;
-// lane e holds head dims 2e, 2e+1, loads kKeysPerRound K and V rows at once,
-// and keeps an online softmax (m, l, o) per query head.  Wave 1 combines the
-// waves' states into the unit's partial, published as tagged words, and in
-// unit c = 0 of each KV head merges the group's S partials (waiting on their
-// tags) into the fp16 output o_t.  The current position's K/V row comes from
-// the tagged exchange words, not from the cache (whose row for this step may
-// still be in flight).
-// Returns false if a bounded wait expired.
+// Stream wave w takes the unit's tiles w - 1, w + 6, ...; its first tile's K and
+// V pieces are requested before the queries are awaited.  The waves that hold
+// no tile poll the queries (a wave's loads complete in order, so behind 32 KB
+// of tile pieces a poll would wait for them) into the unit's own LDS area.
+// Scores: lane j holds key j of the tile (K tile layout); the query sits in one
+// register per head, lane i holding its dim pair i, and each pair reaches every
+// lane by v_readlane, so a score is 64 dot2 products with no cross-lane sum
+// and no LDS access; the tile's maximum is one wave reduction.  The fp16
+// softmax weights are paired by one DPP move and read the same way, and lane e
+// accumulates output dims e and e + 64 as dot2 products of its V pieces (one
+// dim of 8 keys, V tile layout).  Each wave keeps an online softmax (m, l, o)
+// per query head.  Wave 1 combines the waves' states into the unit's partial
+// (tagged words), and in unit c = 0 of each KV head the waves merge the group's
+// S partials (waiting on their tags) into the fp16 output o_t.  The current
+// position's K/V row comes from the tagged exchange words, not from the cache
+// (whose row for this step may still be in flight); the last stream wave of
+// unit 0 folds it in.  Returns false if a bounded wait expired.
 // kQ: a bound on the query heads per KV head (qpg <= kQ), so that an MHA
 // model's unit keeps one head's state in registers and no loop over heads.
 template <int kQ>
-__device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsigned tag_q,
-                                          unsigned tag_a, int pos, int u, int S, int Lc, int kb, unsigned char *lds,
-                                          float *red, int trk = -1) {
+__device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsigned tag_q, unsigned tag_a, int pos,
+                                          int u, const AttnPart &ap, unsigned char *lds, int trk = -1) {
   static_assert(kQ <= kMaxQpg, "query heads per KV head");
   KP &P = fresh(P0);
-  const int tid = tid_x(), wave = wave_id(), lane = lane_id();
+  const int wave = wave_id(), lane = lane_id();
   const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv, half = dh / 2;
+  const int S = ap.S;
   const int g = u % Hkv, c = u / Hkv;   // chunk c = 0 of head g runs on workgroup g
-  const int n = pos + 1;
-  const int j0 = kb + c * Lc;   // kb: the first key (0, or pos - window + 1 in a windowed layer)
-  const int j1 = min(n, j0 + Lc);
-  float *qs = reinterpret_cast<float *>(lds);       // [qpg][dh]
-  float *kcur = qs + qpg * dh;                       // [dh]
-  float *vcur = kcur + dh;                           // [dh]
-  float *wml = vcur + dh;                            // [kWaves][qpg][2] per-wave (m, l)
-  float *wo = wml + kWaves * kMaxQpg * 2;            // [kWaves][qpg][dh] per-wave o
+  const AttnLds al = attn_lds(qpg, dh);
+  _Float16 *q16 = reinterpret_cast<_Float16 *>(lds + al.q16);   // [qpg][dh]
+  float *kcur = reinterpret_cast<float *>(lds + al.kcur);        // [dh]
+  float *vcur = reinterpret_cast<float *>(lds + al.vcur);        // [dh]
+  float *wml = reinterpret_cast<float *>(lds + al.wml);          // [kWaves][kMaxQpg][2] per-wave (m, l)
+  float *wo = reinterpret_cast<float *>(lds + al.wo);            // [kWaves][qpg][dh] per-wave o
   const unsigned long long t0 = now_ticks();
   bool bad = false;
-  // K/V rows of earlier positions are already in the cache: request this wave's
-  // first round of them before waiting for the queries.
-  const bool act = lane < half;                      // lane holds dims 2*lane, 2*lane + 1
-  const int e0 = act ? 2 * lane : 0;
-  const size_t lstride = (size_t)P.max_seq * Hkv * dh;
-  const _Float16 *Kl = reinterpret_cast<const _Float16 *>(P.kcache) + (size_t)l * lstride + (size_t)g * dh + e0;
-  const _Float16 *Vl = reinterpret_cast<const _Float16 *>(P.vcache) + (size_t)l * lstride + (size_t)g * dh + e0;
-  const size_t rstride = (size_t)Hkv * dh;           // elements between positions
-  // The keys and every load of the unit belong to the stream waves (kw = wave - 1):
-  // the sync wave's loads would complete behind its own epilogue stores.
-  constexpr int kKW = kWaves - 1;
+  constexpr int kKW = kNcw;
   const int kwv = wave - 1;
-  unsigned kw[kKeysPerRound], vw[kKeysPerRound];
-  auto load_round = [&](int jb) __attribute__((always_inline)) {
+  const int ta = ap.t0 + c * ap.tpu;                   // this unit's tiles [ta, te)
+  const int te = min(ta + ap.tpu, ap.t0 + ap.nt);
+  const int tfirst = ta + kwv;
+  const int nck = dh >> 3;              // K pieces per tile
+  const int nvh = (dh + 63) >> 6;       // V pieces per key group
+  const unsigned tile_b = (unsigned)(128 * dh);
+  const size_t run_b = (size_t)P.kv_tiles * tile_b;
+  const size_t run0 = ((size_t)l * Hkv + g) * run_b;
+  const Rsrc rk = make_rsrc(reinterpret_cast<const char *>(P.kcache) + run0, (unsigned)run_b);
+  const Rsrc rv = make_rsrc(reinterpret_cast<const char *>(P.vcache) + run0, (unsigned)run_b);
+  // K piece k of a tile: 16 bytes per lane at k KB + 16 lane.  V piece (kg, hh):
+  // dim hh * 64 + lane of key group kg (lanes past head_dim re-read its last dim)
+  const unsigned koff = (unsigned)lane * 16u;
+  const unsigned voff0 = (unsigned)min(lane, dh - 1) * 16u;
+  const unsigned voff1 = (unsigned)min(64 + lane, dh - 1) * 16u;
+  // With more than four query heads per KV head the V pieces are requested once
+  // the scores are done (in the K pieces' registers), so that the heads' states
+  // fit without spilling.
+  constexpr bool kPreV = kQ <= 4;
+  u32x4 kr[16], vr[8][2];
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    const unsigned tb = (unsigned)t * tile_b;
 #pragma unroll
-    for (int k = 0; k < kKeysPerRound; ++k) {
-      const int j = jb + kKW * k;
-      kw[k] = vw[k] = 0u;
-      if (j < j1 && j != pos) {
-        kw[k] = *reinterpret_cast<const unsigned *>(Kl + (size_t)j * rstride);
-        vw[k] = *reinterpret_cast<const unsigned *>(Vl + (size_t)j * rstride);
-      }
+    for (int kg = 0; kg < 8; ++kg) {
+      const unsigned gb = tb + (unsigned)(kg * dh * 16);
+      vr[kg][0] = kv_load(rv, gb + voff0);
+      if (nvh > 1) vr[kg][1] = kv_load(rv, gb + voff1);
     }
   };
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const unsigned tb = (unsigned)t * tile_b;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < nck) kr[k] = kv_load(rk, tb + (unsigned)k * 1024u + koff);
+    if (kPreV) load_v(t);
+  };
   if (kTrace && wave == 1) trace_at(P, trk, 6);
-  if (wave > 0) load_round(j0 + kwv);
-  __syncthreads();   // wave 0 may still be reading the phase scratch this unit reuses
-  if (kTrace && wave == 1) trace_at(P, trk, 7);
+  if (tfirst < te) load_tile(tfirst);
+  if (kTrace && wave == 1) trace_at(P, trk, 0);
   {
+    // The queries (to fp16) and, in unit 0, the current K and V pairs: one
+    // tagged word each, polled by the stream waves that hold no tile (with a
+    // tile in every wave, all of them).  Each thread requests up to four words
+    // at once and re-reads the stale ones.
     const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)g * qpg * dh;
     const size_t nw = (size_t)Hkv * half;
-    const bool has_cur = j0 <= pos && pos < j1;
-    // one tagged word per thread: queries, then the current K pairs, then V pairs
-    const int nq_words = qpg * dh + (has_cur ? dh : 0);
-    for (int i = wave > 0 ? tid - 64 : nq_words; i < nq_words; i += kThreads - 64) {   // stream waves only
-      if (i < qpg * dh) {
-        qs[i] = pay_f(ld_tag_wait(P, qsrc + i, tag_q, t0, bad));
-      } else if (i < qpg * dh + half) {
-        const int e = i - qpg * dh;
-        const u64 w = ld_tag_wait(P, P.kc_t + gen * nw + (size_t)g * half + e, tag_q, t0, bad);
-        const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w);
-        kcur[e] = (float)hv.x;
-        kcur[e + half] = (float)hv.y;
-      } else {
-        const int e = i - qpg * dh - half;
-        const u64 w = ld_tag_wait(P, P.vc_t + gen * nw + (size_t)g * half + e, tag_q, t0, bad);
-        const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w);
-        vcur[2 * e] = (float)hv.x;
-        vcur[2 * e + 1] = (float)hv.y;
+    const int nq = qpg * dh;
+    const int nwords = nq + (c == 0 ? dh : 0);
+    const int busy = min(te - ta, kKW);                  // stream waves holding a tile
+    const int p0 = busy < kKW ? busy : 0;                // first polling stream wave
+    const int npt = (kKW - p0) * 64;                     // polling threads
+    const int me = kwv - p0;
+    auto word = [&](int i) __attribute__((always_inline)) -> const u64 * {
+      if (i < nq) return qsrc + i;
+      if (i < nq + half) return P.kc_t + gen * nw + (size_t)g * half + (i - nq);
+      return P.vc_t + gen * nw + (size_t)g * half + (i - nq - half);
+    };
+    if (me >= 0) {
+      for (int i0 = me * 64 + lane; i0 < nwords; i0 += npt * 4) {
+        u64 w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + k * npt;
+          w[k] = i < nwords ? ld_dev(word(i)) : ((u64)tag_q << 32);
+        }
+        for (;;) {
+          bool stale = false;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) stale |= tag_of(w[k]) != tag_q;
+          if (!stale) break;
+          const unsigned e = ld_dev(&P.err[0]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (tag_of(w[k]) != tag_q) w[k] = ld_dev(word(i0 + k * npt));
+          if (expired(P, t0, tag_q, e)) {
+            bad = true;
+            break;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + k * npt;
+          if (i >= nwords) continue;
+          if (i < nq) {
+            q16[i] = (_Float16)pay_f(w[k]);
+          } else if (i < nq + half) {   // a K word pairs dims (e, e + dh/2)
+            const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w[k]);
+            kcur[i - nq] = (float)hv.x;
+            kcur[i - nq + half] = (float)hv.y;
+          } else {                      // a V word pairs dims (2e, 2e + 1)
+            const int e = i - nq - half;
+            const f16x2 hv = __builtin_bit_cast(f16x2, (unsigned)w[k]);
+            vcur[2 * e] = (float)hv.x;
+            vcur[2 * e + 1] = (float)hv.y;
+          }
+        }
       }
     }
     if (bad) lds_st(&ctl->abort, 1u);
   }
-  __syncthreads();
+  if (kTrace && wave == kWaves - 1) trace_at(P, trk, 1);
+  stream_barrier(ctl);
   if (lds_ld(&ctl->abort)) return false;
   const int trw = wave == 1 ? trk : -1;
   trace_at(P, trw, 3);
 
-  float qr[kQ][2];
-#pragma unroll
-  for (int h = 0; h < kQ; ++h) {
-    qr[h][0] = h < qpg && act ? qs[h * dh + e0] : 0.0f;
-    qr[h][1] = h < qpg && act ? qs[h * dh + e0 + 1] : 0.0f;
-  }
-  float m[kQ], lsum[kQ], o[kQ][2];
+  const float scale = P.inv_sqrt_dh;
+  float m[kQ], ls[kQ], o0[kQ], o1[kQ];
+  unsigned qv[kQ];   // lane i: the fp16 query pair (2i, 2i + 1) of head h
 #pragma unroll
   for (int h = 0; h < kQ; ++h) {
     m[h] = -INFINITY;
-    lsum[h] = 0.0f;
-    o[h][0] = o[h][1] = 0.0f;
+    ls[h] = o0[h] = o1[h] = 0.0f;
+    qv[h] = h < qpg && lane < half ? reinterpret_cast<const unsigned *>(q16 + h * dh)[lane] : 0u;
   }
-  // The current position's K/V row comes from the tagged words staged in LDS
-  // (the cache row may still be in flight): this lane's two dims, repacked to
-  // fp16 (exact: they were fp16) and patched into the round's registers, so the
-  // key loops below treat every key alike.
-  const unsigned kcw = __builtin_bit_cast(unsigned, f16x2{(_Float16)kcur[e0], (_Float16)kcur[e0 + 1]});
-  const unsigned vcw = __builtin_bit_cast(unsigned, f16x2{(_Float16)vcur[e0], (_Float16)vcur[e0 + 1]});
-  for (int jb = wave > 0 ? j0 + kwv : j1; jb < j1; jb += kKW * kKeysPerRound) {
-    if (jb != j0 + kwv) load_round(jb);   // the first round was requested before the queries
-    // (only inside the chunk: a unit whose chunk ends before pos staged no
-    // current row, and its keys past the chunk must stay zero)
-    if (pos < j1 && jb <= pos) {
-#pragma unroll
-      for (int k = 0; k < kKeysPerRound; ++k) {
-        const bool cur = jb + kKW * k == pos;
-        kw[k] = cur ? kcw : kw[k];
-        vw[k] = cur ? vcw : vw[k];
-      }
-    }
-    if (kTrace && wave == 1) {
-      asm volatile("" ::"v"(kw[0]), "v"(vw[0]), "v"(kw[kKeysPerRound - 1]), "v"(vw[kKeysPerRound - 1]));
-      trace_at(P, trk, 8);
-    }
-    // Per query head: scores of this round's keys, online-softmax rescale,
-    // accumulate.  Keys go in groups of four under one (uniform) check, so a
-    // group's four reductions are independent; a key past the chunk (its K/V
-    // registers are zero) scores -inf.
+  for (int t = tfirst; t < te; t += kKW) {
+    if (t != tfirst) load_tile(t);
+    const int j = t * kKvTile + lane;
+    const bool valid = j >= ap.kb && j < pos;
+    unsigned pp[kQ];   // even lanes: fp16 softmax weights of keys (lane, lane + 1)
+    // scores and the online-softmax update (every tile of the run holds at
+    // least one cached key, so the new maximum is finite)
 #pragma unroll
     for (int h = 0; h < kQ; ++h) {
       if (h < qpg) {
-        float sck[kKeysPerRound];
-        float mb = m[h];
+        float s = 0.0f;
 #pragma unroll
-        for (int kg = 0; kg < kKeysPerRound; kg += 4) {
-          if (jb + kKW * kg < j1) {
+        for (int k = 0; k < 16; ++k) {
+          if (k < nck) {
 #pragma unroll
-            for (int k = kg; k < kg + 4; ++k) {
-              const f16x2 kv = __builtin_bit_cast(f16x2, kw[k]);
-              const float sc = wave_sum(qr[h][0] * (float)kv.x + qr[h][1] * (float)kv.y) * P.inv_sqrt_dh;
-              sck[k] = jb + kKW * k < j1 ? sc : -INFINITY;
-              mb = fmaxf(mb, sck[k]);
-            }
-          } else {
-#pragma unroll
-            for (int k = kg; k < kg + 4; ++k) sck[k] = -INFINITY;
-          }
-        }
-        if (kTrace && wave == 1 && h == 0) {
-          asm volatile("" ::"v"(mb));
-          trace_at(P, trk, 10);
-        }
-        const float alpha = __expf(m[h] - mb);   // 0 while m is -inf
-        lsum[h] *= alpha;
-        o[h][0] *= alpha;
-        o[h][1] *= alpha;
-        m[h] = mb;
-#pragma unroll
-        for (int kg = 0; kg < kKeysPerRound; kg += 4) {
-          if (jb + kKW * kg < j1) {
-#pragma unroll
-            for (int k = kg; k < kg + 4; ++k) {
-              const f16x2 vv = __builtin_bit_cast(f16x2, vw[k]);
-              const float pk = __expf(sck[k] - mb);   // 0 past the chunk
-              lsum[h] += pk;
-              o[h][0] += pk * (float)vv.x;
-              o[h][1] += pk * (float)vv.y;
+            for (int mm = 0; mm < 4; ++mm) {
+              const unsigned q2 = (unsigned)__builtin_amdgcn_readlane((int)qv[h], 4 * k + mm);
+              s = __builtin_amdgcn_fdot2(pair_of(kr[k], mm), __builtin_bit_cast(f16x2, q2), s, false);
             }
           }
         }
+        s = valid ? s * scale : -INFINITY;
+        const float mn = fmaxf(m[h], wave_max(s));
+        const float alpha = __expf(m[h] - mn);   // 0 while m is -inf
+        const _Float16 ph = (_Float16)__expf(s - mn);
+        ls[h] = ls[h] * alpha + (float)ph;
+        o0[h] *= alpha;
+        o1[h] *= alpha;
+        m[h] = mn;
+        pp[h] = pair_up(ph);
+      }
+    }
+    if (kTrace && wave == 1 && t == tfirst) trace_at(P, trk, 10);
+    if (!kPreV) load_v(t);
+    // weights x V: lane e accumulates dims e and e + 64 over the tile's keys
+#pragma unroll
+    for (int h = 0; h < kQ; ++h) {
+      if (h < qpg) {
+#pragma unroll
+        for (int kg = 0; kg < 8; ++kg) {
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) {
+            const f16x2 w2 = __builtin_bit_cast(f16x2, (unsigned)__builtin_amdgcn_readlane((int)pp[h], 8 * kg + 2 * mm));
+            o0[h] = __builtin_amdgcn_fdot2(pair_of(vr[kg][0], mm), w2, o0[h], false);
+            if (nvh > 1) o1[h] = __builtin_amdgcn_fdot2(pair_of(vr[kg][1], mm), w2, o1[h], false);
+          }
+        }
+      }
+    }
+  }
+  if (c == 0 && wave == kWaves - 1) {
+    // the current key, from the staged tagged words (its weight rounded to fp16
+    // like every cached key's)
+    const int e2 = lane < half ? 2 * lane : 0;
+#pragma unroll
+    for (int h = 0; h < kQ; ++h) {
+      if (h < qpg) {
+        const _Float16 *qh = q16 + h * dh;
+        const float x = lane < half ? (float)qh[e2] * kcur[e2] + (float)qh[e2 + 1] * kcur[e2 + 1] : 0.0f;
+        const float s = wave_sum(x) * scale;
+        const float mn = fmaxf(m[h], s);
+        const float alpha = __expf(m[h] - mn);
+        const float p = (float)(_Float16)__expf(s - mn);
+        ls[h] = ls[h] * alpha + (lane == 0 ? p : 0.0f);
+        o0[h] = o0[h] * alpha + p * vcur[min(lane, dh - 1)];
+        o1[h] = o1[h] * alpha + (nvh > 1 ? p * vcur[min(64 + lane, dh - 1)] : 0.0f);
+        m[h] = mn;
       }
     }
   }
   trace_at(P, trw, 4);
-  // the stream waves' states -> the unit's partial (wave 0 holds no keys)
+  // the waves' states -> LDS (a wave without keys leaves m = -inf, l = 0)
 #pragma unroll
   for (int h = 0; h < kQ; ++h) {
-    if (h < qpg && wave > 0) {
+    if (h < qpg) {
+      const float lt = wave_sum(ls[h]);
       if (lane == 0) {
         wml[(wave * kMaxQpg + h) * 2 + 0] = m[h];
-        wml[(wave * kMaxQpg + h) * 2 + 1] = lsum[h];
+        wml[(wave * kMaxQpg + h) * 2 + 1] = lt;
       }
-      if (act) *reinterpret_cast<float2 *>(&wo[(wave * qpg + h) * dh + e0]) = make_float2(o[h][0], o[h][1]);
+      float *ow = wo + (size_t)(wave * qpg + h) * dh;
+      if (lane < dh) ow[lane] = o0[h];
+      if (64 + lane < dh) ow[64 + lane] = o1[h];
     }
   }
   // (taken before the barrier: none of it depends on the other waves)
+  const bool act = lane < half;   // lane holds output dims 2 lane, 2 lane + 1
+  const int e0 = act ? 2 * lane : 0;
   const int stride = dh + 2;
   gu64 *pg = (gu64 *)(P.part_t + (size_t)gen * P.part_gen);
   gu64 *o_out = (gu64 *)(P.o_t + (size_t)gen * (P.Hq * dh / 2) + ((size_t)g * qpg * dh + e0) / 2);
@@ -1297,7 +1420,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       a1 += sw * ow[w].y;
     }
   };
-  __syncthreads();
+  stream_barrier(ctl);
   if (wave == 1) {
     trace_at(P, trw, 9);
     gu64 *dst = pg + (size_t)(g * S + c) * qpg * stride;   // partials of head g in chunk order
@@ -1324,15 +1447,15 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     trace_at(P, trw, 5);
   }
   if (c == 0 && S > 1) {
-    // The merging unit (c = 0 of each KV head), all waves.  Stream wave w polls
+    // The merging unit (c = 0 of each KV head), all stream waves.  Stream wave w polls
     // chunks w - 1, w + 6, ... of the group (their (m, l) and this lane's two o
     // dims, up to four chunks' words in flight at once, each pass re-reading
     // every stale word: one round trip per pass), folds them into one online
     // softmax state per head and leaves it in wml / wo; wave 1 then combines
     // the seven states into the head's output.
-    __syncthreads();   // wave 1 has read the unit's own states: wml / wo are free
+    stream_barrier(ctl);   // wave 1 has read the unit's own states: wml / wo are free
     if (wave == 1) trace_at(P, trw, 11);
-    if (wave > 0) {
+    {
       const gu64 *src = pg + (size_t)g * S * qpg * stride;
       const u64 tagw = (u64)tag_a << 32;
       for (int h = 0; h < qpg; ++h) {
@@ -1395,7 +1518,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       }
       if (bad && lane == 0) lds_st(&ctl->abort, 1u);
     }
-    __syncthreads();
+    stream_barrier(ctl);
     if (wave == 1) {
       if (trw >= 0) trace_at(P, trw, 12);
       for (int h = 0; h < qpg; ++h) {
@@ -1409,8 +1532,20 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       trace_at(P, trw, 13);
     }
   }
-  __syncthreads();
+  stream_barrier(ctl);
   return !lds_ld(&ctl->abort);
+}
+
+// attn_unit for this model's query heads per KV head (kQ: the next power of two).
+__device__ __forceinline__ bool attn_run(KP &P, Ctl *ctl, int l, int gen, unsigned tag_q, unsigned tag_a, int pos,
+                                         int u, const AttnPart &ap, unsigned char *lds, int trk) {
+  switch (P.qpg) {
+    case 1: return attn_unit<1>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
+    case 2: return attn_unit<2>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
+    case 3:
+    case 4: return attn_unit<4>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
+    default: return attn_unit<kMaxQpg>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
+  }
 }
 
 // ---------------------------------------------------------------- sampler
@@ -1675,11 +1810,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16 *hl = reinterpret_cast<_Float16 *>(smem + P.lds_h);
   float *part = reinterpret_cast<float *>(smem + P.lds_part);
-  float *red = reinterpret_cast<float *>(smem + P.lds_red);   // 64 floats
   Ctl *ctl = reinterpret_cast<Ctl *>(smem + P.lds_ctl);
   float *xown = reinterpret_cast<float *>(smem + P.lds_xown); // residual rows: output projection
   float *xres = reinterpret_cast<float *>(smem + P.lds_xres); // residual rows: down projection
-  unsigned char *alds = smem + P.lds_h;                       // attention / sampler scratch
+  unsigned char *alds = smem + P.lds_h;                       // sampler scratch (over the staged input)
+  unsigned char *attn_scratch = smem + P.lds_attn;            // attention scratch (stream waves)
   const int b = blockIdx.x, G = P.G, wave = wave_id(), lane = lane_id();
   const int L = P.L, d = P.d, dh = P.dh;
   const bool has_lm = !kPrefill && !P.hidden_io;
@@ -1711,6 +1846,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     if (kTrace)
       for (int i = 0; i < kTraceSlots * (5 * L + 2); ++i) trace_row(P, 0)[i] = 0ull;
     ctl->abort = 0;
+    ctl->abar = 0;
     for (int w = 0; w < kWaves; ++w) ctl->done[w] = 0;
     ctl->status = 0;
   }
@@ -1750,11 +1886,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     for (int t = 0; t < P.n_tokens; ++t) {
       const int pos = P.pos0 + t;
       const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
-      AttnSplit asp(pos, G, P.Hkv, P.window);
+      AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles);
       for (int l = 0; l < L; ++l) {
         const int q0 = t * ngp + 4 * l;
-        const bool win = layer_windowed(P, l);
-        const int S = asp.S[win], Lc = asp.Lc[win], kb = asp.kb[win];
+        const AttnPart &ap = asp.a[layer_windowed(P, l) ? 1 : 0];
         const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
         const int gen = (t * L + l) & 1;
         st.trace_k = t == P.trace_token ? 5 * l + 0 : -1;
@@ -1766,11 +1901,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
                           true))
           return;
         if (lds_ld(&ctl->abort)) return;
-        for (int u = b; u < P.Hkv * S; u += G)
-          if (!(P.qpg == 1 ? attn_unit<1>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, kb, alds, red,
-                                          u == b && t == P.trace_token ? 5 * l + 1 : -1)
-                           : attn_unit<kMaxQpg>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, kb, alds,
-                                                red, u == b && t == P.trace_token ? 5 * l + 1 : -1)))
+        for (int u = b; u < P.Hkv * ap.S; u += G)
+          if (!attn_run(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
+                        u == b && t == P.trace_token ? 5 * l + 1 : -1))
             return;
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
@@ -1812,7 +1945,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     const int pos = P.pos0 + t;
     const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
     if (kPrefill) token = P.in_tokens[t];
-    const AttnSplit asp(pos, G, P.Hkv, P.window);
+    const AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles);
     for (int l = 0; l < L; ++l) {
       KP &Pl = fresh(P);
       sy.P = &Pl;
@@ -1865,13 +1998,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tq = lap(sy, ST_STAGE, tq);
         trace(Pl, t, 5 * l + 0, 0);
         const float *pk = kind_part(part, K_QKV, Pl.part_rows);
-        wait_streams(ctl, q0);
+        if (!wait_streams(ctl, q0)) return;
         tq = lap(sy, ST_STREAMS, tq);
         trace(Pl, t, 5 * l + 0, 1);
         const unsigned tag = lvl + PH_QKV;
-        const size_t kvrow = ((size_t)l * Pl.max_seq + pos) * (size_t)nk;
-        _Float16 *kc = reinterpret_cast<_Float16 *>(Pl.kcache);
-        _Float16 *vc = reinterpret_cast<_Float16 *>(Pl.vcache);
+        // this layer's tile runs of the cache (k_elem / v_elem within a run)
+        const size_t run = (size_t)Pl.kv_tiles * kKvTile * dh;
+        _Float16 *kc = reinterpret_cast<_Float16 *>(Pl.kcache) + (size_t)l * Pl.Hkv * run;
+        _Float16 *vc = reinterpret_cast<_Float16 *>(Pl.vcache) + (size_t)l * Pl.Hkv * run;
         for (int i = lane; i < ge.nrows / 2; i += 64) {
           const float a = row_value(pk, 2 * i) * inv, bb = row_value(pk, 2 * i + 1) * inv;
           const int r = ge.r0 + 2 * i;
@@ -1889,14 +2023,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
               st_tag(qd + k, tag_f(y0, tag));
               st_tag(qd + k + half, tag_f(y1, tag));
             } else {
-              st_dev_h(kc, kvrow + (size_t)hd * dh + k, y0);
-              st_dev_h(kc, kvrow + (size_t)hd * dh + k + half, y1);
+              st_dev_h(kc, (size_t)hd * run + k_elem(dh, pos, k), y0);
+              st_dev_h(kc, (size_t)hd * run + k_elem(dh, pos, k + half), y1);
               st_tag(Pl.kc_t + gen * nkw + (size_t)hd * half + k, tag_h2(y0, y1, tag));
             }
           } else {
             const int rv = r - nq - nk;   // V rows in natural order, pairs (rv, rv + 1)
             const u64 w = tag_h2(a, bb, tag);
-            st_dev(reinterpret_cast<unsigned *>(vc + kvrow + rv), (unsigned)w);
+            int gv, ev;
+            head_split(rv, dh, gv, ev);
+            st_dev_h(vc, (size_t)gv * run + v_elem(dh, pos, ev), a);
+            st_dev_h(vc, (size_t)gv * run + v_elem(dh, pos, ev + 1), bb);
             st_tag(Pl.vc_t + gen * nkw + (size_t)(rv / 2), w);
           }
         }
@@ -1905,23 +2042,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         lap(sy, ST_EPI, tq);
       }
 
-      // ---------------- attention (all waves; split-K, last arriver merges)
-      {
-        const unsigned long long ta = stamp(sy);
-        trace(Pl, t, 5 * l + 1, 0);
-        const bool win = layer_windowed(Pl, l);
-        const int S = asp.S[win], Lc = asp.Lc[win], kb = asp.kb[win];
-        for (int u = b; u < Pl.Hkv * S; u += G)
-          if (!(Pl.qpg == 1 ? attn_unit<1>(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc, kb, alds, red,
-                                           u == b && t == Pl.trace_token ? 5 * l + 1 : -1)
-                            : attn_unit<kMaxQpg>(Pl, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, S, Lc,
-                                                 kb, alds, red, u == b && t == Pl.trace_token ? 5 * l + 1 : -1)))
-            return;
-        trace(Pl, t, 5 * l + 1, 1);
-        publish_vec(Pl, lvl + PH_ATTN);
-        trace(Pl, t, 5 * l + 1, 2);
-        lap(sy, ST_ATTN, ta);
-      }
+      // (attention runs on the stream waves alone, in an LDS area of its own:
+      // the sync wave goes on to poll the output projection's input)
 
       // ---------------- output projection + residual
       {
@@ -1953,7 +2075,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         // projection ago, so this wait is short.
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         asm volatile("" ::: "memory");
-        wait_streams(ctl, q0 + 1);
+        if (!wait_streams(ctl, q0 + 1)) return;
         tk = lap(sy, ST_STREAMS, tk);
         trace(Pl, t, 5 * l + 2, 1);
         const unsigned tag = lvl + PH_O;
@@ -1988,7 +2110,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         const float *pk = kind_part(part, K_GU, Pl.part_rows);
         gu64 *ad = (gu64 *)(Pl.a_t + (size_t)gen * (Pl.F / 2));
         asm volatile("" : "+s"(ad));   // computed now, not after the wait
-        wait_streams(ctl, q0 + 2);
+        if (!wait_streams(ctl, q0 + 2)) return;
         tk = lap(sy, ST_STREAMS, tk);
         trace(Pl, t, 5 * l + 3, 1);
         const unsigned tag = lvl + PH_GU;
@@ -2023,7 +2145,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         u64 *xo = Pl.xout_t + (size_t)gen * d;
         const bool host_out = Pl.hidden_io && l == L - 1;
         const float xo0 = lane < ge.nrows ? xres[lane] : 0.0f;
-        wait_streams(ctl, q0 + 3);
+        if (!wait_streams(ctl, q0 + 3)) return;
         tk = lap(sy, ST_STREAMS, tk);
         trace(Pl, t, 5 * l + 4, 1);
         const unsigned tag = lvl + PH_D;
@@ -2057,7 +2179,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       }
       trace(P, t, 5 * L, 0);
       const float *pk = kind_part(part, K_LM, P.part_rows);
-      wait_streams(ctl, qlm);
+      if (!wait_streams(ctl, qlm)) return;
       trace(P, t, 5 * L, 1);
       float best = -INFINITY;
       int bi = 0x7fffffff;
@@ -2174,6 +2296,28 @@ __global__ void __launch_bounds__(kThreads) lf_test_gumbel_kernel(const float *l
   }
 }
 
+// Natural [n][Hkv][dh] fp16 rows (positions pos0..) <-> the tiled cache of one
+// layer (kc, vc: the layer's first tile run; run: elements per run), one
+// thread per element.
+__global__ void __launch_bounds__(256) lf_kv_copy_kernel(_Float16 *kc, _Float16 *vc, _Float16 *k, _Float16 *v,
+                                                         long long n_elems, int Hkv, int dh, int pos0,
+                                                         long long run, int to_cache) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n_elems; i += (long long)gridDim.x * 256) {
+    const int e = (int)(i % dh);
+    const long long r = i / dh;
+    const int g = (int)(r % Hkv);
+    const int j = pos0 + (int)(r / Hkv);
+    const size_t ki = (size_t)g * run + k_elem(dh, j, e), vi = (size_t)g * run + v_elem(dh, j, e);
+    if (to_cache) {
+      kc[ki] = k[i];
+      vc[vi] = v[i];
+    } else {
+      k[i] = kc[ki];
+      v[i] = vc[vi];
+    }
+  }
+}
+
 // Weight packing: scale every column of an fp16 matrix (rows x 8*cols8,
 // 16-byte aligned) by the fp16 gain of that column (any 2-byte alignment),
 // eight elements per thread.
@@ -2247,6 +2391,22 @@ hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream) 
                            stream);
   return hipLaunchCooperativeKernel(monokernel_symbol(prefill), dim3(p.G), dim3(kThreads), args,
                                     (unsigned)p.lds_bytes, stream);
+}
+
+hipError_t launch_kv_copy(const Params &p, int l, int pos0, int n, void *k, void *v, bool to_cache,
+                          hipStream_t stream) {
+  const long long n_elems = (long long)n * p.Hkv * p.dh;
+  if (n_elems <= 0) return hipSuccess;
+  if (l < 0 || l >= p.L || pos0 < 0 || pos0 + n > p.kv_tiles * kKvTile) return hipErrorInvalidValue;
+  const long long run = (long long)p.kv_tiles * kKvTile * p.dh;
+  _Float16 *kc = reinterpret_cast<_Float16 *>(p.kcache) + (size_t)l * p.Hkv * run;
+  _Float16 *vc = reinterpret_cast<_Float16 *>(p.vcache) + (size_t)l * p.Hkv * run;
+  long long blocks = (n_elems + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(lf_kv_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kc, vc,
+                     reinterpret_cast<_Float16 *>(k), reinterpret_cast<_Float16 *>(v), n_elems, p.Hkv, p.dh, pos0,
+                     run, to_cache ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_scale_columns(void *w, size_t rows, int cols, const void *g, hipStream_t stream) {
