@@ -96,6 +96,8 @@ int validate(const lf_config *c) {
   if (!(c->temperature >= 0.0f)) return fail(nullptr, LF_EINVAL, "temperature must be >= 0");
   if (c->temperature > 0.0f && !(c->flags & LF_GUMBEL) && !(c->top_p > 0.0f))
     return fail(nullptr, LF_EINVAL, "top_p must be > 0");
+  if (!hidden && c->temperature > 0.0f && !(c->flags & LF_GUMBEL) && c->vocab > lf::kSampMaxVocab)
+    return fail(nullptr, LF_EUNSUPPORTED, "nucleus sampling supports vocabularies up to 393216");
   if (c->flags & ~(LF_HIDDEN_IO | LF_STATS | LF_GUMBEL)) return fail(nullptr, LF_EINVAL, "unknown flag bits");
   return LF_OK;
 }
@@ -435,12 +437,13 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);   // one phase kind's partial row sums
   // attention scratch: queries, current K/V row, per-wave (m, l) and per-wave o
   const size_t attn_b = (size_t)lf::attn_lds(P.qpg, dh).bytes;
-  const size_t samp_b = 4096;
-  // h, overlaid by the sampler scratch after the last layer; attention has an area of its own
-  size_t region_a = h_b;
-  if (samp_b > region_a) region_a = samp_b;
+  // the nucleus draw's scratch overlays the staged input and the attention area
+  const size_t samp_b = P.sampling == lf::SAMPLE_NUCLEUS ? (size_t)lf::kSampBytes : 0;
+  // h, then the attention area; the sampler scratch (after the last layer) overlays both
+  size_t region_a = align_up(h_b, 256);
+  if (samp_b > region_a + attn_b) region_a = align_up(samp_b - attn_b, 256);
   P.lds_h = 0;
-  P.lds_attn = (int)align_up(region_a, 256);
+  P.lds_attn = (int)region_a;
   P.lds_red = (int)align_up((size_t)P.lds_attn + attn_b, 256);
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + lf::kCtlBytes;
@@ -697,6 +700,7 @@ int lf_test_sample(const float *logits, int32_t n, float temperature, float top_
                    const int32_t *pos, int32_t m, int32_t *tokens, void *stream) {
   if (!logits || !pos || !tokens || n < 1 || m < 0) return fail(nullptr, LF_EINVAL, "bad argument");
   if (!(temperature > 0.0f) || !(top_p > 0.0f)) return fail(nullptr, LF_EINVAL, "temperature and top_p must be > 0");
+  if (n > lf::kSampMaxVocab) return fail(nullptr, LF_EUNSUPPORTED, "nucleus sampling supports up to 393216 logits");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const float inv_temp = (float)(1.0 / (double)temperature);
   hipError_t e = lf::launch_test_sample(logits, n, inv_temp, top_p, seed, pos, m, tokens, s);

@@ -46,6 +46,9 @@ constexpr int kTraceSlots = 16;          // timestamps per phase (LF_TRACE build
 constexpr int kStageRound = 64 * 40;      // tagged words one staging round reads (buffers are padded to it)
 constexpr int kStageRoundWide = 64 * 56;  // the SwiGLU vector's staging round
 constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB pieces in flight per stream wave (register ring)
+constexpr int kSampBytes = 60 * 1024;      // LDS of the nucleus draw (workgroup 0, after the lm_head)
+constexpr int kSampSegs = 6144;            // 64-index segments the nucleus draw's token search can hold
+constexpr int kSampMaxVocab = kSampSegs * 64;
 
 // Attention scratch in LDS (an area of its own, so the sync wave may stage the
 // next phase's input while the stream waves run attention): fp16 queries [qpg][dh], fp32 current K and V rows [dh] each, fp16

@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstddef>
 #include <mutex>
 
 #include "lf_internal.h"
@@ -150,6 +151,28 @@ __device__ __forceinline__ void wave_argmax(float &best, int &bi) {
 }
 // Whether no active lane has p set (one compare into a scalar lane mask).
 __device__ __forceinline__ bool wave_none(bool p) { return __builtin_amdgcn_ballot_w64(p) == 0ull; }
+// Wave-wide sum of 64-bit integers with the same DPP row steps (each a pair of
+// 32-bit moves and one 64-bit add; integer sums are exact in any order); the
+// total is read back from lane 63 into every lane.
+__device__ __forceinline__ unsigned long long wave_sum_u64_dpp(unsigned long long v) {
+#define LF_DPP_U64(ctrl, rmask)                                                                                 \
+  {                                                                                                            \
+    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)v, (ctrl), (rmask), 0xf, false); \
+    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(v >> 32), (ctrl), (rmask), 0xf, \
+                                                              false);                                          \
+    v += ((unsigned long long)hi << 32) | lo;                                                                  \
+  }
+  LF_DPP_U64(0xB1, 0xf)
+  LF_DPP_U64(0x4E, 0xf)
+  LF_DPP_U64(0x141, 0xf)
+  LF_DPP_U64(0x140, 0xf)
+  LF_DPP_U64(0x142, 0xa)
+  LF_DPP_U64(0x143, 0xc)
+#undef LF_DPP_U64
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
+}
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += (unsigned long long)__shfl_xor((long long)v, m, 64);
@@ -1646,7 +1669,10 @@ __device__ __forceinline__ unsigned long long mass_of(float z, float zmax) {
 #pragma clang fp contract(off)
   const float dz = z - zmax;
   if (dz < -23.0f) return 0ull;
-  return (unsigned long long)(expdef(dz) * 4294967296.0f);
+  // E(dz) 2^32 lies in [0, 2^32]: truncation to an integer is one u32 conversion
+  // below 2^32 (the same value as a u64 one); 2^32 itself (dz = 0) is set apart
+  const float v = expdef(dz) * 4294967296.0f;
+  return v >= 4294967296.0f ? (1ull << 32) : (unsigned long long)(unsigned)v;
 }
 
 // Order key: larger key = earlier in (z descending, index ascending) order.
@@ -1656,14 +1682,36 @@ __device__ __forceinline__ unsigned long long order_key(float z, int i) {
   return ((unsigned long long)b << 32) | (unsigned long long)(0xffffffffu - (unsigned)i);
 }
 
+// Nucleus draw scratch.  Pass 1 histograms the positive masses over 256 bins of
+// d = z* - z (a monotone function of z, so every element of a lower bin comes
+// earlier in the (z desc, index asc) order); the bin that holds the nucleus
+// boundary is then the only one whose order matters, and its elements (the
+// candidates, up to kSampCap) are kept in LDS for the radix select.
+constexpr int kSampBins = 256;
+constexpr int kSampCap = 2048;
+constexpr float kSampBinScale = 256.0f / 24.0f;   // d in [0, 23] -> bins 0 .. 245
+#ifndef LF_SAMP_BATCH
+#define LF_SAMP_BATCH 32
+#endif
+constexpr int kSampBatch = LF_SAMP_BATCH;   // rounds whose logits one thread requests at once
 struct SampLds {
-  unsigned long long mass[256];
-  unsigned cnt[256];
+  // (after the radix select these three arrays, contiguous, hold the segment
+  // sums of the token search: up to kSampSegs segments of 64 indices)
+  unsigned long long hm[kWaves][kSampBins];   // per-wave bin masses (pass 1)
+  unsigned long long ck[kSampCap];            // candidates' order keys
+  unsigned long long cq[kSampCap];            // candidates' masses
+  unsigned long long mass[256];               // bin totals, then one radix pass's digit masses
   unsigned long long wtot[kWaves];
   unsigned long long sel[4];
   float fred[kWaves];
   int ibc[4];
+  unsigned ncand;
 };
+static_assert(sizeof(SampLds) <= kSampBytes, "nucleus scratch exceeds its LDS space");
+static_assert(offsetof(SampLds, ck) == sizeof(unsigned long long) * kWaves * kSampBins &&
+                  offsetof(SampLds, cq) == offsetof(SampLds, ck) + sizeof(unsigned long long) * kSampCap &&
+                  kWaves * kSampBins + 2 * kSampCap == kSampSegs,
+              "segment sums overlay the bin histograms and the candidate list");
 
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, SampLds *s) {
   v = wave_sum_u64(v);
@@ -1675,67 +1723,208 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
   return t;
 }
 
+// Bin of a positive-mass element (d = z* - z <= 23).
+__device__ __forceinline__ int samp_bin(float z, float zmax) {
+#pragma clang fp contract(off)
+  const int b = (int)((zmax - z) * kSampBinScale);
+  return b < kSampBins - 1 ? b : kSampBins - 1;
+}
+
 // Temperature / top-p nucleus sampling with integer masses, by one workgroup:
 // z = logit * inv_temp; q_i = floor(E(z_i - z*) * 2^32) (0 below -23); the
 // nucleus is the shortest prefix of the (z desc, index asc) order whose mass
-// reaches ceil(top_p * C_V) in fp64, found by an 8-pass radix select on a 64-bit
-// order key; the Philox draw t = floor(r * C_N / 2^64) with r from counter
-// (pos, 0, 0, 0); the token is the first nucleus member in index order whose
-// running mass exceeds t.  Thread t owns the contiguous indices
-// [t * blk, t * blk + blk) and re-reads their logits in each pass.
+// reaches ceil(top_p * C_V) in fp64; the Philox draw t = floor(r * C_N / 2^64)
+// with r from counter (pos, 0, 0, 0); the token is the first nucleus member in
+// index order whose running mass exceeds t.  Thread t owns indices t + 512 k
+// (coalesced reads) and re-reads their logits in each pass.  The boundary is
+// found in two steps: the bin histogram gives the boundary bin and the mass of
+// the bins before it; an 8-pass radix select on a 64-bit (z, index) order key
+// then runs over that bin's candidates only (or, when they do not fit in LDS,
+// over every element of the bin).  The token: each wave sums its 64 nucleus
+// masses per round k (64 consecutive indices), an exclusive scan over the
+// (round, wave) sums in index order finds the segment holding t, and a wave
+// scan inside it the index.
+// Wave 0: the first entry i of the order i = 0, 1, .. (entry m[desc ? 255 - i : i]
+// of 256) at which base + the inclusive sum of the entries reaches need; returns
+// its slot in m and, in *before, base + the sum of the entries ahead of it.  Lane
+// l holds entries 4l .. 4l + 3 of the order; one 64-bit wave scan of the lane
+// totals and a ballot find it.  Falls back to the last entry if none does.
+__device__ __forceinline__ int scan_reach(const unsigned long long *m, bool desc, unsigned long long base,
+                                          unsigned long long need, unsigned long long *before) {
+  const int lane = lane_id();
+  unsigned long long e[4], tot = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * lane + k;
+    e[k] = m[desc ? 255 - i : i];
+    tot += e[k];
+  }
+  unsigned long long incl = tot;
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long y = (unsigned long long)__shfl_up((long long)incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  unsigned long long run = base + incl - tot;   // before this lane's first entry
+  int hit = -1;
+  unsigned long long hb = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (hit < 0 && e[k] > 0 && run + e[k] >= need) {
+      hit = 4 * lane + k;
+      hb = run;
+    }
+    run += e[k];
+  }
+  const unsigned long long mask = __builtin_amdgcn_ballot_w64(hit >= 0);
+  int idx;
+  unsigned long long bef;
+  if (mask) {
+    const int src = __builtin_ctzll(mask);
+    idx = __builtin_amdgcn_readlane(hit, src);
+    bef = ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(hb >> 32), src) << 32) |
+          (unsigned)__builtin_amdgcn_readlane((int)(unsigned)hb, src);
+  } else {
+    // (unreachable for consistent inputs: the entries hold at least need)
+    idx = 255;
+    bef = base + (unsigned long long)__shfl((long long)incl, 63, 64);
+  }
+  *before = bef;
+  return desc ? 255 - idx : idx;
+}
+
+// Temperature / top-p nucleus sampling with integer masses, by one workgroup:
+// z = logit * inv_temp; q_i = floor(E(z_i - z*) * 2^32) (0 below -23); the
+// nucleus is the shortest prefix of the (z desc, index asc) order whose mass
+// reaches ceil(top_p * C_V) in fp64; the Philox draw t = floor(r * C_N / 2^64)
+// with r from counter (pos, 0, 0, 0); the token is the first nucleus member in
+// index order whose running mass exceeds t.  Thread t owns indices t + 512 k
+// (coalesced reads, eight rounds' loads in flight at once) and re-reads their
+// logits in each pass.  The boundary is found in two steps: the bin histogram
+// gives the boundary bin and the mass of the bins before it; an 8-pass radix
+// select on a 64-bit (z, index) order key then runs over that bin's candidates
+// only (or, when they do not fit in LDS, over every element of the bin).  The
+// token: each wave sums its 64 nucleus masses per round k (64 consecutive
+// indices), an exclusive scan over the (round, wave) sums in index order finds
+// the segment holding t, and a wave scan inside it the index.
+// lm_max (nullable): the n_lm per-workgroup maxima of the logits, from which z*
+// is taken (the maximum of the rounded products is the rounded product of the
+// maximum) instead of a pass over every logit.
 __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv_temp, float top_p,
-                                           unsigned long long seed, int pos, SampLds *s) {
-  const int tid = tid_x();
-  const int blk = (V + kThreads - 1) / kThreads;
-  const int i0 = tid * blk;
-  auto valid = [&](int j) __attribute__((always_inline)) { return i0 + j < V; };
-  auto zval = [&](int j) __attribute__((always_inline)) -> float { return scaled_logit(logits, i0 + j, inv_temp); };
-  const int nj = blk;
+                                           unsigned long long seed, int pos, SampLds *s,
+                                           lds_u64 *tr = nullptr, const float *lm_max = nullptr, int n_lm = 0) {
+  const int tid = tid_x(), wave = wave_id(), lane = lane_id();
+  auto stamp_at = [&](int j) __attribute__((always_inline)) {   // LF_TRACE builds: stage times
+    if (kTrace && tr && tid == 0) tr[j] = now_ticks();
+  };
+  stamp_at(3);
+  const int nr = (V + kThreads - 1) / kThreads;   // rounds
+  // body(k, i, z) for every round k (index i) of this thread, kSampBatch rounds'
+  // logits requested at once
+  auto each = [&](auto &&body) __attribute__((always_inline)) {
+    for (int k0 = 0; k0 < nr; k0 += kSampBatch) {
+      // (unconditional loads, clamped into range: a guarded load makes the
+      // compiler wait for it at the end of its branch)
+      float zc[kSampBatch];
+#pragma unroll
+      for (int u = 0; u < kSampBatch; ++u)
+        zc[u] = scaled_logit(logits, min((k0 + u) * kThreads + tid, V - 1), inv_temp);
+#pragma unroll
+      for (int u = 0; u < kSampBatch; ++u) {
+        const int i = (k0 + u) * kThreads + tid;
+        if (k0 + u < nr && i < V) body(k0 + u, i, zc[u]);
+      }
+    }
+  };
   float zm = -INFINITY;
-  for (int j = 0; j < nj; ++j)
-    if (valid(j)) zm = fmaxf(zm, zval(j));
+  if (lm_max) {
+#pragma clang fp contract(off)
+    for (int i = tid; i < n_lm; i += kThreads) zm = fmaxf(zm, lm_max[i]);
+    zm = zm * inv_temp;
+  } else {
+    each([&](int, int, float z) __attribute__((always_inline)) { zm = fmaxf(zm, z); });
+  }
   zm = wave_max(zm);
-  if (lane_id() == 0) s->fred[wave_id()] = zm;
+  if (lane == 0) s->fred[wave] = zm;
+  for (int i = tid; i < kWaves * kSampBins; i += kThreads) (&s->hm[0][0])[i] = 0ull;
+  if (tid == 0) s->ncand = 0u;
   __syncthreads();
   float zmax = -INFINITY;
   for (int w = 0; w < kWaves; ++w) zmax = fmaxf(zmax, s->fred[w]);
-  __syncthreads();
+  stamp_at(4);
+  // pass 1: total mass and the per-wave bin histograms of the positive masses
   unsigned long long part = 0;
-  for (int j = 0; j < nj; ++j)
-    if (valid(j)) part += mass_of(zval(j), zmax);
-  const unsigned long long CV = block_sum_u64(part, s);
+  each([&](int, int, float z) __attribute__((always_inline)) {
+    const unsigned long long q = mass_of(z, zmax);
+    part += q;
+    if (q) atomicAdd(&s->hm[wave][samp_bin(z, zmax)], q);
+  });
+  const unsigned long long CV = block_sum_u64(part, s);   // (its barriers also publish the histograms)
   const unsigned long long Mstar = (unsigned long long)ceil((double)top_p * (double)CV);
-  unsigned long long prefix = 0, pmask = 0, above = 0;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kThreads) { s->mass[i] = 0; s->cnt[i] = 0; }
-    __syncthreads();
-    for (int j = 0; j < nj; ++j) {
-      if (valid(j)) {
-        const float z = zval(j);
-        const unsigned long long key = order_key(z, i0 + j);
-        if ((key & pmask) == prefix) {
-          const int dg = (int)((key >> shift) & 255ull);
-          atomicAdd(&s->mass[dg], mass_of(z, zmax));
-          atomicAdd(&s->cnt[dg], 1u);
-        }
+  stamp_at(5);
+  for (int b = tid; b < kSampBins; b += kThreads) {
+    unsigned long long m = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) m += s->hm[w][b];
+    s->mass[b] = m;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // the first bin whose cumulative mass reaches M* (the bins hold C_V >= M*)
+    unsigned long long cum;
+    const int beta = scan_reach(s->mass, false, 0ull, Mstar, &cum);
+    if (lane == 0) {
+      s->sel[0] = (unsigned long long)beta;
+      s->sel[1] = cum;
+    }
+  }
+  __syncthreads();
+  const int beta = (int)s->sel[0];
+  unsigned long long above = s->sel[1];
+  // the boundary bin's elements (positive mass) into the candidate list (the
+  // bin first: it is cheap, and only the boundary bin's masses are needed)
+  each([&](int, int i, float z) __attribute__((always_inline)) {
+    if (samp_bin(z, zmax) != beta) return;
+    const unsigned long long q = mass_of(z, zmax);
+    if (q) {
+      const unsigned c = atomicAdd(&s->ncand, 1u);
+      if (c < (unsigned)kSampCap) {
+        s->ck[c] = order_key(z, i);
+        s->cq[c] = q;
       }
     }
+  });
+  __syncthreads();
+  const unsigned ncand = s->ncand;
+  const bool listed = ncand <= (unsigned)kSampCap;
+  stamp_at(6);
+  // radix select on the order key among the boundary bin's elements
+  unsigned long long prefix = 0, pmask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kThreads) s->mass[i] = 0;
     __syncthreads();
-    if (tid == 0) {
-      unsigned long long cum = 0;
-      int pick = -1, lowest = -1;
-      unsigned long long cum_lowest = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        if (s->cnt[dg] == 0) continue;
-        if (above + cum + s->mass[dg] >= Mstar) { pick = dg; break; }
-        lowest = dg;
-        cum_lowest = cum;
-        cum += s->mass[dg];
+    auto add = [&](unsigned long long key, unsigned long long q) __attribute__((always_inline)) {
+      if ((key & pmask) == prefix) atomicAdd(&s->mass[(int)((key >> shift) & 255ull)], q);
+    };
+    if (listed) {
+      for (unsigned c = (unsigned)tid; c < ncand; c += kThreads) add(s->ck[c], s->cq[c]);
+    } else {
+      each([&](int, int i, float z) __attribute__((always_inline)) {
+        if (samp_bin(z, zmax) != beta) return;
+        const unsigned long long q = mass_of(z, zmax);
+        if (q) add(order_key(z, i), q);
+      });
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // digits in descending key order (earliest first): the first whose
+      // cumulative mass reaches M* holds the boundary
+      unsigned long long bef;
+      const int pick = scan_reach(s->mass, true, above, Mstar, &bef);
+      if (lane == 0) {
+        s->sel[0] = prefix | ((unsigned long long)pick << shift);
+        s->sel[1] = pmask | (255ull << shift);
+        s->sel[2] = bef;
       }
-      if (pick < 0) { pick = lowest; cum = cum_lowest; }   // mass never reached: take every token
-      s->sel[0] = prefix | ((unsigned long long)pick << shift);
-      s->sel[1] = pmask | (255ull << shift);
-      s->sel[2] = above + cum;
     }
     __syncthreads();
     prefix = s->sel[0];
@@ -1743,47 +1932,80 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
     above = s->sel[2];
     __syncthreads();
   }
-  const unsigned long long kappa = prefix;
+  const unsigned long long kappa = prefix;   // the boundary element's key: the nucleus is key >= kappa
+  stamp_at(7);
+  // nucleus masses summed per (round, wave) segment of 64 consecutive indices
+  // (members: every element of a bin before the boundary bin, and in it those
+  // with key >= kappa; a positive mass lies in bins 0 .. 245, so an element of
+  // a later bin or without mass contributes nothing)
+  unsigned long long *segs = &s->hm[0][0];
   unsigned long long local = 0;
-  for (int j = 0; j < nj; ++j) {
-    if (valid(j)) {
-      const float z = zval(j);
-      if (order_key(z, i0 + j) >= kappa) local += mass_of(z, zmax);
-    }
+  auto segment = [&](int k, float z) __attribute__((always_inline)) {
+    const int i = k * kThreads + tid;
+    const int bn = samp_bin(z, zmax);
+    const bool member = i < V && (bn < beta || (bn == beta && order_key(z, i) >= kappa));
+    const unsigned long long q = member ? mass_of(z, zmax) : 0ull;
+    local += q;
+    const unsigned long long sg = wave_sum_u64_dpp(q);
+    if (lane == 0) segs[k * kWaves + wave] = sg;   // segment (k, wave): indices 512 k + 64 wave ..
+  };
+  for (int k0 = 0; k0 < nr; k0 += kSampBatch) {
+    float zc[kSampBatch];
+#pragma unroll
+    for (int u = 0; u < kSampBatch; ++u) zc[u] = scaled_logit(logits, min((k0 + u) * kThreads + tid, V - 1), inv_temp);
+#pragma unroll
+    for (int u = 0; u < kSampBatch; ++u)
+      if (k0 + u < nr) segment(k0 + u, zc[u]);
   }
+  if (tid == 0) s->ibc[0] = -1;
   const unsigned long long CN = block_sum_u64(local, s);
+  stamp_at(8);
   unsigned ctr[4] = {(unsigned)pos, 0u, 0u, 0u};
   philox4x32_10(ctr, (unsigned)(seed & 0xffffffffull), (unsigned)(seed >> 32));
   const unsigned long long r = ((unsigned long long)ctr[1] << 32) | ctr[0];
   const unsigned long long t = __umul64hi(r, CN);
-  // exclusive scan of the per-thread masses (thread order = index order)
-  unsigned long long incl = local;
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long y = (unsigned long long)__shfl_up((long long)incl, off, 64);
-    if (lane_id() >= off) incl += y;
-  }
-  if (lane_id() == 63) s->wtot[wave_id()] = incl;
-  if (tid == 0) s->ibc[0] = -1;
-  __syncthreads();
-  unsigned long long base = 0;
-  for (int w = 0; w < wave_id(); ++w) base += s->wtot[w];
-  const unsigned long long excl = base + incl - local;
-  if (local > 0 && excl <= t && t < excl + local) {
-    unsigned long long run = excl;
-    int found = -1;
-    for (int j = 0; j < nj; ++j) {
-      if (found < 0 && valid(j)) {
-        const float z = zval(j);
-        if (order_key(z, i0 + j) >= kappa) {
-          run += mass_of(z, zmax);
-          if (run > t) found = i0 + j;
-        }
+  if (wave == 0) {
+    // the segment holding t: exclusive scan of the nr * 8 segment sums in index order
+    const int nseg = nr * kWaves;
+    unsigned long long base = 0;
+    for (int c0 = 0; c0 < nseg; c0 += 64) {
+      const int c = c0 + lane;
+      const unsigned long long v = c < nseg ? segs[c] : 0ull;
+      unsigned long long incl = v;
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long y = (unsigned long long)__shfl_up((long long)incl, off, 64);
+        if (lane >= off) incl += y;
       }
+      const unsigned long long ex = base + incl - v;
+      if (v > 0 && ex <= t && t < ex + v) {
+        s->sel[0] = (unsigned long long)c;
+        s->sel[1] = ex;
+      }
+      base += (unsigned long long)__shfl((long long)incl, 63, 64);
     }
-    s->ibc[0] = found;
+  }
+  __syncthreads();
+  const int seg = (int)s->sel[0];
+  if (wave == seg % kWaves) {
+    // inside the segment: the lane whose inclusive running mass first exceeds t
+    const int k = seg / kWaves, i = k * kThreads + tid;
+    unsigned long long q = 0;
+    if (i < V) {
+      const float z = scaled_logit(logits, i, inv_temp);
+      if (order_key(z, i) >= kappa) q = mass_of(z, zmax);
+    }
+    unsigned long long incl = q;
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long y = (unsigned long long)__shfl_up((long long)incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const unsigned long long ex = s->sel[1] + incl - q;
+    if (q > 0 && ex <= t && t < ex + q) s->ibc[0] = i;
   }
   __syncthreads();
   const int tok = s->ibc[0];
+  stamp_at(9);
+  if (kTrace && tr && tid == 0) tr[10] = ncand;
   __syncthreads();
   return tok;
 }
@@ -1922,7 +2144,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
           if (lds_ld(&ctl->abort)) return;
           if (!wait_all_waves(sy, 0, G, lvl_lm, true)) return;
-          sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds));
+          sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds),
+                      t == P.trace_token ? trace_row(P, 5 * L + 1) : nullptr, P.lm_val, G);
         }
       }
     }
@@ -2204,8 +2427,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     if (b == 0) {
       int tok;
       if (P.sampling == SAMPLE_NUCLEUS) {
+        trace(P, t, 5 * L + 1, 0);
         if (!wait_all_waves(sy, 0, G, lvl_lm, true)) { fail(); return; }
-        tok = sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds));
+        trace(P, t, 5 * L + 1, 1);
+        tok = sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds),
+                          t == P.trace_token ? trace_row(P, 5 * L + 1) : nullptr, P.lm_val, G);
       } else {
         if (!poll_level(sy, 0, G, lvl_lm)) {
           fail();
@@ -2257,7 +2483,8 @@ __global__ void lf_test_expdef_kernel(const float *x, float *y, long long n) {
 __global__ void __launch_bounds__(kThreads) lf_test_sample_kernel(const float *logits, int n, float inv_temp,
                                                                  float top_p, unsigned long long seed,
                                                                  const int *pos, int *tokens) {
-  __shared__ SampLds s;
+  extern __shared__ __align__(16) unsigned char samp_lds[];
+  SampLds &s = *reinterpret_cast<SampLds *>(samp_lds);
   const int c = blockIdx.x;
   const int tok = sample_topp(logits + (size_t)c * n, n, inv_temp, top_p, seed, pos[c], &s);
   if (threadIdx.x == 0) tokens[c] = tok;
@@ -2448,8 +2675,15 @@ hipError_t launch_test_gumbel(const float *logits, int n, float inv_temp, unsign
 hipError_t launch_test_sample(const float *logits, int n, float inv_temp, float top_p, unsigned long long seed,
                               const int *pos, int m, int *tokens, hipStream_t stream) {
   if (m <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lf_test_sample_kernel, dim3(m), dim3(kThreads), 0, stream, logits, n, inv_temp, top_p,
-                     seed, pos, tokens);
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&lf_test_sample_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SampLds));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(lf_test_sample_kernel, dim3(m), dim3(kThreads), sizeof(SampLds), stream, logits, n, inv_temp,
+                     top_p, seed, pos, tokens);
   return hipGetLastError();
 }
 
