@@ -263,6 +263,11 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.hidden_io = hidden ? 1 : 0;
   P.window = c.sliding_window;
   P.attn_unit_tiles = lf::kWaves - 1;   // one tile per stream wave
+  // Workgroups without attention units hold back the output projection's first
+  // ring round ~3.5 us (350 ticks of the 100 MHz clock), about one attention
+  // pass at short contexts, so that the K/V loads meet a quieter memory system.
+  P.o_refill_delay = 350;
+  if (const char *s = std::getenv("LF_O_REFILL_DELAY_NS")) P.o_refill_delay = (unsigned)(std::atof(s) / 10.0);
   if (const char *s = std::getenv("LF_ATTN_UNIT_TILES")) {
     const int v = std::atoi(s);
     if (v >= 1 && v <= lf::kWaves - 1) P.attn_unit_tiles = v;

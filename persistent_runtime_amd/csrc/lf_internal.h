@@ -89,6 +89,8 @@ struct Params {
   int hidden_io, sampling;   // sampling: a SampleMode
   int window;                          // sliding-window length (0: none)
   int attn_unit_tiles;                 // most KV tiles per attention unit (1 .. 7)
+  unsigned o_refill_delay;             // ticks (100 MHz) a workgroup without attention units waits
+                                       // after the QKV phase before prefetching the output projection
   unsigned long long window_layers;    // bit l: layer l attends over the window
   int levels_per_token;
   // weights (library-owned, packed)

@@ -2123,10 +2123,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
                           true))
           return;
         if (lds_ld(&ctl->abort)) return;
-        for (int u = b; u < P.Hkv * ap.S; u += G)
-          if (!attn_run(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
-                        u == b && t == P.trace_token ? 5 * l + 1 : -1))
-            return;
+        if (b < P.Hkv * ap.S) {
+          for (int u = b; u < P.Hkv * ap.S; u += G)
+            if (!attn_run(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
+                          u == b && t == P.trace_token ? 5 * l + 1 : -1))
+              return;
+        } else if (2 * P.Hkv * ap.S <= G) {
+          // a workgroup without attention units, while attention runs on few:
+          // hold back the output projection's first round for a while, so that
+          // the K/V loads meet less traffic
+          const unsigned t_qkv = (unsigned)now_ticks();
+          while ((unsigned)now_ticks() - t_qkv < P.o_refill_delay) __builtin_amdgcn_s_sleep(2);
+        }
         if (qkv_rounds) st.refill();
         st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
         if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, stage_spec(P, ctl, K_O, t, l, gen, lvl, xown, xres))) return;
