@@ -2109,52 +2109,49 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       const int pos = P.pos0 + t;
       const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
       AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles);
-      for (int l = 0; l < L; ++l) {
-        const int q0 = t * ngp + 4 * l;
-        const AttnPart &ap = asp.a[layer_windowed(P, l) ? 1 : 0];
+      // The token's GEMV phases (four per layer, then the lm_head) in one loop,
+      // so that the phase code exists once: a layer's instruction footprint then
+      // stays within the instruction cache.
+#pragma clang loop unroll(disable)
+      for (int g = 0; g < ngp; ++g) {
+        const bool lm = g >= 4 * L;
+        const int kind = lm ? K_LM : (g & 3);
+        const int l = lm ? L : (g >> 2);
         const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
         const int gen = (t * L + l) & 1;
-        st.trace_k = t == P.trace_token ? 5 * l + 0 : -1;
+        const bool qkv = kind == K_QKV;
+        st.trace_k = t == P.trace_token ? 5 * l + (qkv || lm ? 0 : kind + 1) : -1;
         // The refill after the QKV phase (the O phase's first round) waits until
         // after attention: this wave's loads complete in order, so attention's
         // K/V loads would otherwise queue behind it.
-        const bool qkv_rounds = st_has_rounds(st, K_QKV, ctl);
-        if (!stream_phase(st, q0 + 0, K_QKV, ctl, hl, part, stage_spec(P, ctl, K_QKV, t, l, gen, lvl, xown, xres),
-                          true))
+        const bool qkv_rounds = qkv && st_has_rounds(st, K_QKV, ctl);
+        if (!stream_phase(st, t * ngp + g, kind, ctl, hl, part, stage_spec(P, ctl, kind, t, l, gen, lvl, xown, xres),
+                          qkv))
           return;
-        if (lds_ld(&ctl->abort)) return;
-        if (b < P.Hkv * ap.S) {
-          for (int u = b; u < P.Hkv * ap.S; u += G)
-            if (!attn_run(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
-                          u == b && t == P.trace_token ? 5 * l + 1 : -1))
-              return;
-        } else if (2 * P.Hkv * ap.S <= G) {
-          // a workgroup without attention units, while attention runs on few:
-          // hold back the output projection's first round for a while, so that
-          // the K/V loads meet less traffic
-          const unsigned t_qkv = (unsigned)now_ticks();
-          while ((unsigned)now_ticks() - t_qkv < P.o_refill_delay) __builtin_amdgcn_s_sleep(2);
-        }
-        if (qkv_rounds) st.refill();
-        st.trace_k = t == P.trace_token ? 5 * l + 2 : -1;
-        if (!stream_phase(st, q0 + 1, K_O, ctl, hl, part, stage_spec(P, ctl, K_O, t, l, gen, lvl, xown, xres))) return;
-        st.trace_k = t == P.trace_token ? 5 * l + 3 : -1;
-        if (!stream_phase(st, q0 + 2, K_GU, ctl, hl, part, stage_spec(P, ctl, K_GU, t, l, gen, lvl, xown, xres))) return;
-        st.trace_k = t == P.trace_token ? 5 * l + 4 : -1;
-        if (!stream_phase(st, q0 + 3, K_D, ctl, hl, part, stage_spec(P, ctl, K_D, t, l, gen, lvl, xown, xres))) return;
-      }
-      if (has_lm) {
-        st.trace_k = t == P.trace_token ? 5 * L : -1;
-        if (!stream_phase(st, t * ngp + 4 * L, K_LM, ctl, hl, part,
-                          stage_spec(P, ctl, K_LM, t, L, 0, lv0 + (unsigned)(L * PH_PER_LAYER), xown, xres)))
-          return;
-        if (b == 0 && P.sampling == SAMPLE_NUCLEUS) {
-          const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
+        if (qkv) {
+          const AttnPart &ap = asp.a[layer_windowed(P, l) ? 1 : 0];
           if (lds_ld(&ctl->abort)) return;
-          if (!wait_all_waves(sy, 0, G, lvl_lm, true)) return;
-          sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds),
-                      t == P.trace_token ? trace_row(P, 5 * L + 1) : nullptr, P.lm_val, G);
+          if (b < P.Hkv * ap.S) {
+            for (int u = b; u < P.Hkv * ap.S; u += G)
+              if (!attn_run(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
+                            u == b && t == P.trace_token ? 5 * l + 1 : -1))
+                return;
+          } else if (2 * P.Hkv * ap.S <= G) {
+            // a workgroup without attention units, while attention runs on few:
+            // hold back the output projection's first round for a while, so that
+            // the K/V loads meet less traffic
+            const unsigned t_qkv = (unsigned)now_ticks();
+            while ((unsigned)now_ticks() - t_qkv < P.o_refill_delay) __builtin_amdgcn_s_sleep(2);
+          }
+          if (qkv_rounds) st.refill();
         }
+      }
+      if (has_lm && b == 0 && P.sampling == SAMPLE_NUCLEUS) {
+        const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
+        if (lds_ld(&ctl->abort)) return;
+        if (!wait_all_waves(sy, 0, G, lvl_lm, true)) return;
+        sample_topp(P.logits, P.V, P.inv_temp, P.top_p, P.seed, pos, reinterpret_cast<SampLds *>(alds),
+                    t == P.trace_token ? trace_row(P, 5 * L + 1) : nullptr, P.lm_val, G);
       }
     }
     if (st.timed && lane == 0) {
