@@ -463,7 +463,20 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (lds_limit <= 0) lds_limit = 65536;
   if ((long long)lds_end > lds_limit)
     return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
-  P.lds_bytes = (int)lds_end;
+  // The LDS left over can hold each stream wave's gate/up prefetch: LF_GU_PF
+  // 1-KB pieces per wave, as many as fit.  Off by default: measured end to end
+  // it costs more (the burst delays the output projection's input) than the
+  // shorter gate/up phase saves.
+  {
+    const long long per_piece = (long long)lf::kNcwHost * 1024;
+    long long fit = ((long long)lds_limit - (long long)lds_end) / per_piece;
+    long long want = 0;
+    if (const char *s = std::getenv("LF_GU_PF")) want = std::atoll(s);
+    if (want < 0) want = 0;
+    P.gu_pf = (int)(want < fit ? want : fit);
+    P.lds_pf = (int)lds_end;
+  }
+  P.lds_bytes = (int)(lds_end + (size_t)P.gu_pf * lf::kNcwHost * 1024);
   P.plain_launch = (std::getenv("LF_PLAIN_LAUNCH") && std::atoi(std::getenv("LF_PLAIN_LAUNCH")) != 0) ? 1 : 0;
   for (int pf = 0; pf < 2; ++pf) {
     if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0), hipFuncAttributeMaxDynamicSharedMemorySize,

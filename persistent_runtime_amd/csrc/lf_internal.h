@@ -8,6 +8,7 @@ namespace lf {
 
 constexpr int kThreads = 512;          // 8 wave64s per workgroup
 constexpr int kWaves = kThreads / 64;
+constexpr int kNcwHost = kWaves - 1;   // stream waves per workgroup
 constexpr int kMaxSplit = 64;          // most split-K chunks per KV head
 // The KV cache of one (layer, KV head) is a run of tiles of kKvTile positions,
 // each 128 * head_dim bytes for K and for V:
@@ -89,6 +90,7 @@ struct Params {
   int hidden_io, sampling;   // sampling: a SampleMode
   int window;                          // sliding-window length (0: none)
   int attn_unit_tiles;                 // most KV tiles per attention unit (1 .. 7)
+  int gu_pf;                           // gate/up pieces per stream wave prefetched into LDS during attention
   unsigned o_refill_delay;             // ticks (100 MHz) a workgroup without attention units waits
                                        // after the QKV phase before prefetching the output projection
   unsigned long long window_layers;    // bit l: layer l attends over the window
@@ -136,7 +138,7 @@ struct Params {
   unsigned long long timeout_ticks;
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_attn, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_bytes;
+  int lds_h, lds_attn, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_pf, lds_bytes;
   int part_rows, hmax;
 };
 

@@ -284,6 +284,9 @@ struct Ctl {
   // The partition of every phase kind among the stream waves, fixed for the
   // launch: computed once so that no phase divides by the pieces per row.
   Slice slice[K_COUNT][kNcw];
+  // The first pieces of each stream wave's gate/up share, prefetched into its
+  // own LDS area before the phase (slice[K_GU] then holds the rest).
+  Slice gu_pf[kNcw];
 };
 static_assert(sizeof(Ctl) <= kCtlBytes, "workgroup control block exceeds its LDS space");
 
@@ -946,6 +949,81 @@ __device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, cons
   return uniform_slice(ctl, kind, st.cw).n > 0;
 }
 
+// Gate/up prefetch.  During attention most workgroups have nothing to stream
+// but the output projection's first round, so each stream wave copies the first
+// pieces of its gate/up share for layer l into an LDS area of its own with
+// direct-to-LDS loads (lane i's 16 bytes to byte 16 i of the piece's KB).  They
+// complete in order with the wave's other loads; the gate/up phase waits for
+// them before it reads the area.
+__device__ __forceinline__ unsigned char *gu_pf_area(const KP &P, int cw) {
+  extern __shared__ __align__(16) unsigned char lf_dyn_lds[];
+  return lf_dyn_lds + P.lds_pf + (size_t)cw * P.gu_pf * 1024;
+}
+__device__ __forceinline__ Slice uniform_gu_pf(const Ctl *ctl, int cw) {
+  const Slice sl = ctl->gu_pf[cw];
+  return Slice{__builtin_amdgcn_readfirstlane(sl.n), __builtin_amdgcn_readfirstlane(sl.row),
+               __builtin_amdgcn_readfirstlane(sl.kp), 0};
+}
+__device__ __forceinline__ void gu_prefetch(KP &P, const Ctl *ctl, int cw, int l) {
+  const Slice ps = uniform_gu_pf(ctl, cw);
+  if (ps.n <= 0) return;
+  const Geo ge = uniform_geo(ctl, K_GU);
+  const int lane = lane_id();
+  const int tailv = ge.kv - (ge.ppr - 1) * 64;
+  const long long adv_last = (long long)ge.kv * 16 - (long long)(ge.ppr - 1) * 1024;
+  const unsigned char *p = phase_base(P, ge, K_GU, l) + ((size_t)ps.row * ge.kv * 16 + (size_t)ps.kp * 1024);
+  unsigned char *dst = gu_pf_area(P, cw);
+  int kp = ps.kp;
+  for (int j = 0; j < ps.n; ++j) {
+    const bool last = kp == ge.ppr - 1;
+    const int v = last ? min(lane, tailv - 1) : lane;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(p + v * 16),
+                                     (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 2);
+    if (last) {
+      kp = 0;
+      p += adv_last;
+    } else {
+      ++kp;
+      p += 1024;
+    }
+  }
+}
+// Use the prefetched pieces: per-lane dot products over each piece, a wave sum
+// into part[row][cw] at every row end and at the wave's last piece (when no
+// ring pieces follow).  Returns the running sum of a row the ring part goes on
+// with.
+__device__ __forceinline__ float gu_pf_consume(const KP &P, const Ctl *ctl, int cw, const _Float16 *h, float *pk,
+                                               const Geo &ge, bool ring_follows) {
+  const Slice ps = uniform_gu_pf(ctl, cw);
+  float acc = 0.0f;
+  if (ps.n <= 0) return acc;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const int lane = lane_id();
+  const int tailv = ge.kv - (ge.ppr - 1) * 64;
+  const unsigned char *src = gu_pf_area(P, cw) + lane * 16;
+  const unsigned char *hb = reinterpret_cast<const unsigned char *>(h);
+  int kp = ps.kp, row = ps.row;
+  for (int j = 0; j < ps.n; ++j) {
+    const bool last = kp == ge.ppr - 1;
+    const int v = last ? min(lane, tailv - 1) : lane;
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(src + j * 1024);
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(hb + kp * 1024 + v * 16);
+    if (!last || lane < tailv) acc = dot8(w, x, acc);
+    if (last || (j == ps.n - 1 && !ring_follows)) {
+      const float sum = wave_sum(acc);
+      if (lane == 0) pk[row * 8 + cw] = sum;
+      acc = 0.0f;
+    }
+    if (last) {
+      kp = 0;
+      ++row;
+    } else {
+      ++kp;
+    }
+  }
+  return acc;
+}
+
 // A stream wave's share of GEMV phase q: consume its pieces round by round from
 // the register ring, refilling each slot as it is freed, and leave one partial
 // row sum per (row, wave) in part[row * 8 + cw].  Returns false if the sync wave
@@ -974,6 +1052,9 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
   const int ppr = ge.ppr, tailv = ge.kv - (ge.ppr - 1) * 64;
   const int n = sl.n;
   const int nr = (n + kRing - 1) / kRing;
+  float acc = 0.0f;
+  if (kind == K_GU && st.P->gu_pf > 0)
+    acc = gu_pf_consume(*st.P, ctl, st.cw, h, kind_part(part, K_GU, fresh(*st.P).part_rows), ge, nr > 0);
   if (nr > 0) {
     // The ring holds this phase's first round.  If the phase has more pieces
     // than one round, the streamer still points into this phase: its cursor
@@ -994,7 +1075,6 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
     ra.tm = tailv >= 64 ? ~0ull : ((1ull << tailv) - 1ull);
     ra.loff = (unsigned)(lane * 16);
     ra.toff = (unsigned)(min(lane, tailv - 1) * 16);
-    float acc = 0.0f;
     stream_rounds(ra, acc);
     if (more) {   // the rounds issued the rest of this phase's pieces
       st.left = 0;
@@ -2061,6 +2141,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       for (int cw = 0; cw < kNcw; ++cw) {
         int lo, hi;
         wave_slice(ge.nrows * ge.ppr, cw, lo, hi);
+        if (k == K_GU) {
+          const int npf = min(hi - lo, P.gu_pf);
+          ctl->gu_pf[cw] = Slice{npf, npf > 0 ? lo / ge.ppr : 0, npf > 0 ? lo % ge.ppr : 0, 0};
+          lo += npf;
+        }
         const int row = lo < hi ? lo / ge.ppr : 0;
         ctl->slice[k][cw] = Slice{hi - lo, row, lo < hi ? lo - row * ge.ppr : 0, 0};
       }
@@ -2144,6 +2229,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
             while ((unsigned)now_ticks() - t_qkv < P.o_refill_delay) __builtin_amdgcn_s_sleep(2);
           }
           if (qkv_rounds) st.refill();
+          if (P.gu_pf > 0) gu_prefetch(P, ctl, st.cw, l);
         }
       }
       if (has_lm && b == 0 && P.sampling == SAMPLE_NUCLEUS) {

@@ -198,6 +198,33 @@ def test_tiny_smaller_grid_same_results(lf, orc, tiny, monkeypatch):
     teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 6), engine=eng)
 
 
+@pytest.mark.parametrize("pieces", [16, 3])
+def test_gate_up_lds_prefetch(lf, orc, tiny, monkeypatch, pieces):
+    """The gate/up prefetch into LDS (off by default): the tiny model's rows of
+    32 vectors (one masked piece per row, whole wave shares in LDS) and the
+    2.2B layer shape, whose 16- or 3-piece prefetch ends inside a row of five
+    pieces, so the ring part goes on with the running row sum."""
+    import torch
+    monkeypatch.setenv("LF_GU_PF", str(pieces))
+    cfg, w = tiny
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 6), engine=eng)
+    cfg = synth.CONFIGS["layer_d2560_kv1024"]
+    w = synth.model_weights(cfg)
+    P = 200
+    k, v = synth.kv_prefill(cfg, P)
+    x = synth.hidden(cfg)
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    eng.kv_fill(0, 0, torch.from_numpy(k[0]).cuda(), torch.from_numpy(v[0]).cuda())
+    eng.set_hidden(torch.from_numpy(x).cuda())
+    eng.decode_step(0, P)
+    got = eng.get_hidden().cpu().numpy()
+    m = orc.Model(cfg, w)
+    m.kv_fill(k, v, 0)
+    ok, err = close(got, m.layer_forward(0, x, P))
+    assert ok, err
+
+
 def test_gqa_and_head64_variants(lf, orc):
     for kw in (dict(n_heads=8, n_kv_heads=2, head_dim=64), dict(n_heads=8, n_kv_heads=1, head_dim=128),
                dict(n_heads=2, n_kv_heads=2, head_dim=128, d_model=512, ffn_dim=1376, vocab=1000)):
