@@ -177,6 +177,8 @@ int lf_query(const lf_state *st, int32_t what);
 #define LF_Q_LDS_BYTES 2
 #define LF_Q_SCRATCH_BYTES 3   /* scratch lf_generate_noalloc uses for this state */
 #define LF_Q_SCRATCH_MAX 4     /* bytes of the static scratch array */
+#define LF_Q_KV_PF 5           /* stream waves per attention unit whose first K/V tile is prefetched into LDS */
+#define LF_Q_GU_PF 6           /* gate/up pieces per stream wave prefetched into LDS */
 
 /* Test hooks, device pointers, on `stream`:
  * lf_test_expdef: y[i] = E(x[i]) with the library's defined exponential.

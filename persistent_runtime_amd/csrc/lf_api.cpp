@@ -455,7 +455,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_xres = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 16);
   P.lds_part = (int)align_up((size_t)P.lds_xres + (size_t)rows_max * 4, 256);   // [kind][rows][8]
   P.lds_trace = (int)align_up((size_t)P.lds_part + 5 * part_b, 256);
-  const size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
+  size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
   P.part_rows = rows_max;
   P.hmax = hmax;
   int lds_limit = 0;
@@ -463,6 +463,22 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (lds_limit <= 0) lds_limit = 65536;
   if ((long long)lds_end > lds_limit)
     return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
+  // The LDS left over can hold the first K/V tile of up to seven stream waves
+  // of an attention unit (LF_KV_PF: how many), then whatever gate/up prefetch
+  // is asked for.  Both are off by default: measured end to end, the attention
+  // that ends ~0.5 us sooner does not move the layer's end (the next exchange
+  // absorbs it) while the other workgroups stream more QKV rows.
+  {
+    const int nvh = (dh + 63) / 64;
+    P.kv_pf_tile = (dh / 8 + 8 * nvh) * 1024;
+    long long fit = ((long long)lds_limit - (long long)lds_end) / P.kv_pf_tile;
+    long long want = 0;
+    if (const char *s = std::getenv("LF_KV_PF")) want = std::atoll(s);
+    if (want < 0 || P.qpg > 4) want = 0;   // the unit variant for more query heads reads no prefetch
+    P.kv_pf = (int)(want < fit ? want : fit);
+    P.lds_kvpf = (int)lds_end;
+    lds_end += (size_t)P.kv_pf * P.kv_pf_tile;
+  }
   // The LDS left over can hold each stream wave's gate/up prefetch: LF_GU_PF
   // 1-KB pieces per wave, as many as fit.  Off by default: measured end to end
   // it costs more (the burst delays the output projection's input) than the
@@ -479,11 +495,11 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_bytes = (int)(lds_end + (size_t)P.gu_pf * lf::kNcwHost * 1024);
   P.plain_launch = (std::getenv("LF_PLAIN_LAUNCH") && std::atoi(std::getenv("LF_PLAIN_LAUNCH")) != 0) ? 1 : 0;
   for (int pf = 0; pf < 2; ++pf) {
-    if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
+    if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0, P.qpg), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  P.lds_bytes)) != hipSuccess)
       return bail(hip_fail(st, e, "set dynamic LDS size"));
     int nblk = 0;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, lf::monokernel_symbol(pf != 0), lf::kThreads,
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, lf::monokernel_symbol(pf != 0, P.qpg), lf::kThreads,
                                                           P.lds_bytes)) != hipSuccess)
       return bail(hip_fail(st, e, "occupancy query"));
     if (nblk < 1) return bail(fail(&st->err, LF_EHIP, "the kernel cannot be resident on a compute unit"));
@@ -683,6 +699,8 @@ int lf_query(const lf_state *st, int32_t what) {
     case LF_Q_LDS_BYTES: return st->P.lds_bytes;
     case LF_Q_SCRATCH_BYTES: return (int)noalloc_layout(st, nullptr, nullptr);
     case LF_Q_SCRATCH_MAX: return (int)lf::kNoallocScratchBytes;
+    case LF_Q_KV_PF: return st->P.kv_pf;
+    case LF_Q_GU_PF: return st->P.gu_pf;
     default: return LF_EINVAL;
   }
 }

@@ -91,6 +91,8 @@ struct Params {
   int window;                          // sliding-window length (0: none)
   int attn_unit_tiles;                 // most KV tiles per attention unit (1 .. 7)
   int gu_pf;                           // gate/up pieces per stream wave prefetched into LDS during attention
+  int kv_pf;                           // stream waves whose first K/V tile is prefetched into LDS (0: off)
+  int kv_pf_tile;                      // LDS bytes of one prefetched tile
   unsigned o_refill_delay;             // ticks (100 MHz) a workgroup without attention units waits
                                        // after the QKV phase before prefetching the output projection
   unsigned long long window_layers;    // bit l: layer l attends over the window
@@ -138,7 +140,7 @@ struct Params {
   unsigned long long timeout_ticks;
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   // LDS layout (byte offsets into dynamic shared memory)
-  int lds_h, lds_attn, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_pf, lds_bytes;
+  int lds_h, lds_attn, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_pf, lds_kvpf, lds_bytes;
   int part_rows, hmax;
 };
 
@@ -166,6 +168,6 @@ hipError_t launch_test_gumbel(const float *logits, int n, float inv_temp, unsign
 hipError_t launch_test_sample(const float *logits, int n, float inv_temp, float top_p,
                               unsigned long long seed, const int *pos, int m, int *tokens,
                               hipStream_t stream);
-const void *monokernel_symbol(bool prefill);
+const void *monokernel_symbol(bool prefill, int qpg);   // the instance for qpg query heads per KV head
 
 }  // namespace lf

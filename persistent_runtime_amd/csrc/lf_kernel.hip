@@ -278,7 +278,8 @@ struct Ctl {
   unsigned done[kWaves];    // per stream wave: last GEMV phase (1-based) it finished
   int status;               // outcome of a barrier-based wait
   unsigned abar;            // arrivals at the stream waves' barrier (kNcw per barrier)
-  int pad[5];
+  int na;                   // workgroups 0 .. na-1 run attention with prefetched tiles (no QKV rows)
+  int pad[4];
   float ssw[kWaves];        // per wave: sum of squares of its share of an RMSNorm input
   Geo geo[K_COUNT];
   // The partition of every phase kind among the stream waves, fixed for the
@@ -314,7 +315,9 @@ __device__ __forceinline__ unsigned long long stamp(const Sync &s) { return s.ti
 
 // LF_TRACE builds: timestamp j (0 input staged, 1 streams done, 2 published;
 // stream wave 1: 3 input seen, 4 first round done, 5 done; wave 0: 6 staging
-// started, 7 tagged input complete, 8 sum of squares; attention, wave 1: 6
+// started, 7 tagged input complete, 8 its first poll back, 9 its poll round
+// trips (a count), and for the QKV phase 12 the layer loop's top, 11 after the
+// row block's read; attention, wave 1: 6
 // unit start, 7 first barrier passed, 3 queries staged, 8 first keys loaded,
 // 10 first scores, 4 keys done, 9 waves' states in LDS, 5 partial stored, and
 // in a merging unit 11 merge start, 12 the waves' folded states in LDS, 13
@@ -334,6 +337,13 @@ __device__ __forceinline__ void trace(KP &P, int t, int k, int j) {
 __device__ __forceinline__ void trace_at(KP &P, int k, int j) {
   if (kTrace && k >= 0 && lane_id() == 0) trace_row(P, k)[j] = now_ticks();
 }
+
+// Mark a loaded value as used.  A load whose result is never read stays
+// "in flight" for the compiler, and where paths merge it then waits for every
+// memory access issued since (stores included) before it reuses the register.
+// Retiring the value where it is already in (it was requested before the loads
+// just waited for) costs no wait.
+__device__ __forceinline__ void retire(unsigned v) { asm volatile("" ::"v"(v)); }
 
 // The bound of a wait started at t0 has expired: record the first such event in
 // the error word (any lane may call; one wins).  Also true once another
@@ -361,7 +371,11 @@ __device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsign
     bool behind = false;
     const unsigned e = ld_dev(&P.err[0]);
     for (int i = lane_id(); i < count; i += 64) behind |= ld_dev(&P.progress[first + i]) < level;
-    if (wave_none(behind)) { ok = true; break; }
+    if (wave_none(behind)) {
+      retire(e);
+      ok = true;
+      break;
+    }
     if (expired(P, t0, level, e)) break;
   }
   s.spin += now_ticks() - t0;
@@ -444,23 +458,34 @@ struct StageSpec {
 // n rounded up to whole slots.  Each pass reads the error word with the data.
 constexpr int kCoopChunk = 8;
 template <class F>
-__device__ __forceinline__ bool coop_fetch(KP &P, const u64 *src, int n, unsigned tag, int wave, F &&use) {
+__device__ __forceinline__ bool coop_fetch(KP &P, const u64 *src, int n, unsigned tag, int wave, F &&use,
+                                           int trk = -1) {
   const int lane = lane_id();
   const unsigned long long t0 = now_ticks();
+  int polls = 0;   // LF_TRACE: round trips of the last chunk
   const int ns = (n + 63) >> 6;
   const int s0 = wave * ns / kWaves, s1 = (wave + 1) * ns / kWaves;
   for (int c0 = s0; c0 < s1; c0 += kCoopChunk) {
     const int m = min(kCoopChunk, s1 - c0);
     const u64 *rp = src + 64 * c0 + lane;
     for (;;) {
+      // The error word first: loads complete in order, so once the words are
+      // in, no load of this loop is left in flight (a load still in flight
+      // into a register the code reuses later would make that reuse wait for
+      // every access issued since, stores included).
+      const unsigned e = ld_dev(&P.err[0]);
       u64 v[kCoopChunk];
 #pragma unroll
       for (int k = 0; k < kCoopChunk; ++k) v[k] = k < m ? ld_dev(rp + 64 * k) : ((u64)tag << 32);
-      const unsigned e = ld_dev(&P.err[0]);
       bool bad = false;
 #pragma unroll
       for (int k = 0; k < kCoopChunk; ++k) bad |= 64 * (c0 + k) + lane < n && tag_of(v[k]) != tag;
+      if (kTrace && trk >= 0) {
+        if (polls == 0) trace_at(P, trk, 8);   // first poll back
+        ++polls;
+      }
       if (wave_none(bad)) {
+        retire(e);
 #pragma unroll
         for (int k = 0; k < kCoopChunk; ++k) {
           const int i = 64 * (c0 + k) + lane;
@@ -471,6 +496,7 @@ __device__ __forceinline__ bool coop_fetch(KP &P, const u64 *src, int n, unsigne
       if (expired(P, t0, tag, e)) return false;
     }
   }
+  if (kTrace && trk >= 0 && lane == 0) trace_row(P, trk)[9] = (unsigned long long)polls;
   return true;
 }
 
@@ -479,7 +505,8 @@ __device__ __forceinline__ bool coop_fetch(KP &P, const u64 *src, int n, unsigne
 // input is read by the sync wave alone.  For RMSNorm inputs each wave leaves
 // the sum of squares of its share in ctl->ssw.  On a timeout the wave sets the
 // abort flag.  The caller then meets the other waves at wg_barrier().
-__device__ __forceinline__ void coop_stage(KP &P, Ctl *ctl, const StageSpec &sp, int wave, _Float16 *h) {
+__device__ __forceinline__ void coop_stage(KP &P, Ctl *ctl, const StageSpec &sp, int wave, _Float16 *h,
+                                           int trk = -1) {
   const int lane = lane_id();
   bool ok = true;
   if (sp.mode == SM_RMS) {
@@ -489,13 +516,13 @@ __device__ __forceinline__ void coop_stage(KP &P, Ctl *ctl, const StageSpec &sp,
       ss += real ? x * x : 0.0f;
       h[i] = (_Float16)x;
       if ((unsigned)(i - sp.cap0) < (unsigned)sp.capn) sp.cap[i - sp.cap0] = x;
-    });
+    }, trk);
     ss = wave_sum(ss);
     if (lane == 0) ctl->ssw[wave] = ss;
   } else if (sp.mode == SM_PAIRS) {
     unsigned *dst = reinterpret_cast<unsigned *>(h);
     ok = coop_fetch(P, sp.src, sp.n, sp.tag, wave,
-                    [&](int i, u64 w, bool) __attribute__((always_inline)) { dst[i] = (unsigned)w; });
+                    [&](int i, u64 w, bool) __attribute__((always_inline)) { dst[i] = (unsigned)w; }, trk);
   }
   if (!ok && lane == 0) lds_st(&ctl->abort, 1u);
   lds_drain();
@@ -1231,6 +1258,43 @@ __device__ __forceinline__ void stream_barrier(Ctl *ctl) {
   asm volatile("" ::: "memory");
 }
 
+// K/V tile prefetch.  The cached tiles of a unit do not depend on the step's
+// queries, so a workgroup that runs attention and streams no QKV rows copies
+// each of its first P.kv_pf stream waves' first tile into LDS during the QKV
+// phase (direct-to-LDS loads, device-scope and non-temporal like kv_load): K
+// pieces 0 .. dh/8-1, then V pieces (key group kg, half hh) at dh/8 + kg nvh + hh,
+// each holding what lane i of that wave's tile load would hold.
+__device__ __forceinline__ bool kv_pf_wave(const KP &P, const Ctl *ctl, int u, int kwv, int tfirst, int te) {
+  return P.kv_pf > 0 && P.qpg <= 4 && u == (int)blockIdx.x && u < ctl->na && kwv < P.kv_pf && tfirst < te;
+}
+__device__ __forceinline__ unsigned char *kv_pf_area(const KP &P, int kwv) {
+  extern __shared__ __align__(16) unsigned char lf_dyn_lds[];
+  return lf_dyn_lds + P.lds_kvpf + (size_t)kwv * P.kv_pf_tile;
+}
+__device__ __forceinline__ void kv_prefetch(KP &P, const Ctl *ctl, int l, int u, const AttnPart &ap, int kwv) {
+  const int Hkv = P.Hkv, dh = P.dh;
+  const int g = u % Hkv, c = u / Hkv;
+  const int ta = ap.t0 + c * ap.tpu;
+  const int te = min(ta + ap.tpu, ap.t0 + ap.nt);
+  const int t = ta + kwv;
+  if (!kv_pf_wave(P, ctl, u, kwv, t, te)) return;
+  const int lane = lane_id();
+  const int nck = dh >> 3, nvh = (dh + 63) >> 6;
+  const size_t tile_b = (size_t)128 * dh;
+  const size_t off = (((size_t)l * Hkv + g) * P.kv_tiles + (size_t)t) * tile_b;
+  const unsigned char *kb = reinterpret_cast<const unsigned char *>(P.kcache) + off;
+  const unsigned char *vb = reinterpret_cast<const unsigned char *>(P.vcache) + off;
+  unsigned char *dst = kv_pf_area(P, kwv);
+  for (int k = 0; k < nck; ++k)
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(kb + k * 1024 + lane * 16),
+                                     (void __attribute__((address_space(3))) *)(dst + k * 1024), 16, 0, 16 | 2);
+  for (int kg = 0; kg < 8; ++kg)
+    for (int hh = 0; hh < nvh; ++hh)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(vb + (size_t)(kg * dh + min(hh * 64 + lane, dh - 1)) * 16),
+          (void __attribute__((address_space(3))) *)(dst + (nck + kg * nvh + hh) * 1024), 16, 0, 16 | 2);
+}
+
 // Lanes 2i of the result hold the fp16 pair (x of lane 2i, x of lane 2i + 1).
 __device__ __forceinline__ unsigned pair_up(_Float16 x) {
   const unsigned lo = (unsigned)__builtin_bit_cast(unsigned short, x);
@@ -1329,7 +1393,22 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     if (kPreV) load_v(t);
   };
   if (kTrace && wave == 1) trace_at(P, trk, 6);
-  if (tfirst < te) load_tile(tfirst);
+  // The first tile, when it was prefetched into LDS during the QKV phase (only
+  // with V requested up front: the other variant has no registers to spare).
+  if (kPreV && kv_pf_wave(P, ctl, u, kwv, tfirst, te)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the direct-to-LDS loads have landed
+    const unsigned char *pft = kv_pf_area(P, kwv) + lane * 16;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < nck) kr[k] = *reinterpret_cast<const u32x4 *>(pft + k * 1024);
+#pragma unroll
+    for (int kg = 0; kg < 8; ++kg) {
+      vr[kg][0] = *reinterpret_cast<const u32x4 *>(pft + (nck + kg * nvh) * 1024);
+      if (nvh > 1) vr[kg][1] = *reinterpret_cast<const u32x4 *>(pft + (nck + kg * nvh + 1) * 1024);
+    }
+  } else if (tfirst < te) {
+    load_tile(tfirst);
+  }
   if (kTrace && wave == 1) trace_at(P, trk, 0);
   {
     // The queries (to fp16) and, in unit 0, the current K and V pairs: one
@@ -1639,17 +1718,10 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   return !lds_ld(&ctl->abort);
 }
 
-// attn_unit for this model's query heads per KV head (kQ: the next power of two).
-__device__ __forceinline__ bool attn_run(KP &P, Ctl *ctl, int l, int gen, unsigned tag_q, unsigned tag_a, int pos,
-                                         int u, const AttnPart &ap, unsigned char *lds, int trk) {
-  switch (P.qpg) {
-    case 1: return attn_unit<1>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
-    case 2: return attn_unit<2>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
-    case 3:
-    case 4: return attn_unit<4>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
-    default: return attn_unit<kMaxQpg>(P, ctl, l, gen, tag_q, tag_a, pos, u, ap, lds, trk);
-  }
-}
+// The kernel is instantiated per attention variant (kQ: the query heads per KV
+// head rounded up to 1, 2, 4 or 8), so each holds one copy of the unit: the
+// largest variant's registers would otherwise set every model's spills.
+__host__ __device__ constexpr int kq_of(int qpg) { return qpg <= 1 ? 1 : qpg == 2 ? 2 : qpg <= 4 ? 4 : kMaxQpg; }
 
 // ---------------------------------------------------------------- sampler
 
@@ -2103,7 +2175,7 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
 // A workgroup reads a phase's input only if it has rows in that phase, so each
 // read is followed by an output that every later phase depends on; a buffer of
 // one generation is rewritten two layers later, after every reader of it.
-template <bool kPrefill>
+template <bool kPrefill, int kQ>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))) lf_monokernel(Params Parg) {
   // Parg is the only argument: read it where the dispatch placed it, at the
   // start of the kernel-argument segment (never through a copy).
@@ -2132,10 +2204,30 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     const int upr[K_COUNT] = {2, 1, 4, 2, 2};
     const int kvs[K_COUNT] = {d / 8, P.Hq * dh / 8, d / 8, P.F / 8, d / 8};
     const int nskip = o_rows_skip(G, P.Hkv);
+    // Workgroups that run attention with prefetched tiles stream no QKV rows:
+    // the units of the launch's last position (the most), if they are few.
+    int na = 0;
+    if (P.kv_pf > 0) {
+      const int pl = P.pos0 + P.n_tokens - 1;
+      const AttnSplit asp(pl, G, P.Hkv, P.window, P.attn_unit_tiles);
+      int smax = asp.a[0].S > asp.a[1].S ? asp.a[0].S : asp.a[1].S;
+      if (P.window > 0) {   // a window's tile count moves by one with the position
+        const AttnPart w1 = attn_part(0, P.window + kKvTile, G, P.Hkv, P.attn_unit_tiles);
+        if (w1.S > smax) smax = w1.S;
+      }
+      na = P.Hkv * smax;
+      if (4 * na > G) na = 0;
+    }
+    ctl->na = na;
     for (int k = 0; k < K_COUNT; ++k) {
       int p0 = 0, p1 = 0;
-      if (k != K_O) block_range(units[k], G, b, p0, p1);
-      else if (b >= nskip) block_range(units[k], G - nskip, b - nskip, p0, p1);
+      if (k == K_QKV) {
+        if (b >= na) block_range(units[k], G - na, b - na, p0, p1);
+      } else if (k != K_O) {
+        block_range(units[k], G, b, p0, p1);
+      } else if (b >= nskip) {
+        block_range(units[k], G - nskip, b - nskip, p0, p1);
+      }
       const Geo ge = Geo{upr[k] * p0, upr[k] * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
       ctl->geo[k] = ge;
       for (int cw = 0; cw < kNcw; ++cw) {
@@ -2210,6 +2302,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         // after attention: this wave's loads complete in order, so attention's
         // K/V loads would otherwise queue behind it.
         const bool qkv_rounds = qkv && st_has_rounds(st, K_QKV, ctl);
+        if (qkv && P.kv_pf > 0 && b < P.Hkv * asp.a[layer_windowed(P, l) ? 1 : 0].S)
+          kv_prefetch(P, ctl, l, b, asp.a[layer_windowed(P, l) ? 1 : 0], st.cw);
         if (!stream_phase(st, t * ngp + g, kind, ctl, hl, part, stage_spec(P, ctl, kind, t, l, gen, lvl, xown, xres),
                           qkv))
           return;
@@ -2218,8 +2312,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           if (lds_ld(&ctl->abort)) return;
           if (b < P.Hkv * ap.S) {
             for (int u = b; u < P.Hkv * ap.S; u += G)
-              if (!attn_run(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
-                            u == b && t == P.trace_token ? 5 * l + 1 : -1))
+              if (!attn_unit<kQ>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
+                                 u == b && t == P.trace_token ? 5 * l + 1 : -1))
                 return;
           } else if (2 * P.Hkv * ap.S <= G) {
             // a workgroup without attention units, while attention runs on few:
@@ -2261,6 +2355,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     if (kPrefill) token = P.in_tokens[t];
     const AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles);
     for (int l = 0; l < L; ++l) {
+      if (kTrace) trace(P, t, 5 * l + 0, 12);
       KP &Pl = fresh(P);
       sy.P = &Pl;
       const unsigned lvl = lv0 + (unsigned)(l * PH_PER_LAYER);
@@ -2278,19 +2373,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
             if (!poll_level(sy, 0, 1, lv0)) { fail(); return; }
             token = ld_dev(Pl.tok_slot);
           }
+          // Nothing left in flight into the layer loop: the loads above are in
+          // already (the token's own round trip aside), and a load the compiler
+          // still counts as pending would make each layer's staging wait for
+          // the previous layer's stores.
+          __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+          asm volatile("" ::: "memory");
         }
-        // rotary factors of this lane's first row pair, loaded before the wait
-        float cs0 = 0.0f, sn0 = 0.0f;
-        if (lane < ge.nrows / 2) {
-          const int r = ge.r0 + 2 * lane;
-          if (r < nq + nk) {
-            int hd, rem;
-            head_split(r < nq ? r : r - nq, dh, hd, rem);
-            const int k = rem >> 1;
-            cs0 = Pl.rope[((size_t)pos * half + k) * 2 + 0];
-            sn0 = Pl.rope[((size_t)pos * half + k) * 2 + 1];
-          }
-        }
+        trace(Pl, t, 5 * l + 0, 11);
         unsigned long long tq = stamp(sy);
         sy.trace_k = t == Pl.trace_token ? 5 * l : -1;
         trace(Pl, t, 5 * l + 0, 6);
@@ -2298,7 +2388,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         const StageSpec sp = stage_spec(Pl, ctl, K_QKV, t, l, gen, lvl, xown, xres);
         if (ge.nrows > 0 || sp.capn > 0) {
           if (l > 0) {
-            coop_stage(Pl, ctl, sp, 0, hl);
+            coop_stage(Pl, ctl, sp, 0, hl, sy.trace_k);
           } else {
             inv = stage_rmsnorm_plain(Pl.hidden_io ? Pl.x_hidden : nullptr,
                                       Pl.hidden_io ? nullptr : emb + (size_t)token * d, d, Pl.eps, hl);
@@ -2311,6 +2401,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         }
         tq = lap(sy, ST_STAGE, tq);
         trace(Pl, t, 5 * l + 0, 0);
+        // Rotary factors of this lane's first row pair, loaded before the wait
+        // for the stream waves (after the input is staged: the staging polls go
+        // out first at the layer's start).
+        float cs0 = 0.0f, sn0 = 0.0f;
+        if (lane < ge.nrows / 2) {
+          const int r = ge.r0 + 2 * lane;
+          if (r < nq + nk) {
+            int hd, rem;
+            head_split(r < nq ? r : r - nq, dh, hd, rem);
+            const int k = rem >> 1;
+            cs0 = Pl.rope[((size_t)pos * half + k) * 2 + 0];
+            sn0 = Pl.rope[((size_t)pos * half + k) * 2 + 1];
+          }
+        }
         const float *pk = kind_part(part, K_QKV, Pl.part_rows);
         if (!wait_streams(ctl, q0)) return;
         tq = lap(sy, ST_STREAMS, tq);
@@ -2366,7 +2470,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         sy.trace_k = t == Pl.trace_token ? 5 * l + 2 : -1;
         trace(Pl, t, 5 * l + 2, 6);
         if (ge.nrows > 0) {
-          coop_stage(Pl, ctl, stage_spec(Pl, ctl, K_O, t, l, gen, lvl, xown, xres), 0, hl);
+          coop_stage(Pl, ctl, stage_spec(Pl, ctl, K_O, t, l, gen, lvl, xown, xres), 0, hl, sy.trace_k);
           trace(Pl, t, 5 * l + 2, 7);
           wg_barrier();
           if (lds_ld(&ctl->abort)) return;
@@ -2413,7 +2517,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         float inv = 0.0f;
         const StageSpec sp = stage_spec(Pl, ctl, K_GU, t, l, gen, lvl, xown, xres);
         if (ge.nrows > 0 || sp.capn > 0) {
-          coop_stage(Pl, ctl, sp, 0, hl);
+          coop_stage(Pl, ctl, sp, 0, hl, sy.trace_k);
           trace(Pl, t, 5 * l + 3, 7);
           wg_barrier();
           if (lds_ld(&ctl->abort)) return;
@@ -2447,7 +2551,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         sy.trace_k = t == Pl.trace_token ? 5 * l + 4 : -1;
         trace(Pl, t, 5 * l + 4, 6);
         if (ge.nrows > 0) {
-          coop_stage(Pl, ctl, stage_spec(Pl, ctl, K_D, t, l, gen, lvl, xown, xres), 0, hl);
+          coop_stage(Pl, ctl, stage_spec(Pl, ctl, K_D, t, l, gen, lvl, xown, xres), 0, hl, sy.trace_k);
           trace(Pl, t, 5 * l + 4, 7);
           wg_barrier();
           if (lds_ld(&ctl->abort)) return;
@@ -2697,17 +2801,25 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-const void *monokernel_symbol(bool prefill) {
-  return prefill ? reinterpret_cast<const void *>(&lf_monokernel<true>)
-                 : reinterpret_cast<const void *>(&lf_monokernel<false>);
+const void *monokernel_symbol(bool prefill, int qpg) {
+  switch (kq_of(qpg)) {
+    case 1: return prefill ? reinterpret_cast<const void *>(&lf_monokernel<true, 1>)
+                           : reinterpret_cast<const void *>(&lf_monokernel<false, 1>);
+    case 2: return prefill ? reinterpret_cast<const void *>(&lf_monokernel<true, 2>)
+                           : reinterpret_cast<const void *>(&lf_monokernel<false, 2>);
+    case 4: return prefill ? reinterpret_cast<const void *>(&lf_monokernel<true, 4>)
+                           : reinterpret_cast<const void *>(&lf_monokernel<false, 4>);
+    default: return prefill ? reinterpret_cast<const void *>(&lf_monokernel<true, kMaxQpg>)
+                            : reinterpret_cast<const void *>(&lf_monokernel<false, kMaxQpg>);
+  }
 }
 
 hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream) {
   void *args[] = {const_cast<Params *>(&p)};
   if (p.plain_launch)
-    return hipLaunchKernel(monokernel_symbol(prefill), dim3(p.G), dim3(kThreads), args, (size_t)p.lds_bytes,
+    return hipLaunchKernel(monokernel_symbol(prefill, p.qpg), dim3(p.G), dim3(kThreads), args, (size_t)p.lds_bytes,
                            stream);
-  return hipLaunchCooperativeKernel(monokernel_symbol(prefill), dim3(p.G), dim3(kThreads), args,
+  return hipLaunchCooperativeKernel(monokernel_symbol(prefill, p.qpg), dim3(p.G), dim3(kThreads), args,
                                     (unsigned)p.lds_bytes, stream);
 }
 

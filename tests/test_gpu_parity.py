@@ -208,7 +208,38 @@ def test_gate_up_lds_prefetch(lf, orc, tiny, monkeypatch, pieces):
     monkeypatch.setenv("LF_GU_PF", str(pieces))
     cfg, w = tiny
     eng = lf.Engine(cfg, lf.upload_weights(w))
+    assert eng.query(lf.LF_Q_GU_PF) == pieces
     teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 6), engine=eng)
+    cfg = synth.CONFIGS["layer_d2560_kv1024"]
+    w = synth.model_weights(cfg)
+    P = 200
+    k, v = synth.kv_prefill(cfg, P)
+    x = synth.hidden(cfg)
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    eng.kv_fill(0, 0, torch.from_numpy(k[0]).cuda(), torch.from_numpy(v[0]).cuda())
+    eng.set_hidden(torch.from_numpy(x).cuda())
+    eng.decode_step(0, P)
+    got = eng.get_hidden().cpu().numpy()
+    m = orc.Model(cfg, w)
+    m.kv_fill(k, v, 0)
+    ok, err = close(got, m.layer_forward(0, x, P))
+    assert ok, err
+
+
+@pytest.mark.parametrize("waves", [7, 2])
+def test_attention_tile_prefetch(lf, orc, monkeypatch, waves):
+    """The K/V tile prefetch into LDS (off by default): the workgroups that run
+    attention stream no QKV rows and copy their stream waves' first tile into LDS
+    during the QKV phase.  With 2 waves prefetching, the other waves' tiles come
+    from the cache as usual.  GQA 8/2 x 64 (three tiles at the last positions) and
+    the 2.2B layer shape at position 200 (four tiles, one unit per head)."""
+    import torch
+    monkeypatch.setenv("LF_KV_PF", str(waves))
+    cfg = synth.scaled_config("tiny_2l_d256", n_heads=8, n_kv_heads=2, head_dim=64, max_seq=256)
+    w = synth.model_weights(cfg, seed=4)
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    assert eng.query(lf.LF_Q_KV_PF) == waves
+    teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 150), engine=eng)
     cfg = synth.CONFIGS["layer_d2560_kv1024"]
     w = synth.model_weights(cfg)
     P = 200
