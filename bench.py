@@ -39,7 +39,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
 METRIC = "batch-1 decode tokens/s + % of HBM-bandwidth roofline (MBU), 1x MI355X"
-KERNEL = "lf_monokernel<false>"
+
+
+def kernel_name(cfg: dict) -> str:
+    """The decode kernel's instance: one per attention variant (query heads per
+    KV head rounded up to 1, 2, 4 or 8)."""
+    qpg = cfg["n_heads"] // cfg["n_kv_heads"]
+    kq = 1 if qpg <= 1 else 2 if qpg == 2 else 4 if qpg <= 4 else 8
+    return f"lf_monokernel<false, {kq}>"
 
 
 def log(*a):
@@ -161,13 +168,14 @@ def write_traffic(d: str, workload: str, K: int, W: int, rotate: int) -> int:
         copies = [v for _, k, v in _counter_rows(os.path.join(d, sub), c) if "copyBuffer" in k]
         cal[c] = copy_bytes / max(copies)   # bytes per counted KiB
     got = {}
+    kname = kernel_name(cfg)
     for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
-        mine = [v for _, k, v in _counter_rows(os.path.join(d, sub), c) if KERNEL in k]
+        mine = [v for _, k, v in _counter_rows(os.path.join(d, sub), c) if kname in k]
         if not mine:
-            raise SystemExit(f"no {KERNEL} dispatch in {sub}")
+            raise SystemExit(f"no {kname} dispatch in {sub}")
         got[c] = sum(mine) / len(mine)   # every decode dispatch is a timed repetition
     alg = launch_bytes(cfg, kind, pos0, K)
-    rec = {"workload": workload, "steps": K, "kernel": KERNEL, "kernel_source_hash": kernel_source_hash(),
+    rec = {"workload": workload, "steps": K, "kernel": kname, "kernel_source_hash": kernel_source_hash(),
            "dispatches": len(mine),
            "fetch_kib_counted": got["FETCH_SIZE"], "write_kib_counted": got["WRITE_SIZE"],
            "fetch_bytes_per_counted_kib": cal["FETCH_SIZE"], "write_bytes_per_counted_kib": cal["WRITE_SIZE"],
@@ -393,7 +401,7 @@ def main() -> int:
     traffic, trec = measured_traffic(args.workload, nbytes)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": nbytes, "kernel": KERNEL, "launch_ms": t}
+            "algorithmic_bytes_per_launch": nbytes, "kernel": kernel_name(cfg), "launch_ms": t}
     if trec is not None:
         roof["traffic_source"] = (f"rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of {trec['dispatches']} launch(es) of "
                                   f"{trec['steps']} steps on this kernel source, copy-calibrated: measured / "

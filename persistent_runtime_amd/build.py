@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblf.so")
+TRACE_LIB = os.path.join(HERE, "liblf_trace.so")   # LF_TRACE build: per-phase timestamps of one token
 SOURCES = [os.path.join(CSRC, "lf_api.cpp"), os.path.join(CSRC, "lf_kernel.hip")]
 ARCH = os.environ.get("LF_OFFLOAD_ARCH", "gfx950")
 
@@ -24,23 +25,26 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def command(out: str) -> list[str]:
+def command(out: str, trace: bool = False) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-command-line-argument",
+            "-Wall", "-Wno-unused-command-line-argument"] + (["-DLF_TRACE"] if trace else []) + [
             "-I", os.path.join(ROOT, "include"), "-x", "hip"] + SOURCES + ["-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compile the library; with ``trace`` the LF_TRACE variant (liblf_trace.so),
+    which a process loads instead with LF_LIB (see phase_trace.py)."""
+    lib = TRACE_LIB if trace else LIB
+    tmp = lib + ".tmp"
+    cmd = command(tmp, trace)
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, trace="--trace" in sys.argv[1:])
     sys.exit(0)
