@@ -263,6 +263,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.hidden_io = hidden ? 1 : 0;
   P.window = c.sliding_window;
   P.attn_unit_tiles = lf::kWaves - 1;   // one tile per stream wave
+  P.attn_split_tiles = 3;
   // Workgroups without attention units hold back the output projection's first
   // ring round ~3.5 us (350 ticks of the 100 MHz clock), about one attention
   // pass at short contexts, so that the K/V loads meet a quieter memory system.
@@ -271,6 +272,10 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (const char *s = std::getenv("LF_ATTN_UNIT_TILES")) {
     const int v = std::atoi(s);
     if (v >= 1 && v <= lf::kWaves - 1) P.attn_unit_tiles = v;
+  }
+  if (const char *s = std::getenv("LF_ATTN_SPLIT_TILES")) {
+    const int v = std::atoi(s);
+    if (v >= 1 && v <= lf::kWaves - 1) P.attn_split_tiles = v;
   }
   P.window_layers = c.sliding_window > 0 ? c.window_layers : 0ull;
   P.levels_per_token = lf::PH_PER_LAYER * c.n_layers + (hidden ? 0 : 2);

@@ -89,7 +89,8 @@ struct Params {
   unsigned flags;
   int hidden_io, sampling;   // sampling: a SampleMode
   int window;                          // sliding-window length (0: none)
-  int attn_unit_tiles;                 // most KV tiles per attention unit (1 .. 7)
+  int attn_unit_tiles;                 // most KV tiles a KV head keeps in one unit (1 .. 7)
+  int attn_split_tiles;                // tiles per unit once a head is split (1 .. 7)
   int gu_pf;                           // gate/up pieces per stream wave prefetched into LDS during attention
   int kv_pf;                           // stream waves whose first K/V tile is prefetched into LDS (0: off)
   int kv_pf_tile;                      // LDS bytes of one prefetched tile

@@ -1157,13 +1157,16 @@ __device__ __forceinline__ bool wait_streams(const Ctl *ctl, int q) {
 // window's first key pos - W + 1); the key at pos itself comes from the QKV
 // phase's tagged words.  The cached keys lie in tiles t0 .. t0 + nt - 1 of
 // kKvTile positions, split into S units of at most tpu consecutive tiles (unit
-// c takes tiles from t0 + c tpu): ceil(nt / ut) units per KV head, at most
-// G / Hkv and kMaxSplit, where ut (at most kNcw: one tile per stream wave) is
-// the plan's tile count per unit.  Unit 0 also takes the current key.
+// c takes tiles from t0 + c tpu): one unit per KV head while its nt tiles are
+// at most ut (at most kNcw: one tile per stream wave), so no merge; past that
+// ceil(nt / us) units, at most G / Hkv and kMaxSplit.  A head that is split
+// anyway gains from short units (a CU keeps only ~60 KB of loads in flight, so
+// a unit's load time grows with its tiles), while one that fits in one unit
+// would pay a merge exchange to split.  Unit 0 also takes the current key.
 struct AttnPart {
   int S, tpu, t0, nt, kb;
 };
-__device__ __forceinline__ AttnPart attn_part(int kb, int pos, int G, int Hkv, int ut) {
+__device__ __forceinline__ AttnPart attn_part(int kb, int pos, int G, int Hkv, int ut, int us) {
   AttnPart a;
   a.kb = kb;
   int smax = G / Hkv;
@@ -1172,7 +1175,7 @@ __device__ __forceinline__ AttnPart attn_part(int kb, int pos, int G, int Hkv, i
   if (pos > kb) {
     a.t0 = kb / kKvTile;
     a.nt = (pos - 1) / kKvTile - a.t0 + 1;
-    int S = (a.nt + ut - 1) / ut;
+    int S = a.nt <= ut ? 1 : (a.nt + us - 1) / us;
     if (S > smax) S = smax;
     a.tpu = (a.nt + S - 1) / S;
     a.S = (a.nt + a.tpu - 1) / a.tpu;   // no unit is left without tiles
@@ -1204,10 +1207,10 @@ __device__ __forceinline__ bool layer_windowed(const KP &P, int l) {
 // layers ([1]).
 struct AttnSplit {
   AttnPart a[2];
-  __device__ __forceinline__ AttnSplit(int pos, int G, int Hkv, int window, int ut) {
+  __device__ __forceinline__ AttnSplit(int pos, int G, int Hkv, int window, int ut, int us) {
     const int n = pos + 1;
-    a[0] = attn_part(0, pos, G, Hkv, ut);
-    a[1] = attn_part(window > 0 && n > window ? n - window : 0, pos, G, Hkv, ut);
+    a[0] = attn_part(0, pos, G, Hkv, ut, us);
+    a[1] = attn_part(window > 0 && n > window ? n - window : 0, pos, G, Hkv, ut, us);
   }
 };
 
@@ -2209,10 +2212,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     int na = 0;
     if (P.kv_pf > 0) {
       const int pl = P.pos0 + P.n_tokens - 1;
-      const AttnSplit asp(pl, G, P.Hkv, P.window, P.attn_unit_tiles);
+      const AttnSplit asp(pl, G, P.Hkv, P.window, P.attn_unit_tiles, P.attn_split_tiles);
       int smax = asp.a[0].S > asp.a[1].S ? asp.a[0].S : asp.a[1].S;
       if (P.window > 0) {   // a window's tile count moves by one with the position
-        const AttnPart w1 = attn_part(0, P.window + kKvTile, G, P.Hkv, P.attn_unit_tiles);
+        const AttnPart w1 = attn_part(0, P.window + kKvTile, G, P.Hkv, P.attn_unit_tiles, P.attn_split_tiles);
         if (w1.S > smax) smax = w1.S;
       }
       na = P.Hkv * smax;
@@ -2285,7 +2288,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     for (int t = 0; t < P.n_tokens; ++t) {
       const int pos = P.pos0 + t;
       const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
-      AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles);
+      AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles, P.attn_split_tiles);
       // The token's GEMV phases (four per layer, then the lm_head) in one loop,
       // so that the phase code exists once: a layer's instruction footprint then
       // stays within the instruction cache.
@@ -2353,7 +2356,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     const int pos = P.pos0 + t;
     const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
     if (kPrefill) token = P.in_tokens[t];
-    const AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles);
+    const AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles, P.attn_split_tiles);
     for (int l = 0; l < L; ++l) {
       if (kTrace) trace(P, t, 5 * l + 0, 12);
       KP &Pl = fresh(P);
