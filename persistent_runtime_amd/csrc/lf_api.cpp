@@ -121,7 +121,7 @@ hipError_t reset_levels(lf_state *st) {
 
 int do_launch(lf_state *st, int token0, int pos0, int n, std::vector<int> *out, bool prefill = false) {
   lf::Params &P = st->P;
-  P.levels_per_token = lf::PH_PER_LAYER * P.L + ((P.hidden_io || prefill) ? 0 : 2);
+  P.levels_per_token = lf::PH_PER_LAYER * P.L + ((P.hidden_io || prefill) ? 0 : 2 + (P.nuc_grid ? lf::kNucLevels : 0));
   const unsigned need = (unsigned)(n + 1) * (unsigned)P.levels_per_token;
   hipError_t e;
   if ((unsigned long long)st->level_base + need >= 0x7fffffffull) {
@@ -186,6 +186,12 @@ size_t noalloc_layout(const lf_state *st, char *base, lf::Params *P) {
     P->part_t = rel(S.part_t);
     P->o_t = rel(S.o_t);
     P->a_t = rel(S.a_t);
+    if (S.nuc_hist) {
+      P->nuc_hist = rel(S.nuc_hist);
+      P->nuc_btot = rel(S.nuc_btot);
+      P->nuc_cand = rel(S.nuc_cand);
+      P->nuc_zmax = rel(S.nuc_zmax);
+    }
     P->progress = reinterpret_cast<unsigned *>(base + prog);
     P->err = reinterpret_cast<unsigned *>(base + errw);
     P->lm_val = reinterpret_cast<float *>(base + lmv);
@@ -405,11 +411,28 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     const size_t pad_words = lf::kStageRound > lf::kStageRoundWide ? lf::kStageRound : lf::kStageRoundWide;
     size_t bytes = 0;
     for (auto &t : ts) bytes += align_up((2 * t.words + pad_words) * 8, 256);
+    // the nucleus draw over the grid: one generation each (its levels order every
+    // reader of one token before any writer of the next)
+    const bool nuc = P.sampling == lf::SAMPLE_NUCLEUS && !hidden;
+    P.nuc_cmax = 2 * ((V / 2 + G - 1) / G);
+    TSlot tn[] = {{&P.nuc_hist, (size_t)lf::kSampBins * G * 2}, {&P.nuc_btot, (size_t)lf::kSampBins * 2},
+                  {&P.nuc_cand, (size_t)G * (3 + (size_t)P.nuc_cmax / 2)}, {&P.nuc_zmax, (size_t)G}};
+    if (nuc)
+      for (auto &t : tn) bytes += align_up(t.words * 8, 256);
     char *xb = (char *)dev_alloc(st, bytes, &e);
     if (!xb) return bail(fail(&st->err, LF_ENOMEM, "exchange buffer allocation failed"));
     (void)hipMemsetAsync(xb, 0, bytes, s);
     size_t o2 = 0;
     for (auto &t : ts) { *t.dst = (unsigned long long *)(xb + o2); o2 += align_up((2 * t.words + pad_words) * 8, 256); }
+    for (auto &t : tn) {
+      if (!nuc) { *t.dst = nullptr; continue; }
+      *t.dst = (unsigned long long *)(xb + o2);
+      o2 += align_up(t.words * 8, 256);
+    }
+    // (workgroup 0's list bookkeeping holds at most kSampBins workgroups; rows
+    // are listed as 16-bit offsets within a workgroup's block)
+    P.nuc_grid = nuc && G <= lf::kSampBins && P.nuc_cmax <= 65536 &&
+                 !(std::getenv("LF_NUC_WG0") && std::atoi(std::getenv("LF_NUC_WG0")) != 0) ? 1 : 0;
     P.part_gen = part_gen;
     st->xbuf = xb;
     st->xbuf_bytes = bytes;
@@ -593,7 +616,7 @@ int lf_generate_noalloc(lf_state *st, int32_t n, int32_t *out_tokens_dev) {
   lf::Params P = st->P;
   noalloc_layout(st, base, &P);
   P.out_tokens = out_tokens_dev;
-  P.levels_per_token = lf::PH_PER_LAYER * P.L + 2;
+  P.levels_per_token = lf::PH_PER_LAYER * P.L + 2 + (P.nuc_grid ? lf::kNucLevels : 0);
   P.n_tokens = n;
   P.trace_token = n / 2;
   P.token0 = st->pending_token;

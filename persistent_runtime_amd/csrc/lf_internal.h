@@ -47,7 +47,8 @@ constexpr int kTraceSlots = 16;          // timestamps per phase (LF_TRACE build
 constexpr int kStageRound = 64 * 40;      // tagged words one staging round reads (buffers are padded to it)
 constexpr int kStageRoundWide = 64 * 56;  // the SwiGLU vector's staging round
 constexpr int kRingSlots = LF_RING_SLOTS;  // 1-KB pieces in flight per stream wave (register ring)
-constexpr int kSampBytes = 60 * 1024;      // LDS of the nucleus draw (workgroup 0, after the lm_head)
+constexpr int kSampBins = 256;             // bins of z* - z in the nucleus draw
+constexpr int kSampBytes = 60 * 1024;      // LDS of the nucleus draw (after the lm_head)
 constexpr int kSampSegs = 6144;            // 64-index segments the nucleus draw's token search can hold
 constexpr int kSampMaxVocab = kSampSegs * 64;
 
@@ -80,6 +81,9 @@ enum LayerPart { LW_QKV = 0, LW_O, LW_GU, LW_D, LW_COUNT };
 // Next-token choice: argmax, nucleus draw by workgroup 0, or Gumbel-max (every
 // lm_head workgroup publishes its best noised score, workgroup 0 reduces them).
 enum SampleMode { SAMPLE_GREEDY = 0, SAMPLE_NUCLEUS = 1, SAMPLE_GUMBEL = 2 };
+// Dependency levels the nucleus draw over the grid adds between the lm_head's
+// level and the token's.
+constexpr int kNucLevels = 3;
 
 struct Params {
   // shape
@@ -125,6 +129,13 @@ struct Params {
   unsigned long long *o_t;               // [2][Hq*dh/2] fp16 pairs of the merged attention output
   unsigned long long *a_t;               // [2][F/2] fp16 pairs of the SwiGLU output
   unsigned long long part_gen;           // words per generation of part_t
+  // the nucleus draw over the grid (nucleus sampling; null otherwise): each
+  // workgroup's masses per bin [256][G][2], bin totals [256][2], records
+  // [G][3 + nuc_cmax / 2] (count, mass before the boundary bin, the boundary
+  // bin's rows two a word), largest logits [G]
+  unsigned long long *nuc_hist, *nuc_btot, *nuc_cand, *nuc_zmax;
+  int nuc_cmax;                          // most lm_head rows of one workgroup
+  int nuc_grid;                          // 1: the draw over the grid, 0: workgroup 0 alone
   float *logits;           // fp32 [V]
   float *lm_val;           // [G] per-workgroup max logit
   int *lm_idx;             // [G] its index

@@ -151,31 +151,48 @@ __device__ __forceinline__ void wave_argmax(float &best, int &bi) {
 }
 // Whether no active lane has p set (one compare into a scalar lane mask).
 __device__ __forceinline__ bool wave_none(bool p) { return __builtin_amdgcn_ballot_w64(p) == 0ull; }
-// Wave-wide sum of 64-bit integers with the same DPP row steps (each a pair of
-// 32-bit moves and one 64-bit add; integer sums are exact in any order); the
-// total is read back from lane 63 into every lane.
-__device__ __forceinline__ unsigned long long wave_sum_u64_dpp(unsigned long long v) {
-#define LF_DPP_U64(ctrl, rmask)                                                                                 \
-  {                                                                                                            \
-    const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)v, (ctrl), (rmask), 0xf, false); \
-    const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(v >> 32), (ctrl), (rmask), 0xf, \
-                                                              false);                                          \
-    v += ((unsigned long long)hi << 32) | lo;                                                                  \
-  }
-  LF_DPP_U64(0xB1, 0xf)
-  LF_DPP_U64(0x4E, 0xf)
-  LF_DPP_U64(0x141, 0xf)
-  LF_DPP_U64(0x140, 0xf)
-  LF_DPP_U64(0x142, 0xa)
-  LF_DPP_U64(0x143, 0xc)
-#undef LF_DPP_U64
+// One DPP move of a 64-bit value (two 32-bit moves); lanes without a source
+// read 0.
+#define LF_DPP_U64(v, ctrl, rmask)                                                                     \
+  (((unsigned long long)(unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)((v) >> 32), (ctrl), (rmask), \
+                                                              0xf, false)                                \
+    << 32) |                                                                                             \
+   (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(v), (ctrl), (rmask), 0xf, false))
+__device__ __forceinline__ unsigned long long lane63_u64(unsigned long long v) {
   const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, 63);
   const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), 63);
   return ((unsigned long long)hi << 32) | lo;
 }
+// Wave-wide sum of 64-bit integers with the same DPP row steps as wave_sum_to63
+// (integer sums are exact in any order), read back from lane 63 into every lane.
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += (unsigned long long)__shfl_xor((long long)v, m, 64);
+  v += LF_DPP_U64(v, 0xB1, 0xf);
+  v += LF_DPP_U64(v, 0x4E, 0xf);
+  v += LF_DPP_U64(v, 0x141, 0xf);
+  v += LF_DPP_U64(v, 0x140, 0xf);
+  v += LF_DPP_U64(v, 0x142, 0xa);
+  v += LF_DPP_U64(v, 0x143, 0xc);
+  return lane63_u64(v);
+}
+// Inclusive prefix sums over the 64 lanes: shifts right by 1, 2, 4 and 8 lanes
+// within each row of 16, then lane 15 of a row added into the next row (rows 1
+// and 3) and lane 31 into rows 2 and 3.
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long v) {
+  v += LF_DPP_U64(v, 0x111, 0xf);   // row_shr:1
+  v += LF_DPP_U64(v, 0x112, 0xf);   // row_shr:2
+  v += LF_DPP_U64(v, 0x114, 0xf);   // row_shr:4
+  v += LF_DPP_U64(v, 0x118, 0xf);   // row_shr:8
+  v += LF_DPP_U64(v, 0x142, 0xa);   // row_bcast:15
+  v += LF_DPP_U64(v, 0x143, 0xc);   // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ unsigned wave_scan_u32(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);
   return v;
 }
 
@@ -1814,10 +1831,13 @@ __device__ __forceinline__ float gumbel_score(float logit, float inv_temp, unsig
 // Plain loads: the caller has taken an agent-scope acquire fence after the
 // logits were published, so this XCD's caches hold no stale copy of them, and
 // the sampler's repeated passes then hit in L2.
-__device__ __forceinline__ float scaled_logit(const float *logits, int i, float inv_temp) {
+__device__ __forceinline__ float scale_logit(float logit, float inv_temp) {
 #pragma clang fp contract(off)
-  float z = logits[i] * inv_temp;
+  float z = logit * inv_temp;
   return z == 0.0f ? 0.0f : z;   // one zero: -0 and +0 order as equal
+}
+__device__ __forceinline__ float scaled_logit(const float *logits, int i, float inv_temp) {
+  return scale_logit(logits[i], inv_temp);
 }
 
 __device__ __forceinline__ unsigned long long mass_of(float z, float zmax) {
@@ -1842,7 +1862,6 @@ __device__ __forceinline__ unsigned long long order_key(float z, int i) {
 // earlier in the (z desc, index asc) order); the bin that holds the nucleus
 // boundary is then the only one whose order matters, and its elements (the
 // candidates, up to kSampCap) are kept in LDS for the radix select.
-constexpr int kSampBins = 256;
 constexpr int kSampCap = 2048;
 constexpr float kSampBinScale = 256.0f / 24.0f;   // d in [0, 23] -> bins 0 .. 245
 #ifndef LF_SAMP_BATCH
@@ -1856,6 +1875,7 @@ struct SampLds {
   unsigned long long ck[kSampCap];            // candidates' order keys
   unsigned long long cq[kSampCap];            // candidates' masses
   unsigned long long mass[256];               // bin totals, then one radix pass's digit masses
+  unsigned char cown[kSampCap];               // (the draw over the grid) each candidate's workgroup
   unsigned long long wtot[kWaves];
   unsigned long long sel[4];
   float fred[kWaves];
@@ -1914,11 +1934,7 @@ __device__ __forceinline__ int scan_reach(const unsigned long long *m, bool desc
     e[k] = m[desc ? 255 - i : i];
     tot += e[k];
   }
-  unsigned long long incl = tot;
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long y = (unsigned long long)__shfl_up((long long)incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  unsigned long long incl = wave_scan_u64(tot);
   unsigned long long run = base + incl - tot;   // before this lane's first entry
   int hit = -1;
   unsigned long long hb = 0;
@@ -1941,7 +1957,7 @@ __device__ __forceinline__ int scan_reach(const unsigned long long *m, bool desc
   } else {
     // (unreachable for consistent inputs: the entries hold at least need)
     idx = 255;
-    bef = base + (unsigned long long)__shfl((long long)incl, 63, 64);
+    bef = base + lane63_u64(incl);
   }
   *before = bef;
   return desc ? 255 - idx : idx;
@@ -2101,7 +2117,7 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
     const bool member = i < V && (bn < beta || (bn == beta && order_key(z, i) >= kappa));
     const unsigned long long q = member ? mass_of(z, zmax) : 0ull;
     local += q;
-    const unsigned long long sg = wave_sum_u64_dpp(q);
+    const unsigned long long sg = wave_sum_u64(q);
     if (lane == 0) segs[k * kWaves + wave] = sg;   // segment (k, wave): indices 512 k + 64 wave ..
   };
   for (int k0 = 0; k0 < nr; k0 += kSampBatch) {
@@ -2126,17 +2142,13 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
     for (int c0 = 0; c0 < nseg; c0 += 64) {
       const int c = c0 + lane;
       const unsigned long long v = c < nseg ? segs[c] : 0ull;
-      unsigned long long incl = v;
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long y = (unsigned long long)__shfl_up((long long)incl, off, 64);
-        if (lane >= off) incl += y;
-      }
+      unsigned long long incl = wave_scan_u64(v);
       const unsigned long long ex = base + incl - v;
       if (v > 0 && ex <= t && t < ex + v) {
         s->sel[0] = (unsigned long long)c;
         s->sel[1] = ex;
       }
-      base += (unsigned long long)__shfl((long long)incl, 63, 64);
+      base += lane63_u64(incl);
     }
   }
   __syncthreads();
@@ -2149,11 +2161,7 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
       const float z = scaled_logit(logits, i, inv_temp);
       if (order_key(z, i) >= kappa) q = mass_of(z, zmax);
     }
-    unsigned long long incl = q;
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned long long y = (unsigned long long)__shfl_up((long long)incl, off, 64);
-      if (lane >= off) incl += y;
-    }
+    unsigned long long incl = wave_scan_u64(q);
     const unsigned long long ex = s->sel[1] + incl - q;
     if (q > 0 && ex <= t && t < ex + q) s->ibc[0] = i;
   }
@@ -2163,6 +2171,430 @@ __device__ __forceinline__ int sample_topp(const float *logits, int V, float inv
   if (kTrace && tr && tid == 0) tr[10] = ncand;
   __syncthreads();
   return tok;
+}
+
+// ---------------------------------------------------------------- the nucleus draw over the grid
+//
+// The same draw as sample_topp (the same integer masses, bins, order keys and
+// Philox draw, so the same token), with the per-logit work spread over the
+// lm_head workgroups, each over its own block of rows (consecutive indices,
+// ascending with the workgroup), and workgroup 0 handling the aggregates.  The
+// sync waves only; each step is one tagged exchange (a 64-bit value is a pair
+// of tagged words, low then high), at the levels after the lm_head's (the
+// largest logit z* of each workgroup comes tagged with the lm_head's level):
+//   +1  each workgroup's masses per bin            hist [bin][G][2]
+//   +2  the bin totals, bin j summed by workgroup j mod G   btot [bin][2]
+//   then every workgroup finds the boundary bin beta from the totals, and
+//   +3  each workgroup's record: its mass in the bins before beta and its rows
+//       in bin beta (16-bit offsets)                 cand [G][3 + cmax / 2]
+// Workgroup 0 then reads the records and the listed rows' logits, finds the
+// boundary key kappa, adds each workgroup's members in bin beta to its mass
+// before beta, and finds the workgroup and the row holding the draw.  With more
+// than kSampCap candidates it finds kappa, and the workgroups' members in bin
+// beta, by scanning every logit itself (slow, exact).
+
+__device__ __forceinline__ void st_tag64(u64 *p, unsigned long long v, unsigned tag) {
+  st_tag(p, ((u64)tag << 32) | (unsigned)v);
+  st_tag(p + 1, ((u64)tag << 32) | (unsigned)(v >> 32));
+}
+
+// Wave 0: the n tagged words at addr(i), i < n, re-read until every one carries
+// tag, then use(i, payload) for each (kCoopChunk slots of 64 words at a time).
+template <int kChunk = kCoopChunk, class A, class F>
+__device__ __forceinline__ bool wave_fetch(KP &P, int n, unsigned tag, A &&addr, F &&use) {
+  const int lane = lane_id();
+  const unsigned long long t0 = now_ticks();
+  for (int b0 = 0; b0 < n; b0 += 64 * kChunk) {
+    u64 v[kChunk];
+    for (;;) {
+      const unsigned e = ld_dev(&P.err[0]);
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) v[k] = ld_dev(addr(min(b0 + 64 * k + lane, n - 1)));
+      bool bad = false;
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) bad |= b0 + 64 * k + lane < n && tag_of(v[k]) != tag;
+      if (wave_none(bad)) {
+        retire(e);
+        break;
+      }
+      if (expired(P, t0, tag, e)) return false;
+    }
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k)
+      if (b0 + 64 * k + lane < n) use(b0 + 64 * k + lane, (unsigned)v[k]);
+  }
+  return true;
+}
+
+// Wave 0 of workgroup 0: the radix select of sample_topp over the candidate
+// list (keys ck, masses cq, n of them): the key of the nucleus boundary, given
+// the mass `above` before bin beta.  rescan: instead of the list, every logit of
+// bin beta (more candidates than the list holds).
+__device__ __forceinline__ unsigned long long nuc_kappa(SampLds *s, unsigned n, bool rescan, const float *logits,
+                                                        int V, float inv_temp, float zmax, int beta,
+                                                        unsigned long long above, unsigned long long Mstar) {
+  const int lane = lane_id();
+  unsigned long long prefix = 0, pmask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = lane; i < 256; i += 64) s->mass[i] = 0;
+    lds_drain();
+    auto add = [&](unsigned long long key, unsigned long long q) __attribute__((always_inline)) {
+      if ((key & pmask) == prefix) atomicAdd(&s->mass[(int)((key >> shift) & 255ull)], q);
+    };
+    if (!rescan) {
+      // 64 candidates a round; when every matching lane has the same digit (the
+      // high bytes of nearby keys), one wave sum and one add instead of 64 adds
+      // to one LDS word
+      for (unsigned c0 = 0; c0 < n; c0 += 64) {
+        const unsigned c = c0 + (unsigned)lane;
+        const unsigned long long key = c < n ? s->ck[c] : 0ull, q = c < n ? s->cq[c] : 0ull;
+        const bool m = c < n && (key & pmask) == prefix;
+        const int dg = (int)((key >> shift) & 255ull);
+        const unsigned long long mm = __builtin_amdgcn_ballot_w64(m);
+        if (mm == 0ull) continue;
+        const int d0 = __builtin_amdgcn_readlane(dg, __builtin_ctzll(mm));
+        if (__builtin_amdgcn_ballot_w64(m && dg != d0) == 0ull) {
+          const unsigned long long sum = wave_sum_u64(m ? q : 0ull);
+          if (lane == 0) atomicAdd(&s->mass[d0], sum);
+        } else if (m) {
+          atomicAdd(&s->mass[dg], q);
+        }
+      }
+    } else {
+      for (int i = lane; i < V; i += 64) {
+        const float z = scaled_logit(logits, i, inv_temp);
+        if (samp_bin(z, zmax) != beta) continue;
+        const unsigned long long q = mass_of(z, zmax);
+        if (q) add(order_key(z, i), q);
+      }
+    }
+    lds_drain();
+    unsigned long long bef;
+    const int pick = scan_reach(s->mass, true, above, Mstar, &bef);
+    prefix |= (unsigned long long)pick << shift;
+    pmask |= 255ull << shift;
+    above = bef;
+  }
+  return prefix;
+}
+
+// Wave 0 of workgroup 0: kappa from the candidate list (keys ck, masses cq, n of
+// them, all in bin beta) without eight radix passes: a histogram of the
+// candidates' masses over 256 sub-bins of bin beta (sub-bin = floor(256 (d -
+// beta)) with d = (z* - z) kSampBinScale, the bin's own formula refined, so a
+// lower sub-bin holds larger z), the sub-bin where the running mass from
+// `above` reaches Mstar, then that sub-bin's candidates ordered by key (each
+// lane ranks one against the others).  Returns false (kappa unset) when that
+// sub-bin holds more than 64 candidates (ties in z): then the radix select.
+__device__ __forceinline__ int nuc_sub(float z, float zmax, int beta) {
+#pragma clang fp contract(off)
+  const float d = (zmax - z) * kSampBinScale - (float)beta;
+  const int sb = (int)(d * 256.0f);
+  return sb < 0 ? 0 : (sb > 255 ? 255 : sb);
+}
+// (s->mass holds the candidates' masses per sub-bin on entry)
+__device__ __forceinline__ bool nuc_kappa_fine(SampLds *s, unsigned n, float zmax, int beta, unsigned long long above,
+                                               unsigned long long Mstar, unsigned long long *kappa) {
+  const int lane = lane_id();
+  auto sub_of = [&](unsigned long long key) __attribute__((always_inline)) -> int {
+    unsigned b = (unsigned)(key >> 32);
+    b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;   // the order key's float bits back
+    return nuc_sub(__uint_as_float(b), zmax, beta);
+  };
+  unsigned long long before;
+  const int sb = scan_reach(s->mass, false, above, Mstar, &before);
+  // the sub-bin's candidates into ibc-free scratch: indices into ck / cq (wave ballots)
+  unsigned *pick = reinterpret_cast<unsigned *>(&s->hm[7][0]);   // up to 64 entries
+  unsigned m = 0;
+  for (unsigned c0 = 0; c0 < n; c0 += 64) {
+    const unsigned c = c0 + (unsigned)lane;
+    const bool in = c < n && sub_of(s->ck[c]) == sb;
+    const unsigned long long mm = __builtin_amdgcn_ballot_w64(in);
+    const unsigned k = m + (unsigned)__builtin_popcountll(mm & ((1ull << lane) - 1ull));
+    if (in && k < 64u) pick[k] = c;
+    m += (unsigned)__builtin_popcountll(mm);
+  }
+  if (m > 64u) return false;
+  lds_drain();
+  // lane j < m: candidate j; its running mass before it = before + the masses of
+  // the sub-bin's larger keys
+  const bool act = (unsigned)lane < m;
+  const unsigned me = act ? pick[lane] : 0u;
+  const unsigned long long key = act ? s->ck[me] : 0ull, q = act ? s->cq[me] : 0ull;
+  unsigned long long run = before;
+  for (unsigned j = 0; j < m; ++j) {
+    const unsigned o = pick[j];
+    const unsigned long long ko = s->ck[o];
+    if (ko > key) run += s->cq[o];
+  }
+  const bool hit = act && run < Mstar && run + q >= Mstar;
+  const unsigned long long hm = __builtin_amdgcn_ballot_w64(hit);
+  if (hm == 0ull) return false;   // (unreachable for consistent masses)
+  const int src = __builtin_ctzll(hm);
+  *kappa = ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(key >> 32), src) << 32) |
+           (unsigned)__builtin_amdgcn_readlane((int)(unsigned)key, src);
+  return true;
+}
+
+// Every workgroup's sync wave, after the lm_head level lvl: the steps above.
+// Returns the token in workgroup 0 (-1 elsewhere), or -2 when a wait expired.
+__device__ __forceinline__ int nucleus_grid(KP &P, Sync &sy, Ctl *ctl, int b, int G, unsigned lvl, int pos,
+                                            unsigned char *lds, int trk = -1) {
+  const int lane = lane_id();
+  // LF_TRACE stamps (slot trk): 3 z* known, 4 bins written, 5 bin totals written,
+  // 6 boundary bin known, 7 record written; workgroup 0: 12 the heads in, 13 the
+  // lists in, 8 the candidates' keys, 14 kappa known, 10 the masses, 11 the
+  // token found; [15] the candidate count
+  auto stamp_at = [&](int j) __attribute__((always_inline)) { trace_at(P, trk, j); };
+  SampLds *s = reinterpret_cast<SampLds *>(lds);
+  unsigned long long *hist = &s->hm[0][0];                       // this workgroup's bins (256)
+  // fetched payloads and workgroup 0's list bookkeeping (5 G + G + kSampCap / 2
+  // words at most: below hm[7], which the sub-bin search uses)
+  unsigned *tmp = reinterpret_cast<unsigned *>(&s->hm[1][0]);
+  const Geo ge = uniform_geo(ctl, K_LM);
+  const int V = P.V, cmax = P.nuc_cmax, cstride = 3 + cmax / 2;
+  const float inv_temp = P.inv_temp;
+  // z*: the lm_head workgroups' maxima, tagged words stored after their logits
+  // were complete (the acquire fence then orders the plain logit loads below)
+  float zm = -INFINITY;
+  if (!wave_fetch(P, G, lvl, [&](int i) { return (const u64 *)P.nuc_zmax + i; },
+                  [&](int, unsigned w) { zm = fmaxf(zm, __uint_as_float(w)); }))
+    return -2;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
+  float zmax;
+  {
+#pragma clang fp contract(off)
+    zmax = wave_max(zm) * inv_temp;
+  }
+  stamp_at(3);
+  // +1: masses per bin of this workgroup's rows
+  for (int j = lane; j < kSampBins; j += 64) hist[j] = 0ull;
+  lds_drain();
+  for (int i = lane; i < ge.nrows; i += 64) {
+    const float z = scaled_logit(P.logits, ge.r0 + i, inv_temp);
+    const unsigned long long q = mass_of(z, zmax);
+    if (q) atomicAdd(&hist[samp_bin(z, zmax)], q);
+  }
+  lds_drain();
+  for (int j = lane; j < kSampBins; j += 64) st_tag64(P.nuc_hist + ((size_t)j * G + b) * 2, hist[j], lvl + 1u);
+  stamp_at(4);
+  // +2: the totals of bins b, b + G, ...
+  for (int j = b; j < kSampBins; j += G) {
+    const u64 *src = P.nuc_hist + (size_t)j * G * 2;
+    if (!wave_fetch(P, 2 * G, lvl + 1u, [&](int i) { return src + i; },
+                    [&](int i, unsigned w) { tmp[i] = w; }))
+      return -2;
+    lds_drain();
+    unsigned long long v = 0;
+    for (int w = lane; w < G; w += 64) v += ((unsigned long long)tmp[2 * w + 1] << 32) | tmp[2 * w];
+    v = wave_sum_u64(v);
+    lds_drain();
+    if (lane == 0) st_tag64(P.nuc_btot + (size_t)j * 2, v, lvl + 2u);
+  }
+  stamp_at(5);
+  // every workgroup: the bin totals, their sum C_V, the target mass M* =
+  // ceil(top_p C_V) and the boundary bin beta (the same values everywhere)
+  if (!wave_fetch(P, 2 * kSampBins, lvl + 2u, [&](int i) { return P.nuc_btot + i; },
+                  [&](int i, unsigned w) { tmp[i] = w; }))
+    return -2;
+  lds_drain();
+  unsigned long long cv = 0;
+  for (int j = lane; j < kSampBins; j += 64) {
+    const unsigned long long m = ((unsigned long long)tmp[2 * j + 1] << 32) | tmp[2 * j];
+    s->mass[j] = m;
+    cv += m;
+  }
+  cv = wave_sum_u64(cv);
+  lds_drain();
+  const unsigned long long Mstar = (unsigned long long)ceil((double)P.top_p * (double)cv);
+  unsigned long long above;   // the mass of the bins before beta
+  const int beta = scan_reach(s->mass, false, 0ull, Mstar, &above);
+  stamp_at(6);
+  // +3: this workgroup's record: word 0 the count of its rows in bin beta (with
+  // a nonzero mass), words 1-2 the mass of its rows in the bins before beta,
+  // words 3.. those rows as 16-bit offsets from its first row, two a word
+  {
+    u64 *cb = P.nuc_cand + (size_t)b * cstride;
+    unsigned short *off16 = reinterpret_cast<unsigned short *>(tmp);
+    unsigned cnt = 0;
+    for (int i0 = 0; i0 < ge.nrows; i0 += 64) {
+      const int i = i0 + lane;
+      bool c = false;
+      if (i < ge.nrows) {
+        const float z = scaled_logit(P.logits, ge.r0 + i, inv_temp);
+        c = mass_of(z, zmax) != 0 && samp_bin(z, zmax) == beta;
+      }
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(c);
+      if (c) off16[cnt + (unsigned)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = (unsigned short)i;
+      cnt += (unsigned)__builtin_popcountll(m);
+    }
+    lds_drain();
+    for (unsigned j = (unsigned)lane; 2 * j < cnt; j += 64) {
+      const unsigned lo = off16[2 * j], hi = 2 * j + 1 < cnt ? off16[2 * j + 1] : 0u;
+      st_tag(cb + 3 + j, ((u64)(lvl + 3u) << 32) | lo | (hi << 16));
+    }
+    unsigned long long pre = 0;
+    for (int j = lane; j < beta; j += 64) pre += hist[j];
+    pre = wave_sum_u64(pre);
+    lds_drain();
+    if (lane == 0) {
+      st_tag64(cb + 1, pre, lvl + 3u);
+      st_tag(cb, ((u64)(lvl + 3u) << 32) | cnt);
+    }
+  }
+  stamp_at(7);
+  if (b != 0) return -1;
+
+  // ---- workgroup 0: every record's head (count, mass before beta)
+  unsigned *head = tmp, *cpre = tmp + 3 * G, *wpre = tmp + 4 * G, *wmap = tmp + 5 * G;
+  const int qb = (V / 2) / G, rb = (V / 2) % G;   // workgroup w's first row: 2 (w qb + min(w, rb))
+  if (!wave_fetch<16>(P, 3 * G, lvl + 3u,
+                  [&](int i) { return (const u64 *)P.nuc_cand + (size_t)(i / 3) * cstride + i % 3; },
+                  [&](int i, unsigned v) { head[i] = v; }))
+    return -2;
+  lds_drain();
+  // exclusive prefixes over the workgroups of the counts (cpre) and of the list
+  // words (wpre); each workgroup's nucleus mass starts as its mass before beta
+  unsigned long long *sums = &s->hm[0][0];
+  unsigned run = 0, wrun = 0;
+  for (int w0 = 0; w0 < G; w0 += 64) {
+    const int w = w0 + lane;
+    const unsigned v = w < G ? head[3 * w] : 0u, vw = (v + 1u) >> 1;
+    const unsigned incl = wave_scan_u32(v), winc = wave_scan_u32(vw);
+    if (w < G) {
+      cpre[w] = run + incl - v;
+      wpre[w] = wrun + winc - vw;
+      sums[w] = ((unsigned long long)head[3 * w + 2] << 32) | head[3 * w + 1];
+    }
+    run += (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+    wrun += (unsigned)__builtin_amdgcn_readlane((int)winc, 63);
+  }
+  lds_drain();
+  const unsigned total = run, nw = wrun;
+  const bool rescan = total > (unsigned)kSampCap;
+  for (int j = lane; j < 256; j += 64) s->mass[j] = 0ull;
+  lds_drain();
+  stamp_at(12);
+  if (kTrace && trk >= 0 && lane == 0) trace_row(P, trk)[15] = total;
+  if (!rescan && total > 0) {
+    // the list words: word i belongs to workgroup wmap[i]; candidate c (in
+    // workgroup then row order) gets its row in ck[c]
+    for (int w = lane; w < G; w += 64) {
+      const unsigned n = (head[3 * w] + 1u) >> 1;
+      for (unsigned k = 0; k < n; ++k) wmap[wpre[w] + k] = (unsigned)w;
+    }
+    lds_drain();
+    if (!wave_fetch<16>(P, (int)nw, lvl + 3u,
+                        [&](int i) {
+                          // (clamped: a word index always stays inside the record area)
+                          const unsigned w = min(wmap[i], (unsigned)G - 1u);
+                          return (const u64 *)P.nuc_cand + (size_t)w * cstride + 3 +
+                                 min((unsigned)i - wpre[w], (unsigned)cstride - 4u);
+                        },
+                        [&](int i, unsigned v) {
+                          const unsigned w = wmap[i], k = 2u * ((unsigned)i - wpre[w]), c = cpre[w] + k;
+                          const unsigned r0 = 2u * (w * (unsigned)qb + min(w, (unsigned)rb));
+                          s->ck[c] = r0 + (v & 0xffffu);
+                          s->cown[c] = (unsigned char)w;
+                          if (k + 1u < head[3 * w]) {
+                            s->ck[c + 1] = r0 + (v >> 16);
+                            s->cown[c + 1] = (unsigned char)w;
+                          }
+                        }))
+      return -2;
+    lds_drain();
+    stamp_at(13);
+    // the candidates' logits (plain loads, kB per lane in flight), their order
+    // keys and masses, and their masses per sub-bin of bin beta
+    constexpr int kB = 16;
+    for (unsigned c0 = 0; c0 < total; c0 += 64 * kB) {
+      int row[kB];
+      float lg[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const unsigned c = c0 + 64 * k + (unsigned)lane;
+        row[k] = c < total ? (int)s->ck[c] : 0;
+        lg[k] = P.logits[row[k]];
+      }
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const unsigned c = c0 + 64 * k + (unsigned)lane;
+        if (c < total) {
+          const float z = scale_logit(lg[k], inv_temp);
+          const unsigned long long q = mass_of(z, zmax);
+          s->ck[c] = order_key(z, row[k]);
+          s->cq[c] = q;
+          atomicAdd(&s->mass[nuc_sub(z, zmax, beta)], q);
+        }
+      }
+    }
+    lds_drain();
+  }
+  stamp_at(8);
+  unsigned long long kappa = 0;
+  if (rescan || !nuc_kappa_fine(s, total, zmax, beta, above, Mstar, &kappa))
+    kappa = nuc_kappa(s, total, rescan, P.logits, V, inv_temp, zmax, beta, above, Mstar);
+  stamp_at(14);
+  // add each workgroup's members in bin beta (key >= kappa) to its mass
+  if (!rescan) {
+    for (unsigned c = (unsigned)lane; c < total; c += 64)
+      if (s->ck[c] >= kappa) atomicAdd(&sums[s->cown[c]], s->cq[c]);
+  } else {
+    const int cut = rb * (qb + 1);
+    auto owner = [&](int r) __attribute__((always_inline)) -> int {
+      const int p = r >> 1;
+      return p < cut ? p / (qb + 1) : rb + (p - cut) / qb;
+    };
+    for (int i = lane; i < V; i += 64) {
+      const float z = scaled_logit(P.logits, i, inv_temp);
+      if (samp_bin(z, zmax) != beta || order_key(z, i) < kappa) continue;
+      const unsigned long long q = mass_of(z, zmax);
+      if (q) atomicAdd(&sums[owner(i)], q);
+    }
+  }
+  lds_drain();
+  unsigned long long cn = 0;
+  for (int w = lane; w < G; w += 64) cn += sums[w];
+  cn = wave_sum_u64(cn);
+  stamp_at(10);
+  auto member_mass = [&](int r) __attribute__((always_inline)) -> unsigned long long {
+    const float z = scaled_logit(P.logits, r, inv_temp);
+    const int bn = samp_bin(z, zmax);
+    return (bn < beta || (bn == beta && order_key(z, r) >= kappa)) ? mass_of(z, zmax) : 0ull;
+  };
+  // the draw t, the workgroup holding it, then its row
+  unsigned ctr[4] = {(unsigned)pos, 0u, 0u, 0u};
+  philox4x32_10(ctr, (unsigned)(P.seed & 0xffffffffull), (unsigned)(P.seed >> 32));
+  const unsigned long long r = ((unsigned long long)ctr[1] << 32) | ctr[0];
+  const unsigned long long t = __umul64hi(r, cn);
+  // exclusive scans in index order: the workgroup w with ex <= t < ex + v, then its row
+  auto find = [&](int n, auto &&val, unsigned long long base, unsigned long long &at) __attribute__((always_inline)) {
+    int hit = -1;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const unsigned long long v = c0 + lane < n ? val(c0 + lane) : 0ull;
+      unsigned long long incl = wave_scan_u64(v);
+      const unsigned long long ex = base + incl - v;
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(v > 0 && ex <= t && t < ex + v);
+      if (m) {
+        const int src = __builtin_ctzll(m);
+        hit = c0 + src;
+        at = ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(ex >> 32), src) << 32) |
+             (unsigned)__builtin_amdgcn_readlane((int)(unsigned)ex, src);
+        break;
+      }
+      base += lane63_u64(incl);
+    }
+    return hit;
+  };
+  unsigned long long wbase = 0, rbase = 0;
+  const int w = find(G, [&](int i) { return sums[i]; }, 0ull, wbase);
+  if (w < 0) return 0;   // (unreachable: the workgroups' masses add up to C_N > t)
+  int p0, p1;
+  block_range(V / 2, G, w, p0, p1);
+  const int row = find(2 * (p1 - p0), [&](int i) { return member_mass(2 * p0 + i); }, wbase, rbase);
+  stamp_at(11);
+  return row < 0 ? 0 : 2 * p0 + row;
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -2329,7 +2761,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           if (P.gu_pf > 0) gu_prefetch(P, ctl, st.cw, l);
         }
       }
-      if (has_lm && b == 0 && P.sampling == SAMPLE_NUCLEUS) {
+      if (has_lm && b == 0 && P.sampling == SAMPLE_NUCLEUS && !P.nuc_grid) {
         const unsigned lvl_lm = lv0 + (unsigned)(L * PH_PER_LAYER) + 1u;
         if (lds_ld(&ctl->abort)) return;
         if (!wait_all_waves(sy, 0, G, lvl_lm, true)) return;
@@ -2618,11 +3050,34 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         st_dev(&P.lm_idx[b], bi);
       }
       publish_sync(P, lvl_lm);
+      // the nucleus draw over the grid polls the maxima as tagged words (the
+      // logits' stores are complete: publish_sync waited for them)
+      if (P.nuc_grid && lane == 0) st_tag(P.nuc_zmax + b, tag_f(best, lvl_lm));
       trace(P, t, 5 * L, 2);
     }
 
-    // ---------------- next token (workgroup 0)
-    if (b == 0) {
+    // ---------------- next token
+    if (P.sampling == SAMPLE_NUCLEUS && P.nuc_grid) {
+      // the nucleus draw over the grid: every workgroup's sync wave takes part
+      trace(P, t, 5 * L + 1, 0);
+      int tok = nucleus_grid(P, sy, ctl, b, G, lvl_lm, pos, alds, t == P.trace_token ? 5 * L + 1 : -1);
+      if (tok == -2) {
+        fail();
+        return;
+      }
+      if (b == 0) {
+        if (tok < 0 || tok >= P.V) {   // never expected; keeps the next embedding read in bounds
+          if (lane == 0) st_dev(&P.err[3], 1u);
+          tok = 0;
+        }
+        if (lane == 0) {
+          st_dev(P.tok_slot, tok);
+          P.out_tokens[t] = tok;
+        }
+        publish_sync(P, lvl_lm + 1u + (unsigned)kNucLevels);
+      }
+      trace(P, t, 5 * L + 1, 2);
+    } else if (b == 0) {
       int tok;
       if (P.sampling == SAMPLE_NUCLEUS) {
         trace(P, t, 5 * L + 1, 0);

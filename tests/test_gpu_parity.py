@@ -264,11 +264,18 @@ def test_gqa_and_head64_variants(lf, orc):
         teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 5))
 
 
-def test_sampling_model_tokens_match_oracle_sampler(lf, orc, tiny):
+@pytest.mark.parametrize("path", ["grid", "grid7", "wg0"])
+def test_sampling_model_tokens_match_oracle_sampler(lf, orc, tiny, monkeypatch, path):
     """Temperature / top-p in the kernel: for the GPU's own logits and counters the
-    oracle sampler picks the same token at every step."""
+    oracle sampler picks the same token at every step.  grid: the draw spread over
+    the lm_head workgroups; grid7: the same on a 7-workgroup grid (fewer
+    workgroups than bins, so each sums several bins); wg0: workgroup 0 alone."""
     cfg, w = tiny
     cfg = dict(cfg, temperature=0.8, top_p=0.9, seed=1234)
+    if path == "grid7":
+        monkeypatch.setenv("LF_GRID", "7")
+    if path == "wg0":
+        monkeypatch.setenv("LF_NUC_WG0", "1")
     eng = lf.Engine(cfg, lf.upload_weights(w))
     tok, pos = 7, 0
     for _ in range(20):
@@ -276,6 +283,48 @@ def test_sampling_model_tokens_match_oracle_sampler(lf, orc, tiny):
         logits = eng.logits().cpu().numpy()
         assert nxt == orc.sample(logits, 0.8, 0.9, 1234, pos)
         tok, pos = nxt, pos + 1
+
+
+@pytest.mark.parametrize("path", ["grid", "grid7", "wg0"])
+def test_nucleus_generate_equals_stepwise(lf, tiny, monkeypatch, path):
+    """Top-p tokens drawn inside one launch of 20 tokens (each token's draw at six
+    levels of its own over the grid) equal those of 20 one-token launches."""
+    cfg, w = tiny
+    cfg = dict(cfg, temperature=0.8, top_p=0.9, seed=99)
+    if path == "grid7":
+        monkeypatch.setenv("LF_GRID", "7")
+    if path == "wg0":
+        monkeypatch.setenv("LF_NUC_WG0", "1")
+    dw = lf.upload_weights(w)
+    a, b = lf.Engine(cfg, dw), lf.Engine(cfg, dw)
+    a.decode_step(5, 0)
+    ga = a.generate(20)
+    tok = b.decode_step(5, 0)
+    gb = []
+    for i in range(20):
+        tok = b.decode_step(tok, 1 + i)
+        gb.append(tok)
+    assert list(ga) == gb
+
+
+@pytest.mark.parametrize("path", ["grid", "wg0"])
+def test_nucleus_flat_logits(lf, orc, tiny, monkeypatch, path):
+    """A zero lm_head: every logit is 0, all 4096 tokens tie in the first bin, more
+    candidates than the list holds, so the boundary key is found by scanning
+    every logit of the bin; the token still equals the oracle sampler's."""
+    cfg, w = tiny
+    cfg = dict(cfg, temperature=0.8, top_p=0.9, seed=7)
+    w = dict(w, lm_head=np.zeros_like(w["lm_head"]))
+    if path == "wg0":
+        monkeypatch.setenv("LF_NUC_WG0", "1")
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    tok = 3
+    for pos in range(4):
+        nxt = eng.decode_step(tok, pos)
+        logits = eng.logits().cpu().numpy()
+        assert not logits.any()
+        assert nxt == orc.sample(logits, 0.8, 0.9, 7, pos)
+        tok = nxt
 
 
 def test_gumbel_model_tokens_match_oracle_sampler(lf, orc, tiny):
