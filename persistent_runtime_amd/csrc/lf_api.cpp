@@ -270,6 +270,8 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.window = c.sliding_window;
   P.attn_unit_tiles = lf::kWaves - 1;   // one tile per stream wave
   P.attn_split_tiles = 3;
+  P.attn_qsplit = 1;
+  if (const char *s = std::getenv("LF_ATTN_QSPLIT")) P.attn_qsplit = std::atoi(s) != 0 ? 1 : 0;
   // Workgroups without attention units hold back the output projection's first
   // ring round ~3.5 us (350 ticks of the 100 MHz clock), about one attention
   // pass at short contexts, so that the K/V loads meet a quieter memory system.
@@ -449,7 +451,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     const int units[5] = {P.nqkv / 2, d, F / 2, d / 2, hidden ? 0 : V / 2};
     const int upr[5] = {2, 1, 4, 2, 2};   // rows per partition unit (as in the kernel)
     for (int k = 0; k < 5; ++k) {
-      const int g = k == 1 ? G - lf::o_rows_skip(G, Hkv) : G;   // the output projection's workgroups
+      const int g = k == 1 ? G - lf::o_rows_skip_max(G, Hkv, P.qpg, P.attn_qsplit) : G;   // the output projection's workgroups
       const int r = upr[k] * ((units[k] + g - 1) / g);
       rows_max = r > rows_max ? r : rows_max;
     }
@@ -504,6 +506,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     if (const char *s = std::getenv("LF_KV_PF")) want = std::atoll(s);
     if (want < 0 || P.qpg > 4) want = 0;   // the unit variant for more query heads reads no prefetch
     P.kv_pf = (int)(want < fit ? want : fit);
+    if (P.kv_pf > 0) P.attn_qsplit = 0;   // the tile prefetch maps units to KV heads directly
     P.lds_kvpf = (int)lds_end;
     lds_end += (size_t)P.kv_pf * P.kv_pf_tile;
   }

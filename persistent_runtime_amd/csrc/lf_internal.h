@@ -31,6 +31,11 @@ __host__ __device__ constexpr size_t v_elem(int dh, int j, int e) {
 // of head g runs on workgroup g); they are the last to finish attention, so
 // with enough workgroups they get no rows of the output projection.
 __host__ __device__ constexpr int o_rows_skip(int G, int Hkv) { return G > 2 * Hkv ? Hkv : 0; }
+// The most workgroups that may skip them: with short heads split by query heads
+// (one unit per query head while 2 Hkv qpg <= G), every unit's workgroup.
+__host__ __device__ constexpr int o_rows_skip_max(int G, int Hkv, int qpg, int qsplit) {
+  return qsplit && qpg > 1 && 2 * Hkv * qpg <= G ? o_rows_skip(G, Hkv * qpg) : o_rows_skip(G, Hkv);
+}
 constexpr int kStatWords = 16;         // uint64 statistics per workgroup (LF_STATS)
 // LF_TRACE builds also record, for one token, three timestamps per phase and
 // workgroup: input staged, stream waves done, published.
@@ -95,6 +100,7 @@ struct Params {
   int window;                          // sliding-window length (0: none)
   int attn_unit_tiles;                 // most KV tiles a KV head keeps in one unit (1 .. 7)
   int attn_split_tiles;                // tiles per unit once a head is split (1 .. 7)
+  int attn_qsplit;                     // 1: a KV head in one unit is split by query heads (GQA)
   int gu_pf;                           // gate/up pieces per stream wave prefetched into LDS during attention
   int kv_pf;                           // stream waves whose first K/V tile is prefetched into LDS (0: off)
   int kv_pf_tile;                      // LDS bytes of one prefetched tile

@@ -1180,10 +1180,15 @@ __device__ __forceinline__ bool wait_streams(const Ctl *ctl, int q) {
 // anyway gains from short units (a CU keeps only ~60 KB of loads in flight, so
 // a unit's load time grows with its tiles), while one that fits in one unit
 // would pay a merge exchange to split.  Unit 0 also takes the current key.
+// A KV head that fits in one unit is further split by query heads (qs, GQA):
+// Q units of qpg / Q query heads each read the same tiles, so a wave scores one
+// query head instead of qpg, while enough workgroups are left (2 Hkv qpg <= G).
+// Units: H = Hkv Q "unit heads" (unit head v: KV head v / Q, query heads
+// v qpg / Q ..), S chunks each; unit u is (v, c) = (u mod H, u / H).
 struct AttnPart {
-  int S, tpu, t0, nt, kb;
+  int S, tpu, t0, nt, kb, Q, H;
 };
-__device__ __forceinline__ AttnPart attn_part(int kb, int pos, int G, int Hkv, int ut, int us) {
+__device__ __forceinline__ AttnPart attn_part(int kb, int pos, int G, int Hkv, int qpg, int qs, int ut, int us) {
   AttnPart a;
   a.kb = kb;
   int smax = G / Hkv;
@@ -1200,6 +1205,8 @@ __device__ __forceinline__ AttnPart attn_part(int kb, int pos, int G, int Hkv, i
     a.t0 = a.nt = a.tpu = 0;
     a.S = 1;
   }
+  a.Q = qs && a.S == 1 && qpg > 1 && 2 * Hkv * qpg <= G ? qpg : 1;
+  a.H = Hkv * a.Q;
   return a;
 }
 
@@ -1224,10 +1231,11 @@ __device__ __forceinline__ bool layer_windowed(const KP &P, int l) {
 // layers ([1]).
 struct AttnSplit {
   AttnPart a[2];
-  __device__ __forceinline__ AttnSplit(int pos, int G, int Hkv, int window, int ut, int us) {
-    const int n = pos + 1;
-    a[0] = attn_part(0, pos, G, Hkv, ut, us);
-    a[1] = attn_part(window > 0 && n > window ? n - window : 0, pos, G, Hkv, ut, us);
+  __device__ __forceinline__ AttnSplit(const KP &P, int pos, int G) {
+    const int n = pos + 1, W = P.window;
+    a[0] = attn_part(0, pos, G, P.Hkv, P.qpg, P.attn_qsplit, P.attn_unit_tiles, P.attn_split_tiles);
+    a[1] = attn_part(W > 0 && n > W ? n - W : 0, pos, G, P.Hkv, P.qpg, P.attn_qsplit, P.attn_unit_tiles,
+                     P.attn_split_tiles);
   }
 };
 
@@ -1363,9 +1371,11 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   static_assert(kQ <= kMaxQpg, "query heads per KV head");
   KP &P = fresh(P0);
   const int wave = wave_id(), lane = lane_id();
-  const int qpg = P.qpg, dh = P.dh, Hkv = P.Hkv, half = dh / 2;
+  const int dh = P.dh, Hkv = P.Hkv, half = dh / 2;
   const int S = ap.S;
-  const int g = u % Hkv, c = u / Hkv;   // chunk c = 0 of head g runs on workgroup g
+  const int qpg = P.qpg / ap.Q;                      // this unit's query heads
+  const int vg = u % ap.H, c = u / ap.H;             // chunk c = 0 of unit head vg runs on workgroup vg
+  const int g = vg / ap.Q;                           // its KV head
   const AttnLds al = attn_lds(qpg, dh);
   _Float16 *q16 = reinterpret_cast<_Float16 *>(lds + al.q16);   // [qpg][dh]
   float *kcur = reinterpret_cast<float *>(lds + al.kcur);        // [dh]
@@ -1435,7 +1445,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     // tagged word each, polled by the stream waves that hold no tile (with a
     // tile in every wave, all of them).  Each thread requests up to four words
     // at once and re-reads the stale ones.
-    const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)g * qpg * dh;
+    const u64 *qsrc = P.q_t + (size_t)gen * P.Hq * dh + (size_t)vg * qpg * dh;
     const size_t nw = (size_t)Hkv * half;
     const int nq = qpg * dh;
     const int nwords = nq + (c == 0 ? dh : 0);
@@ -1596,7 +1606,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   const int e0 = act ? 2 * lane : 0;
   const int stride = dh + 2;
   gu64 *pg = (gu64 *)(P.part_t + (size_t)gen * P.part_gen);
-  gu64 *o_out = (gu64 *)(P.o_t + (size_t)gen * (P.Hq * dh / 2) + ((size_t)g * qpg * dh + e0) / 2);
+  gu64 *o_out = (gu64 *)(P.o_t + (size_t)gen * (P.Hq * dh / 2) + ((size_t)vg * qpg * dh + e0) / 2);
   asm volatile("" : "+s"(pg), "+v"(o_out));
   // Wave 1: combine the stream waves' states of head h (m, l, o for this lane's
   // two dims) left in wml / wo.  Every read is in bounds for every lane (e0 = 0
@@ -1625,7 +1635,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   stream_barrier(ctl);
   if (wave == 1) {
     trace_at(P, trw, 9);
-    gu64 *dst = pg + (size_t)(g * S + c) * qpg * stride;   // partials of head g in chunk order
+    gu64 *dst = pg + (size_t)(vg * S + c) * qpg * stride;   // partials of unit head vg in chunk order
     for (int h = 0; h < qpg; ++h) {
       float M, Ls, a0, a1;
       combine(h, M, Ls, a0, a1);
@@ -1658,7 +1668,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
     stream_barrier(ctl);   // wave 1 has read the unit's own states: wml / wo are free
     if (wave == 1) trace_at(P, trw, 11);
     {
-      const gu64 *src = pg + (size_t)g * S * qpg * stride;
+      const gu64 *src = pg + (size_t)vg * S * qpg * stride;
       const u64 tagw = (u64)tag_a << 32;
       for (int h = 0; h < qpg; ++h) {
         float M = -INFINITY, Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
@@ -2638,16 +2648,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     const int units[K_COUNT] = {P.nqkv / 2, d, P.F / 2, d / 2, P.V / 2};
     const int upr[K_COUNT] = {2, 1, 4, 2, 2};
     const int kvs[K_COUNT] = {d / 8, P.Hq * dh / 8, d / 8, P.F / 8, d / 8};
-    const int nskip = o_rows_skip(G, P.Hkv);
+    // (the units of the launch's first position: with query-split heads every
+    // unit's workgroup, else the merging ones)
+    const AttnSplit asp0(P, P.pos0, G);
+    const int nskip = o_rows_skip(G, asp0.a[0].H);
     // Workgroups that run attention with prefetched tiles stream no QKV rows:
     // the units of the launch's last position (the most), if they are few.
     int na = 0;
     if (P.kv_pf > 0) {
       const int pl = P.pos0 + P.n_tokens - 1;
-      const AttnSplit asp(pl, G, P.Hkv, P.window, P.attn_unit_tiles, P.attn_split_tiles);
+      const AttnSplit asp(P, pl, G);
       int smax = asp.a[0].S > asp.a[1].S ? asp.a[0].S : asp.a[1].S;
       if (P.window > 0) {   // a window's tile count moves by one with the position
-        const AttnPart w1 = attn_part(0, P.window + kKvTile, G, P.Hkv, P.attn_unit_tiles, P.attn_split_tiles);
+        const AttnPart w1 = attn_part(0, P.window + kKvTile, G, P.Hkv, P.qpg, P.attn_qsplit, P.attn_unit_tiles,
+                                      P.attn_split_tiles);
         if (w1.S > smax) smax = w1.S;
       }
       na = P.Hkv * smax;
@@ -2720,7 +2734,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     for (int t = 0; t < P.n_tokens; ++t) {
       const int pos = P.pos0 + t;
       const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
-      AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles, P.attn_split_tiles);
+      AttnSplit asp(P, pos, G);
       // The token's GEMV phases (four per layer, then the lm_head) in one loop,
       // so that the phase code exists once: a layer's instruction footprint then
       // stays within the instruction cache.
@@ -2737,7 +2751,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         // after attention: this wave's loads complete in order, so attention's
         // K/V loads would otherwise queue behind it.
         const bool qkv_rounds = qkv && st_has_rounds(st, K_QKV, ctl);
-        if (qkv && P.kv_pf > 0 && b < P.Hkv * asp.a[layer_windowed(P, l) ? 1 : 0].S)
+        if (qkv && P.kv_pf > 0 && b < asp.a[layer_windowed(P, l) ? 1 : 0].H * asp.a[layer_windowed(P, l) ? 1 : 0].S)
           kv_prefetch(P, ctl, l, b, asp.a[layer_windowed(P, l) ? 1 : 0], st.cw);
         if (!stream_phase(st, t * ngp + g, kind, ctl, hl, part, stage_spec(P, ctl, kind, t, l, gen, lvl, xown, xres),
                           qkv))
@@ -2745,12 +2759,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         if (qkv) {
           const AttnPart &ap = asp.a[layer_windowed(P, l) ? 1 : 0];
           if (lds_ld(&ctl->abort)) return;
-          if (b < P.Hkv * ap.S) {
-            for (int u = b; u < P.Hkv * ap.S; u += G)
+          if (b < ap.H * ap.S) {
+            for (int u = b; u < ap.H * ap.S; u += G)
               if (!attn_unit<kQ>(P, ctl, l, gen, lvl + PH_QKV, lvl + PH_ATTN, pos, u, ap, attn_scratch,
                                  u == b && t == P.trace_token ? 5 * l + 1 : -1))
                 return;
-          } else if (2 * P.Hkv * ap.S <= G) {
+          } else if (2 * ap.H * ap.S <= G) {
             // a workgroup without attention units, while attention runs on few:
             // hold back the output projection's first round for a while, so that
             // the K/V loads meet less traffic
@@ -2788,7 +2802,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     const int pos = P.pos0 + t;
     const unsigned lv0 = P.level_base + (unsigned)t * (unsigned)P.levels_per_token;
     if (kPrefill) token = P.in_tokens[t];
-    const AttnSplit asp(pos, G, P.Hkv, P.window, P.attn_unit_tiles, P.attn_split_tiles);
+    const AttnSplit asp(P, pos, G);
     for (int l = 0; l < L; ++l) {
       if (kTrace) trace(P, t, 5 * l + 0, 12);
       KP &Pl = fresh(P);

@@ -256,7 +256,12 @@ def test_attention_tile_prefetch(lf, orc, monkeypatch, waves):
     assert ok, err
 
 
-def test_gqa_and_head64_variants(lf, orc):
+@pytest.mark.parametrize("qsplit", ["1", "0"])
+def test_gqa_and_head64_variants(lf, orc, monkeypatch, qsplit):
+    """GQA 8/2 at head dim 64, 8/1 at 128 and MHA 2/2: logits against the oracle,
+    with short heads split into one attention unit per query head (the default)
+    and with one unit per KV head."""
+    monkeypatch.setenv("LF_ATTN_QSPLIT", qsplit)
     for kw in (dict(n_heads=8, n_kv_heads=2, head_dim=64), dict(n_heads=8, n_kv_heads=1, head_dim=128),
                dict(n_heads=2, n_kv_heads=2, head_dim=128, d_model=512, ffn_dim=1376, vocab=1000)):
         cfg = synth.scaled_config("tiny_2l_d256", **kw)
@@ -622,10 +627,13 @@ def test_dec2b_gumbel_sampling(lf, orc, dec2b):
         tok = nxt
 
 
-def test_sliding_window_gqa_head96_teacher_forced(lf, orc):
+@pytest.mark.parametrize("qsplit", ["1", "0"])
+def test_sliding_window_gqa_head96_teacher_forced(lf, orc, monkeypatch, qsplit):
     """Sliding-window attention on layers 0 and 2 of three (window 36: the windowed
     layers split 3 ways, the full layer 4 ways at the end), GQA 4/2 heads of dim 96:
-    logits against the oracle at every position, most of them past the window."""
+    logits against the oracle at every position, most of them past the window;
+    short heads split by query heads or not."""
+    monkeypatch.setenv("LF_ATTN_QSPLIT", qsplit)
     cfg = synth.scaled_config("tiny_2l_d256", n_layers=3, d_model=384, n_heads=4, n_kv_heads=2,
                               head_dim=96, ffn_dim=1024, vocab=2000, max_seq=64,
                               sliding_window=36, window_layers=0b101)
