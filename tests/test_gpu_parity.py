@@ -535,8 +535,8 @@ def test_dec8b_gqa_full_shape(lf, orc, dec8b):
     """The ~8B GQA decoder at full size (32 layers, d 4096, 32 query / 8 KV heads of
     dim 128, F 14336, untied vocabulary of 128,256 over the lm_head workgroups):
     teacher-forced steps from position 0; then the cache is filled with 255
-    synthetic rows and the steps at positions 255.. attend over them split across
-    several workgroups per KV head (4 query heads each); then one generate launch
+    synthetic rows and the steps at positions 255.. attend over them (4 tiles per
+    KV head: one attention unit per query head); then one generate launch
     against the oracle's greedy continuation.  Logits within tolerance at every
     step, greedy tokens equal where the oracle's top-2 margin is at least 1e-2."""
     import torch
@@ -625,6 +625,18 @@ def test_dec2b_gumbel_sampling(lf, orc, dec2b):
         assert ok, (pos, err)
         assert nxt == orc.sample_gumbel(got, 0.8, 4242, pos), pos
         tok = nxt
+
+
+def test_gqa_query_split_then_tile_split(lf, orc):
+    """GQA 8/2 heads of dim 64 teacher-forced through position 469.  While a KV
+    head's cached keys fit in one unit (at most 7 tiles of 64 keys: positions up
+    to 448), attention runs one unit per query head.  Past that, each KV head is
+    split into units of about 3 tiles, each with its 4 query heads, and the
+    units' partials are merged.  Logits are checked against the oracle at every
+    position."""
+    cfg = synth.scaled_config("tiny_2l_d256", n_heads=8, n_kv_heads=2, head_dim=64, max_seq=512)
+    w = synth.model_weights(cfg, seed=11)
+    teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 470))
 
 
 @pytest.mark.parametrize("qsplit", ["1", "0"])
