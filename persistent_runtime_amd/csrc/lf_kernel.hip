@@ -1371,6 +1371,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
   static_assert(kQ <= kMaxQpg, "query heads per KV head");
   KP &P = fresh(P0);
   const int wave = wave_id(), lane = lane_id();
+  if (kTrace && wave == 1) trace_at(P, trk, 8);
   const int dh = P.dh, Hkv = P.Hkv, half = dh / 2;
   const int S = ap.S;
   const int qpg = P.qpg / ap.Q;                      // this unit's query heads
@@ -1437,6 +1438,7 @@ __device__ __forceinline__ bool attn_unit(KP &P0, Ctl *ctl, int l, int gen, unsi
       if (nvh > 1) vr[kg][1] = *reinterpret_cast<const u32x4 *>(pft + (nck + kg * nvh + 1) * 1024);
     }
   } else if (tfirst < te) {
+    if (kTrace && wave == 1) trace_at(P, trk, 2);
     load_tile(tfirst);
   }
   if (kTrace && wave == 1) trace_at(P, trk, 0);

@@ -22,7 +22,7 @@ from . import lf
 PHASES = {0: "QKV", 1: "attention", 2: "output projection", 3: "gate/up", 4: "down"}
 SYNC = {6: "staging started", 7: "tagged input in", 0: "input staged", 1: "stream waves done", 2: "published"}
 WAVE1 = {3: "input seen", 5: "done"}
-ATT = {6: "unit start", 0: "first tile requested", 1: "queries polled (last wave)", 3: "queries staged",
+ATT = {8: "unit entered", 6: "unit start", 2: "first tile issue starts", 0: "first tile requested", 1: "queries polled (last wave)", 3: "queries staged",
        10: "first scores", 4: "keys done", 9: "waves' states in LDS", 5: "partial stored",
        11: "merge start", 12: "folded", 13: "merged"}
 
