@@ -580,6 +580,28 @@ def test_dec8b_gqa_full_shape(lf, orc, dec8b):
         assert got[i] == ref[i], i
 
 
+@pytest.mark.timeout(600)
+def test_dec8b_nucleus_full_vocab(lf, orc, dec8b):
+    """Temperature 0.8 / top-p 0.9 on the 8B model: the nucleus draw over the grid
+    at a 128,256-row vocabulary (about 500 lm_head rows per workgroup, listed as
+    16-bit offsets).  For the kernel's own logits and counter, the oracle sampler
+    picks the same token at every step."""
+    import torch
+    cfg, w = dec8b
+    cfg = dict(cfg, temperature=0.8, top_p=0.9, seed=4321)
+    dw = lf.upload_weights(w)
+    eng = lf.Engine(cfg, dw)
+    del dw
+    torch.cuda.empty_cache()
+    tok = int(synth.prompt(cfg, 1)[0])
+    for pos in range(6):
+        nxt = eng.decode_step(tok, pos)
+        logits = eng.logits().cpu().numpy()
+        assert nxt == orc.sample(logits, 0.8, 0.9, 4321, pos), pos
+        tok = nxt
+    eng.close()
+
+
 def test_dec2b_long_context_sampling(lf, orc, dec2b):
     """16K prefilled cache, temperature 0.8 / top-p 0.9 Philox sampling at pos 16384..:
     GPU logits within tolerance of the oracle's, and the token the kernel samples
