@@ -83,8 +83,9 @@ enum Phase { PH_QKV = 1, PH_ATTN = 2, PH_O = 3, PH_GU = 4, PH_D = 5, PH_PER_LAYE
 // starts at wbase + l * layer_stride.
 enum LayerPart { LW_QKV = 0, LW_O, LW_GU, LW_D, LW_COUNT };
 
-// Next-token choice: argmax, nucleus draw by workgroup 0, or Gumbel-max (every
-// lm_head workgroup publishes its best noised score, workgroup 0 reduces them).
+// Next-token choice: argmax, the nucleus draw (over the lm_head workgroups, or
+// by workgroup 0 alone), or Gumbel-max (every lm_head workgroup publishes its
+// best noised score, workgroup 0 reduces them).
 enum SampleMode { SAMPLE_GREEDY = 0, SAMPLE_NUCLEUS = 1, SAMPLE_GUMBEL = 2 };
 // Dependency levels the nucleus draw over the grid adds between the lm_head's
 // level and the token's.

@@ -5,13 +5,15 @@
 // LaneFormer-2B & the monokernel", sections "Pillar 3 - the monokernel runtime"
 // and "Compile-time work partition").  Work is partitioned statically: every
 // matrix is cut into contiguous row blocks, one per workgroup, fixed for the
-// life of the state; attention is cut into (KV head, key chunk) units.
+// life of the state; attention is cut into (KV head, key chunk) units, and a
+// short GQA head into one unit per query head.
 //
 // Roles inside a workgroup.  Wave 0 is the SYNC wave: after each phase it adds
 // the stream waves' partial row sums and runs the phase's epilogue (rotary
 // embedding and the KV-cache append, the residual add, SiLU(gate) * up, the
 // lm_head's local argmax), stores the outputs as tagged exchange words and
-// stores its progress word.  Waves 1..7 are STREAM waves: each walks its own
+// stores its progress word; with temperature and top-p, every workgroup's sync
+// wave takes part in the nucleus draw over its own lm_head rows.  Waves 1..7 are STREAM waves: each walks its own
 // contiguous slice of the workgroup's weight rows, phase after phase, layer
 // after layer, token after token, through a ring of eight 1-KB pieces held in
 // registers the compiler never allocates (v224..v255), loaded with
@@ -32,7 +34,8 @@
 // attention partials are merged by a fixed unit per KV head that waits on the
 // partials' tags.  Untagged data (logits, the per-workgroup argmax partials,
 // the chosen token) use the per-workgroup progress words, stored after the
-// producer's stores complete.  Every wait is bounded: on expiry the workgroup
+// producer's stores complete; the nucleus draw instead polls each workgroup's
+// largest logit as a tagged word stored after that progress word.  Every wait is bounded: on expiry the workgroup
 // writes the error word and returns, every other wait sees it and returns too,
 // so the grid always drains.
 //
