@@ -23,6 +23,8 @@ def lf():
 
 CASES = {
     "tiny_mha": synth.CONFIGS["tiny_2l_d256"],
+    # temperature / top-p: the nucleus draw's exchange buffers live in the array too
+    "tiny_topp": dict(synth.CONFIGS["tiny_2l_d256"], temperature=0.8, top_p=0.9, seed=99),
     # GQA 4/2 heads of dim 96 with a sliding window on two of three layers: other
     # exchange-buffer sizes and several attention chunks per KV head
     "gqa_window": synth.scaled_config("tiny_2l_d256", n_layers=3, d_model=384, n_heads=4, n_kv_heads=2,
