@@ -1242,23 +1242,6 @@ struct AttnSplit {
   }
 };
 
-// Wait for one tagged word; on expiry returns it anyway and sets *bad.  Each
-// retry reads the word and the error word together: one round trip.
-__device__ __forceinline__ u64 ld_tag_wait(KP &P, const u64 *p, unsigned tag, unsigned long long t0,
-                                           bool &bad) {
-  u64 w = ld_dev(p);
-  while (tag_of(w) != tag) {
-    const unsigned e = ld_dev(&P.err[0]);
-    w = ld_dev(p);
-    if (tag_of(w) == tag) break;
-    if (expired(P, t0, tag, e)) {
-      bad = true;
-      break;
-    }
-  }
-  return w;
-}
-
 // A buffer resource over `bytes` bytes from p: loads past the end return zero.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 __device__ __forceinline__ Rsrc make_rsrc(const void *p, unsigned bytes) {
