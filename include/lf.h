@@ -103,9 +103,11 @@ int lf_model_create(const lf_config *config, const lf_weights *weights, void *st
 /* Free everything the state owns.  NULL is ignored. */
 void lf_model_destroy(lf_state *st);
 
-/* One decode step in one launch: consume `token` at position `pos`, write K/V at
- * pos, compute logits, choose the next token (RNG counter = pos) and store it as
- * the pending (next, pos + 1) for lf_generate.  next_token (host, nullable)
+/* One decode step in one launch ("KOG LaneFormer-2B & the monokernel", "Pillar 3
+ * - the monokernel runtime": the whole pass, the token choice included, in one
+ * resident kernel): consume `token` at position `pos`, write K/V at pos, compute
+ * logits, choose the next token (RNG counter = pos) and store it as the pending
+ * (next, pos + 1) for lf_generate.  next_token (host, nullable)
  * receives it.  With LF_HIDDEN_IO: token is ignored, the layers run on the hidden
  * vector and *next_token = -1.
  * Errors: LF_ERANGE (pos outside [0, max_seq), token outside [0, vocab)),
@@ -113,7 +115,9 @@ void lf_model_destroy(lf_state *st);
 int lf_decode_step(lf_state *st, int32_t token, int32_t pos, int32_t *next_token);
 
 /* n decode steps from the pending (token, pos) in ONE launch; each sampled token
- * is fed back on the device.  out_tokens (host, n entries) receives the sampled
+ * is fed back on the device, so no kernel boundary or host round trip separates
+ * tokens (same page, "Pillar 3 - the monokernel runtime" and "The arithmetic that
+ * forces this").  out_tokens (host, n entries) receives the sampled
  * tokens.  Errors: LF_ERANGE (no pending token, n < 1, pos + n > max_seq),
  * LF_ETIMEOUT, LF_EHIP. */
 int lf_generate(lf_state *st, int32_t n, int32_t *out_tokens);
