@@ -323,7 +323,7 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no sharding, no collectives); "
+        print("bench.py: the library runs on one GPU only (no sharding, no collectives); "
               "--gpus N with N > 1 is not supported", file=sys.stderr)
         return 2
 
