@@ -612,17 +612,18 @@ __device__ __forceinline__ StageSpec stage_spec(const KP &P, const Ctl *ctl, int
 
 // The same for a layer-0 input: an fp16 embedding row or the host's fp32
 // vector.  Returns 1 / rms.
-__device__ __forceinline__ float stage_rmsnorm_plain(const float *x_host, const _Float16 *x16, int d, float eps,
-                                                     _Float16 *h) {
+// One source type per instance, and every load unconditional (indices clamped
+// into the row), so that all of a round's loads are in flight at once: a
+// guarded load, or a choice of source inside the loop, made the compiler wait
+// for each load in turn (40 round trips for a 2560-element row).
+template <class T>
+__device__ __forceinline__ float stage_rmsnorm_plain(const T *x, int d, float eps, _Float16 *h) {
   const int lane = lane_id();
   float ss = 0.0f;
   for (int base = 0; base < d; base += 64 * kStageBatch) {
     float v[kStageBatch];
 #pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int i = base + 64 * j + lane;
-      v[j] = i < d ? (x_host ? x_host[i] : (float)x16[i]) : 0.0f;
-    }
+    for (int j = 0; j < kStageBatch; ++j) v[j] = (float)x[min(base + 64 * j + lane, d - 1)];
 #pragma unroll
     for (int j = 0; j < kStageBatch; ++j) {
       const int i = base + 64 * j + lane;
@@ -2827,8 +2828,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           if (l > 0) {
             coop_stage(Pl, ctl, sp, 0, hl, sy.trace_k);
           } else {
-            inv = stage_rmsnorm_plain(Pl.hidden_io ? Pl.x_hidden : nullptr,
-                                      Pl.hidden_io ? nullptr : emb + (size_t)token * d, d, Pl.eps, hl);
+            inv = Pl.hidden_io ? stage_rmsnorm_plain(Pl.x_hidden, d, Pl.eps, hl)
+                               : stage_rmsnorm_plain(emb + (size_t)token * d, d, Pl.eps, hl);
             lds_drain();
           }
           trace(Pl, t, 5 * l + 0, 7);
