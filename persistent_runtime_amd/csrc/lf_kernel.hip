@@ -390,7 +390,15 @@ __device__ __forceinline__ bool poll_level(Sync &s, int first, int count, unsign
   for (;;) {
     bool behind = false;
     const unsigned e = ld_dev(&P.err[0]);
-    for (int i = lane_id(); i < count; i += 64) behind |= ld_dev(&P.progress[first + i]) < level;
+    // up to 256 words a pass with every load in flight (clamped indices; the
+    // copies past count are ignored), not one round trip per 64 words
+    for (int i0 = 0; i0 < count; i0 += 4 * 64) {
+      unsigned v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = ld_dev(&P.progress[first + min(i0 + 64 * k + lane_id(), count - 1)]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) behind |= i0 + 64 * k + lane_id() < count && v[k] < level;
+    }
     if (wave_none(behind)) {
       retire(e);
       ok = true;
@@ -3093,12 +3101,25 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           fail();
           return;
         }
+        // every workgroup's (max, index): all loads in flight at once (clamped
+        // indices; entries past G are ignored), then the comparisons
         float best = -INFINITY;
         int bi = 0x7fffffff;
-        for (int i = lane; i < G; i += 64) {
-          const float v = ld_dev(&P.lm_val[i]);
-          const int ix = ld_dev(&P.lm_idx[i]);
-          if (v > best || (v == best && ix < bi)) { best = v; bi = ix; }
+        for (int i0 = 0; i0 < G; i0 += 4 * 64) {
+          float v[4];
+          int ix[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int i = min(i0 + 64 * k + lane, G - 1);
+            v[k] = ld_dev(&P.lm_val[i]);
+            ix[k] = ld_dev(&P.lm_idx[i]);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (i0 + 64 * k + lane < G && (v[k] > best || (v[k] == best && ix[k] < bi))) {
+              best = v[k];
+              bi = ix[k];
+            }
         }
         wave_argmax(best, bi);
         tok = bi;
