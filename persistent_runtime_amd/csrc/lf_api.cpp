@@ -271,6 +271,28 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.attn_unit_tiles = lf::kWaves - 1;   // one tile per stream wave
   P.attn_split_tiles = 3;
   P.attn_qsplit = 1;
+  // Stream waves 1-3 share their SIMDs with waves 5-7 and are served first
+  // (measured: they finish a phase first, waves 5-7 last, wave 4, beside the
+  // mostly idle sync wave, in between), so they take ~7% more pieces and
+  // waves 5-7 ~7% fewer, within the round caps of wave_counts.
+  {
+    static const int kWaveW[lf::kNcwHost] = {274, 274, 274, 256, 238, 238, 238};
+    for (int k = 0; k < lf::kNcwHost; ++k) P.wave_w[k] = kWaveW[k];
+  }
+  P.wave_w_kinds = 31;
+  if (const char *s = std::getenv("LF_WAVE_W_KINDS")) P.wave_w_kinds = std::atoi(s) & 31;
+  if (const char *s = std::getenv("LF_WAVE_W")) {   // seven ':'-separated weights, 64 .. 1024
+    int v[lf::kNcwHost], n = 0;
+    for (const char *p = s; *p && n < lf::kNcwHost;) {
+      v[n++] = std::atoi(p);
+      while (*p && *p != ':') ++p;
+      if (*p == ':') ++p;
+    }
+    bool ok = n == lf::kNcwHost;
+    for (int k = 0; k < n; ++k) ok = ok && v[k] >= 64 && v[k] <= 1024;
+    if (ok)
+      for (int k = 0; k < lf::kNcwHost; ++k) P.wave_w[k] = v[k];
+  }
   if (const char *s = std::getenv("LF_ATTN_QSPLIT")) P.attn_qsplit = std::atoi(s) != 0 ? 1 : 0;
   // Workgroups without attention units hold back the output projection's first
   // ring round ~3.5 us (350 ticks of the 100 MHz clock), about one attention

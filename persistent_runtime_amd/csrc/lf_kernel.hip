@@ -683,9 +683,34 @@ __device__ __forceinline__ Slice uniform_slice(const Ctl *ctl, int kind, int cw)
 }
 
 // Stream wave cw's share [lo, hi) of the np pieces of a row block (contiguous).
-__device__ __forceinline__ void wave_slice(int np, int cw, int &lo, int &hi) {
-  lo = (cw * np) / kNcw;
-  hi = ((cw + 1) * np) / kNcw;
+// The stream waves' shares of a workgroup's np pieces (counts n[0 .. kNcw)).
+// Waves sharing a SIMD do not stream equally fast (the lower-numbered wave of
+// each pair finishes first), so the shares follow the weights ww; but each
+// wave's pieces are padded to whole rounds of kRing, and a round that holds one
+// real piece costs nearly a full round, so no wave gets more rounds than its
+// equal share needs (one more once that share is eight rounds or more).  The
+// pieces the caps leave over go back to the waves below their caps, lowest
+// weight last.
+__device__ __forceinline__ void wave_counts(int np, const int *ww, int *n) {
+  int wt = 0;
+  for (int k = 0; k < kNcw; ++k) wt += ww[k];
+  int w0 = 0, sum = 0, cap[kNcw];
+  for (int k = 0; k < kNcw; ++k) {
+    const int eq = ((k + 1) * np) / kNcw - (k * np) / kNcw;
+    const int r = (eq + kRing - 1) / kRing;
+    cap[k] = kRing * (r + (r >= 8 ? 1 : 0));
+    const int lo = (int)((long long)np * w0 / wt);
+    w0 += ww[k];
+    const int hi = (int)((long long)np * w0 / wt);
+    n[k] = min(hi - lo, cap[k]);
+    sum += n[k];
+  }
+  for (int pass = 0; pass < 2 && sum < np; ++pass)   // (one pass suffices: the caps hold np)
+    for (int k = 0; k < kNcw && sum < np; ++k) {
+      const int add = min(cap[k] - n[k], np - sum);
+      n[k] += add;
+      sum += add;
+    }
 }
 
 static_assert((kRing & (kRing - 1)) == 0 && kRing <= 32, "ring depth must be a power of two <= 32");
@@ -2665,6 +2690,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       if (4 * na > G) na = 0;
     }
     ctl->na = na;
+    int ww[kNcw], weq[kNcw];
+    for (int k = 0; k < kNcw; ++k) {
+      ww[k] = P.wave_w[k];
+      weq[k] = 1;
+    }
     for (int k = 0; k < K_COUNT; ++k) {
       int p0 = 0, p1 = 0;
       if (k == K_QKV) {
@@ -2676,9 +2706,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
       }
       const Geo ge = Geo{upr[k] * p0, upr[k] * (p1 - p0), kvs[k], (kvs[k] + 63) / 64};
       ctl->geo[k] = ge;
+      int wn[kNcw];
+      wave_counts(ge.nrows * ge.ppr, ((P.wave_w_kinds >> k) & 1) ? ww : weq, wn);
       for (int cw = 0; cw < kNcw; ++cw) {
         int lo, hi;
-        wave_slice(ge.nrows * ge.ppr, cw, lo, hi);
+        lo = hi = 0;
+        for (int c = 0; c <= cw; ++c) {
+          lo = hi;
+          hi += wn[c];
+        }
         if (k == K_GU) {
           const int npf = min(hi - lo, P.gu_pf);
           ctl->gu_pf[cw] = Slice{npf, npf > 0 ? lo / ge.ppr : 0, npf > 0 ? lo % ge.ppr : 0, 0};
