@@ -754,7 +754,10 @@ int lf_query(const lf_state *st, int32_t what) {
     case LF_Q_SCRATCH_MAX: return (int)lf::kNoallocScratchBytes;
     case LF_Q_KV_PF: return st->P.kv_pf;
     case LF_Q_GU_PF: return st->P.gu_pf;
-    default: return LF_EINVAL;
+    case LF_Q_WAVE_W_KINDS: return st->P.wave_w_kinds;
+    default:
+      if (what >= LF_Q_WAVE_W && what < LF_Q_WAVE_W + lf::kNcwHost) return st->P.wave_w[what - LF_Q_WAVE_W];
+      return LF_EINVAL;
   }
 }
 

@@ -210,9 +210,15 @@ def test_gate_up_lds_prefetch(lf, orc, tiny, monkeypatch, pieces):
     eng = lf.Engine(cfg, lf.upload_weights(w))
     assert eng.query(lf.LF_Q_GU_PF) == pieces
     teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 6), engine=eng)
+    layer_d2560_at(lf, orc, 200)
+
+
+def layer_d2560_at(lf, orc, P):
+    """One 2.2B-shaped layer (hidden vector in and out) at position P over a
+    synthetic cache, against the oracle's layer."""
+    import torch
     cfg = synth.CONFIGS["layer_d2560_kv1024"]
     w = synth.model_weights(cfg)
-    P = 200
     k, v = synth.kv_prefill(cfg, P)
     x = synth.hidden(cfg)
     eng = lf.Engine(cfg, lf.upload_weights(w))
@@ -224,6 +230,29 @@ def test_gate_up_lds_prefetch(lf, orc, tiny, monkeypatch, pieces):
     m.kv_fill(k, v, 0)
     ok, err = close(got, m.layer_forward(0, x, P))
     assert ok, err
+    return eng
+
+
+@pytest.mark.parametrize("ww,grid", [("1024:64:64:64:64:64:1024", None), ("64:1024:64:1024:64:1024:64", None),
+                                     ("1024:64:64:64:64:64:1024", "64"), ("256:256:256:256:256:256:256", None)])
+def test_wave_shares_uneven_weights(lf, orc, tiny, monkeypatch, ww, grid):
+    """A workgroup's rows split over its stream waves by extreme weights: the
+    heavy waves hit the cap of whole rounds and the light waves take what is
+    left, so every row is still summed exactly once.  Tiny model teacher-forced
+    and the 2.2B layer shape at position 700 (1-5 rounds of 8 pieces per wave;
+    on a 64-workgroup grid gate/up has 19, where the cap allows one round more
+    than an equal share), and equal weights."""
+    monkeypatch.setenv("LF_WAVE_W", ww)
+    if grid:
+        monkeypatch.setenv("LF_GRID", grid)
+    cfg, w = tiny
+    eng = lf.Engine(cfg, lf.upload_weights(w))
+    want = [int(s) for s in ww.split(":")]
+    assert [eng.query(lf.LF_Q_WAVE_W + k) for k in range(7)] == want
+    assert eng.query(lf.LF_Q_WAVE_W_KINDS) == 31
+    teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 6), engine=eng)
+    eng = layer_d2560_at(lf, orc, 700)
+    assert [eng.query(lf.LF_Q_WAVE_W + k) for k in range(7)] == want
 
 
 @pytest.mark.parametrize("waves", [7, 2])
