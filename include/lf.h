@@ -182,13 +182,14 @@ int lf_query(const lf_state *st, int32_t what);
 #define LF_Q_SCRATCH_BYTES 3   /* scratch lf_generate_noalloc uses for this state */
 #define LF_Q_SCRATCH_MAX 4     /* bytes of the static scratch array */
 #define LF_Q_KV_PF 5           /* stream waves per attention unit whose first K/V tile is prefetched into LDS */
-#define LF_Q_GU_PF 6           /* gate/up pieces per stream wave prefetched into LDS */
+#define LF_Q_GU_PF 6           /* pieces per stream wave of projection LF_Q_PF_KIND prefetched into LDS */
 #define LF_Q_WAVE_W 7          /* + k, k = 0..6: share weight of stream wave k + 1 (a workgroup's rows of a
                                   projection go to its seven stream waves in proportion to these weights, no
                                   wave taking more whole rounds of 8 pieces than an equal share would, plus
                                   one where that is 8 or more) */
 #define LF_Q_WAVE_W_KINDS 14   /* bit mask of the projections split by those weights (QKV 1, O 2, gate/up 4,
                                   down 8, lm_head 16); the others are split equally */
+#define LF_Q_PF_KIND 15        /* the projection LF_Q_GU_PF prefetches: 1 output projection, 2 gate/up */
 
 /* Test hooks, device pointers, on `stream`:
  * lf_test_expdef: y[i] = E(x[i]) with the library's defined exponential.

@@ -532,20 +532,48 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
     P.lds_kvpf = (int)lds_end;
     lds_end += (size_t)P.kv_pf * P.kv_pf_tile;
   }
-  // The LDS left over can hold each stream wave's gate/up prefetch: LF_GU_PF
-  // 1-KB pieces per wave, as many as fit.  Off by default: measured end to end
-  // it costs more (the burst delays the output projection's input) than the
-  // shorter gate/up phase saves.
+  // The LDS left over can hold the first pieces of each stream wave's share of
+  // one projection, loaded while attention runs.  By default that is the output
+  // projection, where a wave's share (at the largest weight) is more than one
+  // ring round and fits whole: the phase then needs no round after its input
+  // arrives, and the ring's refill after attention starts on gate/up.  Where
+  // the share fits the ring (one round) or not the LDS, it is off: measured,
+  // 4 pieces on the 2.2B decode cost 2.8%, 2 (all that fit) on the 8B model
+  // gained nothing.  LF_GU_PF (pieces per wave) with LF_PF_KIND (2 gate/up, the
+  // default then; 1 output projection) overrides the rule.  A gate/up
+  // prefetch costs more than it saves (its burst delays the output
+  // projection's input).
   {
     const long long per_piece = (long long)lf::kNcwHost * 1024;
     long long fit = ((long long)lds_limit - (long long)lds_end) / per_piece;
     long long want = 0;
-    if (const char *s = std::getenv("LF_GU_PF")) want = std::atoll(s);
+    if (const char *s = std::getenv("LF_GU_PF")) {
+      want = std::atoll(s);
+      P.pf_kind = 2;
+      if (const char *k = std::getenv("LF_PF_KIND")) P.pf_kind = std::atoi(k) == 1 ? 1 : 2;
+    } else {
+      const int og = G - lf::o_rows_skip_max(G, Hkv, P.qpg, P.attn_qsplit);
+      const long long o_pieces = (long long)((d + og - 1) / og) * ((Hq * dh + 511) / 512);
+      int wmax = 0, wsum = 0;
+      for (int k = 0; k < lf::kNcwHost; ++k) {
+        wmax = P.wave_w[k] > wmax ? P.wave_w[k] : wmax;
+        wsum += P.wave_w[k];
+      }
+      // a wave's pieces: its weighted share, capped (as the kernel splits them)
+      // at the whole rounds of an equal share, plus one round from 8 rounds on
+      const long long eq = (o_pieces + lf::kNcwHost - 1) / lf::kNcwHost;
+      const long long r = (eq + lf::kRingSlots - 1) / lf::kRingSlots;
+      const long long cap = lf::kRingSlots * (r + (r >= 8 ? 1 : 0));
+      long long share = (o_pieces * wmax + wsum - 1) / wsum;
+      if (share > cap) share = cap;
+      P.pf_kind = 1;
+      if (eq > lf::kRingSlots && share <= fit) want = fit;
+    }
     if (want < 0) want = 0;
-    P.gu_pf = (int)(want < fit ? want : fit);
+    P.pf_n = (int)(want < fit ? want : fit);
     P.lds_pf = (int)lds_end;
   }
-  P.lds_bytes = (int)(lds_end + (size_t)P.gu_pf * lf::kNcwHost * 1024);
+  P.lds_bytes = (int)(lds_end + (size_t)P.pf_n * lf::kNcwHost * 1024);
   P.plain_launch = (std::getenv("LF_PLAIN_LAUNCH") && std::atoi(std::getenv("LF_PLAIN_LAUNCH")) != 0) ? 1 : 0;
   for (int pf = 0; pf < 2; ++pf) {
     if ((e = hipFuncSetAttribute(lf::monokernel_symbol(pf != 0, P.qpg), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -753,8 +781,9 @@ int lf_query(const lf_state *st, int32_t what) {
     case LF_Q_SCRATCH_BYTES: return (int)noalloc_layout(st, nullptr, nullptr);
     case LF_Q_SCRATCH_MAX: return (int)lf::kNoallocScratchBytes;
     case LF_Q_KV_PF: return st->P.kv_pf;
-    case LF_Q_GU_PF: return st->P.gu_pf;
+    case LF_Q_GU_PF: return st->P.pf_n;
     case LF_Q_WAVE_W_KINDS: return st->P.wave_w_kinds;
+    case LF_Q_PF_KIND: return st->P.pf_kind;
     default:
       if (what >= LF_Q_WAVE_W && what < LF_Q_WAVE_W + lf::kNcwHost) return st->P.wave_w[what - LF_Q_WAVE_W];
       return LF_EINVAL;

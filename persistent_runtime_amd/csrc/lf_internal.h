@@ -102,9 +102,10 @@ struct Params {
   int attn_unit_tiles;                 // most KV tiles a KV head keeps in one unit (1 .. 7)
   int attn_split_tiles;                // tiles per unit once a head is split (1 .. 7)
   int attn_qsplit;                     // 1: a KV head in one unit is split by query heads (GQA)
+  int pf_kind;                         // the projection whose first pieces the LDS prefetch takes (2 gate/up, 1 O)
   int wave_w[kNcwHost];                // relative shares of a workgroup's pieces per stream wave (1 .. 7)
   int wave_w_kinds;                    // bit k: phase kind k uses wave_w (else equal shares)
-  int gu_pf;                           // gate/up pieces per stream wave prefetched into LDS during attention
+  int pf_n;                            // pieces per stream wave of projection pf_kind prefetched into LDS during attention
   int kv_pf;                           // stream waves whose first K/V tile is prefetched into LDS (0: off)
   int kv_pf_tile;                      // LDS bytes of one prefetched tile
   unsigned o_refill_delay;             // ticks (100 MHz) a workgroup without attention units waits

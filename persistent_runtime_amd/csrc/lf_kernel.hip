@@ -305,9 +305,9 @@ struct Ctl {
   // The partition of every phase kind among the stream waves, fixed for the
   // launch: computed once so that no phase divides by the pieces per row.
   Slice slice[K_COUNT][kNcw];
-  // The first pieces of each stream wave's gate/up share, prefetched into its
-  // own LDS area before the phase (slice[K_GU] then holds the rest).
-  Slice gu_pf[kNcw];
+  // The first pieces of each stream wave's share of projection P.pf_kind,
+  // prefetched into its own LDS area before the phase (slice[] then holds the rest).
+  Slice pf[kNcw];
 };
 static_assert(sizeof(Ctl) <= kCtlBytes, "workgroup control block exceeds its LDS space");
 
@@ -1030,30 +1030,32 @@ __device__ __forceinline__ bool st_has_rounds(const Streamer &st, int kind, cons
   return uniform_slice(ctl, kind, st.cw).n > 0;
 }
 
-// Gate/up prefetch.  During attention most workgroups have nothing to stream
-// but the output projection's first round, so each stream wave copies the first
-// pieces of its gate/up share for layer l into an LDS area of its own with
+// LDS prefetch of one projection (P.pf_kind: the output projection or gate/up).
+// During attention most workgroups have nothing to stream but the output
+// projection's first round, so each stream wave copies the first pieces of its
+// share of that projection for layer l into an LDS area of its own with
 // direct-to-LDS loads (lane i's 16 bytes to byte 16 i of the piece's KB).  They
-// complete in order with the wave's other loads; the gate/up phase waits for
-// them before it reads the area.
-__device__ __forceinline__ unsigned char *gu_pf_area(const KP &P, int cw) {
+// complete in order with the wave's other loads; the phase waits for them
+// before it reads the area.
+__device__ __forceinline__ unsigned char *pf_area(const KP &P, int cw) {
   extern __shared__ __align__(16) unsigned char lf_dyn_lds[];
-  return lf_dyn_lds + P.lds_pf + (size_t)cw * P.gu_pf * 1024;
+  return lf_dyn_lds + P.lds_pf + (size_t)cw * P.pf_n * 1024;
 }
-__device__ __forceinline__ Slice uniform_gu_pf(const Ctl *ctl, int cw) {
-  const Slice sl = ctl->gu_pf[cw];
+__device__ __forceinline__ Slice uniform_pf(const Ctl *ctl, int cw) {
+  const Slice sl = ctl->pf[cw];
   return Slice{__builtin_amdgcn_readfirstlane(sl.n), __builtin_amdgcn_readfirstlane(sl.row),
                __builtin_amdgcn_readfirstlane(sl.kp), 0};
 }
-__device__ __forceinline__ void gu_prefetch(KP &P, const Ctl *ctl, int cw, int l) {
-  const Slice ps = uniform_gu_pf(ctl, cw);
+__device__ __forceinline__ void lds_prefetch(KP &P, const Ctl *ctl, int cw, int l) {
+  const Slice ps = uniform_pf(ctl, cw);
   if (ps.n <= 0) return;
-  const Geo ge = uniform_geo(ctl, K_GU);
+  const int kind = P.pf_kind;
+  const Geo ge = uniform_geo(ctl, kind);
   const int lane = lane_id();
   const int tailv = ge.kv - (ge.ppr - 1) * 64;
   const long long adv_last = (long long)ge.kv * 16 - (long long)(ge.ppr - 1) * 1024;
-  const unsigned char *p = phase_base(P, ge, K_GU, l) + ((size_t)ps.row * ge.kv * 16 + (size_t)ps.kp * 1024);
-  unsigned char *dst = gu_pf_area(P, cw);
+  const unsigned char *p = phase_base(P, ge, kind, l) + ((size_t)ps.row * ge.kv * 16 + (size_t)ps.kp * 1024);
+  unsigned char *dst = pf_area(P, cw);
   int kp = ps.kp;
   for (int j = 0; j < ps.n; ++j) {
     const bool last = kp == ge.ppr - 1;
@@ -1073,15 +1075,15 @@ __device__ __forceinline__ void gu_prefetch(KP &P, const Ctl *ctl, int cw, int l
 // into part[row][cw] at every row end and at the wave's last piece (when no
 // ring pieces follow).  Returns the running sum of a row the ring part goes on
 // with.
-__device__ __forceinline__ float gu_pf_consume(const KP &P, const Ctl *ctl, int cw, const _Float16 *h, float *pk,
+__device__ __forceinline__ float pf_consume(const KP &P, const Ctl *ctl, int cw, const _Float16 *h, float *pk,
                                                const Geo &ge, bool ring_follows) {
-  const Slice ps = uniform_gu_pf(ctl, cw);
+  const Slice ps = uniform_pf(ctl, cw);
   float acc = 0.0f;
   if (ps.n <= 0) return acc;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const int lane = lane_id();
   const int tailv = ge.kv - (ge.ppr - 1) * 64;
-  const unsigned char *src = gu_pf_area(P, cw) + lane * 16;
+  const unsigned char *src = pf_area(P, cw) + lane * 16;
   const unsigned char *hb = reinterpret_cast<const unsigned char *>(h);
   int kp = ps.kp, row = ps.row;
   for (int j = 0; j < ps.n; ++j) {
@@ -1134,8 +1136,8 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
   const int n = sl.n;
   const int nr = (n + kRing - 1) / kRing;
   float acc = 0.0f;
-  if (kind == K_GU && st.P->gu_pf > 0)
-    acc = gu_pf_consume(*st.P, ctl, st.cw, h, kind_part(part, K_GU, fresh(*st.P).part_rows), ge, nr > 0);
+  if (kind == st.P->pf_kind && st.P->pf_n > 0)
+    acc = pf_consume(*st.P, ctl, st.cw, h, kind_part(part, kind, fresh(*st.P).part_rows), ge, nr > 0);
   if (nr > 0) {
     // The ring holds this phase's first round.  If the phase has more pieces
     // than one round, the streamer still points into this phase: its cursor
@@ -2715,9 +2717,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
           lo = hi;
           hi += wn[c];
         }
-        if (k == K_GU) {
-          const int npf = min(hi - lo, P.gu_pf);
-          ctl->gu_pf[cw] = Slice{npf, npf > 0 ? lo / ge.ppr : 0, npf > 0 ? lo % ge.ppr : 0, 0};
+        if (k == P.pf_kind) {
+          const int npf = min(hi - lo, P.pf_n);
+          ctl->pf[cw] = Slice{npf, npf > 0 ? lo / ge.ppr : 0, npf > 0 ? lo % ge.ppr : 0, 0};
           lo += npf;
         }
         const int row = lo < hi ? lo / ge.ppr : 0;
@@ -2805,7 +2807,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
             while ((unsigned)now_ticks() - t_qkv < P.o_refill_delay) __builtin_amdgcn_s_sleep(2);
           }
           if (qkv_rounds) st.refill();
-          if (P.gu_pf > 0) gu_prefetch(P, ctl, st.cw, l);
+          if (P.pf_n > 0) lds_prefetch(P, ctl, st.cw, l);
         }
       }
       if (has_lm && b == 0 && P.sampling == SAMPLE_NUCLEUS && !P.nuc_grid) {

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("LF_LIB") or os.path.join(HERE, "liblf.so")
 LF_OK, LF_EINVAL, LF_ENOMEM, LF_EHIP, LF_ERANGE, LF_ETIMEOUT, LF_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 LF_HIDDEN_IO, LF_STATS, LF_GUMBEL = 1, 4, 8
 LF_Q_GRID, LF_Q_THREADS, LF_Q_LDS_BYTES, LF_Q_SCRATCH_BYTES, LF_Q_SCRATCH_MAX = 0, 1, 2, 3, 4
-LF_Q_KV_PF, LF_Q_GU_PF, LF_Q_WAVE_W, LF_Q_WAVE_W_KINDS = 5, 6, 7, 14
+LF_Q_KV_PF, LF_Q_GU_PF, LF_Q_WAVE_W, LF_Q_WAVE_W_KINDS, LF_Q_PF_KIND = 5, 6, 7, 14, 15
 LAYER_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 
 # every symbol include/lf.h declares

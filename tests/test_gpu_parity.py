@@ -198,17 +198,19 @@ def test_tiny_smaller_grid_same_results(lf, orc, tiny, monkeypatch):
     teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 6), engine=eng)
 
 
-@pytest.mark.parametrize("pieces", [16, 3])
-def test_gate_up_lds_prefetch(lf, orc, tiny, monkeypatch, pieces):
-    """The gate/up prefetch into LDS (off by default): the tiny model's rows of
-    32 vectors (one masked piece per row, whole wave shares in LDS) and the
-    2.2B layer shape, whose 16- or 3-piece prefetch ends inside a row of five
-    pieces, so the ring part goes on with the running row sum."""
-    import torch
+@pytest.mark.parametrize("pieces,kind", [(16, 2), (3, 2), (16, 1), (3, 1)])
+def test_lds_prefetch(lf, orc, tiny, monkeypatch, pieces, kind):
+    """The LDS prefetch of a projection's first pieces, forced on gate/up (kind
+    2) or the output projection (kind 1): the tiny model's rows of 32 vectors
+    (one masked piece per row, whole wave shares in LDS) and the 2.2B layer
+    shape, whose 16- or 3-piece prefetch ends inside a row of five pieces, so
+    the ring part goes on with the running row sum."""
     monkeypatch.setenv("LF_GU_PF", str(pieces))
+    monkeypatch.setenv("LF_PF_KIND", str(kind))
     cfg, w = tiny
     eng = lf.Engine(cfg, lf.upload_weights(w))
     assert eng.query(lf.LF_Q_GU_PF) == pieces
+    assert eng.query(lf.LF_Q_PF_KIND) == kind
     teacher_forced(lf, orc, cfg, w, synth.prompt(cfg, 6), engine=eng)
     layer_d2560_at(lf, orc, 200)
 
@@ -231,6 +233,16 @@ def layer_d2560_at(lf, orc, P):
     ok, err = close(got, m.layer_forward(0, x, P))
     assert ok, err
     return eng
+
+
+def test_output_projection_prefetch_rule(lf, orc, monkeypatch):
+    """By default the output projection is prefetched into LDS only where a
+    stream wave's share is more than one ring round and fits LDS whole: not at
+    the 2.2B layer shape (about 8 pieces a wave, one round)."""
+    monkeypatch.delenv("LF_GU_PF", raising=False)
+    eng = layer_d2560_at(lf, orc, 300)
+    assert eng.query(lf.LF_Q_PF_KIND) == 1
+    assert eng.query(lf.LF_Q_GU_PF) == 0
 
 
 @pytest.mark.parametrize("ww,grid", [("1024:64:64:64:64:64:1024", None), ("64:1024:64:1024:64:1024:64", None),
@@ -713,7 +725,8 @@ def test_sliding_window_gqa_head96_teacher_forced(lf, orc, monkeypatch, qsplit):
 def test_laneformer_shape_sliding_window_long_context(lf, orc):
     """The LaneFormer-2B-shaped decoder (15 layers, 32/16 heads of dim 96, window
     1024 in 10 layers) with its cache prefilled to 2048: GPU logits within
-    tolerance of the oracle's and the greedy token equal where the margin allows."""
+    tolerance of the oracle's and the greedy token equal where the margin allows
+    (with the output projection prefetched into LDS, as by default at this shape)."""
     import torch
     cfg = synth.CONFIGS["laneformer_15l_swa"]
     w = synth.model_weights(cfg)
@@ -721,6 +734,10 @@ def test_laneformer_shape_sliding_window_long_context(lf, orc):
     P = cfg["kv_prefill"]
     k, v = synth.kv_prefill(cfg, P)
     eng = lf.Engine(cfg, lf.upload_weights(w))
+    # a stream wave's share of the output projection (13 rows of 6 pieces per
+    # workgroup) is more than one ring round: prefetched into LDS whole
+    assert eng.query(lf.LF_Q_PF_KIND) == 1
+    assert eng.query(lf.LF_Q_GU_PF) >= 12
     for l in range(cfg["n_layers"]):
         eng.kv_fill(l, 0, torch.from_numpy(k[l]).cuda(), torch.from_numpy(v[l]).cuda())
     m = orc.Model(cfg, w)
