@@ -468,13 +468,19 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if (!P.out_tokens || !P.in_tokens) return bail(fail(&st->err, LF_ENOMEM, "token buffer allocation failed"));
 
   // ---- LDS layout: [h | part] (also attention / sampler scratch), red, ctl, rings
-  int rows_max = 0;
+  int rows_max = 0, rows_k[5];
   {
     const int units[5] = {P.nqkv / 2, d, F / 2, d / 2, hidden ? 0 : V / 2};
     const int upr[5] = {2, 1, 4, 2, 2};   // rows per partition unit (as in the kernel)
+    // with the K/V tile prefetch, up to a quarter of the grid runs attention
+    // only and the QKV rows go to the other workgroups
+    const char *kvpf = std::getenv("LF_KV_PF");
+    const bool kvpf_asked = kvpf && std::atoll(kvpf) > 0;
     for (int k = 0; k < 5; ++k) {
-      const int g = k == 1 ? G - lf::o_rows_skip_max(G, Hkv, P.qpg, P.attn_qsplit) : G;   // the output projection's workgroups
+      const int g = k == 1 ? G - lf::o_rows_skip_max(G, Hkv, P.qpg, P.attn_qsplit)   // the output projection's workgroups
+                           : (k == 0 && kvpf_asked ? G - G / 4 : G);
       const int r = upr[k] * ((units[k] + g - 1) / g);
+      rows_k[k] = r;
       rows_max = r > rows_max ? r : rows_max;
     }
   }
@@ -491,7 +497,13 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   // an RMSNorm input is written as fp16 elements in whole rounds of words
   const size_t d_elems = round_up((size_t)d, lf::kStageRound);
   if (d_elems * 2 > h_b) h_b = align_up(d_elems * 2, 16);
-  const size_t part_b = align_up((size_t)rows_max * 8 * 4, 16);   // one phase kind's partial row sums
+  // partial row sums [row][8] per phase kind, each kind's area sized for its own rows
+  size_t part_floats = 0;
+  for (int k = 0; k < 5; ++k) {
+    P.psum_off[k] = (int)part_floats;
+    part_floats += align_up((size_t)rows_k[k] * 8, 4);
+  }
+  const size_t part_b = align_up(part_floats * 4, 16);
   // attention scratch: queries, current K/V row, per-wave (m, l) and per-wave o
   const size_t attn_b = (size_t)lf::attn_lds(P.qpg, dh).bytes;
   // the nucleus draw's scratch overlays the staged input and the attention area
@@ -506,9 +518,9 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_xown = P.lds_ctl + lf::kCtlBytes;
   P.lds_xres = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 16);
   P.lds_part = (int)align_up((size_t)P.lds_xres + (size_t)rows_max * 4, 256);   // [kind][rows][8]
-  P.lds_trace = (int)align_up((size_t)P.lds_part + 5 * part_b, 256);
+  P.lds_trace = (int)align_up((size_t)P.lds_part + part_b, 256);
   size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
-  P.part_rows = rows_max;
+  P.psum_total = (int)part_floats;
   P.hmax = hmax;
   int lds_limit = 0;
   (void)hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, st->device);
@@ -535,11 +547,10 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   // The LDS left over can hold the first pieces of each stream wave's share of
   // one projection, loaded while attention runs.  By default that is the output
   // projection, where a wave's share (at the largest weight) is more than one
-  // ring round and fits whole: the phase then needs no round after its input
-  // arrives, and the ring's refill after attention starts on gate/up.  Where
-  // the share fits the ring (one round) or not the LDS, it is off: measured,
-  // 4 pieces on the 2.2B decode cost 2.8%, 2 (all that fit) on the 8B model
-  // gained nothing.  LF_GU_PF (pieces per wave) with LF_PF_KIND (2 gate/up, the
+  // ring round and the pieces that fit take a whole round off the phase (all of
+  // it fitting, the ring's refill after attention starts on gate/up).  Where
+  // the share fits the ring (one round) it is off: measured, 4 pieces on the
+  // 2.2B decode cost 2.8%.  LF_GU_PF (pieces per wave) with LF_PF_KIND (2 gate/up, the
   // default then; 1 output projection) overrides the rule.  A gate/up
   // prefetch costs more than it saves (its burst delays the output
   // projection's input).
@@ -566,8 +577,12 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
       const long long cap = lf::kRingSlots * (r + (r >= 8 ? 1 : 0));
       long long share = (o_pieces * wmax + wsum - 1) / wsum;
       if (share > cap) share = cap;
+      // on where it takes a whole round off the phase (ring rounds left after
+      // the pieces that fit)
+      const long long rounds = (share + lf::kRingSlots - 1) / lf::kRingSlots;
+      const long long left = share > fit ? share - fit : 0;
       P.pf_kind = 1;
-      if (eq > lf::kRingSlots && share <= fit) want = fit;
+      if (eq > lf::kRingSlots && (left + lf::kRingSlots - 1) / lf::kRingSlots < rounds) want = fit;
     }
     if (want < 0) want = 0;
     P.pf_n = (int)(want < fit ? want : fit);

@@ -163,7 +163,8 @@ struct Params {
   int plain_launch;        // 1: ordinary launch instead of a cooperative one
   // LDS layout (byte offsets into dynamic shared memory)
   int lds_h, lds_attn, lds_part, lds_red, lds_ctl, lds_xown, lds_xres, lds_trace, lds_pf, lds_kvpf, lds_bytes;
-  int part_rows, hmax;
+  int psum_off[5];                     // LDS partial row sums: each phase kind's first float
+  int psum_total, hmax;                // floats of all kinds' partial row sums
 };
 
 hipError_t launch_monokernel(const Params &p, bool prefill, hipStream_t stream);

@@ -667,7 +667,7 @@ __device__ __forceinline__ const unsigned char *phase_base(KP &P, const Geo &g, 
 }
 
 // A phase kind's partial row sums in LDS: [rows][8], slot 7 unused.
-__device__ __forceinline__ float *kind_part(float *part, int kind, int rows) { return part + kind * rows * 8; }
+__device__ __forceinline__ float *kind_part(float *part, int off) { return part + off; }
 
 // A phase kind's row block, read from LDS into wave-uniform (scalar) registers.
 __device__ __forceinline__ Geo uniform_geo(const Ctl *ctl, int kind) {
@@ -1137,7 +1137,7 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
   const int nr = (n + kRing - 1) / kRing;
   float acc = 0.0f;
   if (kind == st.P->pf_kind && st.P->pf_n > 0)
-    acc = pf_consume(*st.P, ctl, st.cw, h, kind_part(part, kind, fresh(*st.P).part_rows), ge, nr > 0);
+    acc = pf_consume(*st.P, ctl, st.cw, h, kind_part(part, fresh(*st.P).psum_off[kind]), ge, nr > 0);
   if (nr > 0) {
     // The ring holds this phase's first round.  If the phase has more pieces
     // than one round, the streamer still points into this phase: its cursor
@@ -1148,7 +1148,7 @@ __device__ __forceinline__ bool stream_phase(Streamer &st, int q, int kind, Ctl 
     ra.kpc = (unsigned)sl.kp;
     ra.ppm1 = (unsigned)(ppr - 1);
     ra.hb = lds_addr(h);
-    ra.pa = lds_addr(kind_part(part, kind, fresh(*st.P).part_rows) + sl.row * 8 + st.cw);
+    ra.pa = lds_addr(kind_part(part, fresh(*st.P).psum_off[kind]) + sl.row * 8 + st.cw);
     const bool more = n > kRing;
     ra.ikp = more ? (unsigned)st.kp : 0u;
     ra.ileft = more ? (unsigned)st.left : 0u;
@@ -2733,7 +2733,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
     for (int w = 0; w < kWaves; ++w) ctl->done[w] = 0;
     ctl->status = 0;
   }
-  for (int i = tid_x(); i < K_COUNT * P.part_rows * 8; i += kThreads) part[i] = 0.0f;
+  for (int i = tid_x(); i < P.psum_total; i += kThreads) part[i] = 0.0f;
   __syncthreads();
 
   Sync sy{&P, ctl, 0ull, 0ull, {0ull, 0ull, 0ull, 0ull, 0ull}, -1, (P.flags & 4u) != 0};
@@ -2899,7 +2899,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
             sn0 = Pl.rope[((size_t)pos * half + k) * 2 + 1];
           }
         }
-        const float *pk = kind_part(part, K_QKV, Pl.part_rows);
+        const float *pk = kind_part(part, Pl.psum_off[K_QKV]);
         if (!wait_streams(ctl, q0)) return;
         tq = lap(sy, ST_STREAMS, tq);
         trace(Pl, t, 5 * l + 0, 1);
@@ -2963,7 +2963,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         trace(Pl, t, 5 * l + 2, 0);
         // Before the wait (none of it depends on the stream waves): the output
         // words and the residual of this lane's first row.
-        const float *pk = kind_part(part, K_O, Pl.part_rows);
+        const float *pk = kind_part(part, Pl.psum_off[K_O]);
         u64 *xm = Pl.xmid_t + (size_t)gen * d;
         const int hio = Pl.hidden_io;
         auto residual = [&](int i) __attribute__((always_inline)) {
@@ -3009,7 +3009,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         }
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 3, 0);
-        const float *pk = kind_part(part, K_GU, Pl.part_rows);
+        const float *pk = kind_part(part, Pl.psum_off[K_GU]);
         gu64 *ad = (gu64 *)(Pl.a_t + (size_t)gen * (Pl.F / 2));
         asm volatile("" : "+s"(ad));   // computed now, not after the wait
         if (!wait_streams(ctl, q0 + 2)) return;
@@ -3043,7 +3043,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         tk = lap(sy, ST_STAGE, tk);
         trace(Pl, t, 5 * l + 4, 0);
         // before the wait: output words, this lane's first residual
-        const float *pk = kind_part(part, K_D, Pl.part_rows);
+        const float *pk = kind_part(part, Pl.psum_off[K_D]);
         u64 *xo = Pl.xout_t + (size_t)gen * d;
         const bool host_out = Pl.hidden_io && l == L - 1;
         const float xo0 = lane < ge.nrows ? xres[lane] : 0.0f;
@@ -3080,7 +3080,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(104))
         inv = coop_inv_rms(ctl, d, P.eps);
       }
       trace(P, t, 5 * L, 0);
-      const float *pk = kind_part(part, K_LM, P.part_rows);
+      const float *pk = kind_part(part, P.psum_off[K_LM]);
       if (!wait_streams(ctl, qlm)) return;
       trace(P, t, 5 * L, 1);
       float best = -INFINITY;
