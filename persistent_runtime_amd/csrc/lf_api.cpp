@@ -517,7 +517,7 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   P.lds_ctl = P.lds_red + 256;
   P.lds_xown = P.lds_ctl + lf::kCtlBytes;
   P.lds_xres = (int)align_up((size_t)P.lds_xown + (size_t)rows_max * 4, 16);
-  P.lds_part = (int)align_up((size_t)P.lds_xres + (size_t)rows_max * 4, 256);   // [kind][rows][8]
+  P.lds_part = (int)align_up((size_t)P.lds_xres + (size_t)rows_max * 4, 256);   // per kind: [rows][8]
   P.lds_trace = (int)align_up((size_t)P.lds_part + part_b, 256);
   size_t lds_end = align_up((size_t)P.lds_trace + (lf::kTrace ? (size_t)lf::kTraceSlots * (5 * c.n_layers + 2) * 8 : 0), 256);
   P.psum_total = (int)part_floats;
@@ -528,10 +528,10 @@ int lf_model_create(const lf_config *config, const lf_weights *w, void *stream, 
   if ((long long)lds_end > lds_limit)
     return bail(fail(&st->err, LF_EUNSUPPORTED, "shape needs more LDS than a workgroup can hold"));
   // The LDS left over can hold the first K/V tile of up to seven stream waves
-  // of an attention unit (LF_KV_PF: how many), then whatever gate/up prefetch
-  // is asked for.  Both are off by default: measured end to end, the attention
-  // that ends ~0.5 us sooner does not move the layer's end (the next exchange
-  // absorbs it) while the other workgroups stream more QKV rows.
+  // of an attention unit (LF_KV_PF: how many), then the projection prefetch
+  // below.  The tile prefetch is off by default: measured end to end, the
+  // attention that ends ~0.5 us sooner does not move the layer's end (the next
+  // exchange absorbs it) while the other workgroups stream more QKV rows.
   {
     const int nvh = (dh + 63) / 64;
     P.kv_pf_tile = (dh / 8 + 8 * nvh) * 1024;
