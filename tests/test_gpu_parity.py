@@ -726,7 +726,9 @@ def test_laneformer_shape_sliding_window_long_context(lf, orc):
     """The LaneFormer-2B-shaped decoder (15 layers, 32/16 heads of dim 96, window
     1024 in 10 layers) with its cache prefilled to 2048: GPU logits within
     tolerance of the oracle's and the greedy token equal where the margin allows
-    (with the output projection prefetched into LDS, as by default at this shape)."""
+    (with the output projection prefetched into LDS, as by default at this
+    shape); then one 8-token generate launch from 2048, as the benchmark times
+    it, replayed through the oracle."""
     import torch
     cfg = synth.CONFIGS["laneformer_15l_swa"]
     w = synth.model_weights(cfg)
@@ -743,7 +745,10 @@ def test_laneformer_shape_sliding_window_long_context(lf, orc):
     m = orc.Model(cfg, w)
     m.kv_fill(k, v, 0)
     del k, v
-    tok = int(synth.prompt(dict(cfg, prompt_len=1), 1)[0])
+    # snapshot the oracle's cache so that the generate check restarts from pos P
+    kc, vc = m.kcache.copy(), m.vcache.copy()
+    tok0 = int(synth.prompt(dict(cfg, prompt_len=1), 1)[0])
+    tok = tok0
     for i in range(3):
         pos = P + i
         nxt = eng.decode_step(tok, pos)
@@ -754,6 +759,27 @@ def test_laneformer_shape_sliding_window_long_context(lf, orc):
         if margin(ref) >= 1e-2:
             assert nxt == int(np.argmax(ref)), pos
         tok = int(np.argmax(ref))
+    # the benchmark's launch: one generate from position P.  The oracle replays
+    # the kernel's tokens: each must be an argmax of the oracle's logits within
+    # twice the logit tolerance (the unique argmax where the top-2 margin is at
+    # least 1e-2), and the launch's last logits must match the oracle's.
+    n = 8
+    eng.set_position(tok0, P)
+    got = eng.generate(n)
+    last = eng.logits().cpu().numpy()
+    m.kcache[...] = kc
+    m.vcache[...] = vc
+    del kc, vc
+    tok = tok0
+    for i in range(n):
+        ref = m.decode_step(tok, P + i)
+        tol = 1e-2 * np.abs(ref).max() + 1e-3
+        assert ref[int(got[i])] >= ref.max() - 2 * tol, i
+        if margin(ref) >= 1e-2:
+            assert int(got[i]) == int(np.argmax(ref)), i
+        tok = int(got[i])
+    ok, err = close(last, ref)
+    assert ok, err
 
 
 def test_prefill_one_launch_matches_oracle(lf, orc, tiny):
