@@ -42,6 +42,29 @@ def margin(logits):
     return top[1] - top[0]
 
 
+def replay_generate(eng, m, tok0, pos0, n, kc, vc):
+    """One generate launch of n steps from pos0, replayed through the oracle
+    (restarted from the cache snapshot kc / vc): each kernel token must be an
+    argmax of the oracle's logits within twice the logit tolerance (the unique
+    argmax where the top-2 margin is at least 1e-2), and the launch's last
+    logits must match the oracle's."""
+    eng.set_position(tok0, pos0)
+    got = eng.generate(n)
+    last = eng.logits().cpu().numpy()
+    m.kcache[...] = kc
+    m.vcache[...] = vc
+    tok = tok0
+    for i in range(n):
+        ref = m.decode_step(tok, pos0 + i)
+        tol = 1e-2 * np.abs(ref).max() + 1e-3
+        assert ref[int(got[i])] >= ref.max() - 2 * tol, i
+        if margin(ref) >= 1e-2:
+            assert int(got[i]) == int(np.argmax(ref)), i
+        tok = int(got[i])
+    ok, err = close(last, ref)
+    assert ok, err
+
+
 def teacher_forced(lf, orc, cfg, weights, tokens, pos0=0, engine=None, model=None):
     """Feed the same tokens to both sides; check logits and greedy choice each step."""
     eng = engine or lf.Engine(cfg, lf.upload_weights(weights))
@@ -530,8 +553,7 @@ def test_dec2b_timed_positions_prefill_and_generate(lf, orc, dec2b):
     """The benchmark's own path at the ~2.2B shape: the 127-token prompt in one
     teacher-forced launch, then steps at the timed positions 127.. against the
     oracle (logits within tolerance every step), then one generate launch from
-    position 127 against the oracle's greedy continuation up to the first step
-    whose top-2 margin is below 1e-2."""
+    position 127 replayed through the oracle."""
     cfg, w = dec2b
     orc.set_threads(min(16, os.cpu_count() or 1))
     prompt = synth.prompt(cfg, cfg["prompt_len"])
@@ -553,16 +575,7 @@ def test_dec2b_timed_positions_prefill_and_generate(lf, orc, dec2b):
         if margin(ref) >= 1e-2:
             assert nxt == orc.argmax(ref), pos
         tok = orc.argmax(ref)
-    n = 8
-    eng.set_position(int(prompt[P]), P)
-    got = eng.generate(n)
-    m.kcache[...] = kc
-    m.vcache[...] = vc
-    ref, hist = m.generate(int(prompt[P]), P, n, keep_logits=True)
-    for i in range(n):
-        if margin(hist[i]) < 1e-2:
-            break
-        assert got[i] == ref[i], i
+    replay_generate(eng, m, int(prompt[P]), P, 8, kc, vc)
 
 
 @pytest.fixture(scope="module")
@@ -578,8 +591,9 @@ def test_dec8b_gqa_full_shape(lf, orc, dec8b):
     teacher-forced steps from position 0; then the cache is filled with 255
     synthetic rows and the steps at positions 255.. attend over them (4 tiles per
     KV head: one attention unit per query head); then one generate launch
-    against the oracle's greedy continuation.  Logits within tolerance at every
-    step, greedy tokens equal where the oracle's top-2 margin is at least 1e-2."""
+    replayed through the oracle.  Logits within tolerance at every step, greedy
+    tokens equal where the oracle's top-2 margin is at least 1e-2.  The output
+    projection is prefetched into LDS in part (11 of 24 pieces a wave)."""
     import torch
     cfg, w = dec8b
     orc.set_threads(min(16, os.cpu_count() or 1))
@@ -587,6 +601,7 @@ def test_dec8b_gqa_full_shape(lf, orc, dec8b):
     eng = lf.Engine(cfg, dw)
     del dw
     torch.cuda.empty_cache()
+    assert eng.query(lf.LF_Q_PF_KIND) == 1 and eng.query(lf.LF_Q_GU_PF) >= 8
     m = orc.Model(cfg, w)
     prompt = synth.prompt(cfg, 3)
     teacher_forced(lf, orc, cfg, w, prompt, engine=eng, model=m)
@@ -609,16 +624,7 @@ def test_dec8b_gqa_full_shape(lf, orc, dec8b):
         if margin(ref) >= 1e-2:
             assert nxt == orc.argmax(ref), pos
         tok = orc.argmax(ref)
-    n = 6
-    eng.set_position(tok0, P)
-    got = eng.generate(n)
-    m.kcache[...] = kc
-    m.vcache[...] = vc
-    ref, hist = m.generate(tok0, P, n, keep_logits=True)
-    for i in range(n):
-        if margin(hist[i]) < 1e-2:
-            break
-        assert got[i] == ref[i], i
+    replay_generate(eng, m, tok0, P, 6, kc, vc)
 
 
 @pytest.mark.timeout(600)
@@ -759,27 +765,8 @@ def test_laneformer_shape_sliding_window_long_context(lf, orc):
         if margin(ref) >= 1e-2:
             assert nxt == int(np.argmax(ref)), pos
         tok = int(np.argmax(ref))
-    # the benchmark's launch: one generate from position P.  The oracle replays
-    # the kernel's tokens: each must be an argmax of the oracle's logits within
-    # twice the logit tolerance (the unique argmax where the top-2 margin is at
-    # least 1e-2), and the launch's last logits must match the oracle's.
-    n = 8
-    eng.set_position(tok0, P)
-    got = eng.generate(n)
-    last = eng.logits().cpu().numpy()
-    m.kcache[...] = kc
-    m.vcache[...] = vc
-    del kc, vc
-    tok = tok0
-    for i in range(n):
-        ref = m.decode_step(tok, P + i)
-        tol = 1e-2 * np.abs(ref).max() + 1e-3
-        assert ref[int(got[i])] >= ref.max() - 2 * tol, i
-        if margin(ref) >= 1e-2:
-            assert int(got[i]) == int(np.argmax(ref)), i
-        tok = int(got[i])
-    ok, err = close(last, ref)
-    assert ok, err
+    # the benchmark's launch: one generate from position P
+    replay_generate(eng, m, tok0, P, 8, kc, vc)
 
 
 def test_prefill_one_launch_matches_oracle(lf, orc, tiny):
